@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the skinny BF16 decode projection on one MI355X.
+
+One step is one pass of the whole hot path over the packed Q/K/V/G/F_A/beta
+projection weight [6288, 7168]: six calls out[M, N] = x[M, K] @ W^T with
+M = 1, 2, 4, 8, 16, 32 (BF16 out), each call on the next of 4 distinct weight
+copies (360 MB, past the 256 MiB Infinity Cache), each resolving its kernel
+through the plan's per-M table.  Steps are replayed from captured hipGraphs;
+inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line on stdout:
+  value = weight-stream GB/s over the timed steps (6 * 2NK bytes per step / time)
+  roofline = the projection launches: algorithmic bytes (W + x + out) per
+             launch / average launch time (HIP events on the replay stream),
+             against the 8 TB/s HBM peak
+  cpu_baseline = the fp64 CPU oracle on one step of the same workload
+Diagnostics (per-M times, the plain read ceiling over the same rotated
+weights, the empty-launch floor, parity of the last outputs) go to the JSON's
+extra fields and to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+WORKLOAD = 3
+M_SWEEP = (1, 2, 4, 8, 16, 32)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_bf16(bits):
+    import torch
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).view(torch.bfloat16).cuda()
+
+
+def bf16_values(t):
+    import torch
+    import skinny_inputs as si
+    return si.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+def capture(fn, stream):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+    return g
+
+
+def time_graph(g, stream, reps):
+    """Seconds for `reps` replays of g on `stream` (replays go to the current
+    stream, so the events and the replays share `stream`)."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3
+
+
+class Setup:
+    """Weights, activations, outputs and plans of one workload."""
+
+    def __init__(self, cid, copies=None, out_dtype="bf16"):
+        import torch
+        import skinny_inputs as si
+        import skinny_bf16_decode_amd as sk
+        self.wl = si.WORKLOADS[cid]
+        self.cid = cid
+        self.copies = copies or self.wl.copies
+        self.w_bits = [si.weight(cid, c) for c in range(self.copies)]
+        self.x_bits = si.activations(cid)
+        if self.x_bits.shape[0] < 64:
+            self.x_bits = np.ascontiguousarray(np.resize(self.x_bits, (64, self.wl.k)))
+        self.w = [dev_bf16(b) for b in self.w_bits]
+        self.x = dev_bf16(self.x_bits)
+        self.out_dtype = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        self.out = torch.zeros((self.copies, 64, self.wl.n), dtype=self.out_dtype, device="cuda")
+        t0 = time.time()
+        self.plans = [sk.Prepared(w, self.out_dtype) for w in self.w]
+        self.prepare_s = time.time() - t0
+
+    def run(self, call_index, m):
+        c = call_index % self.copies
+        self.plans[c].run(self.x[:m], self.out[c, :m])
+        return c
+
+    def per_m(self, stream, m, reps=10):
+        """µs per call at token count m, from a graph of 16 * copies calls."""
+        calls = 16 * self.copies
+        g = capture(lambda: [self.run(i, m) for i in range(calls)], stream)
+        time_graph(g, stream, 1)
+        dt = time_graph(g, stream, reps)
+        return 1e6 * dt / (reps * calls)
+
+
+def algorithmic_bytes(n, k, m, out_bytes=2):
+    return 2 * n * k + 2 * m * k + out_bytes * m * n
+
+
+def read_ceiling(setup, stream, reps=10):
+    import torch
+    import skinny_bf16_decode_amd as sk
+    sink = torch.zeros(sk.probe_read_blocks(), dtype=torch.float32, device="cuda")
+    nbytes = setup.wl.weight_bytes
+    calls = 16 * setup.copies
+
+    def body():
+        for i in range(calls):
+            sk.probe_read(setup.w[i % setup.copies].data_ptr(), nbytes, sink.data_ptr())
+    g = capture(body, stream)
+    time_graph(g, stream, 1)
+    dt = time_graph(g, stream, reps)
+    us = 1e6 * dt / (reps * calls)
+    return us, nbytes / us / 1e3
+
+
+def empty_floor(stream, reps=20):
+    import skinny_bf16_decode_amd as sk
+    g = capture(lambda: [sk.probe_empty() for _ in range(64)], stream)
+    time_graph(g, stream, 1)
+    dt = time_graph(g, stream, reps)
+    return 1e6 * dt / (reps * 64)
+
+
+def cpu_baseline(setup):
+    """The oracle on one step of the workload (the six token counts on one
+    weight copy), repeated while under ~10 s; GB/s of weight processed."""
+    import oracle
+    x = setup.x_bits
+    w = setup.w_bits[0]
+    reps, t_total = 0, 0.0
+    while reps < 3 and t_total < 10.0:
+        t0 = time.perf_counter()
+        for m in M_SWEEP:
+            oracle.gemm(x[:m], w)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    step_s = t_total / reps
+    gbps = len(M_SWEEP) * setup.wl.weight_bytes / step_s / 1e9
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"one full step ({len(M_SWEEP)} calls, M={list(M_SWEEP)}, one "
+                      f"[{setup.wl.n},{setup.wl.k}] weight copy), {reps} rep(s), "
+                      f"{step_s:.2f} s per step"}
+
+
+def parity_of_last(setup, last_copy, m, samples=4096):
+    import oracle
+    rng = np.random.default_rng(2024)
+    mi = rng.integers(0, m, size=samples)
+    ni = rng.integers(0, setup.wl.n, size=samples)
+    o, s = oracle.gemm_sampled(setup.x_bits, setup.w_bits[last_copy], mi, ni)
+    got = bf16_values(setup.out[last_copy])[mi, ni]
+    rep = oracle.check(got, o, s, "bf16")
+    return rep
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--extra", action="store_true", help="also time the other workloads (stderr)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the projection would shard W by rows, one shard per GPU, with no exchange "
+              "inside the GEMM); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import skinny_bf16_decode_amd as sk
+    sk.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count} "
+        f"torch={torch.__version__} hip={torch.version.hip}")
+
+    setup = Setup(WORKLOAD)
+    wl = setup.wl
+    log(f"workload {wl.name}: prepare {setup.prepare_s:.2f}s")
+    for m in M_SWEEP:
+        log(f"  M={m:2d}: {setup.plans[0].describe(m)}")
+    stream = torch.cuda.Stream()
+
+    # one graph per starting copy offset (6 calls per step, 4 copies)
+    calls = len(M_SWEEP)
+    offsets = sorted({(calls * s) % setup.copies for s in range(setup.copies)})
+    graphs = {}
+    for off in offsets:
+        graphs[off] = capture(lambda off=off: [setup.run(off + j, m) for j, m in enumerate(M_SWEEP)],
+                              stream)
+
+    def step_graph(i):
+        return graphs[(calls * i) % setup.copies]
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):        # replays, and the events, on `stream`
+        for i in range(args.warmup):
+            step_graph(i).replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step_graph(args.warmup + i).replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed = e0.elapsed_time(e1) / 1e3
+    ms_per_step = 1e3 * elapsed / args.steps
+    weight_bytes_step = calls * wl.weight_bytes
+    value = weight_bytes_step * args.steps / elapsed / 1e9
+    launches = calls * args.steps
+    us_per_launch = 1e6 * elapsed / launches
+    algo_per_launch = sum(algorithmic_bytes(wl.n, wl.k, m) for m in M_SWEEP) / calls
+    achieved = algo_per_launch / us_per_launch / 1e3
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {us_per_launch:.2f} us/call, "
+        f"{value:.1f} GB/s weight stream ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s); host wall {wall:.3f}s")
+
+    # the last call of the last step
+    last_copy = (calls * (args.warmup + args.steps) - 1) % setup.copies
+    rep = parity_of_last(setup, last_copy, M_SWEEP[-1])
+    log(f"parity of the last call (M={M_SWEEP[-1]}, copy {last_copy}): {rep}")
+    if not rep.ok:
+        print(f"parity failure: {rep}", file=sys.stderr)
+        sys.exit(3)
+
+    per_m = {}
+    for m in M_SWEEP:
+        us = setup.per_m(stream, m)
+        gb = wl.weight_bytes / us / 1e3
+        per_m[str(m)] = {"us_per_call": round(us, 3), "weight_gbps": round(gb, 1),
+                         "pct_peak": round(100 * gb / PEAK_GBPS, 1)}
+        log(f"  M={m:2d}: {us:7.2f} us/call  {gb:7.1f} GB/s  {100 * gb / PEAK_GBPS:5.1f}%")
+    ceil_us, ceil_gb = read_ceiling(setup, stream)
+    floor_us = empty_floor(stream)
+    log(f"read ceiling (plain nt stream of the same rotated weights): {ceil_us:.2f} us, "
+        f"{ceil_gb:.1f} GB/s; empty-launch floor {floor_us:.2f} us")
+
+    if args.extra:
+        extra_workloads(stream)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(setup)
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": "µs/call and weight-stream HBM GB/s (% of peak), 6288x7168 at M=1..32",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: out[M,N] = x[M,K] @ W[N,K]^T, N={wl.n}, K={wl.k}, "
+                               f"one step = M in {list(M_SWEEP)}, BF16 in/out, fp32 accumulate, "
+                               f"{setup.copies} rotated weight copies, hipGraph replay",
+                   "N": wl.n, "K": wl.k, "m_values": list(M_SWEEP), "weight_copies": setup.copies},
+        "us_per_call": round(us_per_launch, 3),
+        "pct_of_peak": round(100 * value / PEAK_GBPS, 1),
+        "per_m": per_m,
+        "read_ceiling_gbps": round(ceil_gb, 1),
+        "empty_launch_us": round(floor_us, 3),
+        "parity_last_call": "ok",
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "skinny projection launches (k_dot2 / k_mfma instances of the step)",
+                     "bytes_per_launch": round(algo_per_launch), "us_per_launch": round(us_per_launch, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def extra_workloads(stream):
+    import skinny_inputs as si
+    for cid, od in ((2, "bf16"), (4, "f32"), (4, "bf16"), (5, "bf16"), (1, "f32")):
+        s = Setup(cid, out_dtype=od)
+        for m in s.wl.m_values:
+            us = s.per_m(stream, m)
+            gb = s.wl.weight_bytes / us / 1e3
+            log(f"[{s.wl.name} {od}] M={m:2d}: {us:7.2f} us/call {gb:7.1f} GB/s "
+                f"{100 * gb / PEAK_GBPS:5.1f}% | {s.plans[0].describe(m)}")
+        del s
+        import torch
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

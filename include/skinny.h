@@ -1,0 +1,196 @@
+/*
+ * skinny.h -- C ABI of the MI355X (gfx950) skinny BF16 decode projection.
+ *
+ *   out[M, N] = x[M, K] @ W[N, K]^T,   M = 1..64 tokens, BF16 in,
+ *   fp32 accumulation, BF16 or fp32 out.
+ *
+ * The operation is the one the pages define for their decode GEMMs:
+ * "out[M, N] = x[M, K] @ weight[N, K]^T" (class PreparedWarpSplitK, page
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.warp_splitk")
+ * and "x @ weight.T" (class Projection, page
+ * "vllm.models.glm5next.nvidia.specialized_decode.gemm").  No bias and no
+ * residual is added; out is overwritten.
+ *
+ * Usage follows the pages' prepare-once / run-per-forward split: a prepared
+ * object owns the weight and a per-token-count kernel choice that is fixed
+ * before graph capture, and each forward resolves its kernel with a single
+ * lookup ("vllm.models.kimi_k3.nvidia.low_latency_gemm", module docstring:
+ * the {M: call} plan resolved at install time).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers (W, x, out) are DEVICE pointers on the device that is
+ *    current when the plan is prepared.  The library never dereferences them
+ *    on the host.
+ *  - Matrices are packed row-major: W is [N][K], x is [M][K], out is [M][N],
+ *    each with row pitch equal to its column count.  Pitched views are not
+ *    accepted.
+ *  - Every call returns a status; none aborts or throws.  After a failure,
+ *    skinny_last_error() returns a thread-local text describing it.
+ *  - A stream is passed as a hipStream_t cast to void*; NULL is the null
+ *    stream.
+ */
+#ifndef SKINNY_H
+#define SKINNY_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct skinny_plan skinny_plan; /* opaque; one per prepared weight */
+
+typedef enum {
+    SKINNY_OUT_BF16 = 0, /* out is BF16, rounded to nearest even once */
+    SKINNY_OUT_F32 = 1   /* out is fp32 (the accumulator, unrounded) */
+} skinny_out_dtype;
+
+typedef enum {
+    SKINNY_OK = 0,
+    SKINNY_ERR_INVALID_ARG = 1,   /* null pointer, N <= 0, K <= 0, bad enum/tactic */
+    SKINNY_ERR_SHAPE = 2,         /* K % 8 != 0, or N * K too large */
+    SKINNY_ERR_ALIGN = 3,         /* W or x not 16-byte aligned, out not element aligned */
+    SKINNY_ERR_UNSUPPORTED_M = 4, /* M outside 1..64: caller falls back */
+    SKINNY_ERR_DEVICE = 5,        /* no device, or the current device is not gfx950 */
+    SKINNY_ERR_NOMEM = 6,         /* device or host allocation failed */
+    SKINNY_ERR_HIP = 7            /* a HIP call failed (e.g. prepare during capture) */
+} skinny_status;
+
+/* Largest token count a plan serves. */
+#define SKINNY_MAX_M 64
+
+/* Kernel families. */
+typedef enum {
+    SKINNY_PATH_DOT2 = 0, /* v_dot2_f32_bf16, token tiles 1/2/4/8 */
+    SKINNY_PATH_MFMA = 1  /* v_mfma_f32_16x16x32_bf16, token tiles 16/32/64 */
+} skinny_path;
+
+/*
+ * One tactic: a kernel instance plus its launch shape.  The fields play the
+ * roles of the pages' tactic fields -- the token tile (the padded token
+ * count a tactic serves; "smallest tile >= m" in Projection.__init__), the
+ * output rows per block ("outputs" of SkinnyGemmConfig; the 16- or 32-row
+ * output tiles of the warp split-K page), loads in flight ("unroll"), and the
+ * cross-block K split ("split K" of the split-K projection page's
+ * (M tile, N tile, split K, stages) policies).
+ */
+typedef struct {
+    int path;   /* skinny_path */
+    int mt;     /* token tile: DOT2 1,2,4,8; MFMA 16,32,64 */
+    int rows;   /* weight rows per workgroup: DOT2 1..16 (mt*rows <= 64); MFMA 16,32,64 */
+    int waves;  /* wavefronts per workgroup, splitting K inside it: 1,2,4,8 */
+    int unroll; /* 16-byte weight loads in flight per lane per row: 1,2,4 */
+    int split;  /* workgroups splitting K per row tile (1 = none), 1..16 */
+} skinny_tactic;
+
+/*
+ * skinny_prepare -- build a plan for weight W [N][K] (BF16 bits, device).
+ *
+ * Validates the arguments, then looks up the process-wide tactic table for
+ * (device, N, K, out_dtype); on a miss it times every legal tactic on the
+ * device with cache-cold weight copies and keeps, for each M in 1..64, the
+ * fastest tactic whose token tile is >= M.  Every tactic the table uses is
+ * launched once (warm-up) so that nothing loads lazily under graph capture.
+ * The split-K workspace and arrival counters are allocated here.
+ *
+ * Synchronous.  Must not be called while the device is capturing a graph.
+ * W is NOT copied: the plan keeps the pointer, W must stay allocated until
+ * skinny_destroy, and its values may change between runs.  W is read-only.
+ * Requires: N >= 1, K >= 8, K % 8 == 0, W 16-byte aligned, N * K < 2^31.
+ * Thread-safe.
+ */
+skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype out_dtype,
+                             skinny_plan **plan);
+
+/*
+ * skinny_prepare_tactics -- like skinny_prepare, but with the table given:
+ * table[M - 1] is the tactic used for M tokens (M = 1..64) and must have a
+ * token tile >= M.  No timing is done; tactics are validated and warmed.
+ * Used to force a tactic (tests) or to load a table tuned earlier.
+ */
+skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dtype out_dtype,
+                                     const skinny_tactic *table, skinny_plan **plan);
+
+/*
+ * skinny_run -- out[0:M, :] = x[0:M, :] @ W^T on `stream`, asynchronously.
+ *
+ * One table lookup and one kernel launch; no allocation, synchronisation,
+ * copy or host read of device memory, so it may be captured in a hipGraph.
+ * x: [M][K] BF16 bits, 16-byte aligned.  out: [M][N], BF16 (2-byte aligned)
+ * or fp32 (4-byte aligned) as prepared.  Rows of out at and beyond M, and all
+ * other memory, are not touched; out is written, never read.
+ * A plan holds one split-K workspace: the same plan must not run on two
+ * streams concurrently.  Different plans may.
+ * Errors: SKINNY_ERR_UNSUPPORTED_M for M outside 1..64 (the caller falls back,
+ * as the pages' selectors return None), SKINNY_ERR_INVALID_ARG, SKINNY_ERR_ALIGN,
+ * SKINNY_ERR_HIP if the launch is rejected.
+ */
+skinny_status skinny_run(const skinny_plan *plan, const void *x, void *out, int M, void *stream);
+
+/* 1 if the plan serves M tokens (1 <= M <= 64), else 0 (Projection.supports). */
+int skinny_supports(const skinny_plan *plan, int M);
+
+/* The tactic the plan uses for M tokens. */
+skinny_status skinny_plan_tactic(const skinny_plan *plan, int M, skinny_tactic *out);
+
+/* Human-readable name of the plan's kernel for M tokens, NUL-terminated in buf. */
+skinny_status skinny_describe(const skinny_plan *plan, int M, char *buf, size_t len);
+
+/* Free the plan, its workspace and counters.  Synchronises the device.  NULL is a no-op. */
+void skinny_destroy(skinny_plan *plan);
+
+/* Static text for a status code. */
+const char *skinny_status_string(skinny_status s);
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char *skinny_last_error(void);
+
+/*
+ * skinny_tactic_check -- SKINNY_OK if the tactic is a legal kernel instance and
+ * launch shape for an [N][K] weight, else SKINNY_ERR_INVALID_ARG with the
+ * reason in skinny_last_error().  Host only; no device call.
+ */
+skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K);
+
+/*
+ * skinny_enumerate_tactics -- the candidate tactics the tuner times for an
+ * [N][K] weight.  Writes up to `cap` tactics to buf (buf may be NULL when cap
+ * is 0) and returns the total count, or -1 on bad arguments.  Host only.
+ */
+int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap);
+
+/*
+ * skinny_select_table -- the table rule.  Given `count` candidate tactics and
+ * their measured times in microseconds (times[i] for cand[i]; a negative time
+ * marks a candidate that could not run), fill table[M - 1] for M = 1..64 with
+ * the fastest candidate whose token tile is >= M.  Ties go to the smaller
+ * token tile, then the lower index.  Returns SKINNY_OK, or
+ * SKINNY_ERR_INVALID_ARG if some M has no usable candidate.  Host only.
+ */
+skinny_status skinny_select_table(const skinny_tactic *cand, const double *times_us,
+                                  int count, skinny_tactic *table);
+
+/*
+ * Measurement helpers (not part of the projection).  They put the projection's
+ * timings in context: the decode-step cost the pages care about is streaming
+ * the weight at HBM speed, so a bench compares against what a plain stream of
+ * the same bytes achieves, and against the floor of an empty launch.
+ *
+ * skinny_probe_read -- read `bytes` bytes at `buf` (device, 16-byte aligned,
+ * bytes % 16 == 0) with 16-byte nontemporal loads and write one fp32 partial
+ * sum per workgroup to `sink` (device, at least skinny_probe_read_blocks()
+ * floats), so the loads cannot be elided.  Asynchronous on `stream`.
+ */
+skinny_status skinny_probe_read(const void *buf, size_t bytes, float *sink, void *stream);
+
+/* Workgroups (and sink floats) skinny_probe_read launches. */
+int skinny_probe_read_blocks(void);
+
+/* skinny_probe_empty -- launch one empty 64-lane workgroup on `stream`. */
+skinny_status skinny_probe_empty(void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_H */

@@ -1,0 +1,256 @@
+"""Python binding of libskinny.so, the MI355X skinny BF16 decode projection.
+
+    out[M, N] = x[M, K] @ W[N, K]^T,   M = 1..64
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/skinny.h).  PyTorch supplies device memory
+and streams.  There is no fallback: if the library is missing or the device is
+not gfx950, calls raise.
+
+    plan = Prepared(W)                 # W: torch.bfloat16 [N, K] on cuda
+    plan.run(x, out)                   # x: bf16 [M, K]; out: bf16/f32 [M, N]
+
+Errors follow the pages' wrappers: bad arguments raise ValueError (as
+PreparedWarpSplitK / PreparedProjection do), HIP failures RuntimeError, and an
+unsupported token count raises UnsupportedTokens (the pages' selectors return
+None so the caller falls back).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libskinny.so")
+
+MAX_M = 64
+OUT_BF16 = 0
+OUT_F32 = 1
+PATH_DOT2 = 0
+PATH_MFMA = 1
+
+STATUS = {
+    0: "SKINNY_OK",
+    1: "SKINNY_ERR_INVALID_ARG",
+    2: "SKINNY_ERR_SHAPE",
+    3: "SKINNY_ERR_ALIGN",
+    4: "SKINNY_ERR_UNSUPPORTED_M",
+    5: "SKINNY_ERR_DEVICE",
+    6: "SKINNY_ERR_NOMEM",
+    7: "SKINNY_ERR_HIP",
+}
+
+
+class SkinnyError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class UnsupportedTokens(ValueError):
+    """M outside 1..64: the caller should fall back to another GEMM."""
+
+
+class Tactic(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("mt", ctypes.c_int), ("rows", ctypes.c_int),
+                ("waves", ctypes.c_int), ("unroll", ctypes.c_int), ("split", ctypes.c_int)]
+
+    def astuple(self):
+        return (self.path, self.mt, self.rows, self.waves, self.unroll, self.split)
+
+    def __repr__(self):
+        p = "mfma" if self.path == PATH_MFMA else "dot2"
+        return (f"Tactic({p}, mt={self.mt}, rows={self.rows}, waves={self.waves}, "
+                f"unroll={self.unroll}, split={self.split})")
+
+    def __eq__(self, other):
+        return isinstance(other, Tactic) and self.astuple() == other.astuple()
+
+    def __hash__(self):
+        return hash(self.astuple())
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libskinny.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m skinny_bf16_decode_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    planp = ctypes.c_void_p
+    tp = ctypes.POINTER(Tactic)
+    sig = {
+        "skinny_prepare": (i, [vp, i, i, i, ctypes.POINTER(planp)]),
+        "skinny_prepare_tactics": (i, [vp, i, i, i, tp, ctypes.POINTER(planp)]),
+        "skinny_run": (i, [planp, vp, vp, i, vp]),
+        "skinny_supports": (i, [planp, i]),
+        "skinny_plan_tactic": (i, [planp, i, tp]),
+        "skinny_describe": (i, [planp, i, ctypes.c_char_p, sz]),
+        "skinny_destroy": (None, [planp]),
+        "skinny_status_string": (ctypes.c_char_p, [i]),
+        "skinny_last_error": (ctypes.c_char_p, []),
+        "skinny_tactic_check": (i, [tp, i, i]),
+        "skinny_enumerate_tactics": (i, [i, i, tp, i]),
+        "skinny_select_table": (i, [tp, ctypes.POINTER(ctypes.c_double), i, tp]),
+        "skinny_probe_read": (i, [vp, sz, vp, vp]),
+        "skinny_probe_read_blocks": (i, []),
+        "skinny_probe_empty": (i, [vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().skinny_last_error().decode()
+
+
+def _raise(status: int):
+    if status == 0:
+        return
+    msg = last_error()
+    if status == 4:
+        raise UnsupportedTokens(msg)
+    if status in (1, 2, 3):
+        raise ValueError(f"{STATUS[status]}: {msg}")
+    raise SkinnyError(status, msg)
+
+
+def tactic_check(t: Tactic, n: int, k: int) -> None:
+    _raise(load_library().skinny_tactic_check(ctypes.byref(t), n, k))
+
+
+def enumerate_tactics(n: int, k: int) -> list:
+    lib = load_library()
+    count = lib.skinny_enumerate_tactics(n, k, None, 0)
+    if count < 0:
+        raise ValueError(f"bad shape N={n} K={k}")
+    buf = (Tactic * count)()
+    lib.skinny_enumerate_tactics(n, k, buf, count)
+    return [Tactic(*t.astuple()) for t in buf]
+
+
+def select_table(cands, times_us) -> list:
+    """The per-M table rule: fastest candidate whose token tile covers M."""
+    lib = load_library()
+    n = len(cands)
+    arr = (Tactic * max(n, 1))(*[Tactic(*c.astuple()) for c in cands])
+    tm = (ctypes.c_double * max(n, 1))(*times_us)
+    out = (Tactic * MAX_M)()
+    _raise(lib.skinny_select_table(arr, tm, n, out))
+    return [Tactic(*t.astuple()) for t in out]
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def probe_read(buf_ptr: int, nbytes: int, sink_ptr: int, stream=None) -> None:
+    """Measurement only: stream nbytes from buf with 16-byte nontemporal loads."""
+    _raise(load_library().skinny_probe_read(ctypes.c_void_p(buf_ptr), nbytes,
+                                            ctypes.c_void_p(sink_ptr), _stream_handle(stream)))
+
+
+def probe_read_blocks() -> int:
+    return load_library().skinny_probe_read_blocks()
+
+
+def probe_empty(stream=None) -> None:
+    """Measurement only: one empty launch."""
+    _raise(load_library().skinny_probe_empty(_stream_handle(stream)))
+
+
+class Prepared:
+    """A prepared weight: tactic table, split-K workspace, warmed kernels.
+
+    The plan keeps W's device pointer (not a copy); the tensor is held here so
+    it stays allocated.  ``table`` forces a per-M tactic list (64 entries)
+    instead of tuning on the device.
+    """
+
+    def __init__(self, weight, out_dtype=None, table=None):
+        import torch
+        lib = load_library()
+        if out_dtype is None:
+            out_dtype = torch.bfloat16
+        if weight.dim() != 2 or weight.dtype != torch.bfloat16 or not weight.is_cuda:
+            raise ValueError("weight must be a 2-D torch.bfloat16 tensor on a GPU")
+        if weight.stride() != (weight.shape[1], 1):
+            raise ValueError("weight must be packed row-major [N, K]")
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError(f"unsupported output dtype {out_dtype}")
+        self.weight = weight
+        self.n, self.k = weight.shape
+        self.out_dtype = out_dtype
+        od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+        self._plan = ctypes.c_void_p()
+        with torch.cuda.device(weight.device):
+            if table is None:
+                st = lib.skinny_prepare(weight.data_ptr(), self.n, self.k, od,
+                                        ctypes.byref(self._plan))
+            else:
+                if len(table) != MAX_M:
+                    raise ValueError("table needs one tactic per M = 1..64")
+                arr = (Tactic * MAX_M)(*[Tactic(*t.astuple()) for t in table])
+                st = lib.skinny_prepare_tactics(weight.data_ptr(), self.n, self.k, od, arr,
+                                                ctypes.byref(self._plan))
+        _raise(st)
+
+    def supports(self, tokens: int) -> bool:
+        return bool(load_library().skinny_supports(self._plan, tokens))
+
+    def tactic(self, tokens: int) -> Tactic:
+        t = Tactic()
+        _raise(load_library().skinny_plan_tactic(self._plan, tokens, ctypes.byref(t)))
+        return t
+
+    def describe(self, tokens: int) -> str:
+        buf = ctypes.create_string_buffer(256)
+        _raise(load_library().skinny_describe(self._plan, tokens, buf, 256))
+        return buf.value.decode()
+
+    def run(self, x, out, stream=None):
+        """out[:M] = x @ W^T with M = x.shape[0], on the current (or given) stream."""
+        import torch
+        if x.dim() != 2 or x.shape[1] != self.k or x.dtype != torch.bfloat16:
+            raise ValueError(f"x must be bf16 [M, {self.k}], got {tuple(x.shape)} {x.dtype}")
+        if x.stride() != (self.k, 1):
+            raise ValueError("x must be packed row-major")
+        m = x.shape[0]
+        if out.dim() != 2 or out.shape[1] != self.n or out.shape[0] < m or out.dtype != self.out_dtype:
+            raise ValueError(f"out must be {self.out_dtype} [>= {m}, {self.n}]")
+        if out.stride() != (self.n, 1):
+            raise ValueError("out must be packed row-major")
+        if x.device != self.weight.device or out.device != self.weight.device:
+            raise ValueError("x, out and the weight must be on the same device")
+        self.run_ptr(x.data_ptr(), out.data_ptr(), m, stream)
+        return out
+
+    def run_ptr(self, x_ptr: int, out_ptr: int, m: int, stream=None):
+        """Raw-pointer form of run (used inside graph capture loops)."""
+        _raise(load_library().skinny_run(self._plan, ctypes.c_void_p(x_ptr),
+                                         ctypes.c_void_p(out_ptr), m, _stream_handle(stream)))
+
+    def close(self):
+        if self._plan:
+            load_library().skinny_destroy(self._plan)
+            self._plan = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,539 @@
+// Plans: prepare (validate, tune or take a table, warm, allocate the split-K
+// workspace) and run (one table lookup, one launch).
+//
+// This follows the pages' split between install time and forward time: the
+// static part of the choice is resolved once into an {M: call} plan so that a
+// forward is a single lookup ("vllm.models.kimi_k3.nvidia.low_latency_gemm",
+// module docstring), every kernel a plan can use is compiled and warmed before
+// graph capture (the warmups registered by enable_kimi_k3_low_latency_gemm
+// and Projection.__init__ "compiled before capture"), and the per-part
+// measured tables of that page become a table measured on this chip.  Tuned
+// tables are shared process-wide per (device, N, K, output type), as the
+// split-K projection page's compile cache is shared per shape while weights
+// stay private to each prepared object.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <array>
+#include <map>
+#include <mutex>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#include <tuple>
+#include <vector>
+
+#include "skinny_internal.h"
+
+using namespace skinny;
+
+namespace {
+
+struct Entry {
+    const void *fn = nullptr;
+    unsigned grid = 0, block = 0, lds = 0;
+    int n_tiles = 0;
+    skinny_tactic t{};
+};
+
+}  // namespace
+
+struct skinny_plan {
+    int device = -1;
+    const void *W = nullptr;
+    int N = 0, K = 0;
+    skinny_out_dtype od = SKINNY_OUT_BF16;
+    float *ws = nullptr;
+    unsigned *ctr = nullptr;
+    KArgs base{};
+    Entry e[SKINNY_MAX_M + 1];
+};
+
+namespace {
+
+using Key = std::tuple<int, int, int, int>;   // device, N, K, out dtype
+std::mutex g_cache_mu;
+std::map<Key, std::array<skinny_tactic, SKINNY_MAX_M>> g_cache;
+
+bool env_flag(const char *name)
+{
+    const char *v = getenv(name);
+    return v && *v && strcmp(v, "0") != 0;
+}
+
+int env_int(const char *name, int dflt)
+{
+    const char *v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+skinny_status hip_fail(hipError_t e, const char *what)
+{
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return SKINNY_ERR_HIP;
+}
+
+#define HIP_TRY(expr)                                   \
+    do {                                                \
+        hipError_t e_ = (expr);                         \
+        if (e_ != hipSuccess)                           \
+            return hip_fail(e_, #expr);                 \
+    } while (0)
+
+Entry make_entry(const skinny_tactic &t, int N)
+{
+    Entry en;
+    const KernelInfo *k = find_kernel(t.path, t.mt, t.rows, t.unroll);
+    en.fn = k ? k->fn : nullptr;
+    en.n_tiles = tiles_for(t, N);
+    en.grid = (unsigned)(en.n_tiles * t.split);
+    en.block = (unsigned)(64 * t.waves);
+    en.lds = (unsigned)tactic_lds_bytes(t);
+    en.t = t;
+    return en;
+}
+
+size_t ws_floats(const Entry &en) { return en.t.split > 1 ? (size_t)en.n_tiles * en.t.split * en.t.mt * en.t.rows : 0; }
+
+hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
+{
+    a.n_tiles = en.n_tiles;
+    a.split = en.t.split;
+    a.remap = en.t.split > 1 ? 1 : 0;
+    void *params[] = {&a};
+    return hipLaunchKernel(en.fn, dim3(en.grid), dim3(en.block), params, en.lds, stream);
+}
+
+// Validation shared by the prepare entry points; no HIP call before it passes.
+skinny_status check_prepare_args(const void *W, int N, int K, skinny_out_dtype od, skinny_plan **plan)
+{
+    if (!plan) {
+        set_error("plan out-pointer is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    *plan = nullptr;
+    if (!W) {
+        set_error("W is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (N <= 0 || K <= 0) {
+        set_error("N=%d K=%d must be positive", N, K);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (od != SKINNY_OUT_BF16 && od != SKINNY_OUT_F32) {
+        set_error("out_dtype=%d is not SKINNY_OUT_BF16 or SKINNY_OUT_F32", (int)od);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (K % 8) {
+        set_error("K=%d is not a multiple of 8 (rows must be whole 16-byte chunks)", K);
+        return SKINNY_ERR_SHAPE;
+    }
+    if ((long long)N * K >= (1LL << 31)) {
+        set_error("N*K=%lld exceeds 2^31 - 1 elements", (long long)N * K);
+        return SKINNY_ERR_SHAPE;
+    }
+    if ((uintptr_t)W & 15) {
+        set_error("W=%p is not 16-byte aligned", W);
+        return SKINNY_ERR_ALIGN;
+    }
+    return SKINNY_OK;
+}
+
+skinny_status current_gfx950(int *dev, int *cus)
+{
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count == 0) {
+        set_error("no HIP device");
+        return SKINNY_ERR_DEVICE;
+    }
+    HIP_TRY(hipGetDevice(dev));
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, *dev));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+        set_error("device %d is %s, not gfx950", *dev, prop.gcnArchName);
+        return SKINNY_ERR_DEVICE;
+    }
+    *cus = prop.multiProcessorCount;
+    return SKINNY_OK;
+}
+
+struct DevBuf {
+    void *p = nullptr;
+    ~DevBuf()
+    {
+        if (p)
+            (void)hipFree(p);
+    }
+};
+
+// Time every candidate on cache-cold copies of W and fill the table.
+skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
+                   std::array<skinny_tactic, SKINNY_MAX_M> &table)
+{
+    const int count = skinny_enumerate_tactics(N, K, nullptr, 0);
+    if (count <= 0) {
+        set_error("no candidate tactics for N=%d K=%d", N, K);
+        return SKINNY_ERR_SHAPE;
+    }
+    std::vector<skinny_tactic> cand(count);
+    skinny_enumerate_tactics(N, K, cand.data(), count);
+
+    const size_t wbytes = (size_t)N * K * 2;
+    const size_t cold = (size_t)768 << 20;   // well past the 256 MiB Infinity Cache
+    int copies = (int)std::min<size_t>(16, std::max<size_t>(1, (cold + wbytes - 1) / wbytes));
+    size_t max_ws = 0, max_tiles = 0;
+    for (const skinny_tactic &t : cand) {
+        Entry en = make_entry(t, N);
+        max_ws = std::max(max_ws, ws_floats(en));
+        max_tiles = std::max(max_tiles, (size_t)en.n_tiles);
+    }
+    DevBuf wcopies, xbuf, obuf, wsbuf, ctrbuf;
+    HIP_TRY(hipMalloc(&wcopies.p, wbytes * copies));
+    HIP_TRY(hipMalloc(&xbuf.p, (size_t)SKINNY_MAX_M * K * 2));
+    HIP_TRY(hipMalloc(&obuf.p, (size_t)SKINNY_MAX_M * N * 4));
+    HIP_TRY(hipMalloc(&wsbuf.p, std::max<size_t>(max_ws, 1) * 4));
+    HIP_TRY(hipMalloc(&ctrbuf.p, std::max<size_t>(max_tiles, 1) * 4));
+    hipStream_t st;
+    HIP_TRY(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    struct StreamGuard {
+        hipStream_t s;
+        ~StreamGuard() { (void)hipStreamDestroy(s); }
+    } sg{st};
+    for (int c = 0; c < copies; ++c)
+        HIP_TRY(hipMemcpyAsync((char *)wcopies.p + wbytes * c, W, wbytes, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemsetAsync(xbuf.p, 0, (size_t)SKINNY_MAX_M * K * 2, st));
+    HIP_TRY(hipMemsetAsync(ctrbuf.p, 0, std::max<size_t>(max_tiles, 1) * 4, st));
+    hipEvent_t e0, e1;
+    HIP_TRY(hipEventCreate(&e0));
+    HIP_TRY(hipEventCreate(&e1));
+    struct EventGuard {
+        hipEvent_t a, b;
+        ~EventGuard()
+        {
+            (void)hipEventDestroy(a);
+            (void)hipEventDestroy(b);
+        }
+    } eg{e0, e1};
+
+    KArgs a{};
+    a.x = xbuf.p;
+    a.out = obuf.p;
+    a.ws = (float *)wsbuf.p;
+    a.ctr = (unsigned *)ctrbuf.p;
+    a.N = N;
+    a.K8 = K / 8;
+    a.out_f32 = od == SKINNY_OUT_F32;
+    a.nxcd = nxcd;
+
+    const int iters = std::max(1, env_int("SKINNY_TUNE_ITERS", 2 * copies > 8 ? 2 * copies : 8));
+    std::vector<double> times(count, -1.0);
+    for (int i = 0; i < count; ++i) {
+        const Entry en = make_entry(cand[i], N);
+        a.M = cand[i].mt;
+        a.W = wcopies.p;
+        if (launch(en, a, st) != hipSuccess) {
+            (void)hipGetLastError();
+            continue;
+        }
+        double best = -1.0;
+        for (int rep = 0; rep < 2; ++rep) {
+            HIP_TRY(hipEventRecord(e0, st));
+            bool ok = true;
+            for (int j = 0; j < iters && ok; ++j) {
+                a.W = (const char *)wcopies.p + wbytes * ((j + 1) % copies);
+                ok = launch(en, a, st) == hipSuccess;
+            }
+            HIP_TRY(hipEventRecord(e1, st));
+            HIP_TRY(hipEventSynchronize(e1));
+            if (!ok) {
+                (void)hipGetLastError();
+                best = -1.0;
+                break;
+            }
+            float ms = 0.f;
+            HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+            const double us = 1000.0 * ms / iters;
+            if (best < 0 || us < best)
+                best = us;
+        }
+        times[i] = best;
+    }
+    HIP_TRY(hipStreamSynchronize(st));
+    skinny_status s = skinny_select_table(cand.data(), times.data(), count, table.data());
+    if (env_int("SKINNY_LOG", 0) >= 2) {
+        for (int i = 0; i < count; ++i)
+            fprintf(stderr, "[skinny] cand N=%d K=%d %s mt=%d rows=%d waves=%d unroll=%d split=%d : %.3f us\n",
+                    N, K, cand[i].path == SKINNY_PATH_MFMA ? "mfma" : "dot2", cand[i].mt, cand[i].rows,
+                    cand[i].waves, cand[i].unroll, cand[i].split, times[i]);
+    }
+    if (s == SKINNY_OK && env_flag("SKINNY_LOG")) {
+        fprintf(stderr, "[skinny] tuned N=%d K=%d out=%s over %d candidates, %d weight copies\n", N, K,
+                od == SKINNY_OUT_F32 ? "f32" : "bf16", count, copies);
+    }
+    return s;
+}
+
+skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int dev, int nxcd,
+                         const skinny_tactic *table, skinny_plan **out)
+{
+    for (int m = 1; m <= SKINNY_MAX_M; ++m) {
+        const skinny_tactic &t = table[m - 1];
+        skinny_status s = skinny_tactic_check(&t, N, K);
+        if (s != SKINNY_OK)
+            return s;
+        if (t.mt < m) {
+            set_error("table entry for M=%d has token tile %d < M", m, t.mt);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+    }
+    skinny_plan *p = new (std::nothrow) skinny_plan;
+    if (!p) {
+        set_error("host allocation of the plan failed");
+        return SKINNY_ERR_NOMEM;
+    }
+    p->device = dev;
+    p->W = W;
+    p->N = N;
+    p->K = K;
+    p->od = od;
+    size_t max_ws = 0, max_tiles = 0;
+    for (int m = 1; m <= SKINNY_MAX_M; ++m) {
+        p->e[m] = make_entry(table[m - 1], N);
+        max_ws = std::max(max_ws, ws_floats(p->e[m]));
+        if (table[m - 1].split > 1)
+            max_tiles = std::max(max_tiles, (size_t)p->e[m].n_tiles);
+    }
+    auto fail = [&](skinny_status s) {
+        skinny_destroy(p);
+        return s;
+    };
+    hipError_t e;
+    if (max_ws) {
+        if ((e = hipMalloc(&p->ws, max_ws * 4)) != hipSuccess) {
+            hip_fail(e, "hipMalloc(split-K workspace)");
+            return fail(e == hipErrorOutOfMemory ? SKINNY_ERR_NOMEM : SKINNY_ERR_HIP);
+        }
+        if ((e = hipMalloc(&p->ctr, max_tiles * 4)) != hipSuccess) {
+            hip_fail(e, "hipMalloc(split-K counters)");
+            return fail(e == hipErrorOutOfMemory ? SKINNY_ERR_NOMEM : SKINNY_ERR_HIP);
+        }
+        if ((e = hipMemset(p->ctr, 0, max_tiles * 4)) != hipSuccess) {
+            hip_fail(e, "hipMemset(split-K counters)");
+            return fail(SKINNY_ERR_HIP);
+        }
+    }
+    KArgs &a = p->base;
+    a.W = W;
+    a.ws = p->ws;
+    a.ctr = p->ctr;
+    a.N = N;
+    a.K8 = K / 8;
+    a.out_f32 = od == SKINNY_OUT_F32;
+    a.nxcd = nxcd;
+
+    // Warm every distinct kernel the table uses, on scratch x/out, so that no
+    // code object loads lazily inside a later graph capture.
+    void *xs = nullptr, *os = nullptr;
+    if ((e = hipMalloc(&xs, (size_t)SKINNY_MAX_M * K * 2)) != hipSuccess) {
+        hip_fail(e, "hipMalloc(warm-up x)");
+        return fail(SKINNY_ERR_HIP);
+    }
+    if ((e = hipMalloc(&os, (size_t)SKINNY_MAX_M * N * 4)) != hipSuccess) {
+        (void)hipFree(xs);
+        hip_fail(e, "hipMalloc(warm-up out)");
+        return fail(SKINNY_ERR_HIP);
+    }
+    e = hipMemset(xs, 0, (size_t)SKINNY_MAX_M * K * 2);
+    for (int m = 1; m <= SKINNY_MAX_M && e == hipSuccess; ++m) {
+        bool seen = false;
+        for (int j = 1; j < m; ++j)
+            seen |= memcmp(&p->e[j].t, &p->e[m].t, sizeof(skinny_tactic)) == 0;
+        if (seen)
+            continue;
+        KArgs w = a;
+        w.x = xs;
+        w.out = os;
+        w.M = m;
+        e = launch(p->e[m], w, nullptr);
+    }
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    (void)hipFree(xs);
+    (void)hipFree(os);
+    if (e != hipSuccess) {
+        hip_fail(e, "warm-up launch");
+        return fail(SKINNY_ERR_HIP);
+    }
+    if (env_flag("SKINNY_LOG")) {
+        for (int m = 1; m <= SKINNY_MAX_M; ++m) {
+            char buf[160];
+            skinny_describe(p, m, buf, sizeof buf);
+            fprintf(stderr, "[skinny] N=%d K=%d M=%d -> %s\n", N, K, m, buf);
+        }
+    }
+    *out = p;
+    return SKINNY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype od, skinny_plan **plan)
+{
+    skinny_status s = check_prepare_args(W, N, K, od, plan);
+    if (s != SKINNY_OK)
+        return s;
+    int dev = 0, cus = 0;
+    if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)
+        return s;
+    const int nxcd = cus % 8 == 0 ? 8 : 1;
+    std::array<skinny_tactic, SKINNY_MAX_M> table;
+    {
+        std::lock_guard<std::mutex> lock(g_cache_mu);
+        const Key key{dev, N, K, (int)od};
+        auto it = g_cache.find(key);
+        if (it != g_cache.end()) {
+            table = it->second;
+        } else {
+            if ((s = tune(W, N, K, od, nxcd, table)) != SKINNY_OK)
+                return s;
+            g_cache[key] = table;
+        }
+    }
+    return build_plan(W, N, K, od, dev, nxcd, table.data(), plan);
+}
+
+skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dtype od,
+                                     const skinny_tactic *table, skinny_plan **plan)
+{
+    skinny_status s = check_prepare_args(W, N, K, od, plan);
+    if (s != SKINNY_OK)
+        return s;
+    if (!table) {
+        set_error("table is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    for (int m = 1; m <= SKINNY_MAX_M; ++m) {
+        if ((s = skinny_tactic_check(&table[m - 1], N, K)) != SKINNY_OK)
+            return s;
+        if (table[m - 1].mt < m) {
+            set_error("table entry for M=%d has token tile %d < M", m, table[m - 1].mt);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+    }
+    int dev = 0, cus = 0;
+    if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)
+        return s;
+    return build_plan(W, N, K, od, dev, cus % 8 == 0 ? 8 : 1, table, plan);
+}
+
+skinny_status skinny_run(const skinny_plan *p, const void *x, void *out, int M, void *stream)
+{
+    if (!p) {
+        set_error("plan is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (M < 1 || M > SKINNY_MAX_M) {
+        set_error("M=%d outside 1..%d", M, SKINNY_MAX_M);
+        return SKINNY_ERR_UNSUPPORTED_M;
+    }
+    if (!x || !out) {
+        set_error("x or out is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    const uintptr_t out_align = p->od == SKINNY_OUT_F32 ? 3 : 1;
+    if (((uintptr_t)x & 15) || ((uintptr_t)out & out_align)) {
+        set_error("x=%p must be 16-byte aligned and out=%p element aligned", x, out);
+        return SKINNY_ERR_ALIGN;
+    }
+    const Entry &en = p->e[M];
+    KArgs a = p->base;
+    a.x = x;
+    a.out = out;
+    a.M = M;
+    hipError_t e = launch(en, a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipLaunchKernel");
+    return SKINNY_OK;
+}
+
+int skinny_supports(const skinny_plan *p, int M) { return p && M >= 1 && M <= SKINNY_MAX_M; }
+
+skinny_status skinny_plan_tactic(const skinny_plan *p, int M, skinny_tactic *out)
+{
+    if (!p || !out) {
+        set_error("plan or out is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (M < 1 || M > SKINNY_MAX_M) {
+        set_error("M=%d outside 1..%d", M, SKINNY_MAX_M);
+        return SKINNY_ERR_UNSUPPORTED_M;
+    }
+    *out = p->e[M].t;
+    return SKINNY_OK;
+}
+
+skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len)
+{
+    skinny_tactic t;
+    skinny_status s = skinny_plan_tactic(p, M, &t);
+    if (s != SKINNY_OK)
+        return s;
+    if (!buf || len == 0) {
+        set_error("buf is NULL or empty");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    const Entry &en = p->e[M];
+    snprintf(buf, len, "%s mt=%d rows=%d waves=%d unroll=%d split=%d grid=%u block=%u lds=%u",
+             t.path == SKINNY_PATH_MFMA ? "mfma16x16x32" : "dot2", t.mt, t.rows, t.waves, t.unroll,
+             t.split, en.grid, en.block, en.lds);
+    return SKINNY_OK;
+}
+
+void skinny_destroy(skinny_plan *p)
+{
+    if (!p)
+        return;
+    if (p->ws || p->ctr) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        if (cur != p->device)
+            (void)hipSetDevice(p->device);
+        (void)hipDeviceSynchronize();
+        if (p->ws)
+            (void)hipFree(p->ws);
+        if (p->ctr)
+            (void)hipFree(p->ctr);
+        if (cur != p->device && cur >= 0)
+            (void)hipSetDevice(cur);
+    }
+    delete p;
+}
+
+int skinny_probe_read_blocks(void) { return kProbeReadBlocks; }
+
+skinny_status skinny_probe_read(const void *buf, size_t bytes, float *sink, void *stream)
+{
+    if (!buf || !sink) {
+        set_error("buf or sink is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (((uintptr_t)buf & 15) || (bytes & 15)) {
+        set_error("buf must be 16-byte aligned and bytes a multiple of 16");
+        return SKINNY_ERR_ALIGN;
+    }
+    long chunks = (long)(bytes / 16);
+    void *params[] = {&buf, &chunks, &sink};
+    hipError_t e = hipLaunchKernel(probe_read_fn(), dim3(kProbeReadBlocks), dim3(kProbeReadThreads),
+                                   params, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SKINNY_OK : hip_fail(e, "hipLaunchKernel(probe_read)");
+}
+
+skinny_status skinny_probe_empty(void *stream)
+{
+    hipError_t e = hipLaunchKernel(probe_empty_fn(), dim3(1), dim3(64), nullptr, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SKINNY_OK : hip_fail(e, "hipLaunchKernel(probe_empty)");
+}
+
+}  // extern "C"

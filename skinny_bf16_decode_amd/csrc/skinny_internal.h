@@ -1,0 +1,58 @@
+// Internal declarations shared by the kernels and the host side of the
+// skinny BF16 decode projection library.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/skinny.h"
+
+namespace skinny {
+
+// Arguments of every kernel, passed by value.  W, x are viewed as arrays of
+// 16-byte chunks (8 BF16 values); K8 = K / 8 chunks per row.
+struct KArgs {
+    const void *W;      // [N][K8] chunks
+    const void *x;      // [M][K8] chunks
+    void *out;          // [M][N] BF16 or fp32
+    float *ws;          // split-K partials, [tile][split][mt][rows]
+    unsigned *ctr;      // split-K arrival counters, one per row tile
+    int N;
+    int K8;
+    int M;
+    int n_tiles;        // ceil(N / rows)
+    int split;          // workgroups per row tile along K
+    int out_f32;        // 1: fp32 output, 0: BF16
+    int nxcd;           // XCDs the dispatcher deals workgroups over
+    int remap;          // 1: place the split-K workgroups of a tile on one XCD
+};
+
+// A compiled kernel instance.
+struct KernelInfo {
+    int path, mt, rows, unroll;
+    const void *fn;     // host stub address for hipLaunchKernel
+};
+
+// All compiled instances (defined next to the kernels).
+const KernelInfo *kernel_table(int *count);
+const KernelInfo *find_kernel(int path, int mt, int rows, int unroll);
+
+// Measurement probe kernels (host stub addresses).
+const void *probe_read_fn();
+const void *probe_empty_fn();
+constexpr int kProbeReadBlocks = 2048;
+constexpr int kProbeReadThreads = 256;
+
+// Dynamic LDS bytes a tactic needs.
+size_t tactic_lds_bytes(const skinny_tactic &t);
+
+// Thread-local error text.
+void set_error(const char *fmt, ...);
+
+// Rows of W per tile and tile count for a tactic.
+inline int tiles_for(const skinny_tactic &t, int N) { return (N + t.rows - 1) / t.rows; }
+
+constexpr int kMaxWaves = 8;
+constexpr size_t kMaxLds = 60 * 1024;
+
+}  // namespace skinny

@@ -1,0 +1,169 @@
+// Host-only tactic logic: legality, the tuner's candidate list, the per-M
+// table rule, status texts and the thread-local error text.  Nothing here
+// calls the HIP runtime, so all of it runs (and is tested) without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "skinny_internal.h"
+
+namespace skinny {
+
+static thread_local char g_error[512];
+
+void set_error(const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+}
+
+size_t tactic_lds_bytes(const skinny_tactic &t)
+{
+    if (t.path == SKINNY_PATH_MFMA)
+        return (size_t)t.waves * t.mt * (t.rows + 1) * sizeof(float);
+    return 0;
+}
+
+static bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+}  // namespace skinny
+
+using namespace skinny;
+
+extern "C" {
+
+const char *skinny_status_string(skinny_status s)
+{
+    switch (s) {
+    case SKINNY_OK: return "ok";
+    case SKINNY_ERR_INVALID_ARG: return "invalid argument";
+    case SKINNY_ERR_SHAPE: return "unsupported shape";
+    case SKINNY_ERR_ALIGN: return "misaligned pointer";
+    case SKINNY_ERR_UNSUPPORTED_M: return "token count outside 1..64";
+    case SKINNY_ERR_DEVICE: return "no gfx950 device";
+    case SKINNY_ERR_NOMEM: return "out of memory";
+    case SKINNY_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *skinny_last_error(void) { return g_error; }
+
+skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
+{
+    if (!t) {
+        set_error("tactic is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (N < 1 || K < 8 || K % 8) {
+        set_error("bad shape N=%d K=%d (need N >= 1, K >= 8, K %% 8 == 0)", N, K);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    const int k8 = K / 8;
+    if (!is_pow2(t->waves) || t->waves > kMaxWaves) {
+        set_error("waves=%d: must be 1, 2, 4 or 8", t->waves);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (t->split < 1 || t->split > 16) {
+        set_error("split=%d: must be 1..16", t->split);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (t->path == SKINNY_PATH_DOT2) {
+        if (t->split > k8) {
+            set_error("split=%d exceeds the %d 16-byte chunks of a row", t->split, k8);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+    } else if (t->path == SKINNY_PATH_MFMA) {
+        const int steps = (k8 + 3) / 4;
+        if (t->split > steps) {
+            set_error("split=%d exceeds the %d 32-element K steps of a row", t->split, steps);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+        if (tactic_lds_bytes(*t) > kMaxLds) {
+            set_error("MFMA tactic needs %zu bytes of LDS (limit %zu)", tactic_lds_bytes(*t), kMaxLds);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+    } else {
+        set_error("path=%d: must be 0 (DOT2) or 1 (MFMA)", t->path);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (!find_kernel(t->path, t->mt, t->rows, t->unroll)) {
+        set_error("no compiled kernel for path=%d mt=%d rows=%d unroll=%d", t->path, t->mt, t->rows,
+                  t->unroll);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    return SKINNY_OK;
+}
+
+int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
+{
+    if (N < 1 || K < 8 || K % 8 || cap < 0 || (cap > 0 && !buf))
+        return -1;
+    const int k8 = K / 8;
+    int count = 0;
+    int nk = 0;
+    const KernelInfo *ks = kernel_table(&nk);
+    static const int kWaves[] = {1, 2, 4, 8};
+    static const int kSplits[] = {1, 2, 4, 8};
+    for (int i = 0; i < nk; ++i) {
+        const KernelInfo &k = ks[i];
+        for (int w : kWaves) {
+            for (int s : kSplits) {
+                skinny_tactic t = {k.path, k.mt, k.rows, w, k.unroll, s};
+                if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
+                    continue;
+                const int tiles = (N + k.rows - 1) / k.rows;
+                if (s > 1 && tiles * w >= 8 * 256)
+                    continue;   // enough waves already; a K split only adds traffic
+                if (k.path == SKINNY_PATH_DOT2) {
+                    // each lane of the workgroup should own at least one chunk per
+                    // split, and the unrolled loop should run at least once
+                    const int per_split = k8 / s;
+                    if (per_split < 64 * w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
+                        continue;
+                    if (k.rows * k.unroll > 16)
+                        continue;
+                } else {
+                    const int per_split = ((k8 + 3) / 4) / s;
+                    if (per_split < w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
+                        continue;
+                    if ((k.rows / 16) * k.unroll > 8)
+                        continue;
+                }
+                if (count < cap)
+                    buf[count] = t;
+                ++count;
+            }
+        }
+    }
+    return count;
+}
+
+skinny_status skinny_select_table(const skinny_tactic *cand, const double *times_us, int count,
+                                  skinny_tactic *table)
+{
+    if (!cand || !times_us || !table || count < 0) {
+        set_error("skinny_select_table: NULL argument or negative count");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    for (int m = 1; m <= SKINNY_MAX_M; ++m) {
+        int best = -1;
+        for (int i = 0; i < count; ++i) {
+            if (times_us[i] < 0 || cand[i].mt < m)
+                continue;
+            if (best < 0 || times_us[i] < times_us[best] ||
+                (times_us[i] == times_us[best] && cand[i].mt < cand[best].mt))
+                best = i;
+        }
+        if (best < 0) {
+            set_error("no usable candidate serves M=%d", m);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+        table[m - 1] = cand[best];
+    }
+    return SKINNY_OK;
+}
+
+}  // extern "C"

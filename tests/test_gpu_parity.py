@@ -1,0 +1,287 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Exact probes first -- integer inputs make every fp32 partial sum exact, so any
+correct kernel, in any summation order, must reproduce the oracle bit for bit
+(and the nearest-even BF16 rounding of it) -- then the seeded workloads under
+the stated bound |g - O| <= 1e-3 S + 1e-6 (+ 2^-8 |O| for BF16 output).
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import skinny_inputs as si
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sk():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import skinny_bf16_decode_amd as sk
+    sk.load_library()
+    return sk
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_exact(sk, plan, x_bits, o, m, label):
+    """Run plan on the first m rows, compare bitwise with the exact result."""
+    import torch
+    x = gu.dev_bf16(x_bits[:m])
+    out = gu.out_buffer(plan.n, plan.out_dtype)
+    plan.run(x, out[:m])   # rows [0, m) of a packed [64, N] buffer are a packed [m, N] view
+    torch.cuda.synchronize()
+    assert gu.sentinel_intact(out, m), f"{label}: rows >= M were written"
+    got = gu.host_bits(out)[:m]
+    if plan.out_dtype == torch.float32:
+        want = o[:m].astype(np.float32).view(np.uint32)
+    else:
+        want = oracle.round_bf16(o[:m])
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)[0]
+        raise AssertionError(f"{label}: first mismatch at {tuple(bad)}: got {got[tuple(bad)]:#x} "
+                             f"want {want[tuple(bad)]:#x} (exact {o[tuple(bad)]})")
+
+
+EXACT_SHAPES = [(200, 1032), (48, 4104), (64, 128)]
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("od", ["f32", "bf16"])
+def test_integer_probe_every_tactic(sk, shape, od):
+    """Every candidate tactic, forced, is exact on integer inputs -- at its full
+    token tile and at a ragged M below it.  Shapes have ragged row tiles and K
+    not a multiple of the wave stride (K/8 = 129, 513, 16)."""
+    import torch
+    n, k = shape
+    out_dtype = torch.float32 if od == "f32" else torch.bfloat16
+    x_bits, w_bits = si.small_int_case(1000 + n + k, 64, n, k)
+    o, _ = oracle.gemm(x_bits, w_bits)
+    assert np.all(np.abs(o) < 2 ** 24)
+    w = gu.dev_bf16(w_bits)
+    tactics = sk.enumerate_tactics(n, k)
+    _say(f"[exact] {n}x{k} {od}: {len(tactics)} tactics")
+    for t in tactics:
+        plan = sk.Prepared(w, out_dtype, table=gu.forced_table(t))
+        for m in sorted({t.mt, max(1, t.mt - 3), max(1, t.mt // 2 + 1)}):
+            _check_exact(sk, plan, x_bits, o, m, f"{t} M={m}")
+        plan.close()
+
+
+def test_k_probe_every_tactic(sk):
+    """One nonzero per weight row, at a column that sweeps every residue
+    modulo 8, 64 and 512: any chunk dropped or duplicated at a lane, wave or
+    split boundary shows up as a wrong output."""
+    import torch
+    n, k = 600, 1536
+    x_bits, w_bits, cols, scales = si.k_probe_case(5, 64, n, k)
+    o, _ = oracle.gemm(x_bits, w_bits)
+    want_cf = si.bf16_bits_to_f32(x_bits).astype(np.float64)[:, cols] * scales.astype(np.float64)
+    assert np.array_equal(o, want_cf)
+    w = gu.dev_bf16(w_bits)
+    tactics = sk.enumerate_tactics(n, k)
+    _say(f"[kprobe] {len(tactics)} tactics")
+    for t in tactics:
+        plan = sk.Prepared(w, torch.float32, table=gu.forced_table(t))
+        _check_exact(sk, plan, x_bits, o, t.mt, f"{t}")
+        plan.close()
+
+
+@pytest.mark.parametrize("path", ["tuned", "dot2", "mfma"])
+def test_tie_probe_rounds_to_nearest_even(sk, path):
+    """Exact sums 257, 259, 261, ... lie halfway between BF16 neighbours;
+    nearest-even gives 256, 260, 260, ..., truncation 256, 258, 260, ..."""
+    import torch
+    n, k = 128, 512
+    x_bits, w_bits = si.tie_case(n, k, m=64)
+    o, _ = oracle.gemm(x_bits, w_bits)
+    w = gu.dev_bf16(w_bits)
+    if path == "tuned":
+        plan = sk.Prepared(w, torch.bfloat16)
+    elif path == "dot2":
+        plan = sk.Prepared(w, torch.bfloat16, table=gu.forced_table(sk.Tactic(0, 8, 4, 1, 1, 1)))
+    else:
+        plan = sk.Prepared(w, torch.bfloat16, table=[sk.Tactic(1, 64, 16, 2, 1, 2)] * 64)
+    for m in (1, 5, 8, 16, 33, 64):
+        _check_exact(sk, plan, x_bits, o, m, f"tie {path} M={m}")
+    plan.close()
+
+
+def _bound_check(got, o, s, mode, label):
+    rep = oracle.check(got, o, s, mode)
+    _say(f"  {label}: {rep}")
+    assert rep.ok, f"{label}: {rep}"
+    # Beyond the stated bound: an fp32 accumulator over these lengths sits far
+    # inside it.  Allow 1e-4 S for accumulation, plus the output rounding
+    # (half a BF16 ulp, <= 2^-8 |O|) in BF16 mode.
+    tight = 1e-4 * np.asarray(s) + 1e-6
+    if mode == "bf16":
+        tight = tight + 2.0 ** -8 * np.abs(np.asarray(o))
+    worst = float(np.max(np.abs(np.asarray(got) - np.asarray(o)) / tight)) if np.size(o) else 0.0
+    assert worst <= 1.0, f"{label}: error level above the fp32-accumulation expectation ({worst:.3f})"
+
+
+@pytest.mark.parametrize("cid", [1, 4])
+def test_small_workloads_all_m(sk, cid):
+    """Tuned plans on the tiny and short-K workloads, every M = 1..64 (the
+    activation block is cycled for the tiny workload, which has one row)."""
+    import torch
+    wl = si.WORKLOADS[cid]
+    w_bits = si.weight(cid)
+    x_bits = si.activations(cid)
+    if x_bits.shape[0] < 64:
+        x_bits = np.ascontiguousarray(np.resize(x_bits, (64, wl.k)))
+    o, s = oracle.gemm(x_bits, w_bits)
+    w = gu.dev_bf16(w_bits)
+    for od in wl.out_dtypes:
+        out_dtype = torch.float32 if od == "f32" else torch.bfloat16
+        plan = sk.Prepared(w, out_dtype)
+        for m in range(1, 65):
+            x = gu.dev_bf16(x_bits[:m])
+            out = gu.out_buffer(wl.n, out_dtype)
+            plan.run(x, out[:m])
+            torch.cuda.synchronize()
+            assert gu.sentinel_intact(out, m), (cid, od, m)
+            _bound_check(gu.values(out)[:m], o[:m], s[:m], od, f"cfg{cid} {od} M={m} {plan.describe(m)}")
+        plan.close()
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_decode_workloads(sk, cid):
+    """The [3584, 7168] and [6288, 7168] workloads at full size, tuned, at the
+    timed token counts and at ragged ones, against the whole oracle."""
+    import torch
+    wl = si.WORKLOADS[cid]
+    w_bits = si.weight(cid)
+    x_bits = si.activations(cid)
+    t0 = time.time()
+    o, s = oracle.gemm(x_bits, w_bits)
+    _say(f"[cfg{cid}] oracle {time.time() - t0:.1f}s")
+    w = gu.dev_bf16(w_bits)
+    t0 = time.time()
+    plan = sk.Prepared(w, torch.bfloat16)
+    _say(f"[cfg{cid}] prepare {time.time() - t0:.2f}s")
+    for m in sorted(set(wl.m_values) | {3, 7, 13, 31, 47, 64}):
+        x = gu.dev_bf16(x_bits[:m])
+        out = gu.out_buffer(wl.n, torch.bfloat16)
+        plan.run(x, out[:m])
+        torch.cuda.synchronize()
+        assert gu.sentinel_intact(out, m), (cid, m)
+        _bound_check(gu.values(out)[:m], o[:m], s[:m], "bf16", f"cfg{cid} M={m} {plan.describe(m)}")
+    # a second prepare of the same shape reuses the tuned table
+    t0 = time.time()
+    plan2 = sk.Prepared(w, torch.bfloat16)
+    dt = time.time() - t0
+    _say(f"[cfg{cid}] second prepare {dt:.3f}s")
+    assert all(plan.tactic(m) == plan2.tactic(m) for m in range(1, 65))
+    plan.close()
+    plan2.close()
+
+
+def test_long_k_split_workload_sampled(sk):
+    """[7168, 18432] at its timed token counts, checked on 4096 sampled outputs
+    per M, plus a forced cross-workgroup split-K tactic on both paths."""
+    import torch
+    cid = 5
+    wl = si.WORKLOADS[cid]
+    w_bits = si.weight(cid)
+    x_bits = si.activations(cid)
+    rng = np.random.default_rng(55)
+    w = gu.dev_bf16(w_bits)
+    plans = {"tuned": sk.Prepared(w, torch.bfloat16),
+             "split4": sk.Prepared(w, torch.bfloat16, table=[
+                 sk.Tactic(0, 8, 4, 4, 2, 4) if m <= 8 else sk.Tactic(1, 64, 16, 4, 2, 4)
+                 for m in range(1, 65)])}
+    for m in wl.m_values:
+        mi = rng.integers(0, m, size=4096)
+        ni = rng.integers(0, wl.n, size=4096)
+        o, s = oracle.gemm_sampled(x_bits, w_bits, mi, ni)
+        for name, plan in plans.items():
+            x = gu.dev_bf16(x_bits[:m])
+            out = gu.out_buffer(wl.n, torch.bfloat16)
+            plan.run(x, out[:m])
+            torch.cuda.synchronize()
+            assert gu.sentinel_intact(out, m)
+            got = gu.values(out)[mi, ni]
+            _bound_check(got, o, s, "bf16", f"cfg5 {name} M={m} {plan.describe(m)}")
+    for p in plans.values():
+        p.close()
+
+
+def test_deterministic_and_graph_replay(sk):
+    """Bitwise-identical results across repeated runs and across replays of a
+    captured graph (split-K counters must return to zero after every call)."""
+    import torch
+    n, k = 1024, 4096
+    x_bits, w_bits = si.random_case(77, 64, n, k)
+    w = gu.dev_bf16(w_bits)
+    table = [sk.Tactic(0, 8, 2, 2, 1, 4) if m <= 8 else sk.Tactic(1, 32, 16, 2, 1, 4)
+             for m in range(1, 33)] + [sk.Tactic(1, 64, 16, 2, 1, 2)] * 32
+    plan = sk.Prepared(w, torch.bfloat16, table=table)
+    x = gu.dev_bf16(x_bits)
+    ref = {}
+    for m in (5, 24, 64):
+        out = gu.out_buffer(n, torch.bfloat16)
+        plan.run(x[:m], out[:m])
+        torch.cuda.synchronize()
+        ref[m] = gu.host_bits(out).copy()
+        for _ in range(20):
+            out2 = gu.out_buffer(n, torch.bfloat16)
+            plan.run(x[:m], out2[:m])
+            torch.cuda.synchronize()
+            assert np.array_equal(gu.host_bits(out2), ref[m]), m
+    o, s = oracle.gemm(x_bits, w_bits)
+    for m in ref:
+        _bound_check(si.bf16_bits_to_f32(ref[m][:m]).astype(np.float64), o[:m], s[:m], "bf16",
+                     f"graph-ref M={m}")
+    # graph capture of three calls on one stream
+    outs = {m: gu.out_buffer(n, torch.bfloat16) for m in ref}
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for m in ref:
+                plan.run(x[:m], outs[m][:m])
+    for rep in range(10):
+        for m in ref:
+            outs[m][:m].fill_(0)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for m in ref:
+            assert np.array_equal(gu.host_bits(outs[m]), ref[m]), (rep, m)
+    plan.close()
+
+
+def test_run_errors(sk):
+    import torch
+    n, k = 64, 256
+    _, w_bits = si.random_case(3, 1, n, k)
+    w = gu.dev_bf16(w_bits)
+    plan = sk.Prepared(w, torch.float32, table=[sk.Tactic(1, 64, 16, 1, 1, 1)] * 64)
+    x = gu.dev_bf16(np.zeros((66, k), dtype=np.uint16))
+    out = torch.zeros((66, n), dtype=torch.float32, device="cuda")
+    with pytest.raises(sk.UnsupportedTokens):
+        plan.run(x[:65], out[:65])
+    with pytest.raises(sk.UnsupportedTokens):
+        plan.run_ptr(x.data_ptr(), out.data_ptr(), 0)
+    with pytest.raises(ValueError):
+        plan.run_ptr(x.data_ptr() + 2, out.data_ptr(), 4)      # x not 16-byte aligned
+    with pytest.raises(ValueError):
+        plan.run_ptr(x.data_ptr(), out.data_ptr() + 2, 4)      # fp32 out not 4-byte aligned
+    assert plan.supports(64) and not plan.supports(65) and not plan.supports(0)
+    with pytest.raises(ValueError):
+        sk.Prepared(w, torch.float32, table=[sk.Tactic(0, 1, 1, 1, 1, 1)] * 64)   # tile < M
+    plan.close()
