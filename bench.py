@@ -166,6 +166,36 @@ def cpu_baseline(setup):
                       f"{step_s:.2f} s per step"}
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "skinny_projection_packed_qkvg_6288x7168_msweep.traffic.json")
+
+
+def kernel_name(t):
+    if t.path == 1:
+        return f"k_mfma<{t.mt // 16}, {t.rows // 16}, {t.unroll}>"
+    return f"k_dot2<{t.mt}, {t.rows}, {t.unroll}>"
+
+
+def counted_traffic(setup):
+    """HBM bytes per launch over the step, from the committed rocprofv3 counter
+    record -- only if it was taken on this exact kernel source and covers every
+    kernel the step uses; otherwise None."""
+    import json as _json
+    from skinny_bf16_decode_amd import profiling
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    with open(TRAFFIC_RECORD) as f:
+        rec = _json.load(f)
+    if rec.get("kernel_source_sha256") != profiling.kernel_source_sha():
+        return None
+    total = 0.0
+    for m in M_SWEEP:
+        k = rec["kernels"].get(kernel_name(setup.plans[0].tactic(m)))
+        if k is None:
+            return None
+        total += (k["fetch_kib"] + k["write_kib"]) * 1024.0
+    return total / len(M_SWEEP)
+
+
 def parity_of_last(setup, last_copy, m, samples=4096):
     import oracle
     rng = np.random.default_rng(2024)
@@ -184,6 +214,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--extra", action="store_true", help="also time the other workloads (stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--per-m-reps", type=int, default=10, help="graph replays per token count")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also launch a plain read of one weight copy and a 64 MiB device copy, "
+                         "whose known byte counts scale the HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -253,7 +287,7 @@ def main():
 
     per_m = {}
     for m in M_SWEEP:
-        us = setup.per_m(stream, m)
+        us = setup.per_m(stream, m, reps=args.per_m_reps)
         gb = wl.weight_bytes / us / 1e3
         per_m[str(m)] = {"us_per_call": round(us, 3), "weight_gbps": round(gb, 1),
                          "pct_peak": round(100 * gb / PEAK_GBPS, 1)}
@@ -263,6 +297,8 @@ def main():
     log(f"read ceiling (plain nt stream of the same rotated weights): {ceil_us:.2f} us, "
         f"{ceil_gb:.1f} GB/s; empty-launch floor {floor_us:.2f} us")
 
+    if args.calibrate:
+        calibration_kernels(setup, stream)
     if args.extra:
         extra_workloads(stream)
 
@@ -271,6 +307,10 @@ def main():
         cpu = cpu_baseline(setup)
         log(f"cpu baseline: {cpu}")
 
+    traffic = counted_traffic(setup)
+    if traffic is not None:
+        traffic = round(traffic)
+        log(f"counted HBM traffic per launch: {traffic} B (algorithmic {round(algo_per_launch)} B)")
     line = {
         "metric": "µs/call and weight-stream HBM GB/s (% of peak), 6288x7168 at M=1..32",
         "value": round(value, 1),
@@ -295,12 +335,29 @@ def main():
         "empty_launch_us": round(floor_us, 3),
         "parity_last_call": "ok",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "skinny projection launches (k_dot2 / k_mfma instances of the step)",
                      "bytes_per_launch": round(algo_per_launch), "us_per_launch": round(us_per_launch, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def calibration_kernels(setup, stream):
+    """Kernels of known traffic for scaling rocprofv3's FETCH_SIZE/WRITE_SIZE:
+    k_probe_read reads exactly 2NK bytes of one weight copy; torch's copy
+    reads and writes 64 MiB."""
+    import torch
+    import skinny_bf16_decode_amd as sk
+    sink = torch.zeros(sk.probe_read_blocks(), dtype=torch.float32, device="cuda")
+    src = torch.ones(16 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        sk.probe_read(setup.w[1 % setup.copies].data_ptr(), setup.wl.weight_bytes, sink.data_ptr())
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration: probe_read of {setup.wl.weight_bytes} B, device copy of {src.numel() * 4} B")
 
 
 def extra_workloads(stream):

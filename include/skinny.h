@@ -93,6 +93,13 @@ typedef struct {
  * launched once (warm-up) so that nothing loads lazily under graph capture.
  * The split-K workspace and arrival counters are allocated here.
  *
+ * Tuned tables can persist across processes: when the environment variable
+ * SKINNY_TABLE_CACHE names a file, a table for this chip (arch and CU count)
+ * and shape is loaded from it instead of tuning, and a freshly tuned table is
+ * appended to it.  SKINNY_LOG=1 prints the chosen table, SKINNY_LOG=2 also
+ * every candidate's time; SKINNY_TUNE_ITERS sets the timed launches per
+ * candidate.
+ *
  * Synchronous.  Must not be called while the device is capturing a graph.
  * W is NOT copied: the plan keeps the pointer, W must stay allocated until
  * skinny_destroy, and its values may change between runs.  W is read-only.

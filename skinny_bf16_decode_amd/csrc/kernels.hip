@@ -213,15 +213,44 @@ __device__ __forceinline__ void split_reset(const KArgs &a, int tile)
 }
 
 // ---------------------------------------------------------------------------
-// DOT2 kernel: token tile MT <= 8, R rows per workgroup, U chunks in flight
-// per lane per row.
+// Buffer loads.  Each workgroup builds a buffer resource over its own row
+// tile of W (num_records = valid rows * row bytes) and one over x
+// (num_records = M * row bytes).  A load whose offset falls outside the
+// resource returns zeros without touching memory, so rows >= N of a ragged
+// last tile and token rows >= M read as zero with no branch, and x rows >= M
+// are never read.  Per-lane parts of an address go in the vector offset, the
+// workgroup-uniform stage offset in the scalar offset.  A lane whose chunk is
+// past the end of its K range uses kOffOob, which is out of range for any
+// resource here (tiles are far below 2 GiB).
+// ---------------------------------------------------------------------------
+constexpr unsigned kOffOob = 0x7FFFFFF0u;
+constexpr int kCpolNt = 2;   // nontemporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load_w(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCpolNt);
+}
+
+__device__ __forceinline__ u32x4 load_x(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+// ---------------------------------------------------------------------------
+// DOT2 kernel: token tile MT <= 8, R rows per workgroup, U chunks per lane
+// per pipeline stage.
 //
 // Lane t of the workgroup (T = blockDim.x lanes) takes chunks kb + t,
 // kb + t + T, ... of its K range, for all R rows at once: every wave-wide
 // load is 1 KiB of one row, and the MT x chunks a lane loads are reused over
-// the R rows.  x rows >= M are never read (the row index is clamped to M - 1
-// and the duplicated results are dropped).  Rows >= N are clamped the same
-// way in the last, ragged tile.
+// the R rows.  The K loop is a two-stage register pipeline: the loads of
+// stage j + 1 are issued before stage j is multiplied, so every wave keeps
+// U * (R + MT) 16-byte loads in flight while it computes.
 // ---------------------------------------------------------------------------
 template <int MT, int R, int U>
 __global__ __launch_bounds__(512) void k_dot2(KArgs a)
@@ -229,66 +258,91 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
     constexpr int V = MT * R;   // partial sums per lane, index m * R + r
     __shared__ float red[kMaxWaves][V];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int nthr = blockDim.x, nwaves = nthr >> 6;
     int tile, s;
     block_coords(a, tile, s);
     const int n0 = tile * R;
     const int kb = (int)(((long)s * a.K8) / a.split);
     const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
-
-    const u32x4 *W = static_cast<const u32x4 *>(a.W);
-    const u32x4 *X = static_cast<const u32x4 *>(a.x);
-    const u32x4 *wrow[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        wrow[r] = W + (long)min(n0 + r, a.N - 1) * a.K8 + tid;
-    const u32x4 *xrow[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        xrow[m] = X + (long)min(m, a.M - 1) * a.K8 + tid;
+    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const int rows_valid = min(R, a.N - n0);
+    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)n0 * row_bytes,
+                                (unsigned)rows_valid * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const unsigned lane_off = (unsigned)(kb + tid) * 16u;
+    const unsigned pass_bytes = (unsigned)nthr * 16u;
 
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i)
         acc[i] = 0.f;
 
-    int base = kb;
-    for (; base + U * nthr <= ke; base += U * nthr) {
-        u32x4 wv[U][R], xv[U][MT];
+    const int passes = (ke - kb) / nthr;   // passes in which every lane has a chunk
+    const int stages = passes / U;
+
+    u32x4 wa[U][R], xa[U][MT], wb[U][R], xb[U][MT];
+    auto load = [&](u32x4(&w)[U][R], u32x4(&x)[U][MT], int j) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            const unsigned so = (unsigned)(j * U + u) * pass_bytes;
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                wv[u][r] = load_stream(wrow[r] + base + u * nthr);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
+                w[u][r] = load_w(wres, (unsigned)r * row_bytes + lane_off, so);
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-                xv[u][m] = xrow[m][base + u * nthr];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    acc[m * R + r] = dot8(wv[u][r], xv[u][m], acc[m * R + r]);
-    }
-    for (; base < ke; base += nthr) {
-        if (base + tid < ke) {
-            u32x4 wv[R], xv[MT];
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                wv[r] = load_stream(wrow[r] + base);
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                xv[m] = xrow[m][base];
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    acc[m * R + r] = dot8(wv[r], xv[m], acc[m * R + r]);
+                x[u][m] = load_x(xres, (unsigned)m * row_bytes + lane_off, so);
         }
+        // keep the scheduler from hoisting the previous stage's arithmetic
+        // above these loads: they must be in flight while it runs
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](const u32x4(&w)[U][R], const u32x4(&x)[U][MT]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    acc[m * R + r] = dot8(w[u][r], x[u][m], acc[m * R + r]);
+    };
+    // Loads inside the loop are unconditional: a load under a branch would
+    // leave the two paths with different counts of loads in flight, and the
+    // wait inserted at the join would then drain the whole pipeline.
+    if (stages > 0) {
+        load(wa, xa, 0);
+        int j = 0;
+        for (; j + 2 < stages; j += 2) {
+            load(wb, xb, j + 1);
+            compute(wa, xa);
+            load(wa, xa, j + 2);
+            compute(wb, xb);
+        }
+        if (j + 1 < stages) {
+            load(wb, xb, j + 1);
+            compute(wa, xa);
+            compute(wb, xb);
+        } else {
+            compute(wa, xa);
+        }
+    }
+    // remaining whole passes, then the partial pass (lanes past ke read zeros)
+    for (int p = stages * U; p * nthr < ke - kb; ++p) {
+        const bool ok = kb + tid + p * nthr < ke;
+        const unsigned so = (unsigned)p * pass_bytes;
+        u32x4 w[1][R], x[1][MT];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            w[0][r] = load_w(wres, ok ? (unsigned)r * row_bytes + lane_off : kOffOob, so);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            x[0][m] = load_x(xres, ok ? (unsigned)m * row_bytes + lane_off : kOffOob, so);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                acc[m * R + r] = dot8(w[0][r], x[0][m], acc[m * R + r]);
     }
 
     wave_reduce_transpose<V>(acc, lane);
@@ -337,16 +391,17 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
 
 // ---------------------------------------------------------------------------
 // MFMA kernel: token tile MT = 16 T (T = 1, 2, 4), rows per workgroup
-// NT = 16 RT, U K-steps in flight per wave.
+// NT = 16 RT, U K-steps per wave per pipeline stage.
 //
 // One K-step is 32 K (4 chunks).  In v_mfma_f32_16x16x32_bf16 lane l = 16 g + i
 // supplies A[i][8g .. 8g+7] and B[8g .. 8g+7][i]; here A row i is weight row
 // n0 + 16 rt + i and B column i is token 16 t + i, both at chunk 4 step + g,
 // so lane l loads 16 bytes of one weight row and 16 bytes of one token row.
-// Token columns >= M load zero (x rows >= M are never read).  Wave w of the
-// workgroup takes steps sb + w, sb + w + waves, ... (in-workgroup split-K);
-// the 16x16 fp32 results (lane l holds rows 4 (l / 16) .. +3 of column l % 16)
-// are summed over waves in LDS, laid out [wave][token][row] so that the final
+// Token columns >= M fall outside the x resource and load zeros.  Wave w of
+// the workgroup takes steps sb + w, sb + w + waves, ... (in-workgroup
+// split-K) through the same two-stage pipeline as the DOT2 kernel; the 16x16
+// fp32 results (lane l holds rows 4 (l / 16) .. +3 of column l % 16) are
+// summed over waves in LDS, laid out [wave][token][row] so that the final
 // stores of out[token][n0 + row] are row-contiguous.
 // ---------------------------------------------------------------------------
 template <int T, int RT, int U>
@@ -356,7 +411,8 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
     extern __shared__ float lds[];   // [waves][MT][NTP]
     __shared__ unsigned flag;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int nthr = blockDim.x, nwaves = nthr >> 6;
     int tile, s;
     block_coords(a, tile, s);
@@ -369,19 +425,13 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
     const int se = (int)(((long)(s + 1) * steps) / a.split);
     const int se_full = se < steps_full ? se : steps_full;
 
-    const u32x4 *W = static_cast<const u32x4 *>(a.W);
-    const u32x4 *X = static_cast<const u32x4 *>(a.x);
-    const u32x4 *arow[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-        arow[rt] = W + (long)min(n0 + 16 * rt + i16, a.N - 1) * a.K8 + g;
-    const u32x4 *brow[T];
-    bool bok[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        bok[t] = 16 * t + i16 < a.M;
-        brow[t] = X + (long)min(16 * t + i16, a.M - 1) * a.K8 + g;
-    }
+    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const int rows_valid = min(NT, a.N - n0);
+    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)n0 * row_bytes,
+                                (unsigned)rows_valid * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const unsigned k_off = (unsigned)(4 * (sb + wave) + g) * 16u;   // this lane's first chunk
+    const unsigned step_bytes = (unsigned)nwaves * 64u;             // one step of every wave
 
     f32x4 acc[RT][T];
 #pragma unroll
@@ -390,20 +440,26 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
         for (int t = 0; t < T; ++t)
             acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    int st = sb + wave;
-    for (; st + (U - 1) * nwaves < se_full; st += U * nwaves) {
-        u32x4 av[U][RT], bv[U][T];
+    // this wave's steps: sb + wave + nwaves * q, q = 0 .. qn - 1 (all full)
+    const int first = sb + wave;
+    const int qn = first < se_full ? (se_full - first + nwaves - 1) / nwaves : 0;
+    const int stages = qn / U;
+
+    u32x4 aa[U][RT], ba[U][T], ab[U][RT], bb[U][T];
+    auto load = [&](u32x4(&av)[U][RT], u32x4(&bv)[U][T], int j) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            const unsigned so = (unsigned)(j * U + u) * step_bytes;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-                av[u][rt] = load_stream(arow[rt] + 4 * (st + u * nwaves));
-#pragma unroll
-        for (int u = 0; u < U; ++u)
+                av[u][rt] = load_w(wres, (unsigned)(16 * rt + i16) * row_bytes + k_off, so);
 #pragma unroll
             for (int t = 0; t < T; ++t)
-                bv[u][t] = bok[t] ? brow[t][4 * (st + u * nwaves)] : zero;
+                bv[u][t] = load_x(xres, (unsigned)(16 * t + i16) * row_bytes + k_off, so);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // loads stay ahead of the MFMAs
+    };
+    auto compute = [&](const u32x4(&av)[U][RT], const u32x4(&bv)[U][T]) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -413,23 +469,41 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
                     acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8, av[u][rt]), __builtin_bit_cast(bf16x8, bv[u][t]),
                         acc[rt][t], 0, 0, 0);
+    };
+    if (stages > 0) {   // same pipeline shape as the DOT2 kernel
+        load(aa, ba, 0);
+        int j = 0;
+        for (; j + 2 < stages; j += 2) {
+            load(ab, bb, j + 1);
+            compute(aa, ba);
+            load(aa, ba, j + 2);
+            compute(ab, bb);
+        }
+        if (j + 1 < stages) {
+            load(ab, bb, j + 1);
+            compute(aa, ba);
+            compute(ab, bb);
+        } else {
+            compute(aa, ba);
+        }
     }
-    for (; st < se; st += nwaves) {
-        // remaining whole steps, and the partial last step when K8 % 4 != 0
-        const bool in = (4 * st + g) < a.K8;
-        u32x4 av[RT], bv[T];
+    // remaining whole steps, then the partial last step when K8 % 4 != 0
+    for (int q = stages * U; first + q * nwaves < se; ++q) {
+        const bool ok = 4 * (first + q * nwaves) + g < a.K8;
+        const unsigned so = (unsigned)q * step_bytes;
+        u32x4 av[1][RT], bv[1][T];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-            av[rt] = in ? load_stream(arow[rt] + 4 * st) : zero;
+            av[0][rt] = load_w(wres, ok ? (unsigned)(16 * rt + i16) * row_bytes + k_off : kOffOob, so);
 #pragma unroll
         for (int t = 0; t < T; ++t)
-            bv[t] = (in && bok[t]) ? brow[t][4 * st] : zero;
+            bv[0][t] = load_x(xres, ok ? (unsigned)(16 * t + i16) * row_bytes + k_off : kOffOob, so);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, av[rt]), __builtin_bit_cast(bf16x8, bv[t]),
+                    __builtin_bit_cast(bf16x8, av[0][rt]), __builtin_bit_cast(bf16x8, bv[0][t]),
                     acc[rt][t], 0, 0, 0);
     }
 
@@ -522,18 +596,35 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
 // ---------------------------------------------------------------------------
 
 #define SK_DOT2(MT, R, U) {SKINNY_PATH_DOT2, MT, R, U, (const void *)&k_dot2<MT, R, U>}
-#define SK_DOT2_U(MT, R) SK_DOT2(MT, R, 1), SK_DOT2(MT, R, 2), SK_DOT2(MT, R, 4)
 #define SK_MFMA(T, RT, U) {SKINNY_PATH_MFMA, 16 * T, 16 * RT, U, (const void *)&k_mfma<T, RT, U>}
-#define SK_MFMA_U(T, RT) SK_MFMA(T, RT, 1), SK_MFMA(T, RT, 2), SK_MFMA(T, RT, 4)
 
+// Instances whose double-buffered loads, accumulators and offsets fit in 256
+// VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
 static const KernelInfo kKernels[] = {
-    SK_DOT2_U(1, 1), SK_DOT2_U(1, 2), SK_DOT2_U(1, 4), SK_DOT2_U(1, 8), SK_DOT2_U(1, 16),
-    SK_DOT2_U(2, 1), SK_DOT2_U(2, 2), SK_DOT2_U(2, 4), SK_DOT2_U(2, 8), SK_DOT2_U(2, 16),
-    SK_DOT2_U(4, 1), SK_DOT2_U(4, 2), SK_DOT2_U(4, 4), SK_DOT2_U(4, 8), SK_DOT2_U(4, 16),
-    SK_DOT2_U(8, 1), SK_DOT2_U(8, 2), SK_DOT2_U(8, 4), SK_DOT2_U(8, 8),
-    SK_MFMA_U(1, 1), SK_MFMA_U(1, 2), SK_MFMA_U(1, 4),
-    SK_MFMA_U(2, 1), SK_MFMA_U(2, 2), SK_MFMA_U(2, 4),
-    SK_MFMA_U(4, 1), SK_MFMA_U(4, 2),
+    SK_DOT2(1, 1, 1), SK_DOT2(1, 1, 2), SK_DOT2(1, 1, 4),
+    SK_DOT2(1, 2, 1), SK_DOT2(1, 2, 2), SK_DOT2(1, 2, 4),
+    SK_DOT2(1, 4, 1), SK_DOT2(1, 4, 2), SK_DOT2(1, 4, 4),
+    SK_DOT2(1, 8, 1), SK_DOT2(1, 8, 2),
+    SK_DOT2(1, 16, 1),
+    SK_DOT2(2, 1, 1), SK_DOT2(2, 1, 2), SK_DOT2(2, 1, 4),
+    SK_DOT2(2, 2, 1), SK_DOT2(2, 2, 2), SK_DOT2(2, 2, 4),
+    SK_DOT2(2, 4, 1), SK_DOT2(2, 4, 2),
+    SK_DOT2(2, 8, 1),
+    SK_DOT2(4, 1, 1), SK_DOT2(4, 1, 2), SK_DOT2(4, 1, 4),
+    SK_DOT2(4, 2, 1), SK_DOT2(4, 2, 2),
+    SK_DOT2(4, 4, 1), SK_DOT2(4, 4, 2),
+    SK_DOT2(4, 8, 1),
+    SK_DOT2(8, 1, 1), SK_DOT2(8, 1, 2),
+    SK_DOT2(8, 2, 1),
+    SK_DOT2(8, 4, 1),
+    SK_MFMA(1, 1, 1), SK_MFMA(1, 1, 2), SK_MFMA(1, 1, 4),
+    SK_MFMA(1, 2, 1), SK_MFMA(1, 2, 2), SK_MFMA(1, 2, 4),
+    SK_MFMA(1, 4, 1), SK_MFMA(1, 4, 2),
+    SK_MFMA(2, 1, 1), SK_MFMA(2, 1, 2), SK_MFMA(2, 1, 4),
+    SK_MFMA(2, 2, 1), SK_MFMA(2, 2, 2), SK_MFMA(2, 2, 4),
+    SK_MFMA(2, 4, 1), SK_MFMA(2, 4, 2),
+    SK_MFMA(4, 1, 1), SK_MFMA(4, 1, 2),
+    SK_MFMA(4, 2, 1), SK_MFMA(4, 2, 2),
 };
 
 const KernelInfo *kernel_table(int *count)

@@ -273,6 +273,64 @@ skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
     return s;
 }
 
+// ---------------------------------------------------------------------------
+// Tuned tables persisted across processes (SKINNY_TABLE_CACHE=<file>), keyed
+// like the pages' per-part measured tables by the chip (arch, CU count) and
+// the shape.  One line per table:
+//   skinny-table v1 <arch> <cus> <N> <K> <bf16|f32> <64 x path.mt.rows.waves.unroll.split>
+// A line whose tactics fail validation is ignored.  Writers append.
+// ---------------------------------------------------------------------------
+const char *kTableTag = "skinny-table";
+
+bool load_table_file(const char *path, int cus, int N, int K, skinny_out_dtype od,
+                     std::array<skinny_tactic, SKINNY_MAX_M> &table)
+{
+    FILE *f = fopen(path, "r");
+    if (!f)
+        return false;
+    char line[8192];
+    bool found = false;
+    while (!found && fgets(line, sizeof line, f)) {
+        char tag[32], ver[8], arch[32], ods[8];
+        int c, n, k, pos = 0;
+        if (sscanf(line, "%31s %7s %31s %d %d %d %7s%n", tag, ver, arch, &c, &n, &k, ods, &pos) != 7)
+            continue;
+        if (strcmp(tag, kTableTag) || strcmp(ver, "v1") || strcmp(arch, "gfx950") || c != cus ||
+            n != N || k != K || strcmp(ods, od == SKINNY_OUT_F32 ? "f32" : "bf16"))
+            continue;
+        std::array<skinny_tactic, SKINNY_MAX_M> t;
+        const char *q = line + pos;
+        bool ok = true;
+        for (int m = 1; m <= SKINNY_MAX_M && ok; ++m) {
+            skinny_tactic &e = t[m - 1];
+            int used = 0;
+            ok = sscanf(q, " %d.%d.%d.%d.%d.%d%n", &e.path, &e.mt, &e.rows, &e.waves, &e.unroll,
+                        &e.split, &used) == 6 &&
+                 skinny_tactic_check(&e, N, K) == SKINNY_OK && e.mt >= m;
+            q += used;
+        }
+        if (ok) {
+            table = t;
+            found = true;
+        }
+    }
+    fclose(f);
+    return found;
+}
+
+void save_table_file(const char *path, int cus, int N, int K, skinny_out_dtype od,
+                     const std::array<skinny_tactic, SKINNY_MAX_M> &table)
+{
+    FILE *f = fopen(path, "a");
+    if (!f)
+        return;
+    fprintf(f, "%s v1 gfx950 %d %d %d %s", kTableTag, cus, N, K, od == SKINNY_OUT_F32 ? "f32" : "bf16");
+    for (const skinny_tactic &e : table)
+        fprintf(f, " %d.%d.%d.%d.%d.%d", e.path, e.mt, e.rows, e.waves, e.unroll, e.split);
+    fprintf(f, "\n");
+    fclose(f);
+}
+
 skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int dev, int nxcd,
                          const skinny_tactic *table, skinny_plan **out)
 {
@@ -393,12 +451,19 @@ skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype od, s
         std::lock_guard<std::mutex> lock(g_cache_mu);
         const Key key{dev, N, K, (int)od};
         auto it = g_cache.find(key);
+        const char *file = getenv("SKINNY_TABLE_CACHE");
         if (it != g_cache.end()) {
             table = it->second;
+        } else if (file && *file && load_table_file(file, cus, N, K, od, table)) {
+            if (env_flag("SKINNY_LOG"))
+                fprintf(stderr, "[skinny] N=%d K=%d: table loaded from %s\n", N, K, file);
+            g_cache[key] = table;
         } else {
             if ((s = tune(W, N, K, od, nxcd, table)) != SKINNY_OK)
                 return s;
             g_cache[key] = table;
+            if (file && *file)
+                save_table_file(file, cus, N, K, od, table);
         }
     }
     return build_plan(W, N, K, od, dev, nxcd, table.data(), plan);

@@ -123,13 +123,9 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                     const int per_split = k8 / s;
                     if (per_split < 64 * w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
                         continue;
-                    if (k.rows * k.unroll > 16)
-                        continue;
                 } else {
                     const int per_split = ((k8 + 3) / 4) / s;
                     if (per_split < w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
-                        continue;
-                    if ((k.rows / 16) * k.unroll > 8)
                         continue;
                 }
                 if (count < cap)

@@ -1,0 +1,114 @@
+"""Summaries of rocprofv3 output for the projection kernels.
+
+    python -m skinny_bf16_decode_amd.profiling TRACE_DIR FETCH_CSV WRITE_CSV OUT_MD OUT_JSON \
+        --command "..." --command "..."
+
+Reads the kernel-trace statistics (``*_kernel_stats.csv``) and the per-dispatch
+counter collections of a FETCH_SIZE run and a WRITE_SIZE run (KiB per
+dispatch).  Counter values are scaled by the ratio of the known bytes of a
+calibration kernel to what the counter reports for it: ``k_probe_read``
+streams exactly 2*N*K bytes of one weight copy (FETCH_SIZE), and a 64 MiB
+device-to-device copy writes exactly 64 MiB (WRITE_SIZE).  Writes a short
+Markdown summary and a JSON record of HBM bytes per projection launch, keyed
+by the SHA-256 of the kernel source so that a later kernel change voids it.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(HERE, "csrc", "kernels.hip")
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _short(name: str) -> str:
+    return (name.replace("(skinny::KArgs)", "").replace("skinny::", "")
+            .replace("void ", "").replace("unsigned int __vector(4) const*", "u32x4 const*"))
+
+
+def load_counters(path):
+    rows = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return rows
+
+
+def load_stats(trace_dir):
+    paths = glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))
+    if not paths:
+        raise FileNotFoundError(f"no kernel_stats.csv under {trace_dir}")
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(trace_dir, fetch_csv, write_csv, weight_bytes, copy_bytes=64 << 20):
+    stats = load_stats(trace_dir)
+    fetch = load_counters(fetch_csv)
+    write = load_counters(write_csv)
+    probe = [k for k in fetch if "k_probe_read" in k]
+    copy = [k for k in write if "copyBuffer" in k or "copy" in k.lower()]
+    fetch_scale = weight_bytes / 1024.0 / statistics.mean(fetch[probe[0]]) if probe else None
+    big_copy = [k for k in copy if max(write[k]) >= copy_bytes / 1024 * 0.5]
+    write_scale = (copy_bytes / 1024.0 / max(write[big_copy[0]])) if big_copy else None
+    kernels = {}
+    for k in fetch:
+        if "k_dot2" in k or "k_mfma" in k:
+            f = statistics.mean(fetch[k]) * (fetch_scale or float("nan"))
+            w = statistics.mean(write.get(k, [float("nan")])) * (write_scale or float("nan"))
+            kernels[_short(k)] = {"fetch_kib": round(f, 1), "write_kib": round(w, 1),
+                                  "dispatches": len(fetch[k])}
+    return stats, kernels, fetch_scale, write_scale
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("trace_dir")
+    ap.add_argument("fetch_csv")
+    ap.add_argument("write_csv")
+    ap.add_argument("out_md")
+    ap.add_argument("out_json")
+    ap.add_argument("--weight-bytes", type=int, default=2 * 6288 * 7168)
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--title", default="skinny projection, 6288x7168 M sweep")
+    args = ap.parse_args()
+    stats, kernels, fs, ws = summarize(args.trace_dir, args.fetch_csv, args.write_csv, args.weight_bytes)
+    lines = [f"# {args.title}", "", "Commands (run from the repository root):", ""]
+    lines += [f"    {c}" for c in args.command]
+    lines += ["", "## Kernel trace statistics (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        n = _short(r["Name"])
+        if "k_dot2" in n or "k_mfma" in n or "k_probe" in n:
+            lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+              f"FETCH_SIZE scale factor {fs:.4f} (k_probe_read streams exactly {args.weight_bytes} B); "
+              f"WRITE_SIZE scale factor {ws:.4f} (64 MiB device copy).", "",
+              "| kernel | dispatches | fetch KiB (scaled) | write KiB (scaled) |", "|---|---|---|---|"]
+    for n, v in sorted(kernels.items()):
+        lines.append(f"| `{n}` | {v['dispatches']} | {v['fetch_kib']:.1f} | {v['write_kib']:.1f} |")
+    os.makedirs(os.path.dirname(os.path.abspath(args.out_md)), exist_ok=True)
+    with open(args.out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    rec = {"kernel_source_sha256": kernel_source_sha(), "fetch_scale": fs, "write_scale": ws,
+           "kernels": kernels}
+    with open(args.out_json, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(args.out_md)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+"""The C ABI on the CPU: the library loads, exports every function the
+header declares, rejects bad arguments before touching the device, and the
+tactic logic (legality, candidate list, per-M table rule) behaves as stated.
+No kernel is launched here."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import skinny_bf16_decode_amd as sk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skinny.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(skinny_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert "skinny_prepare" in names and "skinny_run" in names
+    lib = sk.load_library()
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", sk.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (skinny_[a-z_0-9]+)$", out, flags=re.M))
+    assert set(names) <= exported, set(names) - exported
+
+
+def _prepare(ptr, n, k, od=0):
+    lib = sk.load_library()
+    plan = ctypes.c_void_p(123)
+    st = lib.skinny_prepare(ctypes.c_void_p(ptr), n, k, od, ctypes.byref(plan))
+    return st, plan
+
+
+@pytest.mark.parametrize("ptr,n,k,od,want", [
+    (0, 256, 512, 0, 1),            # W NULL
+    (0x1000, 0, 512, 0, 1),         # N <= 0
+    (0x1000, 256, 0, 0, 1),         # K <= 0
+    (0x1000, 256, 512, 7, 1),       # bad out dtype
+    (0x1000, 256, 513, 0, 2),       # K % 8
+    (0x1000, 65536, 65536, 0, 2),   # N*K >= 2^31
+    (0x1001, 256, 512, 0, 3),       # misaligned W
+    (0x1008, 256, 512, 1, 3),
+])
+def test_prepare_rejects_before_any_device_call(ptr, n, k, od, want):
+    st, plan = _prepare(ptr, n, k, od)
+    assert st == want, sk.last_error()
+    assert plan.value is None          # *plan cleared on failure
+    assert sk.last_error()
+
+
+def test_prepare_null_plan_pointer():
+    lib = sk.load_library()
+    assert lib.skinny_prepare(ctypes.c_void_p(0x1000), 16, 64, 0, None) == 1
+
+
+def test_run_argument_errors():
+    lib = sk.load_library()
+    assert lib.skinny_run(None, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000), 4, None) == 1
+    assert lib.skinny_supports(None, 4) == 0
+    assert lib.skinny_describe(None, 4, ctypes.create_string_buffer(8), 8) == 1
+
+
+def test_status_strings():
+    lib = sk.load_library()
+    for code in range(8):
+        assert lib.skinny_status_string(code)
+    assert lib.skinny_status_string(99) == b"unknown status"
+
+
+def T(*a):
+    return sk.Tactic(*a)
+
+
+def test_tactic_check_rules():
+    ok = [T(0, 8, 4, 4, 1, 1), T(0, 1, 16, 1, 1, 8), T(1, 64, 16, 4, 1, 2), T(1, 16, 64, 8, 2, 1)]
+    for t in ok:
+        sk.tactic_check(t, 6288, 7168)
+    bad = [T(0, 3, 1, 1, 1, 1),          # no such token tile
+           T(0, 8, 16, 1, 1, 1),         # mt * rows > 64
+           T(0, 1, 1, 3, 1, 1),          # waves not a power of two
+           T(0, 1, 1, 16, 1, 1),         # too many waves
+           T(0, 1, 1, 1, 3, 1),          # unroll
+           T(0, 1, 1, 1, 1, 0),          # split < 1
+           T(0, 1, 1, 1, 1, 17),         # split > 16
+           T(1, 16, 24, 1, 1, 1),        # rows not a multiple of 16
+           T(1, 64, 64, 8, 1, 1),        # LDS over the limit
+           T(2, 16, 16, 1, 1, 1)]        # no such path
+    for t in bad:
+        with pytest.raises(ValueError):
+            sk.tactic_check(t, 6288, 7168)
+    with pytest.raises(ValueError):
+        sk.tactic_check(T(0, 1, 1, 1, 1, 4), 16, 16)     # split > chunks of a row
+    with pytest.raises(ValueError):
+        sk.tactic_check(T(0, 1, 1, 1, 1, 1), 16, 12)     # K % 8
+
+
+def test_enumeration_is_legal_and_covers_every_tile():
+    for n, k in ((256, 512), (3584, 7168), (6288, 7168), (1536, 128), (7168, 18432), (200, 1032)):
+        cands = sk.enumerate_tactics(n, k)
+        assert cands, (n, k)
+        for t in cands:
+            sk.tactic_check(t, n, k)
+        assert {t.mt for t in cands} == {1, 2, 4, 8, 16, 32, 64}
+        assert len(set(cands)) == len(cands)
+    assert sk.load_library().skinny_enumerate_tactics(0, 64, None, 0) == -1
+
+
+def test_table_rule_with_a_fake_timer():
+    """table[M] = fastest candidate whose token tile >= M; ties to the
+    smaller tile, then the lower index; failed candidates are skipped."""
+    cands = sk.enumerate_tactics(6288, 7168)
+    # fake timer: cost grows with the tile, plus a per-candidate jitter
+    times = [10.0 + 0.1 * t.mt + 0.001 * ((i * 7919) % 101) for i, t in enumerate(cands)]
+    table = sk.select_table(cands, times)
+    for m in range(1, 65):
+        legal = [(times[i], cands[i].mt, i) for i in range(len(cands)) if cands[i].mt >= m]
+        want = cands[min(legal)[2]]
+        assert table[m - 1] == want, m
+        assert table[m - 1].mt >= m
+    # smallest tile >= M wins under a cost that grows with the tile
+    tiles = [1, 2, 4, 4, 8, 8, 8, 8] + [16] * 8 + [32] * 16 + [64] * 32
+    assert [t.mt for t in table] == tiles
+
+
+def test_table_rule_prefers_a_faster_bigger_tile_and_skips_failures():
+    a, b, c = T(0, 1, 1, 1, 1, 1), T(0, 8, 4, 1, 1, 1), T(1, 64, 16, 1, 1, 1)
+    table = sk.select_table([a, b, c], [5.0, 4.0, 9.0])
+    assert table[0] == b                     # tile 8 faster than tile 1 at M=1
+    assert all(t == c for t in table[8:])
+    table = sk.select_table([a, b, c], [5.0, -1.0, 9.0])   # b could not run
+    assert table[0] == a and table[1] == c
+    # equal times: the smaller tile
+    table = sk.select_table([c, b], [4.0, 4.0])
+    assert table[0] == b
+    with pytest.raises(ValueError):
+        sk.select_table([a], [1.0])          # nothing serves M = 2..64
+
+
+def test_python_binding_has_no_fallback(tmp_path):
+    """Loading from a path with no library raises instead of computing elsewhere."""
+    import importlib
+    mod = importlib.import_module("skinny_bf16_decode_amd")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError):
+            mod.load_library(str(tmp_path / "libskinny.so"))
+    finally:
+        mod._lib = saved

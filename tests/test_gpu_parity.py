@@ -201,7 +201,7 @@ def test_long_k_split_workload_sampled(sk):
     w = gu.dev_bf16(w_bits)
     plans = {"tuned": sk.Prepared(w, torch.bfloat16),
              "split4": sk.Prepared(w, torch.bfloat16, table=[
-                 sk.Tactic(0, 8, 4, 4, 2, 4) if m <= 8 else sk.Tactic(1, 64, 16, 4, 2, 4)
+                 sk.Tactic(0, 8, 4, 4, 1, 4) if m <= 8 else sk.Tactic(1, 64, 16, 4, 2, 4)
                  for m in range(1, 65)])}
     for m in wl.m_values:
         mi = rng.integers(0, m, size=4096)
@@ -285,3 +285,30 @@ def test_run_errors(sk):
     with pytest.raises(ValueError):
         sk.Prepared(w, torch.float32, table=[sk.Tactic(0, 1, 1, 1, 1, 1)] * 64)   # tile < M
     plan.close()
+
+
+def test_table_cache_file_round_trip(sk, tmp_path):
+    """SKINNY_TABLE_CACHE: a tuning process appends its table; a second
+    process loads it instead of tuning and chooses the same tactics."""
+    import os
+    import subprocess
+    path = tmp_path / "tables.txt"
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import numpy as np, torch, skinny_inputs as si, skinny_bf16_decode_amd as sk\n"
+        "from tests import gpu_util as gu\n"
+        "x, w = si.random_case(9, 1, 640, 2048)\n"
+        "plan = sk.Prepared(gu.dev_bf16(w), torch.bfloat16)\n"
+        "print('|'.join(repr(plan.tactic(m)) for m in range(1, 65)))\n"
+    ) % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))),)
+    env = dict(os.environ, SKINNY_TABLE_CACHE=str(path), SKINNY_LOG="1")
+    first = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240)
+    assert first.returncode == 0, first.stderr[-2000:]
+    assert "tuned N=640 K=2048" in first.stderr
+    lines = path.read_text().splitlines()
+    assert len(lines) == 1 and lines[0].startswith("skinny-table v1 gfx950 ")
+    second = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240)
+    assert second.returncode == 0, second.stderr[-2000:]
+    assert "table loaded from" in second.stderr and "tuned N=640" not in second.stderr
+    assert first.stdout.strip().splitlines()[-1] == second.stdout.strip().splitlines()[-1]
+    assert len(path.read_text().splitlines()) == 1
