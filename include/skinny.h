@@ -61,8 +61,13 @@ typedef enum {
 
 /* Kernel families. */
 typedef enum {
-    SKINNY_PATH_DOT2 = 0, /* v_dot2_f32_bf16, token tiles 1/2/4/8 */
-    SKINNY_PATH_MFMA = 1  /* v_mfma_f32_16x16x32_bf16, token tiles 16/32/64 */
+    SKINNY_PATH_DOT2 = 0,  /* v_dot2_f32_bf16, token tiles 1/2/4/8; waves split K */
+    SKINNY_PATH_MFMA = 1,  /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; waves split K */
+    SKINNY_PATH_DOT2X = 2, /* v_dot2_f32_bf16, tiles 1/2/4/8; waves own rows, x staged in LDS */
+    SKINNY_PATH_MFMAX = 3, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
+                              W re-laid out and x staged through LDS via registers */
+    SKINNY_PATH_MFMAD = 4  /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
+                              W and x streamed straight into LDS rings (direct-to-LDS loads) */
 } skinny_path;
 
 /*
@@ -76,10 +81,13 @@ typedef enum {
  */
 typedef struct {
     int path;   /* skinny_path */
-    int mt;     /* token tile: DOT2 1,2,4,8; MFMA 16,32,64 */
-    int rows;   /* weight rows per workgroup: DOT2 1..16 (mt*rows <= 64); MFMA 16,32,64 */
-    int waves;  /* wavefronts per workgroup, splitting K inside it: 1,2,4,8 */
-    int unroll; /* 16-byte weight loads in flight per lane per row: 1,2,4 */
+    int mt;     /* token tile: DOT2/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD 16,32,64 */
+    int rows;   /* weight rows per workgroup.  DOT2: 1..16 (mt*rows <= 64);
+                   MFMA: 16,32,64; DOT2X: waves * (1, 2 or 4); MFMAX, MFMAD: 16 * waves */
+    int waves;  /* wavefronts per workgroup: 1,2,4,8 */
+    int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
+                   (MFMAX: 1, its stage is fixed at 32 chunks; MFMAD: the depth of
+                   its LDS rings, 2..4 stages of 32 chunks) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16 */
 } skinny_tactic;
 
@@ -98,7 +106,8 @@ typedef struct {
  * and shape is loaded from it instead of tuning, and a freshly tuned table is
  * appended to it.  SKINNY_LOG=1 prints the chosen table, SKINNY_LOG=2 also
  * every candidate's time; SKINNY_TUNE_ITERS sets the timed launches per
- * candidate.
+ * candidate; SKINNY_XCD_REMAP=0 stops placing the split-K workgroups of a row
+ * tile on one XCD (a plan-time setting, for testing the exchange across XCDs).
  *
  * Synchronous.  Must not be called while the device is capturing a graph.
  * W is NOT copied: the plan keeps the pointer, W must stay allocated until
@@ -184,13 +193,14 @@ skinny_status skinny_select_table(const skinny_tactic *cand, const double *times
  * the same bytes achieves, and against the floor of an empty launch.
  *
  * skinny_probe_read -- read `bytes` bytes at `buf` (device, 16-byte aligned,
- * bytes % 16 == 0) with 16-byte nontemporal loads and write one fp32 partial
- * sum per workgroup to `sink` (device, at least skinny_probe_read_blocks()
- * floats), so the loads cannot be elided.  Asynchronous on `stream`.
+ * bytes % 16 == 0) with 16-byte nontemporal loads, one 64-lane workgroup per
+ * 4 KiB with all four of its loads in flight, and write fp32 partial sums to
+ * `sink` (device, skinny_probe_read_blocks() floats), so the loads cannot be
+ * elided.  Asynchronous on `stream`.
  */
 skinny_status skinny_probe_read(const void *buf, size_t bytes, float *sink, void *stream);
 
-/* Workgroups (and sink floats) skinny_probe_read launches. */
+/* Floats skinny_probe_read may write to its sink. */
 int skinny_probe_read_blocks(void);
 
 /* skinny_probe_empty -- launch one empty 64-lane workgroup on `stream`. */

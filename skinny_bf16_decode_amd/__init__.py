@@ -28,6 +28,10 @@ OUT_BF16 = 0
 OUT_F32 = 1
 PATH_DOT2 = 0
 PATH_MFMA = 1
+PATH_DOT2X = 2
+PATH_MFMAX = 3
+PATH_MFMAD = 4
+PATH_NAMES = {0: "dot2", 1: "mfma", 2: "dot2x", 3: "mfmax", 4: "mfmad"}
 
 STATUS = {
     0: "SKINNY_OK",
@@ -59,7 +63,7 @@ class Tactic(ctypes.Structure):
         return (self.path, self.mt, self.rows, self.waves, self.unroll, self.split)
 
     def __repr__(self):
-        p = "mfma" if self.path == PATH_MFMA else "dot2"
+        p = PATH_NAMES.get(self.path, str(self.path))
         return (f"Tactic({p}, mt={self.mt}, rows={self.rows}, waves={self.waves}, "
                 f"unroll={self.unroll}, split={self.split})")
 

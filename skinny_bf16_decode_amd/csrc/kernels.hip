@@ -185,14 +185,35 @@ __device__ __forceinline__ void wave_reduce_transpose(float *v, int lane)
 }
 
 // ---------------------------------------------------------------------------
-// Cross-workgroup split-K arrival.  Every thread of the workgroup calls it
-// after storing its partials.  Returns true in the workgroup that arrives
-// last for this tile; that workgroup then reads all partials.  The counter is
-// reset by the last arriver, so it is zero again when the kernel ends.
+// Cross-workgroup split-K exchange.
+//
+// Partials are written with agent-scope atomic stores and read back with
+// agent-scope atomic loads; on gfx950 these are the write-through / coherent
+// forms of the plain access (sc1), so no L2 writeback is needed to publish
+// them.  An agent-scope release fence would add one (buffer_wbl2), and those
+// writebacks serialise per XCD.  A workgroup publishes its partial, waits
+// until its own stores have completed (s_waitcnt vmcnt(0): the part of a
+// release that orders prior coherent stores), then bumps the tile's arrival
+// counter with an agent-scope atomic.  The workgroup that sees split - 1
+// arrivals before its own reads every partial in split order, so the sum is
+// deterministic, and resets the counter to zero for the next launch.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void publish_partial(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float read_partial(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Called by every thread of the workgroup after it published its partials.
 __device__ __forceinline__ bool split_arrive_last(const KArgs &a, int tile, unsigned *flag_lds)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // own partial stores done, L2 written back
+    wait_own_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned prev =
@@ -200,10 +221,7 @@ __device__ __forceinline__ bool split_arrive_last(const KArgs &a, int tile, unsi
         *flag_lds = (prev == (unsigned)(a.split - 1)) ? 1u : 0u;
     }
     __syncthreads();
-    const bool last = *flag_lds != 0;
-    if (last)
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see every partial
-    return last;
+    return *flag_lds != 0;
 }
 
 __device__ __forceinline__ void split_reset(const KArgs &a, int tile)
@@ -225,6 +243,12 @@ __device__ __forceinline__ void split_reset(const KArgs &a, int tile)
 // ---------------------------------------------------------------------------
 constexpr unsigned kOffOob = 0x7FFFFFF0u;
 constexpr int kCpolNt = 2;   // nontemporal
+
+// A value the caller knows is the same in every lane, made provably so.  The
+// row counts below come from HIP's min/max, whose results this compiler treats
+// as divergent; a buffer resource built from a "divergent" size is then
+// re-materialised lane by lane around every load.
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes)
 {
@@ -267,7 +291,7 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
     const int kb = (int)(((long)s * a.K8) / a.split);
     const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
     const unsigned row_bytes = (unsigned)a.K8 * 16u;
-    const int rows_valid = min(R, a.N - n0);
+    const int rows_valid = uniform_int(min(R, a.N - n0));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)n0 * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
     const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
@@ -365,24 +389,23 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
             store_out(a, m, n, total);
         return;
     }
-    // split-K: publish this workgroup's partial, the last arriver finalises
+    // split-K: publish this workgroup's partial, the last arriver finalises.
+    // Only wave 0 is left and it holds the whole partial, so the arrival is a
+    // wave-level one (no workgroup barrier once the other waves have exited).
     float *wsp = a.ws + (long)tile * a.split * V;
     if (tid < V)
-        wsp[(long)s * V + tid] = total;
-    // only wave 0 is left and it holds every partial of the tile, so its own
-    // release (wait for its stores, write L2 back) covers the whole partial
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        publish_partial(wsp + (long)s * V + tid, total);
+    wait_own_stores();
     unsigned prev = 0;
     if (lane == 0)
         prev = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev != (unsigned)(a.split - 1))
         return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (live) {
         float sum = 0.f;
         for (int j = 0; j < a.split; ++j)
-            sum += __builtin_nontemporal_load(wsp + (long)j * V + tid);
+            sum += read_partial(wsp + (long)j * V + tid);
         store_out(a, m, n, sum);
     }
     if (lane == 0)
@@ -426,7 +449,7 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
     const int se_full = se < steps_full ? se : steps_full;
 
     const unsigned row_bytes = (unsigned)a.K8 * 16u;
-    const int rows_valid = min(NT, a.N - n0);
+    const int rows_valid = uniform_int(min(NT, a.N - n0));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)n0 * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
     const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
@@ -540,7 +563,7 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
         float v = 0.f;
         for (int w = 0; w < nwaves; ++w)
             v += lds[((long)w * MT + tok) * NTP + row];
-        wsp[(long)s * E + e] = v;
+        publish_partial(wsp + (long)s * E + e, v);
     }
     if (!split_arrive_last(a, tile, &flag))
         return;
@@ -550,8 +573,464 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
             continue;
         float v = 0.f;
         for (int j = 0; j < a.split; ++j)
-            v += __builtin_nontemporal_load(wsp + (long)j * E + e);
+            v += read_partial(wsp + (long)j * E + e);
         store_out(a, tok, n0 + row, v);
+    }
+    split_reset(a, tile);
+}
+
+// ---------------------------------------------------------------------------
+// DOT2X kernel: token tile MT <= 8; each wave owns R rows of the workgroup's
+// row tile (waves * R rows), and the x slice of the workgroup's K range is
+// staged once in LDS, shared by all rows of the workgroup.
+//
+// Every wave streams its own rows over the whole K range of the split: lane
+// l takes chunks kb + l, kb + l + 64, ... of each of its R rows, so a
+// wave-wide load is 1 KiB of one row and U loads per row form U KiB
+// contiguous runs.  The x operands come from LDS (one ds_read per token and
+// chunk, reused over the R rows), which takes them off the vector-memory
+// path: only W flows through it.  No cross-wave reduction is needed; the
+// in-wave transposing reduction finishes each wave's R x MT outputs.
+// ---------------------------------------------------------------------------
+template <int MT, int R, int U>
+__global__ __launch_bounds__(512) void k_dot2x(KArgs a)
+{
+    constexpr int V = MT * R;
+    extern __shared__ u32x4 xs[];   // [MT][kr] chunks of x[0..MT)[kb..ke)
+    __shared__ unsigned flag;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nthr = blockDim.x, nwaves = nthr >> 6;
+    int tile, s;
+    block_coords(a, tile, s);
+    const int n_wg = tile * nwaves * R;        // first row of the workgroup
+    const int n0 = n_wg + wave * R;            // first row of this wave
+    const int kb = (int)(((long)s * a.K8) / a.split);
+    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int kr = ke - kb;
+    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const int rows_valid = uniform_int(max(0, min(R, a.N - n0)));
+    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
+                                (unsigned)rows_valid * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const unsigned lane_off = (unsigned)(kb + lane) * 16u;
+    constexpr unsigned kPass = 64u * 16u;      // one wave-wide pass: 64 chunks
+
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        acc[i] = 0.f;
+
+    const int passes = kr / 64;
+    const int stages = passes / U;
+    u32x4 wa[U][R], wb[U][R];
+    auto load = [&](u32x4(&w)[U][R], int j) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const unsigned so = (unsigned)(j * U + u) * kPass;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                w[u][r] = load_w(wres, (unsigned)r * row_bytes + lane_off, so);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](const u32x4(&w)[U][R], int j) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = lane + 64 * (j * U + u);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const u32x4 xv = xs[m * kr + c];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    acc[m * R + r] = dot8(w[u][r], xv, acc[m * R + r]);
+            }
+        }
+    };
+
+    // First weight stage in flight before the activations are staged.
+    if (stages > 0)
+        load(wa, 0);
+    {
+        const int total = MT * kr;
+        for (int q0 = tid; q0 < total; q0 += 8 * nthr) {
+            u32x4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = q0 + i * nthr;
+                const int m = q / kr, c = q - (q / kr) * kr;
+                v[i] = load_x(xres, q < total ? (unsigned)m * row_bytes + (unsigned)(kb + c) * 16u : kOffOob, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = q0 + i * nthr;
+                if (q < total)
+                    xs[q] = v[i];
+            }
+        }
+    }
+    __syncthreads();
+
+    if (stages > 0) {
+        int j = 0;
+        for (; j + 2 < stages; j += 2) {
+            load(wb, j + 1);
+            compute(wa, j);
+            load(wa, j + 2);
+            compute(wb, j + 1);
+        }
+        if (j + 1 < stages) {
+            load(wb, j + 1);
+            compute(wa, j);
+            compute(wb, j + 1);
+        } else {
+            compute(wa, j);
+        }
+    }
+    for (int p = stages * U; p * 64 < kr; ++p) {
+        const int c = lane + 64 * p;
+        const bool ok = c < kr;
+        const unsigned so = (unsigned)p * kPass;
+        u32x4 w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            w[r] = load_w(wres, ok ? (unsigned)r * row_bytes + lane_off : kOffOob, so);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const u32x4 xv = ok ? xs[m * kr + (ok ? c : 0)] : zero;   // index kept in range
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[m * R + r] = dot8(w[r], xv, acc[m * R + r]);
+        }
+    }
+
+    wave_reduce_transpose<V>(acc, lane);
+    constexpr int kLanesPerValue = 64 / V;
+    const bool holder = (lane & (kLanesPerValue - 1)) == 0;
+    const int idx = lane / kLanesPerValue;     // value index m * R + r
+    const int m = idx / R, r = idx - (idx / R) * R;
+    if (a.split == 1) {
+        if (holder && m < a.M && n0 + r < a.N)
+            store_out(a, m, n0 + r, acc[0]);
+        return;
+    }
+    const int E = nwaves * V;                  // partial values of the workgroup
+    float *wsp = a.ws + (long)tile * a.split * E;
+    if (holder)
+        publish_partial(wsp + (long)s * E + wave * V + idx, acc[0]);
+    if (!split_arrive_last(a, tile, &flag))
+        return;
+    for (int e = tid; e < E; e += nthr) {
+        const int w = e / V, i = e - (e / V) * V;
+        const int mm = i / R, rr = i - (i / R) * R, n = n_wg + w * R + rr;
+        if (mm >= a.M || n >= a.N)
+            continue;
+        float v = 0.f;
+        for (int j = 0; j < a.split; ++j)
+            v += read_partial(wsp + (long)j * E + e);
+        store_out(a, mm, n, v);
+    }
+    split_reset(a, tile);
+}
+
+// ---------------------------------------------------------------------------
+// MFMAX kernel: token tile MT = 16 T; NW waves each own 16 weight rows.
+//
+// The weight is loaded row-contiguously -- each wave-wide load covers two
+// rows x 512 bytes, full 128-byte lines -- into registers, one stage (32
+// chunks = 8 K-steps of 32) ahead, and re-laid out through a wave-private LDS
+// tile [16 rows][32 chunks] (row pitch 528 bytes, so the 16 rows of a column
+// fall on distinct banks) from which each lane reads its A fragment (row i,
+// chunk 4 step + g).  The x window [MT tokens][32 chunks] of the same stage is
+// loaded cooperatively by the workgroup into a double-buffered LDS tile and
+// read as B fragments.  Loading W with the 16-row MFMA pattern directly would
+// split every request into 64-byte halves of lines.
+// ---------------------------------------------------------------------------
+template <int T, int NW>
+__global__ __launch_bounds__(512) void k_mfmax(KArgs a)
+{
+    constexpr int MT = 16 * T;
+    constexpr int KW = kMfmaxChunks;           // chunks per stage
+    constexpr int PITCH = KW + 1;              // row pitch in 16-byte chunks
+    constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
+    static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
+    extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [2][MT][PITCH]
+    __shared__ unsigned flag;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tile, s;
+    block_coords(a, tile, s);
+    const int n_wg = tile * NW * 16;
+    const int n0 = n_wg + wave * 16;
+    const int kb = (int)(((long)s * a.K8) / a.split);
+    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int stages = (ke - kb + KW - 1) / KW;
+    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const int rows_valid = uniform_int(max(0, min(16, a.N - n0)));
+    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
+                                (unsigned)rows_valid * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    u32x4 *wl = sm + wave * 16 * PITCH;
+    u32x4 *xl = sm + NW * 16 * PITCH;
+
+    // weight loads: instruction q covers rows 2q + (lane >> 5), chunk lane & 31
+    const int wrow = lane >> 5, wcol = lane & 31;
+    const int i16 = lane & 15, g = lane >> 4;
+
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Two register buffers: while stage j is written to LDS and multiplied,
+    // the loads of stages j + 1 and j + 2 are in flight.
+    u32x4 wa[8], xa[XL], wb[8], xb[XL];
+    auto load = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
+        const int c = kb + j * KW + wcol;      // this lane's weight chunk
+        const bool wok = j < stages && c < ke;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            wv[q] = load_w(wres, wok ? (unsigned)(2 * q + wrow) * row_bytes + (unsigned)c * 16u : kOffOob, 0);
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            const int e = tid + 64 * NW * i;
+            const int tok = e / KW, cc = kb + j * KW + (e % KW);
+            const bool xok = j < stages && cc < ke;
+            xv[i] = load_x(xres, xok ? (unsigned)tok * row_bytes + (unsigned)cc * 16u : kOffOob, 0);
+        }
+    };
+    auto stage = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
+        u32x4 *xw = xl + (j & 1) * MT * PITCH;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            wl[(2 * q + wrow) * PITCH + wcol] = wv[q];
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            const int e = tid + 64 * NW * i;
+            xw[(e / KW) * PITCH + (e % KW)] = xv[i];
+        }
+        load(wv, xv, j + 2);                   // past the last stage: out of range, no access
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < KW / 4; ++st) {
+            const u32x4 av = wl[i16 * PITCH + 4 * st + g];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const u32x4 bv = xw[(16 * t + i16) * PITCH + 4 * st + g];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+            }
+        }
+    };
+    load(wa, xa, 0);
+    load(wb, xb, 1);
+    int j = 0;
+    for (; j + 1 < stages; j += 2) {
+        stage(wa, xa, j);
+        stage(wb, xb, j + 1);
+    }
+    if (j < stages)
+        stage(wa, xa, j);
+
+    // lane (g, i) holds rows 4g .. 4g+3 (of this wave's 16) of token 16 t + i
+    if (a.split == 1) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int tok = 16 * t + i16;
+            if (tok >= a.M)
+                continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + 4 * g + q;
+                if (n < a.N)
+                    store_out(a, tok, n, acc[t][q]);
+            }
+        }
+        return;
+    }
+    constexpr int E = NW * T * 4 * 64;         // partial values of the workgroup
+    float *wsp = a.ws + (long)tile * a.split * E;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
+    if (!split_arrive_last(a, tile, &flag))
+        return;
+    for (int e = tid; e < E; e += 64 * NW) {
+        const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
+        const int w = wt / T, t = wt - (wt / T) * T;
+        const int tok = 16 * t + (ln & 15), n = n_wg + 16 * w + 4 * (ln >> 4) + q;
+        if (tok >= a.M || n >= a.N)
+            continue;
+        float v = 0.f;
+        for (int j = 0; j < a.split; ++j)
+            v += read_partial(wsp + (long)j * E + e);
+        store_out(a, tok, n, v);
+    }
+    split_reset(a, tile);
+}
+
+// ---------------------------------------------------------------------------
+// MFMAD kernel: token tile MT = 16 T; NW waves each own 16 weight rows; the
+// weight and activation tiles stream straight into LDS rings D stages deep.
+//
+// A stage is 32 K-chunks (512 bytes of a row, 8 MFMA K-steps).  Loads use the
+// direct-to-LDS form of the 16-byte buffer load: lane l of a load writes LDS
+// bytes [16 l, 16 l + 16) of the load's destination, while its global address
+// is free.  Each load covers two rows: lanes 0-31 fill row 2q, lanes 32-63 row
+// 2q + 1, and the lane at LDS position p of row r fetches chunk p ^ r (r < 16),
+// so that the 16 rows of one K column sit in 16 different bank groups when
+// the MFMA fragments are read back (lane (g, i) reads row i, chunk 4 step + g,
+// at position (4 step + g) ^ i).  Loads past the end of a row range, of the
+// weight (rows >= N) or of x (tokens >= M) are out of the buffer resource and
+// write zeros.  The weight ring is private to each wave; the x ring is filled
+// cooperatively and shared, so one barrier per stage orders both its fill
+// and the reuse of its slots.  The loads of D - 1 stages are in flight while a
+// stage is multiplied, and none of it passes through registers.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, u32x4 *lds_dst, unsigned voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, voff, 0, 0, kCpolNt);
+}
+
+template <int T, int NW, int D>
+__global__ __launch_bounds__(512) void k_mfmad(KArgs a)
+{
+    constexpr int MT = 16 * T;
+    constexpr int KW = 32;                       // chunks per stage
+    constexpr int XI = MT / (2 * NW);            // x loads per wave per stage
+    static_assert(XI >= 1 && XI * 2 * NW == MT, "x tile must split evenly over the waves");
+    constexpr int WSLOT = 16 * KW;               // u32x4 per weight slot (8 KiB)
+    constexpr int XSLOT = MT * KW;               // u32x4 per x slot
+    extern __shared__ u32x4 sm[];                // [NW][D][WSLOT] then [D][XSLOT]
+    __shared__ unsigned flag;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tile, s;
+    block_coords(a, tile, s);
+    const int n_wg = tile * NW * 16;
+    const int n0 = n_wg + wave * 16;
+    const int kb = (int)(((long)s * a.K8) / a.split);
+    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int stages = (ke - kb + KW - 1) / KW;
+    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const int rows_valid = uniform_int(max(0, min(16, a.N - n0)));
+    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
+                                (unsigned)rows_valid * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    u32x4 *wring = sm + wave * D * WSLOT;
+    u32x4 *xring = sm + NW * D * WSLOT;
+
+    // DMA lane mapping: row (or token) parity from lane >> 5, LDS position from lane & 31
+    const int half = lane >> 5, pos = lane & 31;
+    const int i16 = lane & 15, g = lane >> 4;
+
+    // Stage j into slot j % D; chunks past the split (or stages past the last)
+    // get an out-of-range offset and land as zeros.  Every call issues exactly
+    // 8 + XI loads on every lane -- the waits below count on it -- so the
+    // validity test is a per-lane select, never a branch.
+    auto issue = [&](int j) {
+        const int slot = j % D;
+        const int cbase = kb + j * KW;
+        const int lim = j < stages ? ke : kb;    // no chunk is valid past the last stage
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 2 * q + half;
+            const int c = cbase + (pos ^ r);
+            const unsigned off = c < lim ? (unsigned)r * row_bytes + (unsigned)c * 16u : kOffOob;
+            dma16(wres, wring + slot * WSLOT + 2 * q * KW, off);
+        }
+#pragma unroll
+        for (int i = 0; i < XI; ++i) {
+            const int pair = wave + NW * i;        // tokens 2 pair, 2 pair + 1
+            const int tok = 2 * pair + half;
+            const int c = cbase + (pos ^ (tok & 15));
+            const unsigned off = c < lim ? (unsigned)tok * row_bytes + (unsigned)c * 16u : kOffOob;
+            dma16(xres, xring + slot * XSLOT + 2 * pair * KW, off);
+        }
+    };
+
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j)
+        issue(j);
+    for (int j = 0; j < stages; ++j) {
+        // this wave's loads of stage j are done once at most D - 2 stages remain outstanding
+        if constexpr (D == 2)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if constexpr (D == 3)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 + XI) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (8 + XI)) : "memory");
+        // Every wave's share of stage j has landed once all waves pass here.
+        // A bare barrier: __syncthreads would also wait for every load in
+        // flight (its release fence), draining the ring.  The asm is a
+        // compiler barrier too, so no LDS read moves above it.
+        asm volatile("s_barrier" ::: "memory");
+        issue(j + D - 1);                        // refills the slot stage j - 1 used
+        const u32x4 *wsl = wring + (j % D) * WSLOT;
+        const u32x4 *xsl = xring + (j % D) * XSLOT;
+#pragma unroll
+        for (int st = 0; st < KW / 4; ++st) {
+            const int p = (4 * st + g) ^ i16;
+            const u32x4 av = wsl[i16 * KW + p];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const u32x4 bv = xsl[(16 * t + i16) * KW + p];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may land after the wave ends
+
+    // lane (g, i) holds rows 4g .. 4g+3 (of this wave's 16) of token 16 t + i
+    if (a.split == 1) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int tok = 16 * t + i16;
+            if (tok >= a.M)
+                continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + 4 * g + q;
+                if (n < a.N)
+                    store_out(a, tok, n, acc[t][q]);
+            }
+        }
+        return;
+    }
+    constexpr int E = NW * T * 4 * 64;           // partial values of the workgroup
+    float *wsp = a.ws + (long)tile * a.split * E;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
+    if (!split_arrive_last(a, tile, &flag))
+        return;
+    for (int e = tid; e < E; e += 64 * NW) {
+        const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
+        const int w = wt / T, t = wt - (wt / T) * T;
+        const int tok = 16 * t + (ln & 15), n = n_wg + 16 * w + 4 * (ln >> 4) + q;
+        if (tok >= a.M || n >= a.N)
+            continue;
+        float v = 0.f;
+        for (int jj = 0; jj < a.split; ++jj)
+            v += read_partial(wsp + (long)jj * E + e);
+        store_out(a, tok, n, v);
     }
     split_reset(a, tile);
 }
@@ -560,30 +1039,29 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
 // Measurement probes: a plain streaming read of a buffer (what the weight
 // stream could reach with no arithmetic around it) and an empty launch.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_probe_read(const u32x4 *buf, long chunks, float *sink)
+// Each one-wave workgroup streams one 4 KiB span with its four 1 KiB loads in
+// flight at once -- the fastest plain-read shape measured on this chip.
+__global__ __launch_bounds__(64) void k_probe_read(const u32x4 *buf, long chunks, float *sink)
 {
-    const long stride = (long)gridDim.x * blockDim.x;
+    const long base = (long)blockIdx.x * 256;          // 256 chunks = 4 KiB per workgroup
+    const int lane = threadIdx.x;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const long c = base + i * 64 + lane;
+        v[i] = c < chunks ? load_stream(buf + c) : zero;
+    }
     float acc = 0.f;
-    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < chunks; i += 4 * stride) {
-        const u32x4 a = load_stream(buf + i), b = load_stream(buf + i + stride);
-        const u32x4 c = load_stream(buf + i + 2 * stride), d = load_stream(buf + i + 3 * stride);
-        const unsigned int a0 = a.x, b0 = b.y, c0 = c.z, d0 = d.w;
-        acc += __uint_as_float(a0 ^ b0) + __uint_as_float(c0 ^ d0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned int a0 = v[i].x, a3 = v[i].w;
+        acc += __uint_as_float(a0 ^ a3);
     }
-    for (; i < chunks; i += stride) {
-        const u32x4 a = load_stream(buf + i);
-        const unsigned int a0 = a.x;
-        acc += __uint_as_float(a0);
-    }
-    __shared__ float part[4];
     for (int off = 32; off > 0; off >>= 1)
         acc += __shfl_xor(acc, off);
-    if ((threadIdx.x & 63) == 0)
-        part[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        sink[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+    if (lane == 0)
+        sink[blockIdx.x & (kProbeSinkFloats - 1)] = acc;
 }
 
 __global__ void k_probe_empty() {}
@@ -597,6 +1075,9 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
 
 #define SK_DOT2(MT, R, U) {SKINNY_PATH_DOT2, MT, R, U, (const void *)&k_dot2<MT, R, U>}
 #define SK_MFMA(T, RT, U) {SKINNY_PATH_MFMA, 16 * T, 16 * RT, U, (const void *)&k_mfma<T, RT, U>}
+#define SK_DOT2X(MT, R, U) {SKINNY_PATH_DOT2X, MT, R, U, (const void *)&k_dot2x<MT, R, U>}
+#define SK_MFMAX(T, NW) {SKINNY_PATH_MFMAX, 16 * T, NW, 1, (const void *)&k_mfmax<T, NW>}
+#define SK_MFMAD(T, NW, D) {SKINNY_PATH_MFMAD, 16 * T, NW, D, (const void *)&k_mfmad<T, NW, D>}
 
 // Instances whose double-buffered loads, accumulators and offsets fit in 256
 // VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
@@ -625,6 +1106,19 @@ static const KernelInfo kKernels[] = {
     SK_MFMA(2, 4, 1), SK_MFMA(2, 4, 2),
     SK_MFMA(4, 1, 1), SK_MFMA(4, 1, 2),
     SK_MFMA(4, 2, 1), SK_MFMA(4, 2, 2),
+    // DOT2X: rows field = rows per wave
+    SK_DOT2X(1, 1, 2), SK_DOT2X(1, 1, 4), SK_DOT2X(1, 2, 2), SK_DOT2X(1, 2, 4), SK_DOT2X(1, 4, 2),
+    SK_DOT2X(2, 1, 2), SK_DOT2X(2, 1, 4), SK_DOT2X(2, 2, 2), SK_DOT2X(2, 2, 4), SK_DOT2X(2, 4, 2),
+    SK_DOT2X(4, 1, 2), SK_DOT2X(4, 1, 4), SK_DOT2X(4, 2, 2), SK_DOT2X(4, 2, 4), SK_DOT2X(4, 4, 2),
+    SK_DOT2X(8, 1, 2), SK_DOT2X(8, 1, 4), SK_DOT2X(8, 2, 2), SK_DOT2X(8, 2, 4), SK_DOT2X(8, 4, 2),
+    // MFMAX: rows field = waves (16 rows each)
+    SK_MFMAX(1, 1), SK_MFMAX(1, 2), SK_MFMAX(1, 4), SK_MFMAX(1, 8),
+    SK_MFMAX(2, 2), SK_MFMAX(2, 4), SK_MFMAX(2, 8),
+    SK_MFMAX(4, 4), SK_MFMAX(4, 8),
+    // MFMAD: rows field = waves (16 rows each), unroll field = pipeline depth
+    SK_MFMAD(1, 2, 4), SK_MFMAD(1, 4, 3), SK_MFMAD(1, 8, 2),
+    SK_MFMAD(2, 2, 4), SK_MFMAD(2, 4, 2), SK_MFMAD(2, 4, 3),
+    SK_MFMAD(4, 2, 3), SK_MFMAD(4, 4, 2),
 };
 
 const KernelInfo *kernel_table(int *count)

@@ -80,26 +80,71 @@ skinny_status hip_fail(hipError_t e, const char *what)
             return hip_fail(e_, #expr);                 \
     } while (0)
 
-Entry make_entry(const skinny_tactic &t, int N)
+Entry make_entry(const skinny_tactic &t, int N, int K)
 {
     Entry en;
-    const KernelInfo *k = find_kernel(t.path, t.mt, t.rows, t.unroll);
+    const KernelInfo *k = tactic_kernel(t);
     en.fn = k ? k->fn : nullptr;
     en.n_tiles = tiles_for(t, N);
     en.grid = (unsigned)(en.n_tiles * t.split);
     en.block = (unsigned)(64 * t.waves);
-    en.lds = (unsigned)tactic_lds_bytes(t);
+    en.lds = (unsigned)tactic_lds_bytes(t, K / 8);
     en.t = t;
     return en;
 }
 
+// Let the LDS-staged kernels use more than the default 64 KiB of dynamic LDS
+// (gfx950 has 160 KiB per CU).  Once per process; failures only make the
+// largest tactics fail to launch, which the tuner skips.
+void raise_lds_limits()
+{
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int dev = 0, max_lds = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return;
+        int nk = 0;
+        const KernelInfo *ks = kernel_table(&nk);
+        for (int i = 0; i < nk; ++i)
+            if (ks[i].path == SKINNY_PATH_DOT2X || ks[i].path == SKINNY_PATH_MFMAX ||
+                ks[i].path == SKINNY_PATH_MFMAD)
+                (void)hipFuncSetAttribute(ks[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+        (void)hipGetLastError();
+    });
+}
+
 size_t ws_floats(const Entry &en) { return en.t.split > 1 ? (size_t)en.n_tiles * en.t.split * en.t.mt * en.t.rows : 0; }
+
+// Static LDS of a kernel plus the device's per-workgroup limit, looked up
+// once per kernel.  A dispatch over the limit would abort the queue, so
+// launches that would exceed it are refused here instead.
+bool lds_fits(const void *fn, unsigned dynamic_bytes)
+{
+    static std::mutex mu;
+    static std::map<const void *, size_t> static_lds;
+    static int max_lds = -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (max_lds < 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            max_lds = 64 * 1024;
+    }
+    auto it = static_lds.find(fn);
+    if (it == static_lds.end()) {
+        hipFuncAttributes attr{};
+        const size_t st = hipFuncGetAttributes(&attr, fn) == hipSuccess ? attr.sharedSizeBytes : kStaticLdsReserve;
+        it = static_lds.emplace(fn, st).first;
+    }
+    return it->second + dynamic_bytes <= (size_t)max_lds;
+}
 
 hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
 {
     a.n_tiles = en.n_tiles;
     a.split = en.t.split;
-    a.remap = en.t.split > 1 ? 1 : 0;
+    a.remap = (en.t.split > 1 && a.nxcd > 1) ? 1 : 0;
     void *params[] = {&a};
     return hipLaunchKernel(en.fn, dim3(en.grid), dim3(en.block), params, en.lds, stream);
 }
@@ -183,7 +228,7 @@ skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
     int copies = (int)std::min<size_t>(16, std::max<size_t>(1, (cold + wbytes - 1) / wbytes));
     size_t max_ws = 0, max_tiles = 0;
     for (const skinny_tactic &t : cand) {
-        Entry en = make_entry(t, N);
+        Entry en = make_entry(t, N, K);
         max_ws = std::max(max_ws, ws_floats(en));
         max_tiles = std::max(max_tiles, (size_t)en.n_tiles);
     }
@@ -228,7 +273,9 @@ skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
     const int iters = std::max(1, env_int("SKINNY_TUNE_ITERS", 2 * copies > 8 ? 2 * copies : 8));
     std::vector<double> times(count, -1.0);
     for (int i = 0; i < count; ++i) {
-        const Entry en = make_entry(cand[i], N);
+        const Entry en = make_entry(cand[i], N, K);
+        if (!en.fn || !lds_fits(en.fn, en.lds))
+            continue;
         a.M = cand[i].mt;
         a.W = wcopies.p;
         if (launch(en, a, st) != hipSuccess) {
@@ -262,8 +309,8 @@ skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
     skinny_status s = skinny_select_table(cand.data(), times.data(), count, table.data());
     if (env_int("SKINNY_LOG", 0) >= 2) {
         for (int i = 0; i < count; ++i)
-            fprintf(stderr, "[skinny] cand N=%d K=%d %s mt=%d rows=%d waves=%d unroll=%d split=%d : %.3f us\n",
-                    N, K, cand[i].path == SKINNY_PATH_MFMA ? "mfma" : "dot2", cand[i].mt, cand[i].rows,
+            fprintf(stderr, "[skinny] cand N=%d K=%d path=%d mt=%d rows=%d waves=%d unroll=%d split=%d : %.3f us\n",
+                    N, K, cand[i].path, cand[i].mt, cand[i].rows,
                     cand[i].waves, cand[i].unroll, cand[i].split, times[i]);
     }
     if (s == SKINNY_OK && env_flag("SKINNY_LOG")) {
@@ -356,7 +403,13 @@ skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int d
     p->od = od;
     size_t max_ws = 0, max_tiles = 0;
     for (int m = 1; m <= SKINNY_MAX_M; ++m) {
-        p->e[m] = make_entry(table[m - 1], N);
+        p->e[m] = make_entry(table[m - 1], N, K);
+        if (!p->e[m].fn || !lds_fits(p->e[m].fn, p->e[m].lds)) {
+            set_error("table entry for M=%d needs %u bytes of dynamic LDS, more than the device allows "
+                      "with the kernel's static LDS", m, p->e[m].lds);
+            delete p;
+            return SKINNY_ERR_INVALID_ARG;
+        }
         max_ws = std::max(max_ws, ws_floats(p->e[m]));
         if (table[m - 1].split > 1)
             max_tiles = std::max(max_tiles, (size_t)p->e[m].n_tiles);
@@ -387,7 +440,9 @@ skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int d
     a.N = N;
     a.K8 = K / 8;
     a.out_f32 = od == SKINNY_OUT_F32;
-    a.nxcd = nxcd;
+    // SKINNY_XCD_REMAP=0 turns off the placement of a tile's split-K
+    // workgroups on one XCD (then the partial exchange crosses XCDs).
+    a.nxcd = env_int("SKINNY_XCD_REMAP", 1) ? nxcd : 1;
 
     // Warm every distinct kernel the table uses, on scratch x/out, so that no
     // code object loads lazily inside a later graph capture.
@@ -445,6 +500,7 @@ skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype od, s
     int dev = 0, cus = 0;
     if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)
         return s;
+    raise_lds_limits();
     const int nxcd = cus % 8 == 0 ? 8 : 1;
     std::array<skinny_tactic, SKINNY_MAX_M> table;
     {
@@ -490,6 +546,7 @@ skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dty
     int dev = 0, cus = 0;
     if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)
         return s;
+    raise_lds_limits();
     return build_plan(W, N, K, od, dev, cus % 8 == 0 ? 8 : 1, table, plan);
 }
 
@@ -550,9 +607,10 @@ skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len
         return SKINNY_ERR_INVALID_ARG;
     }
     const Entry &en = p->e[M];
+    static const char *const kNames[] = {"dot2", "mfma16x16x32", "dot2x", "mfmax16x16x32", "mfmad16x16x32"};
     snprintf(buf, len, "%s mt=%d rows=%d waves=%d unroll=%d split=%d grid=%u block=%u lds=%u",
-             t.path == SKINNY_PATH_MFMA ? "mfma16x16x32" : "dot2", t.mt, t.rows, t.waves, t.unroll,
-             t.split, en.grid, en.block, en.lds);
+             (t.path >= 0 && t.path <= 4) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
+             en.grid, en.block, en.lds);
     return SKINNY_OK;
 }
 
@@ -576,7 +634,7 @@ void skinny_destroy(skinny_plan *p)
     delete p;
 }
 
-int skinny_probe_read_blocks(void) { return kProbeReadBlocks; }
+int skinny_probe_read_blocks(void) { return kProbeSinkFloats; }
 
 skinny_status skinny_probe_read(const void *buf, size_t bytes, float *sink, void *stream)
 {
@@ -589,9 +647,14 @@ skinny_status skinny_probe_read(const void *buf, size_t bytes, float *sink, void
         return SKINNY_ERR_ALIGN;
     }
     long chunks = (long)(bytes / 16);
+    const long blocks = (chunks + 255) / 256;
+    if (blocks < 1 || blocks > 0x7FFFFFFF) {
+        set_error("probe_read: %zu bytes out of range", bytes);
+        return SKINNY_ERR_INVALID_ARG;
+    }
     void *params[] = {&buf, &chunks, &sink};
-    hipError_t e = hipLaunchKernel(probe_read_fn(), dim3(kProbeReadBlocks), dim3(kProbeReadThreads),
-                                   params, 0, (hipStream_t)stream);
+    hipError_t e = hipLaunchKernel(probe_read_fn(), dim3((unsigned)blocks), dim3(64), params, 0,
+                                   (hipStream_t)stream);
     return e == hipSuccess ? SKINNY_OK : hip_fail(e, "hipLaunchKernel(probe_read)");
 }
 

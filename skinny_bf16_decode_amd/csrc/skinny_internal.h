@@ -37,14 +37,17 @@ struct KernelInfo {
 const KernelInfo *kernel_table(int *count);
 const KernelInfo *find_kernel(int path, int mt, int rows, int unroll);
 
+// The compiled instance a tactic runs (KernelInfo.rows is rows per workgroup
+// for DOT2/MFMA, rows per wave for DOT2X, waves for MFMAX), or nullptr.
+const KernelInfo *tactic_kernel(const skinny_tactic &t);
+
 // Measurement probe kernels (host stub addresses).
 const void *probe_read_fn();
 const void *probe_empty_fn();
-constexpr int kProbeReadBlocks = 2048;
-constexpr int kProbeReadThreads = 256;
+constexpr int kProbeSinkFloats = 4096;   // power of two; sink[] size of skinny_probe_read
 
-// Dynamic LDS bytes a tactic needs.
-size_t tactic_lds_bytes(const skinny_tactic &t);
+// Dynamic LDS bytes a tactic needs for rows of K8 16-byte chunks.
+size_t tactic_lds_bytes(const skinny_tactic &t, int K8);
 
 // Thread-local error text.
 void set_error(const char *fmt, ...);
@@ -53,6 +56,16 @@ void set_error(const char *fmt, ...);
 inline int tiles_for(const skinny_tactic &t, int N) { return (N + t.rows - 1) / t.rows; }
 
 constexpr int kMaxWaves = 8;
-constexpr size_t kMaxLds = 60 * 1024;
+constexpr size_t kMaxLds = 60 * 1024;          // in-WG split-K paths (DOT2, MFMA)
+// LDS-staged paths (DOT2X, MFMAX, MFMAD) may use a CU's whole 160 KiB, less a
+// reserve for the kernels' own static __shared__ variables: a dispatch whose
+// static + dynamic LDS exceeds the device limit is not rejected at launch but
+// aborts the queue.  Launches are also checked against the exact static size.
+constexpr size_t kStaticLdsReserve = 1024;
+constexpr size_t kMaxLdsStaged = 160 * 1024 - kStaticLdsReserve;
+constexpr int kMfmaxChunks = 32;               // K chunks per MFMAX stage
+inline size_t mfmax_lds_bytes(int waves, int mt) { return (size_t)(16 * waves + 2 * mt) * (kMfmaxChunks + 1) * 16; }
+// MFMAD: per wave `depth` weight slots of 16 rows x 32 chunks, plus `depth` x slots of mt x 32 chunks
+inline size_t mfmad_lds_bytes(int waves, int mt, int depth) { return (size_t)depth * (16 * waves + mt) * 32 * 16; }
 
 }  // namespace skinny

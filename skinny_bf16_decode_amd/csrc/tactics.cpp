@@ -19,11 +19,43 @@ void set_error(const char *fmt, ...)
     va_end(ap);
 }
 
-size_t tactic_lds_bytes(const skinny_tactic &t)
+size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
 {
-    if (t.path == SKINNY_PATH_MFMA)
+    switch (t.path) {
+    case SKINNY_PATH_MFMA:
         return (size_t)t.waves * t.mt * (t.rows + 1) * sizeof(float);
-    return 0;
+    case SKINNY_PATH_DOT2X:
+        return (size_t)t.mt * ((K8 + t.split - 1) / t.split) * 16;
+    case SKINNY_PATH_MFMAX:
+        return mfmax_lds_bytes(t.waves, t.mt);
+    case SKINNY_PATH_MFMAD:
+        return mfmad_lds_bytes(t.waves, t.mt, t.unroll);
+    default:
+        return 0;
+    }
+}
+
+const KernelInfo *tactic_kernel(const skinny_tactic &t)
+{
+    switch (t.path) {
+    case SKINNY_PATH_DOT2:
+    case SKINNY_PATH_MFMA:
+        return find_kernel(t.path, t.mt, t.rows, t.unroll);
+    case SKINNY_PATH_DOT2X:
+        if (t.waves < 1 || t.rows % t.waves)
+            return nullptr;
+        return find_kernel(t.path, t.mt, t.rows / t.waves, t.unroll);
+    case SKINNY_PATH_MFMAX:
+        if (t.rows != 16 * t.waves || t.unroll != 1)
+            return nullptr;
+        return find_kernel(t.path, t.mt, t.waves, 1);
+    case SKINNY_PATH_MFMAD:
+        if (t.rows != 16 * t.waves)
+            return nullptr;
+        return find_kernel(t.path, t.mt, t.waves, t.unroll);
+    default:
+        return nullptr;
+    }
 }
 
 static bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -70,7 +102,8 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
         set_error("split=%d: must be 1..16", t->split);
         return SKINNY_ERR_INVALID_ARG;
     }
-    if (t->path == SKINNY_PATH_DOT2) {
+    if (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_DOT2X || t->path == SKINNY_PATH_MFMAX ||
+        t->path == SKINNY_PATH_MFMAD) {
         if (t->split > k8) {
             set_error("split=%d exceeds the %d 16-byte chunks of a row", t->split, k8);
             return SKINNY_ERR_INVALID_ARG;
@@ -81,15 +114,16 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             set_error("split=%d exceeds the %d 32-element K steps of a row", t->split, steps);
             return SKINNY_ERR_INVALID_ARG;
         }
-        if (tactic_lds_bytes(*t) > kMaxLds) {
-            set_error("MFMA tactic needs %zu bytes of LDS (limit %zu)", tactic_lds_bytes(*t), kMaxLds);
-            return SKINNY_ERR_INVALID_ARG;
-        }
     } else {
-        set_error("path=%d: must be 0 (DOT2) or 1 (MFMA)", t->path);
+        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX) or 4 (MFMAD)", t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
-    if (!find_kernel(t->path, t->mt, t->rows, t->unroll)) {
+    const size_t lds_limit = (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
+    if (tactic_lds_bytes(*t, k8) > lds_limit) {
+        set_error("tactic needs %zu bytes of LDS (limit %zu)", tactic_lds_bytes(*t, k8), lds_limit);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (!tactic_kernel(*t)) {
         set_error("no compiled kernel for path=%d mt=%d rows=%d unroll=%d", t->path, t->mt, t->rows,
                   t->unroll);
         return SKINNY_ERR_INVALID_ARG;
@@ -106,15 +140,22 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
     int nk = 0;
     const KernelInfo *ks = kernel_table(&nk);
     static const int kWaves[] = {1, 2, 4, 8};
-    static const int kSplits[] = {1, 2, 4, 8};
+    static const int kSplits[] = {1, 2, 3, 4, 5, 6, 8};
     for (int i = 0; i < nk; ++i) {
         const KernelInfo &k = ks[i];
         for (int w : kWaves) {
             for (int s : kSplits) {
                 skinny_tactic t = {k.path, k.mt, k.rows, w, k.unroll, s};
+                if (k.path == SKINNY_PATH_DOT2X)
+                    t.rows = k.rows * w;                 // k.rows is rows per wave
+                if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD) {
+                    if (w != k.rows)                     // k.rows is the wave count
+                        continue;
+                    t.rows = 16 * w;
+                }
                 if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                     continue;
-                const int tiles = (N + k.rows - 1) / k.rows;
+                const int tiles = (N + t.rows - 1) / t.rows;
                 if (s > 1 && tiles * w >= 8 * 256)
                     continue;   // enough waves already; a K split only adds traffic
                 if (k.path == SKINNY_PATH_DOT2) {
@@ -122,6 +163,13 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                     // split, and the unrolled loop should run at least once
                     const int per_split = k8 / s;
                     if (per_split < 64 * w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
+                        continue;
+                } else if (k.path == SKINNY_PATH_DOT2X) {
+                    // every wave streams the whole split: one full pipeline stage at least
+                    if (k8 / s < 64 * k.unroll)
+                        continue;
+                } else if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD) {
+                    if (k8 / s < 2 * kMfmaxChunks)
                         continue;
                 } else {
                     const int per_split = ((k8 + 3) / 4) / s;

@@ -312,3 +312,25 @@ def test_table_cache_file_round_trip(sk, tmp_path):
     assert "table loaded from" in second.stderr and "tuned N=640" not in second.stderr
     assert first.stdout.strip().splitlines()[-1] == second.stdout.strip().splitlines()[-1]
     assert len(path.read_text().splitlines()) == 1
+
+
+@pytest.mark.parametrize("remap", ["1", "0"])
+def test_split_k_exchange_exact(sk, remap, monkeypatch):
+    """Every split-K candidate, with the split workgroups of a tile placed on
+    one XCD (default) and dealt over all XCDs (SKINNY_XCD_REMAP=0): the
+    partial exchange must still be exact on integer inputs, and the arrival
+    counters must be back at zero (a second call gives the same bits)."""
+    import torch
+    monkeypatch.setenv("SKINNY_XCD_REMAP", remap)
+    n, k = 392, 4096
+    x_bits, w_bits = si.small_int_case(31, 64, n, k)
+    o, _ = oracle.gemm(x_bits, w_bits)
+    w = gu.dev_bf16(w_bits)
+    tactics = [t for t in sk.enumerate_tactics(n, k) if t.split > 1]
+    _say(f"[split remap={remap}] {len(tactics)} tactics")
+    assert {t.path for t in tactics} == {0, 1, 2, 3, 4}
+    for t in tactics:
+        plan = sk.Prepared(w, torch.float32, table=gu.forced_table(t))
+        for rep in range(2):
+            _check_exact(sk, plan, x_bits, o, t.mt, f"{t} remap={remap} call {rep}")
+        plan.close()
