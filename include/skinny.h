@@ -66,8 +66,11 @@ typedef enum {
     SKINNY_PATH_DOT2X = 2, /* v_dot2_f32_bf16, tiles 1/2/4/8; waves own rows, x staged in LDS */
     SKINNY_PATH_MFMAX = 3, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
                               W re-laid out and x staged through LDS via registers */
-    SKINNY_PATH_MFMAD = 4  /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
+    SKINNY_PATH_MFMAD = 4, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
                               W and x streamed straight into LDS rings (direct-to-LDS loads) */
+    SKINNY_PATH_MFMAS = 5  /* MFMAD under a stream-K schedule: one workgroup per slot the chip
+                              holds at once, each taking an equal share of (row tile, K stage)
+                              units; split must be 1 */
 } skinny_path;
 
 /*
@@ -81,13 +84,13 @@ typedef enum {
  */
 typedef struct {
     int path;   /* skinny_path */
-    int mt;     /* token tile: DOT2/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD 16,32,64 */
+    int mt;     /* token tile: DOT2/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD/MFMAS 16,32,64 */
     int rows;   /* weight rows per workgroup.  DOT2: 1..16 (mt*rows <= 64);
-                   MFMA: 16,32,64; DOT2X: waves * (1, 2 or 4); MFMAX, MFMAD: 16 * waves */
+                   MFMA: 16,32,64; DOT2X: waves * (1, 2 or 4); MFMAX, MFMAD, MFMAS: 16 * waves */
     int waves;  /* wavefronts per workgroup: 1,2,4,8 */
     int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
-                   (MFMAX: 1, its stage is fixed at 32 chunks; MFMAD: the depth of
-                   its LDS rings, 2..4 stages of 32 chunks) */
+                   (MFMAX: 1, its stage is fixed at 32 chunks; MFMAD, MFMAS: the
+                   depth of their LDS rings, 2..4 stages of 32 chunks) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16 */
 } skinny_tactic;
 

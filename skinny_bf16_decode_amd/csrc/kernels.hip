@@ -1036,6 +1036,199 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// MFMAS kernel: the MFMAD pipeline under a stream-K schedule.
+//
+// The work is the flat list of units (row tile t, K stage k), t < n_tiles,
+// k < spt = ceil(K / 256), and workgroup g of G takes units [g U / G,
+// (g + 1) U / G) -- the same amount of weight for every workgroup, and G is
+// the number of workgroups that fit on the chip at once, so no CU idles and
+// no workgroup waits for a second round.  The DMA pipeline runs through the
+// whole range, across tile boundaries; the accumulators are flushed at the
+// end of every tile segment.  A segment that covers its whole tile is stored
+// directly.  A tile cut by a range boundary is shared by consecutive
+// workgroups: each publishes its partial in slot (g - first workgroup of the
+// tile) and, after its loop, arrives on the tile's counter; the last to
+// arrive sums the slots in order (deterministic) and stores.  Only the first
+// and the last segment of a workgroup can be cut.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int sk_owner(unsigned u, unsigned units, unsigned G)
+{
+    // the workgroup whose range [g U / G, (g + 1) U / G) contains unit u
+    return (int)((((unsigned long long)u + 1) * G - 1) / units);
+}
+
+template <int T, int NW, int D>
+__global__ __launch_bounds__(512) void k_mfmas(KArgs a)
+{
+    constexpr int MT = 16 * T;
+    constexpr int KW = 32;
+    constexpr int XI = MT / (2 * NW);
+    static_assert(XI >= 1 && XI * 2 * NW == MT, "x tile must split evenly over the waves");
+    constexpr int WSLOT = 16 * KW, XSLOT = MT * KW;
+    constexpr int E = NW * T * 4 * 64;           // partial values of a tile
+    extern __shared__ u32x4 sm[];
+    __shared__ unsigned last_flag[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned G = gridDim.x, gi = blockIdx.x;
+    const int spt = a.sk_spt;
+    const unsigned units = (unsigned)a.n_tiles * (unsigned)spt;
+    const unsigned u0 = (unsigned)(((unsigned long long)gi * units) / G);
+    const unsigned u1 = (unsigned)(((unsigned long long)(gi + 1) * units) / G);
+    const int count = (int)(u1 - u0);
+    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    u32x4 *wring = sm + wave * D * WSLOT;
+    u32x4 *xring = sm + NW * D * WSLOT;
+    const int half = lane >> 5, pos = lane & 31;
+    const int i16 = lane & 15, g = lane >> 4;
+
+    // issue pointer: the unit the next issue() loads
+    int is_tile = (int)(u0 / (unsigned)spt), is_step = (int)(u0 % (unsigned)spt);
+    int issued = 0;
+    auto issue = [&]() {
+        const int j = issued++;
+        const bool live = j < count;
+        const int slot = j % D;
+        const int n0 = is_tile * NW * 16 + wave * 16;
+        const int rows_valid = uniform_int(live ? max(0, min(16, a.N - n0)) : 0);
+        const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
+                                    (unsigned)rows_valid * row_bytes);
+        const int cbase = is_step * KW;
+        const int lim = live ? a.K8 : 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 2 * q + half;
+            const int c = cbase + (pos ^ r);
+            const unsigned off = c < lim ? (unsigned)r * row_bytes + (unsigned)c * 16u : kOffOob;
+            dma16(wres, wring + slot * WSLOT + 2 * q * KW, off);
+        }
+#pragma unroll
+        for (int i = 0; i < XI; ++i) {
+            const int pair = wave + NW * i;
+            const int tok = 2 * pair + half;
+            const int c = cbase + (pos ^ (tok & 15));
+            const unsigned off = c < lim ? (unsigned)tok * row_bytes + (unsigned)c * 16u : kOffOob;
+            dma16(xres, xring + slot * XSLOT + 2 * pair * KW, off);
+        }
+        if (++is_step == spt) {
+            is_step = 0;
+            ++is_tile;
+        }
+    };
+
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // compute pointer and the (at most two) cut segments this workgroup publishes
+    int c_tile = is_tile, c_step = is_step, seg_start = is_step;
+    int cut_tile[2] = {-1, -1};
+    int ncut = 0;
+
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j)
+        issue();
+    for (int j = 0; j < count; ++j) {
+        if constexpr (D == 2)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if constexpr (D == 3)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 + XI) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (8 + XI)) : "memory");
+        asm volatile("s_barrier" ::: "memory");
+        issue();
+        const u32x4 *wsl = wring + (j % D) * WSLOT;
+        const u32x4 *xsl = xring + (j % D) * XSLOT;
+#pragma unroll
+        for (int st = 0; st < KW / 4; ++st) {
+            const int p = (4 * st + g) ^ i16;
+            const u32x4 av = wsl[i16 * KW + p];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const u32x4 bv = xsl[(16 * t + i16) * KW + p];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+            }
+        }
+        const bool seg_end = c_step == spt - 1 || j == count - 1;
+        if (seg_end) {
+            const int n0 = c_tile * NW * 16 + wave * 16;
+            if (seg_start == 0 && c_step == spt - 1) {
+                // the whole tile is ours: store it
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int tok = 16 * t + i16;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = n0 + 4 * g + q;
+                        if (tok < a.M && n < a.N)
+                            store_out(a, tok, n, acc[t][q]);
+                    }
+                }
+            } else {
+                const int part = (int)gi - sk_owner((unsigned)c_tile * spt, units, G);
+                float *wsp = a.ws + ((long)c_tile * a.sk_parts + part) * E;
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        publish_partial(wsp + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
+                cut_tile[ncut < 2 ? ncut : 1] = c_tile;
+                ++ncut;
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (++c_step == spt) {
+            c_step = 0;
+            ++c_tile;
+        }
+        if (seg_end)
+            seg_start = c_step;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // partials published, no DMA in flight
+    __syncthreads();
+    if (tid == 0) {
+        for (int k = 0; k < 2; ++k) {
+            last_flag[k] = 0;
+            if (k < ncut) {
+                const int t = cut_tile[k];
+                const int parts = sk_owner((unsigned)(t + 1) * spt - 1, units, G) -
+                                  sk_owner((unsigned)t * spt, units, G) + 1;
+                const unsigned prev =
+                    __hip_atomic_fetch_add(a.ctr + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last_flag[k] = prev == (unsigned)(parts - 1) ? (unsigned)parts : 0u;
+            }
+        }
+    }
+    __syncthreads();
+    for (int k = 0; k < 2 && k < ncut; ++k) {
+        const int parts = (int)last_flag[k];
+        if (!parts)
+            continue;
+        const int t = cut_tile[k];
+        const float *wsp = a.ws + (long)t * a.sk_parts * E;
+        for (int e = tid; e < E; e += 64 * NW) {
+            const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
+            const int w = wt / T, tt = wt - (wt / T) * T;
+            const int tok = 16 * tt + (ln & 15), n = t * NW * 16 + 16 * w + 4 * (ln >> 4) + q;
+            if (tok >= a.M || n >= a.N)
+                continue;
+            float v = 0.f;
+            for (int pp = 0; pp < parts; ++pp)
+                v += read_partial(wsp + (long)pp * E + e);
+            store_out(a, tok, n, v);
+        }
+        if (tid == 0)
+            __hip_atomic_store(a.ctr + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Measurement probes: a plain streaming read of a buffer (what the weight
 // stream could reach with no arithmetic around it) and an empty launch.
 // ---------------------------------------------------------------------------
@@ -1078,6 +1271,7 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
 #define SK_DOT2X(MT, R, U) {SKINNY_PATH_DOT2X, MT, R, U, (const void *)&k_dot2x<MT, R, U>}
 #define SK_MFMAX(T, NW) {SKINNY_PATH_MFMAX, 16 * T, NW, 1, (const void *)&k_mfmax<T, NW>}
 #define SK_MFMAD(T, NW, D) {SKINNY_PATH_MFMAD, 16 * T, NW, D, (const void *)&k_mfmad<T, NW, D>}
+#define SK_MFMAS(T, NW, D) {SKINNY_PATH_MFMAS, 16 * T, NW, D, (const void *)&k_mfmas<T, NW, D>}
 
 // Instances whose double-buffered loads, accumulators and offsets fit in 256
 // VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
@@ -1119,6 +1313,10 @@ static const KernelInfo kKernels[] = {
     SK_MFMAD(1, 2, 4), SK_MFMAD(1, 4, 3), SK_MFMAD(1, 8, 2),
     SK_MFMAD(2, 2, 4), SK_MFMAD(2, 4, 2), SK_MFMAD(2, 4, 3),
     SK_MFMAD(4, 2, 3), SK_MFMAD(4, 4, 2),
+    // MFMAS: rows field = waves, unroll field = pipeline depth; stream-K grid
+    SK_MFMAS(1, 1, 4), SK_MFMAS(1, 2, 2), SK_MFMAS(1, 2, 3), SK_MFMAS(1, 2, 4), SK_MFMAS(1, 4, 2),
+    SK_MFMAS(1, 4, 3), SK_MFMAS(2, 1, 3), SK_MFMAS(2, 2, 2), SK_MFMAS(2, 2, 3), SK_MFMAS(2, 4, 2),
+    SK_MFMAS(4, 2, 2), SK_MFMAS(4, 2, 3), SK_MFMAS(4, 4, 2),
 };
 
 const KernelInfo *kernel_table(int *count)

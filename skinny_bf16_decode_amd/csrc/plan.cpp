@@ -33,6 +33,7 @@ struct Entry {
     const void *fn = nullptr;
     unsigned grid = 0, block = 0, lds = 0;
     int n_tiles = 0;
+    int sk_spt = 0, sk_parts = 0;   // stream-K: stages per tile, partial slots per tile
     skinny_tactic t{};
 };
 
@@ -80,6 +81,39 @@ skinny_status hip_fail(hipError_t e, const char *what)
             return hip_fail(e_, #expr);                 \
     } while (0)
 
+int device_cus()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 1;
+    return cus;
+}
+
+// Stream-K grid and partial slots: as many workgroups as fit on the chip at
+// once (at most one per unit), and for each tile the number of workgroups
+// whose unit range meets it -- the same owner formula the kernel uses.
+void stream_k_shape(Entry &en, int K)
+{
+    const unsigned spt = (unsigned)((K / 8 + kMfmaxChunks - 1) / kMfmaxChunks);
+    const unsigned units = (unsigned)en.n_tiles * spt;
+    int per_cu = 0;
+    if (!en.fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, en.fn, (int)en.block, en.lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    (void)hipGetLastError();
+    unsigned G = (unsigned)(per_cu * device_cus());
+    if (G > units)
+        G = units;
+    auto owner = [&](unsigned u) { return (int)((((unsigned long long)u + 1) * G - 1) / units); };
+    int parts = 1;
+    for (int t = 0; t < en.n_tiles; ++t)
+        parts = std::max(parts, owner((unsigned)(t + 1) * spt - 1) - owner((unsigned)t * spt) + 1);
+    en.grid = G;
+    en.sk_spt = (int)spt;
+    en.sk_parts = parts;
+}
+
 Entry make_entry(const skinny_tactic &t, int N, int K)
 {
     Entry en;
@@ -90,6 +124,8 @@ Entry make_entry(const skinny_tactic &t, int N, int K)
     en.block = (unsigned)(64 * t.waves);
     en.lds = (unsigned)tactic_lds_bytes(t, K / 8);
     en.t = t;
+    if (t.path == SKINNY_PATH_MFMAS)
+        stream_k_shape(en, K);
     return en;
 }
 
@@ -108,13 +144,20 @@ void raise_lds_limits()
         const KernelInfo *ks = kernel_table(&nk);
         for (int i = 0; i < nk; ++i)
             if (ks[i].path == SKINNY_PATH_DOT2X || ks[i].path == SKINNY_PATH_MFMAX ||
-                ks[i].path == SKINNY_PATH_MFMAD)
+                ks[i].path == SKINNY_PATH_MFMAD || ks[i].path == SKINNY_PATH_MFMAS)
                 (void)hipFuncSetAttribute(ks[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         (void)hipGetLastError();
     });
 }
 
-size_t ws_floats(const Entry &en) { return en.t.split > 1 ? (size_t)en.n_tiles * en.t.split * en.t.mt * en.t.rows : 0; }
+size_t ws_floats(const Entry &en)
+{
+    if (en.t.path == SKINNY_PATH_MFMAS)
+        return (size_t)en.n_tiles * en.sk_parts * en.t.mt * en.t.rows;
+    return en.t.split > 1 ? (size_t)en.n_tiles * en.t.split * en.t.mt * en.t.rows : 0;
+}
+
+bool uses_counters(const Entry &en) { return en.t.split > 1 || en.t.path == SKINNY_PATH_MFMAS; }
 
 // Static LDS of a kernel plus the device's per-workgroup limit, looked up
 // once per kernel.  A dispatch over the limit would abort the queue, so
@@ -145,6 +188,8 @@ hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
     a.n_tiles = en.n_tiles;
     a.split = en.t.split;
     a.remap = (en.t.split > 1 && a.nxcd > 1) ? 1 : 0;
+    a.sk_spt = en.sk_spt;
+    a.sk_parts = en.sk_parts;
     void *params[] = {&a};
     return hipLaunchKernel(en.fn, dim3(en.grid), dim3(en.block), params, en.lds, stream);
 }
@@ -411,7 +456,7 @@ skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int d
             return SKINNY_ERR_INVALID_ARG;
         }
         max_ws = std::max(max_ws, ws_floats(p->e[m]));
-        if (table[m - 1].split > 1)
+        if (uses_counters(p->e[m]))
             max_tiles = std::max(max_tiles, (size_t)p->e[m].n_tiles);
     }
     auto fail = [&](skinny_status s) {
@@ -607,9 +652,10 @@ skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len
         return SKINNY_ERR_INVALID_ARG;
     }
     const Entry &en = p->e[M];
-    static const char *const kNames[] = {"dot2", "mfma16x16x32", "dot2x", "mfmax16x16x32", "mfmad16x16x32"};
+    static const char *const kNames[] = {"dot2", "mfma16x16x32", "dot2x", "mfmax16x16x32", "mfmad16x16x32",
+                                         "mfmas16x16x32"};
     snprintf(buf, len, "%s mt=%d rows=%d waves=%d unroll=%d split=%d grid=%u block=%u lds=%u",
-             (t.path >= 0 && t.path <= 4) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
+             (t.path >= 0 && t.path <= 5) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
              en.grid, en.block, en.lds);
     return SKINNY_OK;
 }

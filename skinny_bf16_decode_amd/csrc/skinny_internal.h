@@ -25,6 +25,10 @@ struct KArgs {
     int out_f32;        // 1: fp32 output, 0: BF16
     int nxcd;           // XCDs the dispatcher deals workgroups over
     int remap;          // 1: place the split-K workgroups of a tile on one XCD
+    // stream-K schedule (MFMAS): units = n_tiles * sk_spt stages of 32 chunks,
+    // dealt evenly over gridDim.x workgroups; sk_parts partial slots per tile
+    int sk_spt;
+    int sk_parts;
 };
 
 // A compiled kernel instance.

@@ -29,6 +29,7 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
     case SKINNY_PATH_MFMAX:
         return mfmax_lds_bytes(t.waves, t.mt);
     case SKINNY_PATH_MFMAD:
+    case SKINNY_PATH_MFMAS:
         return mfmad_lds_bytes(t.waves, t.mt, t.unroll);
     default:
         return 0;
@@ -50,6 +51,7 @@ const KernelInfo *tactic_kernel(const skinny_tactic &t)
             return nullptr;
         return find_kernel(t.path, t.mt, t.waves, 1);
     case SKINNY_PATH_MFMAD:
+    case SKINNY_PATH_MFMAS:
         if (t.rows != 16 * t.waves)
             return nullptr;
         return find_kernel(t.path, t.mt, t.waves, t.unroll);
@@ -102,8 +104,12 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
         set_error("split=%d: must be 1..16", t->split);
         return SKINNY_ERR_INVALID_ARG;
     }
+    if (t->path == SKINNY_PATH_MFMAS && t->split != 1) {
+        set_error("split=%d: the stream-K path schedules K itself, split must be 1", t->split);
+        return SKINNY_ERR_INVALID_ARG;
+    }
     if (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_DOT2X || t->path == SKINNY_PATH_MFMAX ||
-        t->path == SKINNY_PATH_MFMAD) {
+        t->path == SKINNY_PATH_MFMAD || t->path == SKINNY_PATH_MFMAS) {
         if (t->split > k8) {
             set_error("split=%d exceeds the %d 16-byte chunks of a row", t->split, k8);
             return SKINNY_ERR_INVALID_ARG;
@@ -115,7 +121,7 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             return SKINNY_ERR_INVALID_ARG;
         }
     } else {
-        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX) or 4 (MFMAD)", t->path);
+        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD) or 5 (MFMAS)", t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
     const size_t lds_limit = (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
@@ -148,11 +154,13 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                 skinny_tactic t = {k.path, k.mt, k.rows, w, k.unroll, s};
                 if (k.path == SKINNY_PATH_DOT2X)
                     t.rows = k.rows * w;                 // k.rows is rows per wave
-                if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD) {
+                if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD || k.path == SKINNY_PATH_MFMAS) {
                     if (w != k.rows)                     // k.rows is the wave count
                         continue;
                     t.rows = 16 * w;
                 }
+                if (k.path == SKINNY_PATH_MFMAS && s != 1)
+                    continue;
                 if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                     continue;
                 const int tiles = (N + t.rows - 1) / t.rows;
@@ -168,7 +176,8 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                     // every wave streams the whole split: one full pipeline stage at least
                     if (k8 / s < 64 * k.unroll)
                         continue;
-                } else if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD) {
+                } else if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD ||
+                           k.path == SKINNY_PATH_MFMAS) {
                     if (k8 / s < 2 * kMfmaxChunks)
                         continue;
                 } else {

@@ -334,3 +334,45 @@ def test_split_k_exchange_exact(sk, remap, monkeypatch):
         for rep in range(2):
             _check_exact(sk, plan, x_bits, o, t.mt, f"{t} remap={remap} call {rep}")
         plan.close()
+
+
+def test_stream_k_repeats_and_graph_replays(sk):
+    """The stream-K path shares cut tiles between workgroups through arrival
+    counters; they must be back at zero after every call, so repeated calls
+    and graph replays give bit-identical results, within the bound."""
+    import torch
+    n, k = 1000, 5120
+    x_bits, w_bits = si.random_case(91, 64, n, k)
+    o, s = oracle.gemm(x_bits, w_bits)
+    w = gu.dev_bf16(w_bits)
+    x = gu.dev_bf16(x_bits)
+    cands = [t for t in sk.enumerate_tactics(n, k) if t.path == sk.PATH_MFMAS]
+    assert cands
+    for t in cands:
+        plan = sk.Prepared(w, torch.bfloat16, table=gu.forced_table(t))
+        outs = {m: gu.out_buffer(n, torch.bfloat16) for m in (t.mt - 5, t.mt)}
+        ref = {}
+        for m, out in outs.items():
+            plan.run(x[:m], out[:m])
+            torch.cuda.synchronize()
+            ref[m] = gu.host_bits(out).copy()
+            _bound_check(si.bf16_bits_to_f32(ref[m][:m]).astype(np.float64), o[:m], s[:m], "bf16",
+                         f"{t} M={m}")
+            assert gu.sentinel_intact(out, m)
+        stream = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for m, out in outs.items():
+                    plan.run(x[:m], out[:m])
+        for rep in range(4):
+            for m in outs:
+                outs[m][:m].fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for m in outs:
+                assert np.array_equal(gu.host_bits(outs[m]), ref[m]), (t, rep, m)
+        del g
+        plan.close()
