@@ -208,6 +208,34 @@ __device__ __forceinline__ float read_partial(const float *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The last arriver's sum of a thread's N output values over the partial
+// slots: v[i] = sum over p < parts, in slot order from 0, of slot p at
+// offset off[i] (slots `stride` floats apart).  The loads of four slots are
+// all issued before the first add, so the reduction costs ceil(parts / 4)
+// memory round trips instead of parts x N.
+template <int N>
+__device__ __forceinline__ void sum_partials(const float *wsp, long stride, int parts, const int (&off)[N],
+                                             float (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = 0.f;
+    for (int p0 = 0; p0 < parts; p0 += 4) {
+        float r[4][N];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                r[k][i] = p0 + k < parts ? read_partial(wsp + (long)(p0 + k) * stride + off[i]) : 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (p0 + k < parts)
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    v[i] += r[k][i];
+    }
+}
+
 __device__ __forceinline__ void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Called by every thread of the workgroup after it published its partials.
@@ -249,6 +277,17 @@ constexpr int kCpolNt = 2;   // nontemporal
 // as divergent; a buffer resource built from a "divergent" size is then
 // re-materialised lane by lane around every load.
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A per-lane offset that is either a real offset or kOffOob.  Passing it
+// through an empty asm keeps it a plain select: otherwise this compiler may
+// split the load into two branch arms (one per offset), and the branches
+// bring their own waits on every load in flight.
+__device__ __forceinline__ unsigned lane_off(bool ok, unsigned off)
+{
+    unsigned r = ok ? off : kOffOob;
+    asm volatile("" : "+v"(r));
+    return r;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes)
 {
@@ -403,10 +442,10 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
     if (prev != (unsigned)(a.split - 1))
         return;
     if (live) {
-        float sum = 0.f;
-        for (int j = 0; j < a.split; ++j)
-            sum += read_partial(wsp + (long)j * V + tid);
-        store_out(a, m, n, sum);
+        const int off[1] = {tid};
+        float sum[1];
+        sum_partials<1>(wsp, V, a.split, off, sum);
+        store_out(a, m, n, sum[0]);
     }
     if (lane == 0)
         __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -567,14 +606,20 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
     }
     if (!split_arrive_last(a, tile, &flag))
         return;
-    for (int e = tid; e < E; e += nthr) {
-        const int tok = e / NT, row = e - (e / NT) * NT;
-        if (tok >= mlim || n0 + row >= a.N)
-            continue;
-        float v = 0.f;
-        for (int j = 0; j < a.split; ++j)
-            v += read_partial(wsp + (long)j * E + e);
-        store_out(a, tok, n0 + row, v);
+    for (int e0 = tid; e0 < E; e0 += 4 * nthr) {
+        int off[4];
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            off[i] = min(e0 + i * nthr, E - 1);
+        sum_partials<4>(wsp, E, a.split, off, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = e0 + i * nthr;
+            const int tok = e / NT, row = e - (e / NT) * NT;
+            if (e < E && tok < mlim && n0 + row < a.N)
+                store_out(a, tok, n0 + row, v[i]);
+        }
     }
     split_reset(a, tile);
 }
@@ -722,17 +767,47 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
         publish_partial(wsp + (long)s * E + wave * V + idx, acc[0]);
     if (!split_arrive_last(a, tile, &flag))
         return;
-    for (int e = tid; e < E; e += nthr) {
-        const int w = e / V, i = e - (e / V) * V;
-        const int mm = i / R, rr = i - (i / R) * R, n = n_wg + w * R + rr;
-        if (mm >= a.M || n >= a.N)
-            continue;
-        float v = 0.f;
-        for (int j = 0; j < a.split; ++j)
-            v += read_partial(wsp + (long)j * E + e);
-        store_out(a, mm, n, v);
+    for (int e0 = tid; e0 < E; e0 += 4 * nthr) {
+        int off[4];
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            off[k] = min(e0 + k * nthr, E - 1);
+        sum_partials<4>(wsp, E, a.split, off, v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = e0 + k * nthr;
+            const int w = e / V, i = e - (e / V) * V;
+            const int mm = i / R, rr = i - (i / R) * R, n = n_wg + w * R + rr;
+            if (e < E && mm < a.M && n < a.N)
+                store_out(a, mm, n, v[k]);
+        }
     }
     split_reset(a, tile);
+}
+
+// The last arriver of a tile whose partials are MFMA accumulator fragments
+// (value e = ((wave T + t) 4 + q) 64 + lane: token 16 t + lane % 16, row
+// 16 wave + 4 (lane / 16) + q of the tile) sums the slots and stores.
+template <int T, int NW>
+__device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, const float *wsp, int E, int parts, int n_wg)
+{
+    constexpr int EPT = 4 * T;                 // values per thread: E = 64 NW EPT
+    int off[EPT];
+    float v[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+        off[i] = (int)threadIdx.x + 64 * NW * i;
+    sum_partials<EPT>(wsp, E, parts, off, v);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = off[i];
+        const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
+        const int w = wt / T, t = wt - (wt / T) * T;
+        const int tok = 16 * t + (ln & 15), n = n_wg + 16 * w + 4 * (ln >> 4) + q;
+        if (tok < a.M && n < a.N)
+            store_out(a, tok, n, v[i]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -861,17 +936,7 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
             publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
     if (!split_arrive_last(a, tile, &flag))
         return;
-    for (int e = tid; e < E; e += 64 * NW) {
-        const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
-        const int w = wt / T, t = wt - (wt / T) * T;
-        const int tok = 16 * t + (ln & 15), n = n_wg + 16 * w + 4 * (ln >> 4) + q;
-        if (tok >= a.M || n >= a.N)
-            continue;
-        float v = 0.f;
-        for (int j = 0; j < a.split; ++j)
-            v += read_partial(wsp + (long)j * E + e);
-        store_out(a, tok, n, v);
-    }
+    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg);
     split_reset(a, tile);
 }
 
@@ -1021,35 +1086,37 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
             publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
     if (!split_arrive_last(a, tile, &flag))
         return;
-    for (int e = tid; e < E; e += 64 * NW) {
-        const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
-        const int w = wt / T, t = wt - (wt / T) * T;
-        const int tok = 16 * t + (ln & 15), n = n_wg + 16 * w + 4 * (ln >> 4) + q;
-        if (tok >= a.M || n >= a.N)
-            continue;
-        float v = 0.f;
-        for (int jj = 0; jj < a.split; ++jj)
-            v += read_partial(wsp + (long)jj * E + e);
-        store_out(a, tok, n, v);
-    }
+    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg);
     split_reset(a, tile);
 }
 
 // ---------------------------------------------------------------------------
-// MFMAS kernel: the MFMAD pipeline under a stream-K schedule.
+// MFMAS kernel: token tile MT = 16 T, NW waves each own 16 rows of a
+// 16 NW-row tile, under a stream-K schedule, with U weight stages in flight
+// in registers.
 //
 // The work is the flat list of units (row tile t, K stage k), t < n_tiles,
 // k < spt = ceil(K / 256), and workgroup g of G takes units [g U / G,
-// (g + 1) U / G) -- the same amount of weight for every workgroup, and G is
-// the number of workgroups that fit on the chip at once, so no CU idles and
-// no workgroup waits for a second round.  The DMA pipeline runs through the
-// whole range, across tile boundaries; the accumulators are flushed at the
-// end of every tile segment.  A segment that covers its whole tile is stored
-// directly.  A tile cut by a range boundary is shared by consecutive
-// workgroups: each publishes its partial in slot (g - first workgroup of the
-// tile) and, after its loop, arrives on the tile's counter; the last to
-// arrive sums the slots in order (deterministic) and stores.  Only the first
-// and the last segment of a workgroup can be cut.
+// (g + 1) U / G): the same amount of weight for every workgroup, and G is at
+// most the number of workgroups that fit on the chip at once, so no CU idles
+// and no workgroup waits for a second round.  A stage is 32 K-chunks (512
+// bytes of each row).  The weight is loaded row-contiguously (each wave-wide
+// load is two rows x 512 bytes) into registers U stages ahead, and re-laid
+// out through a wave-private LDS tile [16 rows][33 chunks] from which lane
+// (g, i) reads its A fragment (row i, chunk 4 step + g); the x window
+// [MT tokens][32 chunks] of a stage is loaded by the whole workgroup into a
+// double-buffered LDS tile and read as B fragments, so x is fetched once per
+// 16 NW rows.
+//
+// A range meets at most two cut tiles: the tile it starts in (unless it
+// starts at the tile's first stage) and the tile it ends in (unless it ends
+// at the tile's last stage); the tiles between are whole and stored as they
+// complete.  A cut tile is shared by consecutive workgroups: each publishes
+// its fp32 partial in slot (g - first workgroup of the tile), arrives on the
+// tile's counter, and the last to arrive sums the slots in order
+// (deterministic) and stores.  The partial of the first cut tile is kept in
+// registers until the loop is over: a store in flight between the loads
+// would hold up the waits on every load issued after it.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int sk_owner(unsigned u, unsigned units, unsigned G)
 {
@@ -1057,175 +1124,212 @@ __device__ __forceinline__ int sk_owner(unsigned u, unsigned units, unsigned G)
     return (int)((((unsigned long long)u + 1) * G - 1) / units);
 }
 
-template <int T, int NW, int D>
+template <int T, int NW, int U>
 __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
 {
     constexpr int MT = 16 * T;
-    constexpr int KW = 32;
-    constexpr int XI = MT / (2 * NW);
-    static_assert(XI >= 1 && XI * 2 * NW == MT, "x tile must split evenly over the waves");
-    constexpr int WSLOT = 16 * KW, XSLOT = MT * KW;
-    constexpr int E = NW * T * 4 * 64;           // partial values of a tile
-    extern __shared__ u32x4 sm[];
+    constexpr int KW = kMfmaxChunks;           // chunks per stage
+    constexpr int PITCH = KW + 1;              // row pitch in 16-byte chunks
+    constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
+    static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
+    static_assert(U >= 2 && U <= 4, "two to four stages in flight");
+    constexpr int E = NW * T * 4 * 64;         // partial values of a tile
+    extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [2][MT][PITCH]
     __shared__ unsigned last_flag[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const unsigned G = gridDim.x, gi = blockIdx.x;
-    const int spt = a.sk_spt;
-    const unsigned units = (unsigned)a.n_tiles * (unsigned)spt;
+    const unsigned spt = (unsigned)a.sk_spt;
+    const unsigned units = (unsigned)a.n_tiles * spt;
     const unsigned u0 = (unsigned)(((unsigned long long)gi * units) / G);
     const unsigned u1 = (unsigned)(((unsigned long long)(gi + 1) * units) / G);
     const int count = (int)(u1 - u0);
     const unsigned row_bytes = (unsigned)a.K8 * 16u;
     const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
-    u32x4 *wring = sm + wave * D * WSLOT;
-    u32x4 *xring = sm + NW * D * WSLOT;
-    const int half = lane >> 5, pos = lane & 31;
+    u32x4 *wl = sm + wave * 16 * PITCH;
+    u32x4 *xl = sm + NW * 16 * PITCH;
+    const int wrow = lane >> 5, wcol = lane & 31;
     const int i16 = lane & 15, g = lane >> 4;
 
-    // issue pointer: the unit the next issue() loads
-    int is_tile = (int)(u0 / (unsigned)spt), is_step = (int)(u0 % (unsigned)spt);
+    // loads: stage j of the range is unit u0 + j
+    unsigned ld_tile = u0 / spt, ld_step = u0 - ld_tile * spt;
     int issued = 0;
-    auto issue = [&]() {
-        const int j = issued++;
-        const bool live = j < count;
-        const int slot = j % D;
-        const int n0 = is_tile * NW * 16 + wave * 16;
+    auto load = [&](u32x4(&wv)[8], u32x4(&xv)[XL]) {
+        const bool live = issued++ < count;
+        const int n0 = (int)ld_tile * NW * 16 + wave * 16;
         const int rows_valid = uniform_int(live ? max(0, min(16, a.N - n0)) : 0);
         const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
                                     (unsigned)rows_valid * row_bytes);
-        const int cbase = is_step * KW;
+        const int cbase = (int)ld_step * KW;
         const int lim = live ? a.K8 : 0;
+        const int c = cbase + wcol;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int r = 2 * q + half;
-            const int c = cbase + (pos ^ r);
-            const unsigned off = c < lim ? (unsigned)r * row_bytes + (unsigned)c * 16u : kOffOob;
-            dma16(wres, wring + slot * WSLOT + 2 * q * KW, off);
-        }
+        for (int q = 0; q < 8; ++q)
+            wv[q] = load_w(wres, lane_off(c < lim, (unsigned)(2 * q + wrow) * row_bytes + (unsigned)c * 16u), 0);
 #pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            const int pair = wave + NW * i;
-            const int tok = 2 * pair + half;
-            const int c = cbase + (pos ^ (tok & 15));
-            const unsigned off = c < lim ? (unsigned)tok * row_bytes + (unsigned)c * 16u : kOffOob;
-            dma16(xres, xring + slot * XSLOT + 2 * pair * KW, off);
+        for (int i = 0; i < XL; ++i) {
+            const int e = tid + 64 * NW * i;
+            const int tok = e / KW, cc = cbase + (e % KW);
+            xv[i] = load_x(xres, lane_off(cc < lim, (unsigned)tok * row_bytes + (unsigned)cc * 16u), 0);
         }
-        if (++is_step == spt) {
-            is_step = 0;
-            ++is_tile;
-        }
+        const bool wrap = ld_step + 1 == spt;
+        ld_step = wrap ? 0u : ld_step + 1;
+        ld_tile = wrap ? ld_tile + 1 : ld_tile;
     };
 
-    f32x4 acc[T];
+    f32x4 acc[T], acc_first[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int t = 0; t < T; ++t) {
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_first[t] = acc[t];
+    }
+    unsigned c_tile = ld_tile, c_step = ld_step;   // the unit multiplied next
+    bool seg_whole_start = c_step == 0;            // current segment starts at stage 0
+    int first_cut = -1;                            // cut tile met first, partial in acc_first
 
-    // compute pointer and the (at most two) cut segments this workgroup publishes
-    int c_tile = is_tile, c_step = is_step, seg_start = is_step;
-    int cut_tile[2] = {-1, -1};
-    int ncut = 0;
-
+    auto store_tile = [&](int tile, const f32x4(&v)[T]) {
+        const int n0 = tile * NW * 16 + wave * 16;
 #pragma unroll
-    for (int j = 0; j < D - 1; ++j)
-        issue();
-    for (int j = 0; j < count; ++j) {
-        if constexpr (D == 2)
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if constexpr (D == 3)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 + XI) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (8 + XI)) : "memory");
-        asm volatile("s_barrier" ::: "memory");
-        issue();
-        const u32x4 *wsl = wring + (j % D) * WSLOT;
-        const u32x4 *xsl = xring + (j % D) * XSLOT;
+        for (int t = 0; t < T; ++t) {
+            const int tok = 16 * t + i16;
 #pragma unroll
-        for (int st = 0; st < KW / 4; ++st) {
-            const int p = (4 * st + g) ^ i16;
-            const u32x4 av = wsl[i16 * KW + p];
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const u32x4 bv = xsl[(16 * t + i16) * KW + p];
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + 4 * g + q;
+                if (tok < a.M && n < a.N)
+                    store_out(a, tok, n, v[t][q]);
             }
         }
-        const bool seg_end = c_step == spt - 1 || j == count - 1;
-        if (seg_end) {
-            const int n0 = c_tile * NW * 16 + wave * 16;
-            if (seg_start == 0 && c_step == spt - 1) {
-                // the whole tile is ours: store it
+    };
+    auto publish = [&](int tile, const f32x4(&v)[T]) {
+        const int part = (int)gi - sk_owner((unsigned)tile * spt, units, G);
+        float *wsp = a.ws + ((long)tile * a.sk_parts + part) * E;
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const int tok = 16 * t + i16;
+        for (int t = 0; t < T; ++t)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int n = n0 + 4 * g + q;
-                        if (tok < a.M && n < a.N)
-                            store_out(a, tok, n, acc[t][q]);
-                    }
-                }
-            } else {
-                const int part = (int)gi - sk_owner((unsigned)c_tile * spt, units, G);
-                float *wsp = a.ws + ((long)c_tile * a.sk_parts + part) * E;
+            for (int q = 0; q < 4; ++q)
+                publish_partial(wsp + ((wave * T + t) * 4 + q) * 64 + lane, v[t][q]);
+    };
+
+    auto stage = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
+        u32x4 *xw = xl + (j & 1) * MT * PITCH;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            wl[(2 * q + wrow) * PITCH + wcol] = wv[q];
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            const int e = tid + 64 * NW * i;
+            xw[(e / KW) * PITCH + (e % KW)] = xv[i];
+        }
+        load(wv, xv);                          // stage j + U (past the range: no memory access)
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        if (j >= count)
+            return;
+        // fragments are read four K-steps at a time, so one LDS round trip
+        // feeds 4 T MFMAs
+#pragma unroll
+        for (int h = 0; h < KW / 16; ++h) {
+            u32x4 av[4], bv[4][T];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                av[s] = wl[i16 * PITCH + 4 * (4 * h + s) + g];
 #pragma unroll
                 for (int t = 0; t < T; ++t)
+                    bv[s][t] = xw[(16 * t + i16) * PITCH + 4 * (4 * h + s) + g];
+            }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        publish_partial(wsp + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
-                cut_tile[ncut < 2 ? ncut : 1] = c_tile;
-                ++ncut;
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, av[s]), __builtin_bit_cast(bf16x8, bv[s][t]), acc[t], 0, 0, 0);
+        }
+        // a segment ends at its tile's last stage or at the range's last
+        // stage; the segment of the range's last stage is handled after the
+        // loop
+        if (j < count - 1 && c_step == spt - 1) {
+            if (seg_whole_start) {
+                store_tile((int)c_tile, acc);
+            } else {                           // the range's first segment, cut
+                first_cut = (int)c_tile;
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    acc_first[t] = acc[t];
             }
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            seg_whole_start = true;
         }
-        if (++c_step == spt) {
-            c_step = 0;
-            ++c_tile;
+        if (j < count - 1) {
+            const bool wrap = c_step + 1 == spt;
+            c_step = wrap ? 0u : c_step + 1;
+            c_tile = wrap ? c_tile + 1 : c_tile;
         }
-        if (seg_end)
-            seg_start = c_step;
+    };
+
+    // the prologue loads stay in stage order (sched_barrier), so that the
+    // loads of the stage multiplied first are the oldest in flight
+    u32x4 w0[8], x0[XL], w1[8], x1[XL], w2[8], x2[XL], w3[8], x3[XL];
+    load(w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (U >= 3) {
+        load(w2, x2);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // partials published, no DMA in flight
+    if constexpr (U >= 4) {
+        load(w3, x3);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Whole rounds of U stages, the stages past `count` idle: an exit from
+    // the middle of a round would give the loop a path on which the newest
+    // loads are not the ones the next round waits for, and every round would
+    // then wait for all of its loads.
+    for (int j = 0; j < count; j += U) {
+        stage(w0, x0, j);
+        stage(w1, x1, j + 1);
+        if constexpr (U >= 3)
+            stage(w2, x2, j + 2);
+        if constexpr (U >= 4)
+            stage(w3, x3, j + 3);
+    }
+
+    // The last segment (c_tile, stages up to c_step) is whole if it started
+    // at stage 0 and reached the tile's last stage.
+    const bool last_whole = seg_whole_start && c_step == spt - 1;
+    const int last_cut = last_whole ? -1 : (int)c_tile;
+    if (first_cut >= 0)
+        publish(first_cut, acc_first);
+    if (last_cut >= 0)
+        publish(last_cut, acc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // partials published
     __syncthreads();
+    auto arrive = [&](int t) -> unsigned {
+        if (t < 0)
+            return 0u;
+        const int parts = sk_owner((unsigned)(t + 1) * spt - 1, units, G) - sk_owner((unsigned)t * spt, units, G) + 1;
+        const unsigned prev = __hip_atomic_fetch_add(a.ctr + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return prev == (unsigned)(parts - 1) ? (unsigned)parts : 0u;
+    };
     if (tid == 0) {
-        for (int k = 0; k < 2; ++k) {
-            last_flag[k] = 0;
-            if (k < ncut) {
-                const int t = cut_tile[k];
-                const int parts = sk_owner((unsigned)(t + 1) * spt - 1, units, G) -
-                                  sk_owner((unsigned)t * spt, units, G) + 1;
-                const unsigned prev =
-                    __hip_atomic_fetch_add(a.ctr + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                last_flag[k] = prev == (unsigned)(parts - 1) ? (unsigned)parts : 0u;
-            }
-        }
+        last_flag[0] = arrive(first_cut);
+        last_flag[1] = arrive(last_cut);
     }
+    if (last_whole)
+        store_tile((int)c_tile, acc);
     __syncthreads();
-    for (int k = 0; k < 2 && k < ncut; ++k) {
-        const int parts = (int)last_flag[k];
+    auto finalize = [&](int t, int parts) {
         if (!parts)
-            continue;
-        const int t = cut_tile[k];
-        const float *wsp = a.ws + (long)t * a.sk_parts * E;
-        for (int e = tid; e < E; e += 64 * NW) {
-            const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
-            const int w = wt / T, tt = wt - (wt / T) * T;
-            const int tok = 16 * tt + (ln & 15), n = t * NW * 16 + 16 * w + 4 * (ln >> 4) + q;
-            if (tok >= a.M || n >= a.N)
-                continue;
-            float v = 0.f;
-            for (int pp = 0; pp < parts; ++pp)
-                v += read_partial(wsp + (long)pp * E + e);
-            store_out(a, tok, n, v);
-        }
+            return;
+        finalize_mfma_tile<T, NW>(a, a.ws + (long)t * a.sk_parts * E, E, parts, t * NW * 16);
         if (tid == 0)
             __hip_atomic_store(a.ctr + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    };
+    finalize(first_cut, (int)last_flag[0]);
+    finalize(last_cut, (int)last_flag[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1314,9 +1418,8 @@ static const KernelInfo kKernels[] = {
     SK_MFMAD(2, 2, 4), SK_MFMAD(2, 4, 2), SK_MFMAD(2, 4, 3),
     SK_MFMAD(4, 2, 3), SK_MFMAD(4, 4, 2),
     // MFMAS: rows field = waves, unroll field = pipeline depth; stream-K grid
-    SK_MFMAS(1, 1, 4), SK_MFMAS(1, 2, 2), SK_MFMAS(1, 2, 3), SK_MFMAS(1, 2, 4), SK_MFMAS(1, 4, 2),
-    SK_MFMAS(1, 4, 3), SK_MFMAS(2, 1, 3), SK_MFMAS(2, 2, 2), SK_MFMAS(2, 2, 3), SK_MFMAS(2, 4, 2),
-    SK_MFMAS(4, 2, 2), SK_MFMAS(4, 2, 3), SK_MFMAS(4, 4, 2),
+    SK_MFMAS(1, 2, 3), SK_MFMAS(1, 4, 2), SK_MFMAS(1, 4, 3), SK_MFMAS(1, 4, 4), SK_MFMAS(1, 8, 2),
+    SK_MFMAS(2, 4, 2), SK_MFMAS(2, 4, 3), SK_MFMAS(2, 8, 2),
 };
 
 const KernelInfo *kernel_table(int *count)

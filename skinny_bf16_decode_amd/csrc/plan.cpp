@@ -90,9 +90,10 @@ int device_cus()
     return cus;
 }
 
-// Stream-K grid and partial slots: as many workgroups as fit on the chip at
-// once (at most one per unit), and for each tile the number of workgroups
-// whose unit range meets it -- the same owner formula the kernel uses.
+// Stream-K grid and partial slots: split workgroups per CU, or as many as
+// fit on a CU at once if fewer (and at most one per unit), and for each tile
+// the number of workgroups whose unit range meets it -- the same owner
+// formula the kernel uses.
 void stream_k_shape(Entry &en, int K)
 {
     const unsigned spt = (unsigned)((K / 8 + kMfmaxChunks - 1) / kMfmaxChunks);
@@ -102,7 +103,8 @@ void stream_k_shape(Entry &en, int K)
         per_cu < 1)
         per_cu = 1;
     (void)hipGetLastError();
-    unsigned G = (unsigned)(per_cu * device_cus());
+    // the tactic's split field caps the workgroups per CU
+    unsigned G = (unsigned)(std::min(per_cu, en.t.split) * device_cus());
     if (G > units)
         G = units;
     auto owner = [&](unsigned u) { return (int)((((unsigned long long)u + 1) * G - 1) / units); };

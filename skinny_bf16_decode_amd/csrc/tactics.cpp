@@ -27,9 +27,9 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
     case SKINNY_PATH_DOT2X:
         return (size_t)t.mt * ((K8 + t.split - 1) / t.split) * 16;
     case SKINNY_PATH_MFMAX:
+    case SKINNY_PATH_MFMAS:
         return mfmax_lds_bytes(t.waves, t.mt);
     case SKINNY_PATH_MFMAD:
-    case SKINNY_PATH_MFMAS:
         return mfmad_lds_bytes(t.waves, t.mt, t.unroll);
     default:
         return 0;
@@ -104,8 +104,8 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
         set_error("split=%d: must be 1..16", t->split);
         return SKINNY_ERR_INVALID_ARG;
     }
-    if (t->path == SKINNY_PATH_MFMAS && t->split != 1) {
-        set_error("split=%d: the stream-K path schedules K itself, split must be 1", t->split);
+    if (t->path == SKINNY_PATH_MFMAS && t->split > 4) {
+        set_error("split=%d: for the stream-K path split is workgroups per CU, 1..4", t->split);
         return SKINNY_ERR_INVALID_ARG;
     }
     if (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_DOT2X || t->path == SKINNY_PATH_MFMAX ||
@@ -159,12 +159,12 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                         continue;
                     t.rows = 16 * w;
                 }
-                if (k.path == SKINNY_PATH_MFMAS && s != 1)
-                    continue;
+                if (k.path == SKINNY_PATH_MFMAS && s > 3)
+                    continue;                            // split: workgroups per CU
                 if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                     continue;
                 const int tiles = (N + t.rows - 1) / t.rows;
-                if (s > 1 && tiles * w >= 8 * 256)
+                if (s > 1 && tiles * w >= 8 * 256 && k.path != SKINNY_PATH_MFMAS)
                     continue;   // enough waves already; a K split only adds traffic
                 if (k.path == SKINNY_PATH_DOT2) {
                     // each lane of the workgroup should own at least one chunk per
@@ -176,8 +176,10 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                     // every wave streams the whole split: one full pipeline stage at least
                     if (k8 / s < 64 * k.unroll)
                         continue;
-                } else if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD ||
-                           k.path == SKINNY_PATH_MFMAS) {
+                } else if (k.path == SKINNY_PATH_MFMAS) {
+                    if (k8 < 2 * kMfmaxChunks)
+                        continue;
+                } else if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD) {
                     if (k8 / s < 2 * kMfmaxChunks)
                         continue;
                 } else {
