@@ -68,9 +68,11 @@ typedef enum {
                               W re-laid out and x staged through LDS via registers */
     SKINNY_PATH_MFMAD = 4, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
                               W and x streamed straight into LDS rings (direct-to-LDS loads) */
-    SKINNY_PATH_MFMAS = 5  /* MFMAX's register-to-LDS pipeline under a stream-K schedule: one
+    SKINNY_PATH_MFMAS = 5, /* MFMAX's register-to-LDS pipeline under a stream-K schedule: one
                               workgroup per slot the chip holds at once, each taking an equal
                               share of (row tile, K stage) units */
+    SKINNY_PATH_MFMAR = 6  /* the MFMAS kernel on a data-parallel grid: one workgroup per
+                              (row tile, K split), split = 1 meaning no exchange at all */
 } skinny_path;
 
 /*
@@ -84,14 +86,14 @@ typedef enum {
  */
 typedef struct {
     int path;   /* skinny_path */
-    int mt;     /* token tile: DOT2/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD/MFMAS 16,32,64 */
+    int mt;     /* token tile: DOT2/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD/MFMAS/MFMAR 16,32,64 */
     int rows;   /* weight rows per workgroup.  DOT2: 1..16 (mt*rows <= 64);
-                   MFMA: 16,32,64; DOT2X: waves * (1, 2 or 4); MFMAX, MFMAD, MFMAS: 16 * waves */
+                   MFMA: 16,32,64; DOT2X: waves * (1, 2 or 4); MFMAX, MFMAD, MFMAS, MFMAR: 16 * waves */
     int waves;  /* wavefronts per workgroup: 1,2,4,8 */
     int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
                    (MFMAX: 1, its stage is fixed at 32 chunks; MFMAD: the depth of
-                   its LDS rings, 2..4 stages of 32 chunks; MFMAS: weight stages of
-                   32 chunks in flight in registers, 2..4) */
+                   its LDS rings, 2..4 stages of 32 chunks; MFMAS, MFMAR: weight
+                   stages of 32 chunks in flight in registers, 2..4) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16; MFMAS: the
                    stream-K grid, in workgroups per CU (1..4, capped at what fits) */
 } skinny_tactic;

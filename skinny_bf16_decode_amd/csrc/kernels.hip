@@ -890,14 +890,37 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
         load(wv, xv, j + 2);                   // past the last stage: out of range, no access
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        if constexpr (T <= 2) {
+            // fragments are read four K-steps at a time, so one LDS round
+            // trip feeds 4 T MFMAs
 #pragma unroll
-        for (int st = 0; st < KW / 4; ++st) {
-            const u32x4 av = wl[i16 * PITCH + 4 * st + g];
+            for (int h = 0; h < KW / 16; ++h) {
+                u32x4 av[4], bv[4][T];
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const u32x4 bv = xw[(16 * t + i16) * PITCH + 4 * st + g];
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    av[s4] = wl[i16 * PITCH + 4 * (4 * h + s4) + g];
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        bv[s4][t] = xw[(16 * t + i16) * PITCH + 4 * (4 * h + s4) + g];
+                }
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s4]),
+                                                                         __builtin_bit_cast(bf16x8, bv[s4][t]),
+                                                                         acc[t], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < KW / 4; ++st) {
+                const u32x4 av = wl[i16 * PITCH + 4 * st + g];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const u32x4 bv = xw[(16 * t + i16) * PITCH + 4 * st + g];
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+                }
             }
         }
     };

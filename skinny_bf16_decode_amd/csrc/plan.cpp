@@ -90,21 +90,26 @@ int device_cus()
     return cus;
 }
 
-// Stream-K grid and partial slots: split workgroups per CU, or as many as
-// fit on a CU at once if fewer (and at most one per unit), and for each tile
-// the number of workgroups whose unit range meets it -- the same owner
-// formula the kernel uses.
+// Stream-K grid and partial slots.  MFMAS: split workgroups per CU, or as
+// many as fit on a CU at once if fewer; MFMAR: one workgroup per (tile, K
+// split).  Either way at most one per unit, and for each tile the number of
+// workgroups whose unit range meets it -- the same owner formula the kernel
+// uses.
 void stream_k_shape(Entry &en, int K)
 {
     const unsigned spt = (unsigned)((K / 8 + kMfmaxChunks - 1) / kMfmaxChunks);
     const unsigned units = (unsigned)en.n_tiles * spt;
-    int per_cu = 0;
-    if (!en.fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, en.fn, (int)en.block, en.lds) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    (void)hipGetLastError();
-    // the tactic's split field caps the workgroups per CU
-    unsigned G = (unsigned)(std::min(per_cu, en.t.split) * device_cus());
+    unsigned G;
+    if (en.t.path == SKINNY_PATH_MFMAR) {
+        G = (unsigned)en.n_tiles * (unsigned)en.t.split;
+    } else {
+        int per_cu = 0;
+        if (!en.fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, en.fn, (int)en.block, en.lds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        (void)hipGetLastError();
+        G = (unsigned)(std::min(per_cu, en.t.split) * device_cus());
+    }
     if (G > units)
         G = units;
     auto owner = [&](unsigned u) { return (int)((((unsigned long long)u + 1) * G - 1) / units); };
@@ -126,7 +131,7 @@ Entry make_entry(const skinny_tactic &t, int N, int K)
     en.block = (unsigned)(64 * t.waves);
     en.lds = (unsigned)tactic_lds_bytes(t, K / 8);
     en.t = t;
-    if (t.path == SKINNY_PATH_MFMAS)
+    if (t.path == SKINNY_PATH_MFMAS || t.path == SKINNY_PATH_MFMAR)
         stream_k_shape(en, K);
     return en;
 }
@@ -154,12 +159,17 @@ void raise_lds_limits()
 
 size_t ws_floats(const Entry &en)
 {
-    if (en.t.path == SKINNY_PATH_MFMAS)
-        return (size_t)en.n_tiles * en.sk_parts * en.t.mt * en.t.rows;
+    if (en.t.path == SKINNY_PATH_MFMAS || en.t.path == SKINNY_PATH_MFMAR)
+        return en.sk_parts > 1 ? (size_t)en.n_tiles * en.sk_parts * en.t.mt * en.t.rows : 0;
     return en.t.split > 1 ? (size_t)en.n_tiles * en.t.split * en.t.mt * en.t.rows : 0;
 }
 
-bool uses_counters(const Entry &en) { return en.t.split > 1 || en.t.path == SKINNY_PATH_MFMAS; }
+bool uses_counters(const Entry &en)
+{
+    if (en.t.path == SKINNY_PATH_MFMAS || en.t.path == SKINNY_PATH_MFMAR)
+        return en.sk_parts > 1;
+    return en.t.split > 1;
+}
 
 // Static LDS of a kernel plus the device's per-workgroup limit, looked up
 // once per kernel.  A dispatch over the limit would abort the queue, so
@@ -655,9 +665,9 @@ skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len
     }
     const Entry &en = p->e[M];
     static const char *const kNames[] = {"dot2", "mfma16x16x32", "dot2x", "mfmax16x16x32", "mfmad16x16x32",
-                                         "mfmas16x16x32"};
+                                         "mfmas16x16x32", "mfmar16x16x32"};
     snprintf(buf, len, "%s mt=%d rows=%d waves=%d unroll=%d split=%d grid=%u block=%u lds=%u",
-             (t.path >= 0 && t.path <= 5) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
+             (t.path >= 0 && t.path <= 6) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
              en.grid, en.block, en.lds);
     return SKINNY_OK;
 }

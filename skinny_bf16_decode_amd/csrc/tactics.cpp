@@ -28,6 +28,7 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
         return (size_t)t.mt * ((K8 + t.split - 1) / t.split) * 16;
     case SKINNY_PATH_MFMAX:
     case SKINNY_PATH_MFMAS:
+    case SKINNY_PATH_MFMAR:
         return mfmax_lds_bytes(t.waves, t.mt);
     case SKINNY_PATH_MFMAD:
         return mfmad_lds_bytes(t.waves, t.mt, t.unroll);
@@ -55,6 +56,10 @@ const KernelInfo *tactic_kernel(const skinny_tactic &t)
         if (t.rows != 16 * t.waves)
             return nullptr;
         return find_kernel(t.path, t.mt, t.waves, t.unroll);
+    case SKINNY_PATH_MFMAR:                    // the MFMAS kernels, another grid
+        if (t.rows != 16 * t.waves)
+            return nullptr;
+        return find_kernel(SKINNY_PATH_MFMAS, t.mt, t.waves, t.unroll);
     default:
         return nullptr;
     }
@@ -114,6 +119,12 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             set_error("split=%d exceeds the %d 16-byte chunks of a row", t->split, k8);
             return SKINNY_ERR_INVALID_ARG;
         }
+    } else if (t->path == SKINNY_PATH_MFMAR) {
+        const int stages = (k8 + kMfmaxChunks - 1) / kMfmaxChunks;
+        if (t->split > stages) {
+            set_error("split=%d exceeds the %d K stages of %d chunks", t->split, stages, kMfmaxChunks);
+            return SKINNY_ERR_INVALID_ARG;
+        }
     } else if (t->path == SKINNY_PATH_MFMA) {
         const int steps = (k8 + 3) / 4;
         if (t->split > steps) {
@@ -121,7 +132,7 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             return SKINNY_ERR_INVALID_ARG;
         }
     } else {
-        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD) or 5 (MFMAS)", t->path);
+        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD), 5 (MFMAS) or 6 (MFMAR)", t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
     const size_t lds_limit = (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
@@ -149,47 +160,54 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
     static const int kSplits[] = {1, 2, 3, 4, 5, 6, 8};
     for (int i = 0; i < nk; ++i) {
         const KernelInfo &k = ks[i];
-        for (int w : kWaves) {
-            for (int s : kSplits) {
-                skinny_tactic t = {k.path, k.mt, k.rows, w, k.unroll, s};
-                if (k.path == SKINNY_PATH_DOT2X)
-                    t.rows = k.rows * w;                 // k.rows is rows per wave
-                if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD || k.path == SKINNY_PATH_MFMAS) {
-                    if (w != k.rows)                     // k.rows is the wave count
+        // the stream-K kernels also run on a data-parallel grid (MFMAR)
+        const int paths[2] = {k.path, k.path == SKINNY_PATH_MFMAS ? SKINNY_PATH_MFMAR : -1};
+        for (int path : paths) {
+            if (path < 0)
+                continue;
+            for (int w : kWaves) {
+                for (int s : kSplits) {
+                    skinny_tactic t = {path, k.mt, k.rows, w, k.unroll, s};
+                    if (path == SKINNY_PATH_DOT2X)
+                        t.rows = k.rows * w;             // k.rows is rows per wave
+                    if (path == SKINNY_PATH_MFMAX || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAS ||
+                        path == SKINNY_PATH_MFMAR) {
+                        if (w != k.rows)                 // k.rows is the wave count
+                            continue;
+                        t.rows = 16 * w;
+                    }
+                    if (path == SKINNY_PATH_MFMAS && s > 3)
+                        continue;                        // split: workgroups per CU
+                    if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                         continue;
-                    t.rows = 16 * w;
+                    const int tiles = (N + t.rows - 1) / t.rows;
+                    if (s > 1 && tiles * w >= 8 * 256 && path != SKINNY_PATH_MFMAS)
+                        continue;   // enough waves already; a K split only adds traffic
+                    if (path == SKINNY_PATH_DOT2) {
+                        // each lane of the workgroup should own at least one chunk per
+                        // split, and the unrolled loop should run at least once
+                        const int per_split = k8 / s;
+                        if (per_split < 64 * w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
+                            continue;
+                    } else if (path == SKINNY_PATH_DOT2X) {
+                        // every wave streams the whole split: one full pipeline stage at least
+                        if (k8 / s < 64 * k.unroll)
+                            continue;
+                    } else if (path == SKINNY_PATH_MFMAS) {
+                        if (k8 < 2 * kMfmaxChunks)
+                            continue;
+                    } else if (path == SKINNY_PATH_MFMAX || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAR) {
+                        if (k8 / s < 2 * kMfmaxChunks)
+                            continue;
+                    } else {
+                        const int per_split = ((k8 + 3) / 4) / s;
+                        if (per_split < w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
+                            continue;
+                    }
+                    if (count < cap)
+                        buf[count] = t;
+                    ++count;
                 }
-                if (k.path == SKINNY_PATH_MFMAS && s > 3)
-                    continue;                            // split: workgroups per CU
-                if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
-                    continue;
-                const int tiles = (N + t.rows - 1) / t.rows;
-                if (s > 1 && tiles * w >= 8 * 256 && k.path != SKINNY_PATH_MFMAS)
-                    continue;   // enough waves already; a K split only adds traffic
-                if (k.path == SKINNY_PATH_DOT2) {
-                    // each lane of the workgroup should own at least one chunk per
-                    // split, and the unrolled loop should run at least once
-                    const int per_split = k8 / s;
-                    if (per_split < 64 * w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
-                        continue;
-                } else if (k.path == SKINNY_PATH_DOT2X) {
-                    // every wave streams the whole split: one full pipeline stage at least
-                    if (k8 / s < 64 * k.unroll)
-                        continue;
-                } else if (k.path == SKINNY_PATH_MFMAS) {
-                    if (k8 < 2 * kMfmaxChunks)
-                        continue;
-                } else if (k.path == SKINNY_PATH_MFMAX || k.path == SKINNY_PATH_MFMAD) {
-                    if (k8 / s < 2 * kMfmaxChunks)
-                        continue;
-                } else {
-                    const int per_split = ((k8 + 3) / 4) / s;
-                    if (per_split < w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
-                        continue;
-                }
-                if (count < cap)
-                    buf[count] = t;
-                ++count;
             }
         }
     }

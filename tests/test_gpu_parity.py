@@ -328,7 +328,7 @@ def test_split_k_exchange_exact(sk, remap, monkeypatch):
     w = gu.dev_bf16(w_bits)
     tactics = [t for t in sk.enumerate_tactics(n, k) if t.split > 1]
     _say(f"[split remap={remap}] {len(tactics)} tactics")
-    assert {t.path for t in tactics} == {0, 1, 2, 3, 4, 5}   # MFMAS: split = workgroups per CU
+    assert {t.path for t in tactics} == {0, 1, 2, 3, 4, 5, 6}   # MFMAS: split = workgroups per CU
     for t in tactics:
         plan = sk.Prepared(w, torch.float32, table=gu.forced_table(t))
         for rep in range(2):
@@ -346,7 +346,7 @@ def test_stream_k_repeats_and_graph_replays(sk):
     o, s = oracle.gemm(x_bits, w_bits)
     w = gu.dev_bf16(w_bits)
     x = gu.dev_bf16(x_bits)
-    cands = [t for t in sk.enumerate_tactics(n, k) if t.path == sk.PATH_MFMAS]
+    cands = [t for t in sk.enumerate_tactics(n, k) if t.path in (sk.PATH_MFMAS, sk.PATH_MFMAR)]
     assert cands
     for t in cands:
         plan = sk.Prepared(w, torch.bfloat16, table=gu.forced_table(t))
