@@ -72,7 +72,8 @@ typedef enum {
                               workgroup per slot the chip holds at once, each taking an equal
                               share of (row tile, K stage) units */
     SKINNY_PATH_MFMAR = 6  /* the MFMAS kernel on a data-parallel grid: one workgroup per
-                              (row tile, K split), split = 1 meaning no exchange at all */
+                              (row range, K split), with at least CUs / split equal row
+                              ranges of at most 16 * waves rows; split = 1: no exchange */
 } skinny_path;
 
 /*

@@ -788,9 +788,11 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
 
 // The last arriver of a tile whose partials are MFMA accumulator fragments
 // (value e = ((wave T + t) 4 + q) 64 + lane: token 16 t + lane % 16, row
-// 16 wave + 4 (lane / 16) + q of the tile) sums the slots and stores.
+// n_wg + 16 wave + 4 (lane / 16) + q) sums the slots and stores the rows
+// below n_end.
 template <int T, int NW>
-__device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, const float *wsp, int E, int parts, int n_wg)
+__device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, const float *wsp, int E, int parts, int n_wg,
+                                                   int n_end)
 {
     constexpr int EPT = 4 * T;                 // values per thread: E = 64 NW EPT
     int off[EPT];
@@ -805,7 +807,7 @@ __device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, const float *
         const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
         const int w = wt / T, t = wt - (wt / T) * T;
         const int tok = 16 * t + (ln & 15), n = n_wg + 16 * w + 4 * (ln >> 4) + q;
-        if (tok < a.M && n < a.N)
+        if (tok < a.M && n < n_end)
             store_out(a, tok, n, v[i]);
     }
 }
@@ -959,7 +961,7 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
             publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
     if (!split_arrive_last(a, tile, &flag))
         return;
-    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg);
+    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg, a.N);
     split_reset(a, tile);
 }
 
@@ -1109,27 +1111,32 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
             publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
     if (!split_arrive_last(a, tile, &flag))
         return;
-    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg);
+    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg, a.N);
     split_reset(a, tile);
 }
 
 // ---------------------------------------------------------------------------
-// MFMAS kernel: token tile MT = 16 T, NW waves each own 16 rows of a
-// 16 NW-row tile, under a stream-K schedule, with U weight stages in flight
-// in registers.
+// MFMAS kernel: token tile MT = 16 T, NW waves each own 16 rows of a row
+// tile of at most 16 NW rows, under a stream-K schedule, with U weight
+// stages in flight in registers.
 //
 // The work is the flat list of units (row tile t, K stage k), t < n_tiles,
 // k < spt = ceil(K / 256), and workgroup g of G takes units [g U / G,
-// (g + 1) U / G): the same amount of weight for every workgroup, and G is at
-// most the number of workgroups that fit on the chip at once, so no CU idles
-// and no workgroup waits for a second round.  A stage is 32 K-chunks (512
-// bytes of each row).  The weight is loaded row-contiguously (each wave-wide
-// load is two rows x 512 bytes) into registers U stages ahead, and re-laid
-// out through a wave-private LDS tile [16 rows][33 chunks] from which lane
-// (g, i) reads its A fragment (row i, chunk 4 step + g); the x window
-// [MT tokens][32 chunks] of a stage is loaded by the whole workgroup into a
-// double-buffered LDS tile and read as B fragments, so x is fetched once per
-// 16 NW rows.
+// (g + 1) U / G).  Tile t is the row range [t N / n_tiles, (t + 1) N /
+// n_tiles), so tiles differ by at most one row.  With G = the workgroups
+// that fit on the chip at once (MFMAS), every workgroup streams the same
+// amount of weight and none waits for a second round; with G = n_tiles
+// (MFMAR, split 1) each workgroup owns one whole tile, and n_tiles may be
+// raised to the CU count so that every CU gets one equal row range and no
+// partial sums are exchanged.
+//
+// A stage is 32 K-chunks (512 bytes of each row).  The weight is loaded
+// row-contiguously (each wave-wide load is two rows x 512 bytes) into
+// registers U stages ahead, and re-laid out through a wave-private LDS tile
+// [16 rows][33 chunks] from which lane (g, i) reads its A fragment (row i,
+// chunk 4 step + g); the x window [MT tokens][32 chunks] of a stage is
+// loaded by the whole workgroup into a double-buffered LDS tile and read as
+// B fragments, so x is fetched once per tile, not once per wave.
 //
 // A range meets at most two cut tiles: the tile it starts in (unless it
 // starts at the tile's first stage) and the tile it ends in (unless it ends
@@ -1138,8 +1145,8 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
 // its fp32 partial in slot (g - first workgroup of the tile), arrives on the
 // tile's counter, and the last to arrive sums the slots in order
 // (deterministic) and stores.  The partial of the first cut tile is kept in
-// registers until the loop is over: a store in flight between the loads
-// would hold up the waits on every load issued after it.
+// registers until the loop is over, so that every exchange store is issued
+// after the last weight load.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int sk_owner(unsigned u, unsigned units, unsigned G)
 {
@@ -1174,14 +1181,19 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
     u32x4 *xl = sm + NW * 16 * PITCH;
     const int wrow = lane >> 5, wcol = lane & 31;
     const int i16 = lane & 15, g = lane >> 4;
+    // tile t is the row range [t N / n_tiles, (t + 1) N / n_tiles), at most
+    // 16 NW rows; wave w multiplies its rows 16 w .. 16 w + 15
+    auto tile_row = [&](unsigned t) {
+        return uniform_int((int)(((unsigned long long)t * (unsigned)a.N) / (unsigned)a.n_tiles));
+    };
 
     // loads: stage j of the range is unit u0 + j
     unsigned ld_tile = u0 / spt, ld_step = u0 - ld_tile * spt;
     int issued = 0;
     auto load = [&](u32x4(&wv)[8], u32x4(&xv)[XL]) {
         const bool live = issued++ < count;
-        const int n0 = (int)ld_tile * NW * 16 + wave * 16;
-        const int rows_valid = uniform_int(live ? max(0, min(16, a.N - n0)) : 0);
+        const int n0 = tile_row(ld_tile) + wave * 16;
+        const int rows_valid = uniform_int(live ? max(0, min(16, tile_row(ld_tile + 1) - n0)) : 0);
         const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
                                     (unsigned)rows_valid * row_bytes);
         const int cbase = (int)ld_step * KW;
@@ -1212,14 +1224,14 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
     int first_cut = -1;                            // cut tile met first, partial in acc_first
 
     auto store_tile = [&](int tile, const f32x4(&v)[T]) {
-        const int n0 = tile * NW * 16 + wave * 16;
+        const int n0 = tile_row((unsigned)tile) + wave * 16, n_end = tile_row((unsigned)tile + 1);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             const int tok = 16 * t + i16;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = n0 + 4 * g + q;
-                if (tok < a.M && n < a.N)
+                if (tok < a.M && n < n_end)
                     store_out(a, tok, n, v[t][q]);
             }
         }
@@ -1347,7 +1359,8 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
     auto finalize = [&](int t, int parts) {
         if (!parts)
             return;
-        finalize_mfma_tile<T, NW>(a, a.ws + (long)t * a.sk_parts * E, E, parts, t * NW * 16);
+        finalize_mfma_tile<T, NW>(a, a.ws + (long)t * a.sk_parts * E, E, parts, tile_row((unsigned)t),
+                                  tile_row((unsigned)t + 1));
         if (tid == 0)
             __hip_atomic_store(a.ctr + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };

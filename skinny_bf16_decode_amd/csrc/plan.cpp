@@ -127,6 +127,11 @@ Entry make_entry(const skinny_tactic &t, int N, int K)
     const KernelInfo *k = tactic_kernel(t);
     en.fn = k ? k->fn : nullptr;
     en.n_tiles = tiles_for(t, N);
+    if (t.path == SKINNY_PATH_MFMAR) {
+        // equal row ranges, at least as many (x split) as there are CUs
+        const int want = (device_cus() + t.split - 1) / t.split;
+        en.n_tiles = std::min(N, std::max(en.n_tiles, want));
+    }
     en.grid = (unsigned)(en.n_tiles * t.split);
     en.block = (unsigned)(64 * t.waves);
     en.lds = (unsigned)tactic_lds_bytes(t, K / 8);
