@@ -1,15 +1,19 @@
 /*
  * skinny.h -- C ABI of the MI355X (gfx950) skinny BF16 decode projection.
  *
- *   out[M, N] = x[M, K] @ W[N, K]^T,   M = 1..64 tokens, BF16 in,
- *   fp32 accumulation, BF16 or fp32 out.
+ *   out[M, N] = x[M, K] @ W[N, K]^T (+ residual[M, N]),   M = 1..64 tokens,
+ *   BF16 (or FP16) in, fp32 accumulation, BF16 or fp32 out.
  *
  * The operation is the one the pages define for their decode GEMMs:
  * "out[M, N] = x[M, K] @ weight[N, K]^T" (class PreparedWarpSplitK, page
  * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.warp_splitk")
  * and "x @ weight.T" (class Projection, page
- * "vllm.models.glm5next.nvidia.specialized_decode.gemm").  No bias and no
- * residual is added; out is overwritten.
+ * "vllm.models.glm5next.nvidia.specialized_decode.gemm").  No bias is added;
+ * out is overwritten.  skinny_run_ex can add a residual (the `residual` of
+ * try_low_latency_gemm, page "vllm.models.kimi_k3.nvidia.low_latency_gemm")
+ * and takes row pitches, and skinny_prepare_ex FP16 weights and pitched
+ * weights (class PreparedProjection and matrix_view, page
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.projection").
  *
  * Usage follows the pages' prepare-once / run-per-forward split: a prepared
  * object owns the weight and a per-token-count kernel choice that is fixed
@@ -21,9 +25,9 @@
  *  - All data pointers (W, x, out) are DEVICE pointers on the device that is
  *    current when the plan is prepared.  The library never dereferences them
  *    on the host.
- *  - Matrices are packed row-major: W is [N][K], x is [M][K], out is [M][N],
- *    each with row pitch equal to its column count.  Pitched views are not
- *    accepted.
+ *  - Matrices are row-major: W is [N][K], x is [M][K], out is [M][N].  The
+ *    plain entry points take them packed (row pitch = column count); the _ex
+ *    entry points take a row pitch (in elements) for each.
  *  - Every call returns a status; none aborts or throws.  After a failure,
  *    skinny_last_error() returns a thread-local text describing it.
  *  - A stream is passed as a hipStream_t cast to void*; NULL is the null
@@ -44,6 +48,11 @@ typedef enum {
     SKINNY_OUT_BF16 = 0, /* out is BF16, rounded to nearest even once */
     SKINNY_OUT_F32 = 1   /* out is fp32 (the accumulator, unrounded) */
 } skinny_out_dtype;
+
+typedef enum {
+    SKINNY_IN_BF16 = 0, /* W and x are BF16 (v_dot2_f32_bf16, bf16 MFMA) */
+    SKINNY_IN_F16 = 1   /* W and x are FP16 (v_dot2_f32_f16, f16 MFMA) */
+} skinny_in_dtype;
 
 typedef enum {
     SKINNY_OK = 0,
@@ -134,6 +143,42 @@ skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype out_d
  */
 skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dtype out_dtype,
                                      const skinny_tactic *table, skinny_plan **plan);
+
+/*
+ * skinny_prepare_ex -- skinny_prepare for a weight with a row pitch and an
+ * input type: W[n][k] is element n * ldw + k, ldw >= K, ldw % 8 == 0 (the
+ * 16-byte row pitch PreparedProjection requires), and W (and every x run
+ * with the plan) holds BF16 or FP16 values as in_dtype says.  Tables are
+ * tuned and cached per (device, N, K, in_dtype, out_dtype); the pitch does
+ * not change the tactic.  Errors as skinny_prepare, plus
+ * SKINNY_ERR_INVALID_ARG for a bad in_dtype and SKINNY_ERR_SHAPE for a bad
+ * ldw.  skinny_prepare(W, N, K, od, plan) is
+ * skinny_prepare_ex(W, N, K, K, SKINNY_IN_BF16, od, plan).
+ */
+skinny_status skinny_prepare_ex(const void *W, int N, int K, int ldw, skinny_in_dtype in_dtype,
+                                skinny_out_dtype out_dtype, skinny_plan **plan);
+
+/* skinny_prepare_tactics for a weight with a row pitch and an input type. */
+skinny_status skinny_prepare_tactics_ex(const void *W, int N, int K, int ldw, skinny_in_dtype in_dtype,
+                                        skinny_out_dtype out_dtype, const skinny_tactic *table,
+                                        skinny_plan **plan);
+
+/*
+ * skinny_run_ex -- out[m][n] = sum_k x[m][k] W[n][k] (+ residual[m][n]) for
+ * m < M, n < N, on `stream`, asynchronously; the fused-residual epilogue of
+ * try_low_latency_gemm(x, weight, residual) when residual is not NULL.
+ *
+ * x[m][k] is element m * ldx + k (ldx >= K, ldx % 8 == 0, x 16-byte aligned,
+ * the plan's input type).  out[m][n] is element m * ldo + n (ldo >= N).
+ * residual (NULL for none) has the out type and element m * ldr + n
+ * (ldr >= N); it is added in fp32 to the fp32 sum before the one rounding to
+ * BF16.  residual may be out itself (with ldr == ldo: out += x W^T) but must
+ * not otherwise overlap out.  Elements of out outside rows < M and columns
+ * < N are not touched.  Everything else as skinny_run, which is
+ * skinny_run_ex(plan, x, K, NULL, 0, out, N, M, stream).
+ */
+skinny_status skinny_run_ex(const skinny_plan *plan, const void *x, int ldx, const void *residual, int ldr,
+                            void *out, int ldo, int M, void *stream);
 
 /*
  * skinny_run -- out[0:M, :] = x[0:M, :] @ W^T on `stream`, asynchronously.

@@ -14,6 +14,15 @@ bound.  The arithmetic is in ``oracle.c`` (plain loops, OpenMP over rows of W).
 The checker (``check``) applies the stated bound:
   fp32 output:  |g - O| <= 1e-3 * S + 1e-6
   BF16 output:  the same plus 2^-8 * |O| (one BF16 rounding of the result).
+
+``dtype="f16"`` reads x and W as FP16 instead of BF16 (the two weight types
+of class PreparedProjection on the page
+"vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.projection").
+``gemm_residual`` is ``O + R`` for a residual R given as values: the
+``residual`` of try_low_latency_gemm on the page
+"vllm.models.kimi_k3.nvidia.low_latency_gemm", read as an addend of the
+product.  With a residual the checker also allows the one fp32 rounding of
+the addition (2^-23 * |O + R|).
 """
 from __future__ import annotations
 
@@ -50,6 +59,15 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_gemm.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, _f64p, _f64p]
     lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm_t.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, _f64p, _f64p]
+    lib.oracle_gemm_t.restype = ctypes.c_int
+    lib.oracle_gemm_sampled_t.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, _i32p, _i32p, ctypes.c_long,
+                                          _f64p, _f64p]
+    lib.oracle_gemm_sampled_t.restype = ctypes.c_int
+    lib.oracle_decode_f16.argtypes = [_u16p, ctypes.c_long, _f64p]
+    lib.oracle_decode_f16.restype = None
     lib.oracle_gemm_sampled.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, _i32p, _i32p, ctypes.c_long,
                                         _f64p, _f64p]
@@ -78,10 +96,17 @@ def _u16(a):
     return a, a.ctypes.data_as(_u16p)
 
 
-def gemm(x_bits, w_bits, lib=None):
+def _f16_flag(dtype: str) -> int:
+    if dtype not in ("bf16", "f16"):
+        raise ValueError(dtype)
+    return int(dtype == "f16")
+
+
+def gemm(x_bits, w_bits, lib=None, dtype: str = "bf16"):
     """(O, S) = (x @ W^T, |x| @ |W|^T products summed) in float64.
 
-    x_bits: uint16 [M, K] BF16 bits; w_bits: uint16 [N, K] BF16 bits.
+    x_bits: uint16 [M, K] bits; w_bits: uint16 [N, K] bits, BF16 or (dtype
+    "f16") FP16.
     """
     lib = lib or _get()
     x, xp = _u16(x_bits)
@@ -92,13 +117,23 @@ def gemm(x_bits, w_bits, lib=None):
     n = w.shape[0]
     o = np.zeros((m, n), dtype=np.float64)
     s = np.zeros((m, n), dtype=np.float64)
-    rc = lib.oracle_gemm(xp, wp, m, n, k, o.ctypes.data_as(_f64p), s.ctypes.data_as(_f64p))
+    rc = lib.oracle_gemm_t(xp, wp, m, n, k, _f16_flag(dtype), o.ctypes.data_as(_f64p),
+                           s.ctypes.data_as(_f64p))
     if rc != 0:
         raise RuntimeError("oracle_gemm failed")
     return o, s
 
 
-def gemm_sampled(x_bits, w_bits, mi, ni, lib=None):
+def gemm_residual(x_bits, w_bits, r, lib=None, dtype: str = "bf16"):
+    """(O + R, S): the product plus a residual R [M, N] given as values."""
+    o, s = gemm(x_bits, w_bits, lib=lib, dtype=dtype)
+    r = np.asarray(r, dtype=np.float64)
+    if r.shape != o.shape:
+        raise ValueError(f"residual {r.shape} vs product {o.shape}")
+    return o + r, s
+
+
+def gemm_sampled(x_bits, w_bits, mi, ni, lib=None, dtype: str = "bf16"):
     """Elements (mi[i], ni[i]) of (O, S), for checks at sizes too big to do whole."""
     lib = lib or _get()
     x, xp = _u16(x_bits)
@@ -111,9 +146,9 @@ def gemm_sampled(x_bits, w_bits, mi, ni, lib=None):
     ni = np.ascontiguousarray(ni, dtype=np.int32)
     o = np.zeros(mi.shape[0], dtype=np.float64)
     s = np.zeros(mi.shape[0], dtype=np.float64)
-    rc = lib.oracle_gemm_sampled(xp, wp, m, n, k, mi.ctypes.data_as(_i32p),
-                                 ni.ctypes.data_as(_i32p), mi.shape[0],
-                                 o.ctypes.data_as(_f64p), s.ctypes.data_as(_f64p))
+    rc = lib.oracle_gemm_sampled_t(xp, wp, m, n, k, _f16_flag(dtype), mi.ctypes.data_as(_i32p),
+                                   ni.ctypes.data_as(_i32p), mi.shape[0],
+                                   o.ctypes.data_as(_f64p), s.ctypes.data_as(_f64p))
     if rc != 0:
         raise RuntimeError("oracle_gemm_sampled failed (index out of range?)")
     return o, s
@@ -137,6 +172,15 @@ def decode_bf16(bits, lib=None) -> np.ndarray:
     return out
 
 
+def decode_f16(bits, lib=None) -> np.ndarray:
+    """FP16 bits to float64 (exact)."""
+    lib = lib or _get()
+    b, bp = _u16(bits)
+    out = np.zeros(b.shape, dtype=np.float64)
+    lib.oracle_decode_f16(bp, b.size, out.ctypes.data_as(_f64p))
+    return out
+
+
 def threads(lib=None) -> int:
     return (lib or _get()).oracle_threads()
 
@@ -148,6 +192,7 @@ def threads(lib=None) -> int:
 REL = 1e-3
 ABS = 1e-6
 BF16_REL = 2.0 ** -8
+F32_ADD_REL = 2.0 ** -23
 
 
 @dataclass
@@ -165,9 +210,12 @@ class Report:
                 f"nan={self.nan} first_bad={self.first_bad}")
 
 
-def bound(o, s, mode: str):
-    """The allowed |g - O| per element for output mode "f32" or "bf16"."""
+def bound(o, s, mode: str, residual: bool = False):
+    """The allowed |g - O| per element for output mode "f32" or "bf16"
+    (O including the residual when there is one)."""
     b = REL * np.asarray(s, dtype=np.float64) + ABS
+    if residual:
+        b = b + F32_ADD_REL * np.abs(np.asarray(o, dtype=np.float64))
     if mode == "bf16":
         b = b + BF16_REL * np.abs(np.asarray(o, dtype=np.float64))
     elif mode != "f32":
@@ -175,7 +223,7 @@ def bound(o, s, mode: str):
     return b
 
 
-def check(g, o, s, mode: str) -> Report:
+def check(g, o, s, mode: str, residual: bool = False) -> Report:
     """Compare a result g (float values, already decoded) with the oracle."""
     g = np.asarray(g, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
@@ -183,7 +231,7 @@ def check(g, o, s, mode: str) -> Report:
     if g.shape != o.shape:
         raise ValueError(f"shape {g.shape} vs oracle {o.shape}")
     err = np.abs(g - o)
-    b = bound(o, s, mode)
+    b = bound(o, s, mode, residual)
     nan = int(np.count_nonzero(~np.isfinite(g)))
     bad = ~(err <= b)
     n_bad = int(np.count_nonzero(bad))

@@ -18,6 +18,12 @@
  * Besides O it returns S[m][n] = sum_k |x[m][k] * W[n][k]|, which scales the
  * parity tolerance (|gpu - O| <= 1e-3 * S + 1e-6 for fp32 output).
  *
+ * The _t entry points take the input type: BF16 (f16 = 0) or FP16 (f16 = 1),
+ * the two weight types class PreparedProjection accepts on the page
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.projection".
+ * Every FP16 value is also exactly a double, and a product of two has at most
+ * 22 significant bits, so the same precision argument holds.
+ *
  * Precision: every BF16 value is exactly a double; every product of two BF16
  * values has at most 16 significant bits and is exact in double; the sums are
  * taken in double with k ascending.  For K <= 2^20 and the value ranges used,
@@ -40,30 +46,50 @@ static double bf16_to_double(uint16_t bits)
     return (double)f;
 }
 
-/* Decode a BF16 matrix into doubles (rows * cols values). */
-static double *decode(const uint16_t *src, long rows, long cols)
+/*
+ * IEEE 754 binary16: sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent 0 is zero or subnormal (fraction * 2^-24); exponent 31 is
+ * infinity (fraction 0) or NaN; otherwise (1024 + fraction) * 2^(e - 25).
+ */
+static double f16_to_double(uint16_t bits)
+{
+    const int sign = bits >> 15, e = (bits >> 10) & 0x1F, f = bits & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+static double to_double(uint16_t bits, int f16) { return f16 ? f16_to_double(bits) : bf16_to_double(bits); }
+
+/* Decode a BF16 or FP16 matrix into doubles (rows * cols values). */
+static double *decode(const uint16_t *src, long rows, long cols, int f16)
 {
     double *dst = (double *)malloc(sizeof(double) * (size_t)(rows * cols));
     if (!dst)
         return NULL;
     for (long i = 0; i < rows * cols; ++i)
-        dst[i] = bf16_to_double(src[i]);
+        dst[i] = to_double(src[i], f16);
     return dst;
 }
 
 /*
- * Full product.  x: [M][K] BF16 bits, w: [N][K] BF16 bits, row-major.
- * o, s: [M][N] doubles (s may be NULL).  Returns 0, or -1 on bad sizes or
- * allocation failure.
+ * Full product.  x: [M][K] bits, w: [N][K] bits, row-major, BF16 (f16 = 0)
+ * or FP16 (f16 = 1).  o, s: [M][N] doubles (s may be NULL).  Returns 0, or -1
+ * on bad sizes or allocation failure.
  */
-int oracle_gemm(const uint16_t *x, const uint16_t *w, int M, int N, int K,
-                double *o, double *s)
+int oracle_gemm_t(const uint16_t *x, const uint16_t *w, int M, int N, int K, int f16,
+                  double *o, double *s)
 {
     if (M < 0 || N < 0 || K < 0 || (M > 0 && N > 0 && (!x || !w || !o)))
         return -1;
     if (M == 0 || N == 0)
         return 0;
-    double *xd = decode(x, M, K);
+    double *xd = decode(x, M, K, f16);
     if (!xd)
         return -1;
     int failed = 0;
@@ -77,7 +103,7 @@ int oracle_gemm(const uint16_t *x, const uint16_t *w, int M, int N, int K,
 #pragma omp for schedule(static)
             for (int n = 0; n < N; ++n) {
                 for (int k = 0; k < K; ++k)
-                    wrow[k] = bf16_to_double(w[(long)n * K + k]);
+                    wrow[k] = to_double(w[(long)n * K + k], f16);
                 for (int m = 0; m < M; ++m) {
                     const double *xr = xd + (long)m * K;
                     double acc = 0.0, mag = 0.0;
@@ -98,13 +124,20 @@ int oracle_gemm(const uint16_t *x, const uint16_t *w, int M, int N, int K,
     return failed ? -1 : 0;
 }
 
+/* BF16 inputs. */
+int oracle_gemm(const uint16_t *x, const uint16_t *w, int M, int N, int K,
+                double *o, double *s)
+{
+    return oracle_gemm_t(x, w, M, N, K, 0, o, s);
+}
+
 /*
  * Selected elements only: for i < count, element (mi[i], ni[i]) of the same
  * product.  Lets large shapes be checked on a sample.
  */
-int oracle_gemm_sampled(const uint16_t *x, const uint16_t *w, int M, int N, int K,
-                        const int *mi, const int *ni, long count,
-                        double *o, double *s)
+int oracle_gemm_sampled_t(const uint16_t *x, const uint16_t *w, int M, int N, int K, int f16,
+                          const int *mi, const int *ni, long count,
+                          double *o, double *s)
 {
     if (M < 0 || N < 0 || K < 0 || count < 0)
         return -1;
@@ -117,7 +150,7 @@ int oracle_gemm_sampled(const uint16_t *x, const uint16_t *w, int M, int N, int 
         const uint16_t *wr = w + (long)ni[i] * K;
         double acc = 0.0, mag = 0.0;
         for (int k = 0; k < K; ++k) {
-            double p = bf16_to_double(xr[k]) * bf16_to_double(wr[k]);
+            double p = to_double(xr[k], f16) * to_double(wr[k], f16);
             acc += p;
             mag += fabs(p);
         }
@@ -126,6 +159,13 @@ int oracle_gemm_sampled(const uint16_t *x, const uint16_t *w, int M, int N, int 
             s[i] = mag;
     }
     return 0;
+}
+
+int oracle_gemm_sampled(const uint16_t *x, const uint16_t *w, int M, int N, int K,
+                        const int *mi, const int *ni, long count,
+                        double *o, double *s)
+{
+    return oracle_gemm_sampled_t(x, w, M, N, K, 0, mi, ni, count, o, s);
 }
 
 /*
@@ -183,6 +223,13 @@ void oracle_decode_bf16(const uint16_t *bits, long count, double *out)
 {
     for (long i = 0; i < count; ++i)
         out[i] = bf16_to_double(bits[i]);
+}
+
+/* Widen FP16 bit patterns to doubles (exact). */
+void oracle_decode_f16(const uint16_t *bits, long count, double *out)
+{
+    for (long i = 0; i < count; ++i)
+        out[i] = f16_to_double(bits[i]);
 }
 
 /* Threads an OpenMP parallel region uses here (for reporting). */

@@ -26,6 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libskinny.so")
 MAX_M = 64
 OUT_BF16 = 0
 OUT_F32 = 1
+IN_BF16 = 0
+IN_F16 = 1
 PATH_DOT2 = 0
 PATH_MFMA = 1
 PATH_DOT2X = 2
@@ -95,7 +97,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "skinny_prepare": (i, [vp, i, i, i, ctypes.POINTER(planp)]),
         "skinny_prepare_tactics": (i, [vp, i, i, i, tp, ctypes.POINTER(planp)]),
+        "skinny_prepare_ex": (i, [vp, i, i, i, i, i, ctypes.POINTER(planp)]),
+        "skinny_prepare_tactics_ex": (i, [vp, i, i, i, i, i, tp, ctypes.POINTER(planp)]),
         "skinny_run": (i, [planp, vp, vp, i, vp]),
+        "skinny_run_ex": (i, [planp, vp, i, vp, i, vp, i, i, vp]),
         "skinny_supports": (i, [planp, i]),
         "skinny_plan_tactic": (i, [planp, i, tp]),
         "skinny_describe": (i, [planp, i, ctypes.c_char_p, sz]),
@@ -183,8 +188,10 @@ class Prepared:
     """A prepared weight: tactic table, split-K workspace, warmed kernels.
 
     The plan keeps W's device pointer (not a copy); the tensor is held here so
-    it stays allocated.  ``table`` forces a per-M tactic list (64 entries)
-    instead of tuning on the device.
+    it stays allocated.  ``weight`` is BF16 or FP16 [N, K] with unit column
+    stride and a row pitch that is a multiple of 8 elements (16 bytes); x must
+    then have the same type.  ``table`` forces a per-M tactic list (64
+    entries) instead of tuning on the device.
     """
 
     def __init__(self, weight, out_dtype=None, table=None):
@@ -192,27 +199,30 @@ class Prepared:
         lib = load_library()
         if out_dtype is None:
             out_dtype = torch.bfloat16
-        if weight.dim() != 2 or weight.dtype != torch.bfloat16 or not weight.is_cuda:
-            raise ValueError("weight must be a 2-D torch.bfloat16 tensor on a GPU")
-        if weight.stride() != (weight.shape[1], 1):
-            raise ValueError("weight must be packed row-major [N, K]")
+        if weight.dim() != 2 or weight.dtype not in (torch.bfloat16, torch.float16) or not weight.is_cuda:
+            raise ValueError("weight must be a 2-D torch.bfloat16 or torch.float16 tensor on a GPU")
+        if weight.stride(1) != 1 or weight.stride(0) < weight.shape[1]:
+            raise ValueError("weight rows must have unit stride and a pitch >= K")
         if out_dtype not in (torch.bfloat16, torch.float32):
             raise ValueError(f"unsupported output dtype {out_dtype}")
         self.weight = weight
         self.n, self.k = weight.shape
+        self.in_dtype = weight.dtype
         self.out_dtype = out_dtype
         od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+        idt = IN_F16 if weight.dtype == torch.float16 else IN_BF16
+        ldw = weight.stride(0)
         self._plan = ctypes.c_void_p()
         with torch.cuda.device(weight.device):
             if table is None:
-                st = lib.skinny_prepare(weight.data_ptr(), self.n, self.k, od,
-                                        ctypes.byref(self._plan))
+                st = lib.skinny_prepare_ex(weight.data_ptr(), self.n, self.k, ldw, idt, od,
+                                           ctypes.byref(self._plan))
             else:
                 if len(table) != MAX_M:
                     raise ValueError("table needs one tactic per M = 1..64")
                 arr = (Tactic * MAX_M)(*[Tactic(*t.astuple()) for t in table])
-                st = lib.skinny_prepare_tactics(weight.data_ptr(), self.n, self.k, od, arr,
-                                                ctypes.byref(self._plan))
+                st = lib.skinny_prepare_tactics_ex(weight.data_ptr(), self.n, self.k, ldw, idt, od, arr,
+                                                   ctypes.byref(self._plan))
         _raise(st)
 
     def supports(self, tokens: int) -> bool:
@@ -228,27 +238,47 @@ class Prepared:
         _raise(load_library().skinny_describe(self._plan, tokens, buf, 256))
         return buf.value.decode()
 
-    def run(self, x, out, stream=None):
-        """out[:M] = x @ W^T with M = x.shape[0], on the current (or given) stream."""
+    def run(self, x, out, stream=None, residual=None):
+        """out[:M] = x @ W^T (+ residual[:M]) with M = x.shape[0], on the current
+        (or given) stream.  x, out and residual may be row-pitched views with
+        unit column stride; residual has out's dtype and may be out itself."""
         import torch
-        if x.dim() != 2 or x.shape[1] != self.k or x.dtype != torch.bfloat16:
-            raise ValueError(f"x must be bf16 [M, {self.k}], got {tuple(x.shape)} {x.dtype}")
-        if x.stride() != (self.k, 1):
-            raise ValueError("x must be packed row-major")
+        if x.dim() != 2 or x.shape[1] != self.k or x.dtype != self.in_dtype:
+            raise ValueError(f"x must be {self.in_dtype} [M, {self.k}], got {tuple(x.shape)} {x.dtype}")
         m = x.shape[0]
         if out.dim() != 2 or out.shape[1] != self.n or out.shape[0] < m or out.dtype != self.out_dtype:
             raise ValueError(f"out must be {self.out_dtype} [>= {m}, {self.n}]")
-        if out.stride() != (self.n, 1):
-            raise ValueError("out must be packed row-major")
-        if x.device != self.weight.device or out.device != self.weight.device:
-            raise ValueError("x, out and the weight must be on the same device")
-        self.run_ptr(x.data_ptr(), out.data_ptr(), m, stream)
+        for name, t in (("x", x), ("out", out)) + ((("residual", residual),) if residual is not None else ()):
+            if t.stride(1) != 1 and t.shape[1] > 1:
+                raise ValueError(f"{name} rows must have unit stride")
+            if t.device != self.weight.device:
+                raise ValueError(f"{name} and the weight must be on the same device")
+        if residual is not None and (residual.dim() != 2 or residual.shape[1] != self.n or
+                                     residual.shape[0] < m or residual.dtype != self.out_dtype):
+            raise ValueError(f"residual must be {self.out_dtype} [>= {m}, {self.n}]")
+        ldx = x.stride(0) if m > 1 else self.k
+        ldo = out.stride(0) if out.shape[0] > 1 else self.n
+        if residual is None:
+            self.run_ptr(x.data_ptr(), out.data_ptr(), m, stream, ldx=ldx, ldo=ldo)
+        else:
+            ldr = residual.stride(0) if residual.shape[0] > 1 else self.n
+            self.run_ptr(x.data_ptr(), out.data_ptr(), m, stream, ldx=ldx, ldo=ldo,
+                         res_ptr=residual.data_ptr(), ldr=ldr)
         return out
 
-    def run_ptr(self, x_ptr: int, out_ptr: int, m: int, stream=None):
+    def run_ptr(self, x_ptr: int, out_ptr: int, m: int, stream=None, ldx=None, ldo=None, res_ptr=None,
+                ldr=None):
         """Raw-pointer form of run (used inside graph capture loops)."""
-        _raise(load_library().skinny_run(self._plan, ctypes.c_void_p(x_ptr),
-                                         ctypes.c_void_p(out_ptr), m, _stream_handle(stream)))
+        lib = load_library()
+        if ldx is None and ldo is None and res_ptr is None:
+            _raise(lib.skinny_run(self._plan, ctypes.c_void_p(x_ptr), ctypes.c_void_p(out_ptr), m,
+                                  _stream_handle(stream)))
+            return
+        _raise(lib.skinny_run_ex(self._plan, ctypes.c_void_p(x_ptr), self.k if ldx is None else ldx,
+                                 ctypes.c_void_p(res_ptr) if res_ptr else None,
+                                 (self.n if ldr is None else ldr) if res_ptr else 0,
+                                 ctypes.c_void_p(out_ptr), self.n if ldo is None else ldo, m,
+                                 _stream_handle(stream)))
 
     def close(self):
         if self._plan:

@@ -54,16 +54,45 @@ __device__ __forceinline__ u32x4 load_stream(const u32x4 *p) { return __builtin_
 // whatever the component named, so components are copied to scalars first.
 __device__ __forceinline__ bf16x2 as_bf16x2(unsigned int word) { return __builtin_bit_cast(bf16x2, word); }
 
-// 8-element BF16 dot product accumulated into acc (4 x v_dot2_f32_bf16).
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+// The same for two FP16 values.
+__device__ __forceinline__ f16x2 as_f16x2(unsigned int word) { return __builtin_bit_cast(f16x2, word); }
+
+// 8-element dot product accumulated into acc: 4 x v_dot2_f32_bf16, or
+// 4 x v_dot2_f32_f16 for FP16 inputs (H).  Both multiply exactly and add in
+// fp32.
+template <bool H>
 __device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc)
 {
     const unsigned int w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
     const unsigned int x0 = x.x, x1 = x.y, x2 = x.z, x3 = x.w;
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(x0), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(x1), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(x2), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(x3), acc, false);
+    if constexpr (H) {
+        acc = __builtin_amdgcn_fdot2(as_f16x2(w0), as_f16x2(x0), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(w1), as_f16x2(x1), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(w2), as_f16x2(x2), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(w3), as_f16x2(x3), acc, false);
+    } else {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(x0), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(x1), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(x2), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(x3), acc, false);
+    }
     return acc;
+}
+
+// One 16x16x32 MFMA step, c += a b, with a and b holding 8 BF16 (or, H,
+// FP16) values per lane.
+template <bool H>
+__device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (H)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
 }
 
 // Workgroup -> (row tile, K split).  The dispatcher deals consecutive
@@ -83,9 +112,14 @@ __device__ __forceinline__ void block_coords(const KArgs &a, int &tile, int &s)
     s = idx - tile * a.split;
 }
 
+// out[m][n] = v (+ res[m][n], added in fp32 before the one rounding to BF16)
 __device__ __forceinline__ void store_out(const KArgs &a, int m, int n, float v)
 {
-    const long off = (long)m * a.N + n;
+    const long off = (long)m * a.ldo + n;
+    if (a.res) {
+        const long roff = (long)m * a.ldr + n;
+        v += a.out_f32 ? static_cast<const float *>(a.res)[roff] : (float)static_cast<const __bf16 *>(a.res)[roff];
+    }
     if (a.out_f32)
         static_cast<float *>(a.out)[off] = v;
     else
@@ -315,7 +349,7 @@ __device__ __forceinline__ u32x4 load_x(__amdgpu_buffer_rsrc_t r, unsigned voff,
 // stage j + 1 are issued before stage j is multiplied, so every wave keeps
 // U * (R + MT) 16-byte loads in flight while it computes.
 // ---------------------------------------------------------------------------
-template <int MT, int R, int U>
+template <int MT, int R, int U, bool H>
 __global__ __launch_bounds__(512) void k_dot2(KArgs a)
 {
     constexpr int V = MT * R;   // partial sums per lane, index m * R + r
@@ -329,11 +363,11 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
     const int n0 = tile * R;
     const int kb = (int)(((long)s * a.K8) / a.split);
     const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
-    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(min(R, a.N - n0));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)n0 * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
     const unsigned lane_off = (unsigned)(kb + tid) * 16u;
     const unsigned pass_bytes = (unsigned)nthr * 16u;
 
@@ -355,7 +389,7 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
                 w[u][r] = load_w(wres, (unsigned)r * row_bytes + lane_off, so);
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-                x[u][m] = load_x(xres, (unsigned)m * row_bytes + lane_off, so);
+                x[u][m] = load_x(xres, (unsigned)m * x_pitch + lane_off, so);
         }
         // keep the scheduler from hoisting the previous stage's arithmetic
         // above these loads: they must be in flight while it runs
@@ -368,7 +402,7 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    acc[m * R + r] = dot8(w[u][r], x[u][m], acc[m * R + r]);
+                    acc[m * R + r] = dot8<H>(w[u][r], x[u][m], acc[m * R + r]);
     };
     // Loads inside the loop are unconditional: a load under a branch would
     // leave the two paths with different counts of loads in flight, and the
@@ -400,12 +434,12 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
             w[0][r] = load_w(wres, ok ? (unsigned)r * row_bytes + lane_off : kOffOob, so);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            x[0][m] = load_x(xres, ok ? (unsigned)m * row_bytes + lane_off : kOffOob, so);
+            x[0][m] = load_x(xres, ok ? (unsigned)m * x_pitch + lane_off : kOffOob, so);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-                acc[m * R + r] = dot8(w[0][r], x[0][m], acc[m * R + r]);
+                acc[m * R + r] = dot8<H>(w[0][r], x[0][m], acc[m * R + r]);
     }
 
     wave_reduce_transpose<V>(acc, lane);
@@ -466,7 +500,7 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
 // summed over waves in LDS, laid out [wave][token][row] so that the final
 // stores of out[token][n0 + row] are row-contiguous.
 // ---------------------------------------------------------------------------
-template <int T, int RT, int U>
+template <int T, int RT, int U, bool H>
 __global__ __launch_bounds__(512) void k_mfma(KArgs a)
 {
     constexpr int MT = 16 * T, NT = 16 * RT, NTP = NT + 1;
@@ -487,11 +521,11 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
     const int se = (int)(((long)(s + 1) * steps) / a.split);
     const int se_full = se < steps_full ? se : steps_full;
 
-    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(min(NT, a.N - n0));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)n0 * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
     const unsigned k_off = (unsigned)(4 * (sb + wave) + g) * 16u;   // this lane's first chunk
     const unsigned step_bytes = (unsigned)nwaves * 64u;             // one step of every wave
 
@@ -517,7 +551,7 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
                 av[u][rt] = load_w(wres, (unsigned)(16 * rt + i16) * row_bytes + k_off, so);
 #pragma unroll
             for (int t = 0; t < T; ++t)
-                bv[u][t] = load_x(xres, (unsigned)(16 * t + i16) * row_bytes + k_off, so);
+                bv[u][t] = load_x(xres, (unsigned)(16 * t + i16) * x_pitch + k_off, so);
         }
         __builtin_amdgcn_sched_barrier(0);   // loads stay ahead of the MFMAs
     };
@@ -528,9 +562,7 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int t = 0; t < T; ++t)
-                    acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, av[u][rt]), __builtin_bit_cast(bf16x8, bv[u][t]),
-                        acc[rt][t], 0, 0, 0);
+                    acc[rt][t] = mma16<H>(av[u][rt], bv[u][t], acc[rt][t]);
     };
     if (stages > 0) {   // same pipeline shape as the DOT2 kernel
         load(aa, ba, 0);
@@ -559,14 +591,12 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
             av[0][rt] = load_w(wres, ok ? (unsigned)(16 * rt + i16) * row_bytes + k_off : kOffOob, so);
 #pragma unroll
         for (int t = 0; t < T; ++t)
-            bv[0][t] = load_x(xres, ok ? (unsigned)(16 * t + i16) * row_bytes + k_off : kOffOob, so);
+            bv[0][t] = load_x(xres, ok ? (unsigned)(16 * t + i16) * x_pitch + k_off : kOffOob, so);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int t = 0; t < T; ++t)
-                acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, av[0][rt]), __builtin_bit_cast(bf16x8, bv[0][t]),
-                    acc[rt][t], 0, 0, 0);
+                acc[rt][t] = mma16<H>(av[0][rt], bv[0][t], acc[rt][t]);
     }
 
     // accumulator fragments -> LDS [wave][token][row]
@@ -637,7 +667,7 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
 // path: only W flows through it.  No cross-wave reduction is needed; the
 // in-wave transposing reduction finishes each wave's R x MT outputs.
 // ---------------------------------------------------------------------------
-template <int MT, int R, int U>
+template <int MT, int R, int U, bool H>
 __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
 {
     constexpr int V = MT * R;
@@ -654,11 +684,11 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
     const int kb = (int)(((long)s * a.K8) / a.split);
     const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
     const int kr = ke - kb;
-    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(max(0, min(R, a.N - n0)));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
     const unsigned lane_off = (unsigned)(kb + lane) * 16u;
     constexpr unsigned kPass = 64u * 16u;      // one wave-wide pass: 64 chunks
 
@@ -689,7 +719,7 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
                 const u32x4 xv = xs[m * kr + c];
 #pragma unroll
                 for (int r = 0; r < R; ++r)
-                    acc[m * R + r] = dot8(w[u][r], xv, acc[m * R + r]);
+                    acc[m * R + r] = dot8<H>(w[u][r], xv, acc[m * R + r]);
             }
         }
     };
@@ -705,7 +735,7 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
             for (int i = 0; i < 8; ++i) {
                 const int q = q0 + i * nthr;
                 const int m = q / kr, c = q - (q / kr) * kr;
-                v[i] = load_x(xres, q < total ? (unsigned)m * row_bytes + (unsigned)(kb + c) * 16u : kOffOob, 0);
+                v[i] = load_x(xres, q < total ? (unsigned)m * x_pitch + (unsigned)(kb + c) * 16u : kOffOob, 0);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -747,7 +777,7 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
             const u32x4 xv = ok ? xs[m * kr + (ok ? c : 0)] : zero;   // index kept in range
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                acc[m * R + r] = dot8(w[r], xv, acc[m * R + r]);
+                acc[m * R + r] = dot8<H>(w[r], xv, acc[m * R + r]);
         }
     }
 
@@ -825,7 +855,7 @@ __device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, const float *
 // read as B fragments.  Loading W with the 16-row MFMA pattern directly would
 // split every request into 64-byte halves of lines.
 // ---------------------------------------------------------------------------
-template <int T, int NW>
+template <int T, int NW, bool H>
 __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
 {
     constexpr int MT = 16 * T;
@@ -845,11 +875,11 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
     const int kb = (int)(((long)s * a.K8) / a.split);
     const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
     const int stages = (ke - kb + KW - 1) / KW;
-    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(max(0, min(16, a.N - n0)));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
     u32x4 *wl = sm + wave * 16 * PITCH;
     u32x4 *xl = sm + NW * 16 * PITCH;
 
@@ -876,7 +906,7 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
             const int e = tid + 64 * NW * i;
             const int tok = e / KW, cc = kb + j * KW + (e % KW);
             const bool xok = j < stages && cc < ke;
-            xv[i] = load_x(xres, xok ? (unsigned)tok * row_bytes + (unsigned)cc * 16u : kOffOob, 0);
+            xv[i] = load_x(xres, xok ? (unsigned)tok * x_pitch + (unsigned)cc * 16u : kOffOob, 0);
         }
     };
     auto stage = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
@@ -909,9 +939,7 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
                 for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
                     for (int t = 0; t < T; ++t)
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s4]),
-                                                                         __builtin_bit_cast(bf16x8, bv[s4][t]),
-                                                                         acc[t], 0, 0, 0);
+                        acc[t] = mma16<H>(av[s4], bv[s4][t], acc[t]);
             }
         } else {
 #pragma unroll
@@ -920,8 +948,7 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const u32x4 bv = xw[(16 * t + i16) * PITCH + 4 * st + g];
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+                    acc[t] = mma16<H>(av, bv, acc[t]);
                 }
             }
         }
@@ -990,7 +1017,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, u32x4 *lds_dst, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, voff, 0, 0, kCpolNt);
 }
 
-template <int T, int NW, int D>
+template <int T, int NW, int D, bool H>
 __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
 {
     constexpr int MT = 16 * T;
@@ -1011,11 +1038,11 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
     const int kb = (int)(((long)s * a.K8) / a.split);
     const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
     const int stages = (ke - kb + KW - 1) / KW;
-    const unsigned row_bytes = (unsigned)a.K8 * 16u;
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(max(0, min(16, a.N - n0)));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
     u32x4 *wring = sm + wave * D * WSLOT;
     u32x4 *xring = sm + NW * D * WSLOT;
 
@@ -1043,7 +1070,7 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
             const int pair = wave + NW * i;        // tokens 2 pair, 2 pair + 1
             const int tok = 2 * pair + half;
             const int c = cbase + (pos ^ (tok & 15));
-            const unsigned off = c < lim ? (unsigned)tok * row_bytes + (unsigned)c * 16u : kOffOob;
+            const unsigned off = c < lim ? (unsigned)tok * x_pitch + (unsigned)c * 16u : kOffOob;
             dma16(xres, xring + slot * XSLOT + 2 * pair * KW, off);
         }
     };
@@ -1079,8 +1106,7 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const u32x4 bv = xsl[(16 * t + i16) * KW + p];
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+                acc[t] = mma16<H>(av, bv, acc[t]);
             }
         }
     }
@@ -1154,7 +1180,7 @@ __device__ __forceinline__ int sk_owner(unsigned u, unsigned units, unsigned G)
     return (int)((((unsigned long long)u + 1) * G - 1) / units);
 }
 
-template <int T, int NW, int U>
+template <int T, int NW, int U, bool H>
 __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
 {
     constexpr int MT = 16 * T;
@@ -1175,8 +1201,8 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
     const unsigned u0 = (unsigned)(((unsigned long long)gi * units) / G);
     const unsigned u1 = (unsigned)(((unsigned long long)(gi + 1) * units) / G);
     const int count = (int)(u1 - u0);
-    const unsigned row_bytes = (unsigned)a.K8 * 16u;
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * row_bytes);
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
     u32x4 *wl = sm + wave * 16 * PITCH;
     u32x4 *xl = sm + NW * 16 * PITCH;
     const int wrow = lane >> 5, wcol = lane & 31;
@@ -1206,7 +1232,7 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
         for (int i = 0; i < XL; ++i) {
             const int e = tid + 64 * NW * i;
             const int tok = e / KW, cc = cbase + (e % KW);
-            xv[i] = load_x(xres, lane_off(cc < lim, (unsigned)tok * row_bytes + (unsigned)cc * 16u), 0);
+            xv[i] = load_x(xres, lane_off(cc < lim, (unsigned)tok * x_pitch + (unsigned)cc * 16u), 0);
         }
         const bool wrap = ld_step + 1 == spt;
         ld_step = wrap ? 0u : ld_step + 1;
@@ -1277,8 +1303,7 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int t = 0; t < T; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, av[s]), __builtin_bit_cast(bf16x8, bv[s][t]), acc[t], 0, 0, 0);
+                    acc[t] = mma16<H>(av[s], bv[s][t], acc[t]);
         }
         // a segment ends at its tile's last stage or at the range's last
         // stage; the segment of the range's last stage is handled after the
@@ -1406,12 +1431,16 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
 // Instance table
 // ---------------------------------------------------------------------------
 
-#define SK_DOT2(MT, R, U) {SKINNY_PATH_DOT2, MT, R, U, (const void *)&k_dot2<MT, R, U>}
-#define SK_MFMA(T, RT, U) {SKINNY_PATH_MFMA, 16 * T, 16 * RT, U, (const void *)&k_mfma<T, RT, U>}
-#define SK_DOT2X(MT, R, U) {SKINNY_PATH_DOT2X, MT, R, U, (const void *)&k_dot2x<MT, R, U>}
-#define SK_MFMAX(T, NW) {SKINNY_PATH_MFMAX, 16 * T, NW, 1, (const void *)&k_mfmax<T, NW>}
-#define SK_MFMAD(T, NW, D) {SKINNY_PATH_MFMAD, 16 * T, NW, D, (const void *)&k_mfmad<T, NW, D>}
-#define SK_MFMAS(T, NW, D) {SKINNY_PATH_MFMAS, 16 * T, NW, D, (const void *)&k_mfmas<T, NW, D>}
+// Every instance is compiled for BF16 (half = 0) and FP16 (half = 1) inputs.
+#define SK_PAIR(PATH, MT, ROWS, U, KERNEL, ...)                                                        \
+    {PATH, MT, ROWS, U, 0, (const void *)&KERNEL<__VA_ARGS__, false>},                               \
+        {PATH, MT, ROWS, U, 1, (const void *)&KERNEL<__VA_ARGS__, true>}
+#define SK_DOT2(MT, R, U) SK_PAIR(SKINNY_PATH_DOT2, MT, R, U, k_dot2, MT, R, U)
+#define SK_MFMA(T, RT, U) SK_PAIR(SKINNY_PATH_MFMA, 16 * T, 16 * RT, U, k_mfma, T, RT, U)
+#define SK_DOT2X(MT, R, U) SK_PAIR(SKINNY_PATH_DOT2X, MT, R, U, k_dot2x, MT, R, U)
+#define SK_MFMAX(T, NW) SK_PAIR(SKINNY_PATH_MFMAX, 16 * T, NW, 1, k_mfmax, T, NW)
+#define SK_MFMAD(T, NW, D) SK_PAIR(SKINNY_PATH_MFMAD, 16 * T, NW, D, k_mfmad, T, NW, D)
+#define SK_MFMAS(T, NW, D) SK_PAIR(SKINNY_PATH_MFMAS, 16 * T, NW, D, k_mfmas, T, NW, D)
 
 // Instances whose double-buffered loads, accumulators and offsets fit in 256
 // VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
@@ -1464,10 +1493,10 @@ const KernelInfo *kernel_table(int *count)
     return kKernels;
 }
 
-const KernelInfo *find_kernel(int path, int mt, int rows, int unroll)
+const KernelInfo *find_kernel(int path, int mt, int rows, int unroll, int half)
 {
     for (const KernelInfo &k : kKernels)
-        if (k.path == path && k.mt == mt && k.rows == rows && k.unroll == unroll)
+        if (k.path == path && k.mt == mt && k.rows == rows && k.unroll == unroll && k.half == half)
             return &k;
     return nullptr;
 }

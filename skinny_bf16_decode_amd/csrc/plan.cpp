@@ -43,6 +43,8 @@ struct skinny_plan {
     int device = -1;
     const void *W = nullptr;
     int N = 0, K = 0;
+    int ldw = 0;                     // W row pitch, elements
+    int half = 0;                    // 1: FP16 inputs
     skinny_out_dtype od = SKINNY_OUT_BF16;
     float *ws = nullptr;
     unsigned *ctr = nullptr;
@@ -52,7 +54,7 @@ struct skinny_plan {
 
 namespace {
 
-using Key = std::tuple<int, int, int, int>;   // device, N, K, out dtype
+using Key = std::tuple<int, int, int, int, int>;   // device, N, K, in dtype, out dtype
 std::mutex g_cache_mu;
 std::map<Key, std::array<skinny_tactic, SKINNY_MAX_M>> g_cache;
 
@@ -121,10 +123,10 @@ void stream_k_shape(Entry &en, int K)
     en.sk_parts = parts;
 }
 
-Entry make_entry(const skinny_tactic &t, int N, int K)
+Entry make_entry(const skinny_tactic &t, int N, int K, int half)
 {
     Entry en;
-    const KernelInfo *k = tactic_kernel(t);
+    const KernelInfo *k = tactic_kernel(t, half);
     en.fn = k ? k->fn : nullptr;
     en.n_tiles = tiles_for(t, N);
     if (t.path == SKINNY_PATH_MFMAR) {
@@ -212,7 +214,8 @@ hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
 }
 
 // Validation shared by the prepare entry points; no HIP call before it passes.
-skinny_status check_prepare_args(const void *W, int N, int K, skinny_out_dtype od, skinny_plan **plan)
+skinny_status check_prepare_args(const void *W, int N, int K, int ldw, int in_dtype, skinny_out_dtype od,
+                                 skinny_plan **plan)
 {
     if (!plan) {
         set_error("plan out-pointer is NULL");
@@ -231,8 +234,20 @@ skinny_status check_prepare_args(const void *W, int N, int K, skinny_out_dtype o
         set_error("out_dtype=%d is not SKINNY_OUT_BF16 or SKINNY_OUT_F32", (int)od);
         return SKINNY_ERR_INVALID_ARG;
     }
+    if (in_dtype != SKINNY_IN_BF16 && in_dtype != SKINNY_IN_F16) {
+        set_error("in_dtype=%d is not SKINNY_IN_BF16 or SKINNY_IN_F16", in_dtype);
+        return SKINNY_ERR_INVALID_ARG;
+    }
     if (K % 8) {
         set_error("K=%d is not a multiple of 8 (rows must be whole 16-byte chunks)", K);
+        return SKINNY_ERR_SHAPE;
+    }
+    if (ldw < K || ldw % 8) {
+        set_error("ldw=%d must be >= K=%d and a multiple of 8 (a 16-byte row pitch)", ldw, K);
+        return SKINNY_ERR_SHAPE;
+    }
+    if ((long long)ldw * 16 * 2 >= (1LL << 31)) {
+        set_error("ldw=%d: 16 rows of W must span less than 2 GiB", ldw);
         return SKINNY_ERR_SHAPE;
     }
     if ((long long)N * K >= (1LL << 31)) {
@@ -274,7 +289,7 @@ struct DevBuf {
 };
 
 // Time every candidate on cache-cold copies of W and fill the table.
-skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
+skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int nxcd,
                    std::array<skinny_tactic, SKINNY_MAX_M> &table)
 {
     const int count = skinny_enumerate_tactics(N, K, nullptr, 0);
@@ -290,7 +305,7 @@ skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
     int copies = (int)std::min<size_t>(16, std::max<size_t>(1, (cold + wbytes - 1) / wbytes));
     size_t max_ws = 0, max_tiles = 0;
     for (const skinny_tactic &t : cand) {
-        Entry en = make_entry(t, N, K);
+        Entry en = make_entry(t, N, K, half);
         max_ws = std::max(max_ws, ws_floats(en));
         max_tiles = std::max(max_tiles, (size_t)en.n_tiles);
     }
@@ -306,8 +321,10 @@ skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
         hipStream_t s;
         ~StreamGuard() { (void)hipStreamDestroy(s); }
     } sg{st};
+    // packed copies of W (its pitch does not change the tactic)
     for (int c = 0; c < copies; ++c)
-        HIP_TRY(hipMemcpyAsync((char *)wcopies.p + wbytes * c, W, wbytes, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpy2DAsync((char *)wcopies.p + wbytes * c, (size_t)K * 2, W, (size_t)ldw * 2, (size_t)K * 2, N,
+                                 hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemsetAsync(xbuf.p, 0, (size_t)SKINNY_MAX_M * K * 2, st));
     HIP_TRY(hipMemsetAsync(ctrbuf.p, 0, std::max<size_t>(max_tiles, 1) * 4, st));
     hipEvent_t e0, e1;
@@ -331,11 +348,13 @@ skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
     a.K8 = K / 8;
     a.out_f32 = od == SKINNY_OUT_F32;
     a.nxcd = nxcd;
+    a.w_pitch = a.x_pitch = (unsigned)K * 2u;
+    a.ldo = a.ldr = N;
 
     const int iters = std::max(1, env_int("SKINNY_TUNE_ITERS", 2 * copies > 8 ? 2 * copies : 8));
     std::vector<double> times(count, -1.0);
     for (int i = 0; i < count; ++i) {
-        const Entry en = make_entry(cand[i], N, K);
+        const Entry en = make_entry(cand[i], N, K, half);
         if (!en.fn || !lds_fits(en.fn, en.lds))
             continue;
         a.M = cand[i].mt;
@@ -386,12 +405,12 @@ skinny_status tune(const void *W, int N, int K, skinny_out_dtype od, int nxcd,
 // Tuned tables persisted across processes (SKINNY_TABLE_CACHE=<file>), keyed
 // like the pages' per-part measured tables by the chip (arch, CU count) and
 // the shape.  One line per table:
-//   skinny-table v1 <arch> <cus> <N> <K> <bf16|f32> <64 x path.mt.rows.waves.unroll.split>
+//   skinny-table v2 <arch> <cus> <N> <K> <bf16|f16 in> <bf16|f32 out> <64 x path.mt.rows.waves.unroll.split>
 // A line whose tactics fail validation is ignored.  Writers append.
 // ---------------------------------------------------------------------------
 const char *kTableTag = "skinny-table";
 
-bool load_table_file(const char *path, int cus, int N, int K, skinny_out_dtype od,
+bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
                      std::array<skinny_tactic, SKINNY_MAX_M> &table)
 {
     FILE *f = fopen(path, "r");
@@ -400,12 +419,13 @@ bool load_table_file(const char *path, int cus, int N, int K, skinny_out_dtype o
     char line[8192];
     bool found = false;
     while (!found && fgets(line, sizeof line, f)) {
-        char tag[32], ver[8], arch[32], ods[8];
+        char tag[32], ver[8], arch[32], ins[8], ods[8];
         int c, n, k, pos = 0;
-        if (sscanf(line, "%31s %7s %31s %d %d %d %7s%n", tag, ver, arch, &c, &n, &k, ods, &pos) != 7)
+        if (sscanf(line, "%31s %7s %31s %d %d %d %7s %7s%n", tag, ver, arch, &c, &n, &k, ins, ods, &pos) != 8)
             continue;
-        if (strcmp(tag, kTableTag) || strcmp(ver, "v1") || strcmp(arch, "gfx950") || c != cus ||
-            n != N || k != K || strcmp(ods, od == SKINNY_OUT_F32 ? "f32" : "bf16"))
+        if (strcmp(tag, kTableTag) || strcmp(ver, "v2") || strcmp(arch, "gfx950") || c != cus ||
+            n != N || k != K || strcmp(ins, half ? "f16" : "bf16") ||
+            strcmp(ods, od == SKINNY_OUT_F32 ? "f32" : "bf16"))
             continue;
         std::array<skinny_tactic, SKINNY_MAX_M> t;
         const char *q = line + pos;
@@ -427,20 +447,21 @@ bool load_table_file(const char *path, int cus, int N, int K, skinny_out_dtype o
     return found;
 }
 
-void save_table_file(const char *path, int cus, int N, int K, skinny_out_dtype od,
+void save_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
                      const std::array<skinny_tactic, SKINNY_MAX_M> &table)
 {
     FILE *f = fopen(path, "a");
     if (!f)
         return;
-    fprintf(f, "%s v1 gfx950 %d %d %d %s", kTableTag, cus, N, K, od == SKINNY_OUT_F32 ? "f32" : "bf16");
+    fprintf(f, "%s v2 gfx950 %d %d %d %s %s", kTableTag, cus, N, K, half ? "f16" : "bf16",
+            od == SKINNY_OUT_F32 ? "f32" : "bf16");
     for (const skinny_tactic &e : table)
         fprintf(f, " %d.%d.%d.%d.%d.%d", e.path, e.mt, e.rows, e.waves, e.unroll, e.split);
     fprintf(f, "\n");
     fclose(f);
 }
 
-skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int dev, int nxcd,
+skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int dev, int nxcd,
                          const skinny_tactic *table, skinny_plan **out)
 {
     for (int m = 1; m <= SKINNY_MAX_M; ++m) {
@@ -462,10 +483,12 @@ skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int d
     p->W = W;
     p->N = N;
     p->K = K;
+    p->ldw = ldw;
+    p->half = half;
     p->od = od;
     size_t max_ws = 0, max_tiles = 0;
     for (int m = 1; m <= SKINNY_MAX_M; ++m) {
-        p->e[m] = make_entry(table[m - 1], N, K);
+        p->e[m] = make_entry(table[m - 1], N, K, half);
         if (!p->e[m].fn || !lds_fits(p->e[m].fn, p->e[m].lds)) {
             set_error("table entry for M=%d needs %u bytes of dynamic LDS, more than the device allows "
                       "with the kernel's static LDS", m, p->e[m].lds);
@@ -502,6 +525,9 @@ skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int d
     a.N = N;
     a.K8 = K / 8;
     a.out_f32 = od == SKINNY_OUT_F32;
+    a.w_pitch = (unsigned)ldw * 2u;
+    a.x_pitch = (unsigned)K * 2u;       // per call
+    a.ldo = a.ldr = N;                  // per call
     // SKINNY_XCD_REMAP=0 turns off the placement of a tile's split-K
     // workgroups on one XCD (then the partial exchange crosses XCDs).
     a.nxcd = env_int("SKINNY_XCD_REMAP", 1) ? nxcd : 1;
@@ -554,11 +580,13 @@ skinny_status build_plan(const void *W, int N, int K, skinny_out_dtype od, int d
 
 extern "C" {
 
-skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype od, skinny_plan **plan)
+skinny_status skinny_prepare_ex(const void *W, int N, int K, int ldw, skinny_in_dtype in_dtype,
+                                skinny_out_dtype od, skinny_plan **plan)
 {
-    skinny_status s = check_prepare_args(W, N, K, od, plan);
+    skinny_status s = check_prepare_args(W, N, K, ldw, (int)in_dtype, od, plan);
     if (s != SKINNY_OK)
         return s;
+    const int half = in_dtype == SKINNY_IN_F16;
     int dev = 0, cus = 0;
     if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)
         return s;
@@ -567,30 +595,35 @@ skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype od, s
     std::array<skinny_tactic, SKINNY_MAX_M> table;
     {
         std::lock_guard<std::mutex> lock(g_cache_mu);
-        const Key key{dev, N, K, (int)od};
+        const Key key{dev, N, K, half, (int)od};
         auto it = g_cache.find(key);
         const char *file = getenv("SKINNY_TABLE_CACHE");
         if (it != g_cache.end()) {
             table = it->second;
-        } else if (file && *file && load_table_file(file, cus, N, K, od, table)) {
+        } else if (file && *file && load_table_file(file, cus, N, K, half, od, table)) {
             if (env_flag("SKINNY_LOG"))
                 fprintf(stderr, "[skinny] N=%d K=%d: table loaded from %s\n", N, K, file);
             g_cache[key] = table;
         } else {
-            if ((s = tune(W, N, K, od, nxcd, table)) != SKINNY_OK)
+            if ((s = tune(W, N, K, ldw, half, od, nxcd, table)) != SKINNY_OK)
                 return s;
             g_cache[key] = table;
             if (file && *file)
-                save_table_file(file, cus, N, K, od, table);
+                save_table_file(file, cus, N, K, half, od, table);
         }
     }
-    return build_plan(W, N, K, od, dev, nxcd, table.data(), plan);
+    return build_plan(W, N, K, ldw, half, od, dev, nxcd, table.data(), plan);
 }
 
-skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dtype od,
-                                     const skinny_tactic *table, skinny_plan **plan)
+skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype od, skinny_plan **plan)
 {
-    skinny_status s = check_prepare_args(W, N, K, od, plan);
+    return skinny_prepare_ex(W, N, K, K, SKINNY_IN_BF16, od, plan);
+}
+
+skinny_status skinny_prepare_tactics_ex(const void *W, int N, int K, int ldw, skinny_in_dtype in_dtype,
+                                        skinny_out_dtype od, const skinny_tactic *table, skinny_plan **plan)
+{
+    skinny_status s = check_prepare_args(W, N, K, ldw, (int)in_dtype, od, plan);
     if (s != SKINNY_OK)
         return s;
     if (!table) {
@@ -609,10 +642,17 @@ skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dty
     if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)
         return s;
     raise_lds_limits();
-    return build_plan(W, N, K, od, dev, cus % 8 == 0 ? 8 : 1, table, plan);
+    return build_plan(W, N, K, ldw, in_dtype == SKINNY_IN_F16, od, dev, cus % 8 == 0 ? 8 : 1, table, plan);
 }
 
-skinny_status skinny_run(const skinny_plan *p, const void *x, void *out, int M, void *stream)
+skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dtype od,
+                                     const skinny_tactic *table, skinny_plan **plan)
+{
+    return skinny_prepare_tactics_ex(W, N, K, K, SKINNY_IN_BF16, od, table, plan);
+}
+
+skinny_status skinny_run_ex(const skinny_plan *p, const void *x, int ldx, const void *residual, int ldr,
+                            void *out, int ldo, int M, void *stream)
 {
     if (!p) {
         set_error("plan is NULL");
@@ -626,20 +666,50 @@ skinny_status skinny_run(const skinny_plan *p, const void *x, void *out, int M, 
         set_error("x or out is NULL");
         return SKINNY_ERR_INVALID_ARG;
     }
-    const uintptr_t out_align = p->od == SKINNY_OUT_F32 ? 3 : 1;
-    if (((uintptr_t)x & 15) || ((uintptr_t)out & out_align)) {
-        set_error("x=%p must be 16-byte aligned and out=%p element aligned", x, out);
+    if (ldx < p->K || ldx % 8 || ldo < p->N || (residual && ldr < p->N)) {
+        set_error("ldx=%d (>= K=%d, multiple of 8), ldo=%d and ldr=%d (>= N=%d) out of range", ldx, p->K, ldo,
+                  ldr, p->N);
+        return SKINNY_ERR_SHAPE;
+    }
+    const size_t osz = p->od == SKINNY_OUT_F32 ? 4 : 2;
+    if ((long long)ldx * (SKINNY_MAX_M * 2) >= (1LL << 31)) {
+        set_error("ldx=%d: 64 rows of x must span less than 2 GiB", ldx);
+        return SKINNY_ERR_SHAPE;
+    }
+    if (((uintptr_t)x & 15) || ((uintptr_t)out & (osz - 1)) || ((uintptr_t)residual & (osz - 1))) {
+        set_error("x=%p must be 16-byte aligned, out=%p and residual=%p element aligned", x, out, residual);
         return SKINNY_ERR_ALIGN;
+    }
+    if (residual && residual != out) {
+        // the residual must be out itself or lie apart from it
+        const char *o0 = (const char *)out, *o1 = o0 + ((size_t)(M - 1) * ldo + p->N) * osz;
+        const char *r0 = (const char *)residual, *r1 = r0 + ((size_t)(M - 1) * ldr + p->N) * osz;
+        if (r0 < o1 && o0 < r1) {
+            set_error("residual=%p overlaps out=%p without being it", residual, out);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+    } else if (residual && ldr != ldo) {
+        set_error("residual is out but ldr=%d != ldo=%d", ldr, ldo);
+        return SKINNY_ERR_INVALID_ARG;
     }
     const Entry &en = p->e[M];
     KArgs a = p->base;
     a.x = x;
     a.out = out;
+    a.res = residual;
     a.M = M;
+    a.x_pitch = (unsigned)ldx * 2u;
+    a.ldo = ldo;
+    a.ldr = residual ? ldr : ldo;
     hipError_t e = launch(en, a, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "hipLaunchKernel");
     return SKINNY_OK;
+}
+
+skinny_status skinny_run(const skinny_plan *p, const void *x, void *out, int M, void *stream)
+{
+    return skinny_run_ex(p, x, p ? p->K : 0, nullptr, 0, out, p ? p->N : 0, M, stream);
 }
 
 int skinny_supports(const skinny_plan *p, int M) { return p && M >= 1 && M <= SKINNY_MAX_M; }

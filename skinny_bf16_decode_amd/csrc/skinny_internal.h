@@ -9,12 +9,14 @@
 
 namespace skinny {
 
-// Arguments of every kernel, passed by value.  W, x are viewed as arrays of
-// 16-byte chunks (8 BF16 values); K8 = K / 8 chunks per row.
+// Arguments of every kernel, passed by value.  W, x are viewed as rows of
+// 16-byte chunks (8 BF16 or FP16 values); K8 = K / 8 chunks per row, rows
+// w_pitch / x_pitch bytes apart.
 struct KArgs {
-    const void *W;      // [N][K8] chunks
-    const void *x;      // [M][K8] chunks
-    void *out;          // [M][N] BF16 or fp32
+    const void *W;      // [N] rows of K8 chunks, w_pitch bytes apart
+    const void *x;      // [M] rows of K8 chunks, x_pitch bytes apart
+    void *out;          // [M][ldo] BF16 or fp32
+    const void *res;    // [M][ldr], the out type, added before the store; or NULL
     float *ws;          // split-K partials, [tile][split][mt][rows]
     unsigned *ctr;      // split-K arrival counters, one per row tile
     int N;
@@ -29,21 +31,28 @@ struct KArgs {
     // dealt evenly over gridDim.x workgroups; sk_parts partial slots per tile
     int sk_spt;
     int sk_parts;
+    unsigned w_pitch;   // bytes between rows of W (multiple of 16)
+    unsigned x_pitch;   // bytes between rows of x (multiple of 16)
+    int ldo;            // elements between rows of out
+    int ldr;            // elements between rows of res
 };
 
 // A compiled kernel instance.
 struct KernelInfo {
     int path, mt, rows, unroll;
+    int half;           // 0: BF16 inputs, 1: FP16 inputs
     const void *fn;     // host stub address for hipLaunchKernel
 };
 
 // All compiled instances (defined next to the kernels).
 const KernelInfo *kernel_table(int *count);
-const KernelInfo *find_kernel(int path, int mt, int rows, int unroll);
+const KernelInfo *find_kernel(int path, int mt, int rows, int unroll, int half);
 
-// The compiled instance a tactic runs (KernelInfo.rows is rows per workgroup
-// for DOT2/MFMA, rows per wave for DOT2X, waves for MFMAX), or nullptr.
-const KernelInfo *tactic_kernel(const skinny_tactic &t);
+// The compiled instance a tactic runs for BF16 (half = 0) or FP16 inputs
+// (KernelInfo.rows is rows per workgroup for DOT2/MFMA, rows per wave for
+// DOT2X, waves for MFMAX/MFMAD/MFMAS), or nullptr.  Every instance exists for
+// both input types, so a tactic's legality does not depend on it.
+const KernelInfo *tactic_kernel(const skinny_tactic &t, int half = 0);
 
 // Measurement probe kernels (host stub addresses).
 const void *probe_read_fn();

@@ -37,29 +37,29 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
     }
 }
 
-const KernelInfo *tactic_kernel(const skinny_tactic &t)
+const KernelInfo *tactic_kernel(const skinny_tactic &t, int half)
 {
     switch (t.path) {
     case SKINNY_PATH_DOT2:
     case SKINNY_PATH_MFMA:
-        return find_kernel(t.path, t.mt, t.rows, t.unroll);
+        return find_kernel(t.path, t.mt, t.rows, t.unroll, half);
     case SKINNY_PATH_DOT2X:
         if (t.waves < 1 || t.rows % t.waves)
             return nullptr;
-        return find_kernel(t.path, t.mt, t.rows / t.waves, t.unroll);
+        return find_kernel(t.path, t.mt, t.rows / t.waves, t.unroll, half);
     case SKINNY_PATH_MFMAX:
         if (t.rows != 16 * t.waves || t.unroll != 1)
             return nullptr;
-        return find_kernel(t.path, t.mt, t.waves, 1);
+        return find_kernel(t.path, t.mt, t.waves, 1, half);
     case SKINNY_PATH_MFMAD:
     case SKINNY_PATH_MFMAS:
         if (t.rows != 16 * t.waves)
             return nullptr;
-        return find_kernel(t.path, t.mt, t.waves, t.unroll);
+        return find_kernel(t.path, t.mt, t.waves, t.unroll, half);
     case SKINNY_PATH_MFMAR:                    // the MFMAS kernels, another grid
         if (t.rows != 16 * t.waves)
             return nullptr;
-        return find_kernel(SKINNY_PATH_MFMAS, t.mt, t.waves, t.unroll);
+        return find_kernel(SKINNY_PATH_MFMAS, t.mt, t.waves, t.unroll, half);
     default:
         return nullptr;
     }
@@ -160,6 +160,8 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
     static const int kSplits[] = {1, 2, 3, 4, 5, 6, 8};
     for (int i = 0; i < nk; ++i) {
         const KernelInfo &k = ks[i];
+        if (k.half)
+            continue;                                    // the same tactics as the BF16 twin
         // the stream-K kernels also run on a data-parallel grid (MFMAR)
         const int paths[2] = {k.path, k.path == SKINNY_PATH_MFMAS ? SKINNY_PATH_MFMAR : -1};
         for (int path : paths) {

@@ -81,8 +81,19 @@ def bf16_bits_to_f32(b) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def draw(seed: int, shape, dist) -> np.ndarray:
-    """Draw float32 values of the given distribution and return BF16 bits."""
+def f32_to_f16_bits(a) -> np.ndarray:
+    """Pack float32 values as FP16 bit patterns (NumPy's nearest-even cast)."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b) -> np.ndarray:
+    """Widen FP16 bit patterns to float32 (exact)."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def draw(seed: int, shape, dist, dtype: str = "bf16") -> np.ndarray:
+    """Draw float32 values of the given distribution and return BF16 (or,
+    dtype "f16", FP16) bits."""
     rng = np.random.default_rng(seed)
     if dist[0] == "normal":
         v = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(dist[1])
@@ -90,7 +101,7 @@ def draw(seed: int, shape, dist) -> np.ndarray:
         v = rng.random(size=shape, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
     else:
         raise ValueError(f"unknown distribution {dist!r}")
-    return f32_to_bf16_bits(v)
+    return f32_to_f16_bits(v) if dtype == "f16" else f32_to_bf16_bits(v)
 
 
 def weight(cid: int, copy: int = 0) -> np.ndarray:
@@ -110,11 +121,18 @@ def activations(cid: int) -> np.ndarray:
 
 
 def random_case(seed: int, m: int, n: int, k: int, w_sigma: float = 0.05,
-                x_sigma: float = 1.0):
-    """A generic normal (x, W) pair of BF16 bits for parity sweeps."""
-    x = draw(seed * 2 + 1, (m, k), ("normal", x_sigma))
-    wt = draw(seed * 2 + 2, (n, k), ("normal", w_sigma))
+                x_sigma: float = 1.0, dtype: str = "bf16"):
+    """A generic normal (x, W) pair of BF16 (or FP16) bits for parity sweeps."""
+    x = draw(seed * 2 + 1, (m, k), ("normal", x_sigma), dtype)
+    wt = draw(seed * 2 + 2, (n, k), ("normal", w_sigma), dtype)
     return x, wt
+
+
+def residual_case(seed: int, m: int, n: int, out: str = "bf16", sigma: float = 1.0):
+    """A normal residual [m, n]: BF16 bits (out "bf16") or float32 values."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal(size=(m, n), dtype=np.float32) * np.float32(sigma)
+    return f32_to_bf16_bits(v) if out == "bf16" else v
 
 
 # ----------------------------------------------------------------------------
@@ -122,11 +140,13 @@ def random_case(seed: int, m: int, n: int, k: int, w_sigma: float = 0.05,
 # oracle (and the tests' own closed forms), never from here.
 # ----------------------------------------------------------------------------
 
-def small_int_case(seed: int, m: int, n: int, k: int, lo: int = -3, hi: int = 3):
-    """Integer-valued BF16 inputs in [lo, hi] (exact in BF16)."""
+def small_int_case(seed: int, m: int, n: int, k: int, lo: int = -3, hi: int = 3, dtype: str = "bf16"):
+    """Integer-valued BF16 (or FP16) inputs in [lo, hi] (exact in both)."""
     rng = np.random.default_rng(seed)
     x = rng.integers(lo, hi + 1, size=(m, k)).astype(np.float32)
     wt = rng.integers(lo, hi + 1, size=(n, k)).astype(np.float32)
+    if dtype == "f16":
+        return f32_to_f16_bits(x), f32_to_f16_bits(wt)
     return f32_to_bf16_bits(x), f32_to_bf16_bits(wt)
 
 

@@ -170,8 +170,57 @@ def pin_decode(lib):
         assert Fraction(float(g)) == _bf16_value(int(p)), hex(int(p))
 
 
+def pin_decode_f16(lib):
+    """FP16 widening against NumPy's own float16 on every bit pattern, and
+    against the format's definition on a few."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode_f16(pats, lib=lib)
+    ref = pats.view(np.float16).astype(np.float64)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), hex(int(pats[~same][0]))
+    assert np.array_equal(np.signbit(got[~np.isnan(got)]), np.signbit(ref[~np.isnan(ref)]))
+    for p, want in ((0x3C00, 1.0), (0x0001, 2.0 ** -24), (0x03FF, 1023 * 2.0 ** -24), (0x0400, 2.0 ** -14),
+                    (0x7BFF, 65504.0), (0xC500, -5.0)):
+        assert oracle.decode_f16(np.array([p], dtype=np.uint16), lib=lib)[0] == want, hex(p)
+
+
+def pin_f16_products(lib):
+    """FP16 inputs: exact against Python integers on small shapes, and within
+    1e-12 S of NumPy float64 on a random case."""
+    rng = np.random.default_rng(23)
+    for m, n, k in ((1, 1, 1), (2, 3, 4), (3, 5, 17), (4, 2, 33)):
+        xi = rng.integers(-8, 9, size=(m, k))
+        wi = rng.integers(-8, 9, size=(n, k))
+        o, s = oracle.gemm(si.f32_to_f16_bits(xi), si.f32_to_f16_bits(wi), lib=lib, dtype="f16")
+        want = xi @ wi.T
+        assert np.array_equal(o, want.astype(np.float64)), (m, n, k)
+        assert np.array_equal(s, (np.abs(xi) @ np.abs(wi).T).astype(np.float64)), (m, n, k)
+    x, w = si.random_case(29, 5, 40, 300, dtype="f16")
+    o, s = oracle.gemm(x, w, lib=lib, dtype="f16")
+    ref = x.view(np.float16).astype(np.float64) @ w.view(np.float16).astype(np.float64).T
+    assert np.all(np.abs(o - ref) <= 1e-12 * s)
+    mi, ni = np.array([0, 4, 2]), np.array([39, 0, 17])
+    os_, ss = oracle.gemm_sampled(x, w, mi, ni, lib=lib, dtype="f16")
+    assert np.array_equal(os_, o[mi, ni]) and np.array_equal(ss, s[mi, ni])
+
+
+def pin_residual(lib):
+    """O + R: exact against Python integers, and R = 0 gives the product."""
+    rng = np.random.default_rng(31)
+    m, n, k = 3, 7, 20
+    xi = rng.integers(-5, 6, size=(m, k))
+    wi = rng.integers(-5, 6, size=(n, k))
+    ri = rng.integers(-100, 101, size=(m, n))
+    o, s = oracle.gemm_residual(_bits_of_ints(xi), _bits_of_ints(wi), ri.astype(np.float64), lib=lib)
+    assert np.array_equal(o, (xi @ wi.T + ri).astype(np.float64))
+    o0, s0 = oracle.gemm(_bits_of_ints(xi), _bits_of_ints(wi), lib=lib)
+    oz, sz = oracle.gemm_residual(_bits_of_ints(xi), _bits_of_ints(wi), np.zeros((m, n)), lib=lib)
+    assert np.array_equal(oz, o0) and np.array_equal(sz, s0) and np.array_equal(s, s0)
+
+
 ALL_PINS = (pin_bruteforce_integers, pin_onehot, pin_linearity, pin_numpy,
-            pin_sampled_matches_full, pin_round_bf16, pin_decode)
+            pin_sampled_matches_full, pin_round_bf16, pin_decode, pin_decode_f16,
+            pin_f16_products, pin_residual)
 
 
 def run_all(lib):

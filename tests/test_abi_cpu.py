@@ -59,6 +59,30 @@ def test_prepare_rejects_before_any_device_call(ptr, n, k, od, want):
     assert sk.last_error()
 
 
+@pytest.mark.parametrize("n,k,ldw,idt,od,want", [
+    (256, 512, 504, 0, 0, 2),       # ldw < K
+    (256, 512, 516, 0, 0, 2),       # ldw % 8
+    (256, 512, 512, 2, 0, 1),       # bad in dtype
+    (256, 512, 512, -1, 1, 1),
+    (256, 512, 1 << 26, 0, 0, 2),   # 16 rows of W past 2 GiB
+])
+def test_prepare_ex_rejects_before_any_device_call(n, k, ldw, idt, od, want):
+    lib = sk.load_library()
+    plan = ctypes.c_void_p(123)
+    st = lib.skinny_prepare_ex(ctypes.c_void_p(0x1000), n, k, ldw, idt, od, ctypes.byref(plan))
+    assert st == want, sk.last_error()
+    assert plan.value is None
+    plan = ctypes.c_void_p(123)
+    st = lib.skinny_prepare_tactics_ex(ctypes.c_void_p(0x1000), n, k, ldw, idt, od, None, ctypes.byref(plan))
+    assert st == want, sk.last_error()
+
+
+def test_run_ex_null_plan():
+    lib = sk.load_library()
+    assert lib.skinny_run_ex(None, ctypes.c_void_p(0x1000), 512, None, 0, ctypes.c_void_p(0x1000), 256, 4,
+                             None) == 1
+
+
 def test_prepare_null_plan_pointer():
     lib = sk.load_library()
     assert lib.skinny_prepare(ctypes.c_void_p(0x1000), 16, 64, 0, None) == 1

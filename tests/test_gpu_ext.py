@@ -1,0 +1,242 @@
+"""Parity of the extended entry points (through the C ABI) with the CPU
+oracle: FP16 inputs and pitched weights (class PreparedProjection and
+matrix_view, page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.
+projection"), pitched x / out, and the fused residual (the `residual` of
+try_low_latency_gemm, page "vllm.models.kimi_k3.nvidia.low_latency_gemm").
+
+As in test_gpu_parity: integer inputs make every fp32 partial sum exact, so
+those cases are compared bit for bit; random cases use the stated bound.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import skinny_inputs as si
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sk():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import skinny_bf16_decode_amd as sk
+    sk.load_library()
+    return sk
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_f16(bits):
+    import torch
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).view(torch.float16).cuda()
+
+
+def _want_bits(o, out_dtype):
+    import torch
+    if out_dtype == torch.float32:
+        return o.astype(np.float32).view(np.uint32)
+    return oracle.round_bf16(o)
+
+
+def _tight(got, o, s, mode, label, residual=False):
+    """Beyond the stated bound: fp32 accumulation sits far inside it.  Allow
+    1e-4 S, plus the output rounding in BF16 mode and the residual add."""
+    tight = 1e-4 * np.asarray(s) + 1e-6
+    if mode == "bf16":
+        tight = tight + 2.0 ** -8 * np.abs(np.asarray(o))
+    if residual:
+        tight = tight + 2.0 ** -23 * np.abs(np.asarray(o))
+    worst = float(np.max(np.abs(np.asarray(got) - np.asarray(o)) / tight))
+    assert worst <= 1.0, f"{label}: error level above the fp32-accumulation expectation ({worst:.3f})"
+
+
+def _one_per_path(sk, n, k):
+    """The first enumerated tactic of every (path, token tile, split > 1) kind."""
+    seen, pick = set(), []
+    for t in sk.enumerate_tactics(n, k):
+        key = (t.path, t.mt, t.split > 1)
+        if key not in seen:
+            seen.add(key)
+            pick.append(t)
+    return pick
+
+
+def test_f16_integer_probe_every_tactic(sk):
+    """Every candidate tactic, forced, on FP16 integer inputs: exact."""
+    import torch
+    n, k = 200, 1032
+    x_bits, w_bits = si.small_int_case(77, 64, n, k, dtype="f16")
+    o, _ = oracle.gemm(x_bits, w_bits, dtype="f16")
+    w = dev_f16(w_bits)
+    tactics = sk.enumerate_tactics(n, k)
+    _say(f"[f16 exact] {len(tactics)} tactics")
+    for t in tactics:
+        plan = sk.Prepared(w, torch.float32, table=gu.forced_table(t))
+        for m in sorted({t.mt, max(1, t.mt - 3)}):
+            out = gu.out_buffer(n, torch.float32)
+            plan.run(dev_f16(x_bits[:m]), out[:m])
+            torch.cuda.synchronize()
+            assert gu.sentinel_intact(out, m), f"{t} M={m}: rows >= M written"
+            got = gu.host_bits(out)[:m]
+            want = _want_bits(o[:m], torch.float32)
+            assert np.array_equal(got, want), f"{t} M={m}"
+        plan.close()
+
+
+@pytest.mark.parametrize("od", ["f32", "bf16"])
+def test_f16_decode_workload_within_bound(sk, od):
+    """FP16 weights and activations of the square decode shape (W N(0, 0.02),
+    x N(0, 1)), tuned, at every listed M."""
+    import torch
+    n, k = 3584, 7168
+    out_dtype = torch.float32 if od == "f32" else torch.bfloat16
+    w_bits = si.draw(si.seed_for(2, 1, 0), (n, k), ("normal", 0.02), "f16")
+    x_bits = si.draw(si.seed_for(2, 2, 0), (64, k), ("normal", 1.0), "f16")
+    o, s = oracle.gemm(x_bits[:32], w_bits, dtype="f16")
+    plan = sk.Prepared(dev_f16(w_bits), out_dtype)
+    x = dev_f16(x_bits)
+    for m in (1, 2, 4, 8, 16, 32):
+        out = gu.out_buffer(n, out_dtype)
+        plan.run(x[:m], out[:m])
+        torch.cuda.synchronize()
+        assert gu.sentinel_intact(out, m)
+        got = gu.values(out)[:m]
+        rep = oracle.check(got, o[:m], s[:m], od)
+        _say(f"[f16 {od}] M={m} {plan.describe(m)}: {rep}")
+        assert rep.ok, (m, str(rep))
+        _tight(got, o[:m], s[:m], od, f"M={m}")
+    plan.close()
+
+
+@pytest.mark.parametrize("od", ["f32", "bf16"])
+@pytest.mark.parametrize("inplace", [False, True], ids=["separate", "inplace"])
+def test_residual_exact(sk, od, inplace):
+    """out = x W^T + R on integer inputs and an integer residual, for one
+    tactic of every path (with and without a K split): exact.  In place, out
+    holds R on entry."""
+    import torch
+    n, k = 392, 2048
+    out_dtype = torch.float32 if od == "f32" else torch.bfloat16
+    x_bits, w_bits = si.small_int_case(41, 64, n, k)
+    rng = np.random.default_rng(43)
+    r_int = rng.integers(-200, 201, size=(64, n))
+    o, _ = oracle.gemm_residual(x_bits, w_bits, r_int.astype(np.float64))
+    w = gu.dev_bf16(w_bits)
+    if out_dtype == torch.float32:
+        r_dev = torch.from_numpy(r_int.astype(np.float32)).cuda()
+    else:
+        r_dev = gu.dev_bf16(si.f32_to_bf16_bits(r_int.astype(np.float32)))
+    tactics = _one_per_path(sk, n, k)
+    assert {t.path for t in tactics} == {0, 1, 2, 3, 4, 5, 6}
+    _say(f"[residual {od} {'inplace' if inplace else 'separate'}] {len(tactics)} tactics")
+    for t in tactics:
+        plan = sk.Prepared(w, out_dtype, table=gu.forced_table(t))
+        for m in sorted({t.mt, max(1, t.mt - 3)}):
+            out = gu.out_buffer(n, out_dtype)
+            x = gu.dev_bf16(x_bits[:m])
+            if inplace:
+                out[:m].copy_(r_dev[:m])
+                plan.run(x, out[:m], residual=out[:m])
+            else:
+                plan.run(x, out[:m], residual=r_dev[:m])
+            torch.cuda.synchronize()
+            assert gu.sentinel_intact(out, m), f"{t} M={m}"
+            got = gu.host_bits(out)[:m]
+            assert np.array_equal(got, _want_bits(o[:m], out_dtype)), f"{t} M={m}"
+        plan.close()
+
+
+def test_residual_random_within_bound(sk):
+    """A BF16 residual on the packed decode shape, tuned plan."""
+    import torch
+    n, k = 6288, 7168
+    w_bits = si.weight(3)
+    x_bits = si.activations(3)
+    r_bits = si.residual_case(47, 32, n)
+    r_val = si.bf16_bits_to_f32(r_bits).astype(np.float64)
+    o, s = oracle.gemm_residual(x_bits[:32], w_bits, r_val)
+    plan = sk.Prepared(gu.dev_bf16(w_bits), torch.bfloat16)
+    x = gu.dev_bf16(x_bits)
+    r = gu.dev_bf16(r_bits)
+    for m in (1, 8, 32):
+        out = gu.out_buffer(n, torch.bfloat16)
+        plan.run(x[:m], out[:m], residual=r[:m])
+        torch.cuda.synchronize()
+        got = gu.values(out)[:m]
+        rep = oracle.check(got, o[:m], s[:m], "bf16", residual=True)
+        _say(f"[residual bf16] M={m}: {rep}")
+        assert rep.ok, (m, str(rep))
+        _tight(got, o[:m], s[:m], "bf16", f"M={m}", residual=True)
+    plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_pitched_views_exact(sk, dtype):
+    """W with row pitch K + 24, x with K + 40, out with N + 7: the padding of
+    W and x holds garbage that must not be read into the result, and out's
+    padding columns must stay untouched."""
+    import torch
+    n, k = 300, 1536
+    ldw, ldx, ldo = k + 24, k + 40, n + 7
+    x_bits, w_bits = si.small_int_case(53, 64, n, k, dtype=dtype)
+    o, _ = oracle.gemm(x_bits, w_bits, dtype=dtype)
+    junk = 0x7E00 if dtype == "f16" else 0x7FC0          # NaN patterns in the pads
+    wp = np.full((n, ldw), junk, dtype=np.uint16)
+    wp[:, :k] = w_bits
+    xp = np.full((64, ldx), junk, dtype=np.uint16)
+    xp[:, :k] = x_bits
+    to_dev = dev_f16 if dtype == "f16" else gu.dev_bf16
+    w = to_dev(wp)[:, :k]
+    x = to_dev(xp)[:, :k]
+    assert w.stride() == (ldw, 1) and x.stride() == (ldx, 1)
+    tactics = _one_per_path(sk, n, k)
+    for t in tactics:
+        plan = sk.Prepared(w, torch.float32, table=gu.forced_table(t))
+        for m in sorted({t.mt, max(2, t.mt - 3)}):
+            buf = gu.out_buffer(ldo, torch.float32)
+            out = buf[:, :n]
+            plan.run(x[:m], out[:m])
+            torch.cuda.synchronize()
+            bits = gu.host_bits(buf)
+            assert np.all(bits[:m, n:] == gu.SENTINEL_F32), f"{t} M={m}: padding columns written"
+            assert np.all(bits[m:] == gu.SENTINEL_F32), f"{t} M={m}: rows >= M written"
+            assert np.array_equal(bits[:m, :n], _want_bits(o[:m], torch.float32)), f"{t} M={m}"
+        plan.close()
+
+
+def test_run_ex_argument_errors(sk):
+    """Pitches below the row length, unaligned pitches and a residual that
+    overlaps out without being it are refused before any launch."""
+    import ctypes
+    import torch
+    n, k = 64, 256
+    lib = sk.load_library()
+    w = gu.dev_bf16(si.small_int_case(1, 1, n, k)[1])
+    plan = sk.Prepared(w, torch.float32, table=[sk.Tactic(1, 64, 16, 1, 1, 1)] * 64)
+    x = torch.zeros((4, k + 8), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((8, n + 8), dtype=torch.float32, device="cuda")
+    p = plan._plan
+    xp, op = ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr())
+    assert lib.skinny_run_ex(p, xp, k - 8, None, 0, op, n, 4, None) == 2        # ldx < K
+    assert lib.skinny_run_ex(p, xp, k + 4, None, 0, op, n, 4, None) == 2        # ldx % 8
+    assert lib.skinny_run_ex(p, xp, k, None, 0, op, n - 1, 4, None) == 2        # ldo < N
+    r = ctypes.c_void_p(out.data_ptr() + 4 * 3)                                 # overlaps out
+    assert lib.skinny_run_ex(p, xp, k, r, n, op, n, 4, None) == 1
+    assert lib.skinny_run_ex(p, xp, k, op, n + 8, op, n, 4, None) == 1          # out, other pitch
+    assert lib.skinny_run_ex(p, xp, k, op, n, op, n, 4, None) == 0              # in place: fine
+    assert lib.skinny_run_ex(p, xp, k, None, 0, op, n, 65, None) == 4
+    torch.cuda.synchronize()
+    plan.close()
+    with pytest.raises(ValueError):
+        sk.Prepared(w[:, :250], torch.float32)                                  # K % 8 != 0

@@ -306,7 +306,8 @@ def test_table_cache_file_round_trip(sk, tmp_path):
     assert first.returncode == 0, first.stderr[-2000:]
     assert "tuned N=640 K=2048" in first.stderr
     lines = path.read_text().splitlines()
-    assert len(lines) == 1 and lines[0].startswith("skinny-table v1 gfx950 ")
+    assert len(lines) == 1 and lines[0].startswith("skinny-table v2 gfx950 ")
+    assert lines[0].split()[4:8] == ["640", "2048", "bf16", "bf16"], lines[0][:80]
     second = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240)
     assert second.returncode == 0, second.stderr[-2000:]
     assert "table loaded from" in second.stderr and "tuned N=640" not in second.stderr

@@ -30,8 +30,14 @@ MUTATIONS = {
     "dropped_first_term": ("for (int k = 0; k < K; ++k) {\n                        double p",
                            "for (int k = 1; k < K; ++k) {\n                        double p"),
     "sign_flip": ("acc += p;\n                        mag", "acc -= p;\n                        mag"),
-    "transposed_weight": ("wrow[k] = bf16_to_double(w[(long)n * K + k]);",
-                          "wrow[k] = bf16_to_double(w[(long)k * N + n]);"),
+    "transposed_weight": ("wrow[k] = to_double(w[(long)n * K + k], f16);",
+                          "wrow[k] = to_double(w[(long)k * N + n], f16);"),
+    "f16_exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    "f16_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "f16_read_as_bf16": ("return f16 ? f16_to_double(bits) : bf16_to_double(bits);",
+                         "return bf16_to_double(bits);"),
+    "f16_sampled_ignores_type": ("double p = to_double(xr[k], f16) * to_double(wr[k], f16);",
+                                 "double p = to_double(xr[k], 0) * to_double(wr[k], f16);"),
     "x_row_stride": ("const double *xr = xd + (long)m * K;",
                      "const double *xr = xd + (long)m;"),
     "output_transposed": ("o[(long)m * N + n] = acc;", "o[(long)n * M + m] = acc;"),
