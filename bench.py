@@ -360,8 +360,53 @@ def calibration_kernels(setup, stream):
     log(f"calibration: probe_read of {setup.wl.weight_bytes} B, device copy of {src.numel() * 4} B")
 
 
+def kda_overlap(stream):
+    """The KDA decode projection (packed [6288, 7168] QKVG on the main stream,
+    F_A/beta then F_B [1536, 128] on an auxiliary stream) against the same
+    three products on one stream, each from a graph of 16 projections over 4
+    rotated packed-weight copies."""
+    import torch
+    import skinny_inputs as si
+    from skinny_bf16_decode_amd.kda import KdaProjection
+    copies = 4
+    f_b = dev_bf16(si.weight(4))
+    packed = [dev_bf16(si.weight(3, c)) for c in range(copies)]
+    x = dev_bf16(si.activations(3))
+    projs = [KdaProjection(w, f_b) for w in packed]
+    aux = torch.cuda.Stream()
+    events = [(torch.cuda.Event(), torch.cuda.Event()) for _ in range(16 * copies)]
+    for m in (1, 4, 8, 16, 32):
+        outs = [p.outputs(m) for p in projs]
+
+        def overlapped():
+            for i in range(16 * copies):
+                projs[i % copies].run(x[:m], outs[i % copies], aux, events[i])
+
+        def serial():
+            for i in range(16 * copies):
+                projs[i % copies].run_serial(x[:m], outs[i % copies])
+
+        pouts = [p.packed_outputs(m) for p in projs]
+
+        def packed():
+            for i in range(16 * copies):
+                projs[i % copies].run_packed(x[:m], *pouts[i % copies])
+
+        res = {}
+        for name, fn in (("serial", serial), ("overlapped", overlapped), ("packed", packed)):
+            g = capture(fn, stream)
+            time_graph(g, stream, 1)
+            res[name] = 1e6 * time_graph(g, stream, 10) / (10 * 16 * copies)
+        log(f"[kda projection] M={m:2d}: three products on one stream {res['serial']:7.2f} us, "
+            f"F_A/beta->F_B on a second stream {res['overlapped']:7.2f} us, "
+            f"one packed product then F_B {res['packed']:7.2f} us per projection")
+    for p in projs:
+        p.close()
+
+
 def extra_workloads(stream):
     import skinny_inputs as si
+    kda_overlap(stream)
     for cid, od in ((2, "bf16"), (4, "f32"), (4, "bf16"), (5, "bf16"), (1, "f32")):
         s = Setup(cid, out_dtype=od)
         for m in s.wl.m_values:

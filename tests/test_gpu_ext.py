@@ -240,3 +240,66 @@ def test_run_ex_argument_errors(sk):
     plan.close()
     with pytest.raises(ValueError):
         sk.Prepared(w[:, :250], torch.float32)                                  # K % 8 != 0
+
+
+def test_kda_projection_two_streams(sk):
+    """The KDA decode projection with its F_A/beta -> F_B branch on a second
+    stream: every output matches the oracle (F_B against the oracle applied
+    to the F_A output the GPU produced), and equals, bit for bit, the same
+    products run on one stream -- also when captured in a graph and replayed."""
+    import torch
+    from skinny_bf16_decode_amd import kda
+    w_bits = si.weight(3)
+    fb_bits = si.weight(4)
+    x_bits = si.activations(3)
+    proj = kda.KdaProjection(gu.dev_bf16(w_bits), gu.dev_bf16(fb_bits))
+    aux = torch.cuda.Stream()
+    events = (torch.cuda.Event(), torch.cuda.Event())
+    x = gu.dev_bf16(x_bits)
+    rows_fab = kda.F_A_ROWS + kda.BETA_ROWS
+    for m in (1, 8, 32):
+        out = proj.outputs(m)
+        proj.run(x[:m], out, aux, events)
+        torch.cuda.synchronize()
+        o, s = oracle.gemm(x_bits[:m], w_bits[:kda.QKVG_ROWS + rows_fab])
+        rep = oracle.check(gu.values(out.qkvg), o[:, :kda.QKVG_ROWS], s[:, :kda.QKVG_ROWS], "bf16")
+        assert rep.ok, f"qkvg M={m}: {rep}"
+        rep = oracle.check(gu.values(out.fab), o[:, kda.QKVG_ROWS:], s[:, kda.QKVG_ROWS:], "bf16")
+        assert rep.ok, f"F_A/beta M={m}: {rep}"
+        fa_bits = gu.host_bits(out.fab)[:, :kda.F_A_ROWS]
+        o2, s2 = oracle.gemm(np.ascontiguousarray(fa_bits), fb_bits)
+        rep = oracle.check(gu.values(out.f_b), o2, s2, "bf16")
+        assert rep.ok, f"F_B M={m}: {rep}"
+        _say(f"[kda] M={m}: qkvg/fab/f_b within bound")
+        ref = [gu.host_bits(t).copy() for t in (out.qkvg, out.fab, out.f_b)]
+        ser = proj.outputs(m)
+        proj.run_serial(x[:m], ser)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (ser.qkvg, ser.fab, ser.f_b)):
+            assert np.array_equal(a, gu.host_bits(b))
+        stream = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        gout = proj.outputs(m)
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                proj.run(x[:m], gout, aux, events)
+        for rep_i in range(3):
+            for t in (gout.qkvg, gout.fab, gout.f_b):
+                t.fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(ref, (gout.qkvg, gout.fab, gout.f_b)):
+                assert np.array_equal(a, gu.host_bits(b)), f"graph replay {rep_i} M={m}"
+        pk, fbo = proj.packed_outputs(m)
+        proj.run_packed(x[:m], pk, fbo)
+        torch.cuda.synchronize()
+        rows = kda.QKVG_ROWS + rows_fab
+        rep = oracle.check(gu.values(pk)[:, :rows], o, s, "bf16")
+        assert rep.ok, f"packed M={m}: {rep}"
+        fa_bits = np.ascontiguousarray(gu.host_bits(pk)[:, kda.QKVG_ROWS:kda.QKVG_ROWS + kda.F_A_ROWS])
+        o3, s3 = oracle.gemm(fa_bits, fb_bits)
+        rep = oracle.check(gu.values(fbo), o3, s3, "bf16")
+        assert rep.ok, f"packed F_B M={m}: {rep}"
+    proj.close()
