@@ -80,9 +80,13 @@ typedef enum {
     SKINNY_PATH_MFMAS = 5, /* MFMAX's register-to-LDS pipeline under a stream-K schedule: one
                               workgroup per slot the chip holds at once, each taking an equal
                               share of (row tile, K stage) units */
-    SKINNY_PATH_MFMAR = 6  /* the MFMAS kernel on a data-parallel grid: one workgroup per
+    SKINNY_PATH_MFMAR = 6, /* the MFMAS kernel on a data-parallel grid: one workgroup per
                               (row range, K split), with at least CUs / split equal row
                               ranges of at most 16 * waves rows; split = 1: no exchange */
+    SKINNY_PATH_MFMAK = 7  /* tiles 16/32: one workgroup per equal row range (at least
+                              split x CUs ranges of at most `rows` rows) over all of K;
+                              waves = rows / 16 row groups x K groups, whose partial sums
+                              are added in LDS: no exchange between workgroups */
 } skinny_path;
 
 /*
@@ -96,16 +100,19 @@ typedef enum {
  */
 typedef struct {
     int path;   /* skinny_path */
-    int mt;     /* token tile: DOT2/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD/MFMAS/MFMAR 16,32,64 */
+    int mt;     /* token tile: DOT2/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD/MFMAS/MFMAR/MFMAK 16,32,64 */
     int rows;   /* weight rows per workgroup.  DOT2: 1..16 (mt*rows <= 64);
-                   MFMA: 16,32,64; DOT2X: waves * (1, 2 or 4); MFMAX, MFMAD, MFMAS, MFMAR: 16 * waves */
+                   MFMA: 16,32,64; DOT2X: waves * (1, 2 or 4); MFMAX, MFMAD, MFMAS, MFMAR: 16 * waves; MFMAK: 16 or 32 (row
+                   groups of 16), with waves a multiple of rows / 16 */
     int waves;  /* wavefronts per workgroup: 1,2,4,8 */
     int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
                    (MFMAX: 1, its stage is fixed at 32 chunks; MFMAD: the depth of
-                   its LDS rings, 2..4 stages of 32 chunks; MFMAS, MFMAR: weight
-                   stages of 32 chunks in flight in registers, 2..4) */
+                   its LDS rings, 2..4 stages of 32 chunks; MFMAS, MFMAR, MFMAK:
+                   weight stages of 32 chunks in flight in registers, 2..4) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16; MFMAS: the
-                   stream-K grid, in workgroups per CU (1..4, capped at what fits) */
+                   stream-K grid, in workgroups per CU (1..4, capped at what fits);
+                   MFMAK: row ranges per CU (1 or 2), K is never split between
+                   workgroups */
 } skinny_tactic;
 
 /*

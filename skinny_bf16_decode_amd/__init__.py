@@ -35,7 +35,8 @@ PATH_MFMAX = 3
 PATH_MFMAD = 4
 PATH_MFMAS = 5
 PATH_MFMAR = 6
-PATH_NAMES = {0: "dot2", 1: "mfma", 2: "dot2x", 3: "mfmax", 4: "mfmad", 5: "mfmas", 6: "mfmar"}
+PATH_MFMAK = 7
+PATH_NAMES = {0: "dot2", 1: "mfma", 2: "dot2x", 3: "mfmax", 4: "mfmad", 5: "mfmas", 6: "mfmar", 7: "mfmak"}
 
 STATUS = {
     0: "SKINNY_OK",

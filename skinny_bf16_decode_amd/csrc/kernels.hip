@@ -1394,6 +1394,166 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// MFMAK kernel: token tile MT = 16 T; a workgroup owns one row range of at
+// most 16 RT rows and the whole of K, with RT x KS waves: wave (rt, ks)
+// multiplies rows 16 rt .. 16 rt + 15 of the range over every KS-th K stage
+// starting at stage ks, and the KS partial sums of a row group are added in
+// LDS at the end (in ks order), so no partial sum leaves the workgroup.
+//
+// The grid has n_tiles = max(ceil(N / 16 RT), split x CUs) equal row ranges
+// [t N / n_tiles, (t + 1) N / n_tiles): with N / 16 RT below the CU count
+// every CU gets the same number of rows (6288 rows: 24 or 25 per CU), which
+// 16-row MFMA tiles alone cannot do without sharing tiles between
+// workgroups.  The weight path is MFMAS's: row-contiguous loads U iterations
+// ahead in registers, re-laid out through a wave-private LDS tile; the x
+// window of an iteration covers KS stages, [MT tokens][32 KS chunks], loaded
+// by the whole workgroup into a double-buffered LDS tile.
+// ---------------------------------------------------------------------------
+template <int T, int RT, int KS, int U, bool H>
+__global__ __launch_bounds__(512) void k_mfmak(KArgs a)
+{
+    constexpr int MT = 16 * T;
+    constexpr int NW = RT * KS;
+    constexpr int KW = kMfmaxChunks;           // chunks per wave per iteration
+    constexpr int PITCH = KW + 1;
+    constexpr int XW = KS * KW;                // x window width, chunks
+    constexpr int XP = XW + 1;                 // its row pitch
+    constexpr int XL = (MT * XW) / (64 * NW);  // x chunks per thread per iteration
+    static_assert(XL >= 1 && XL * 64 * NW == MT * XW, "x window must split evenly over the waves");
+    static_assert(U >= 2 && U <= 4, "two to four iterations in flight");
+    extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [2][MT][XP]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rt = wave % RT, ks = wave / RT;
+    const unsigned tile = blockIdx.x;
+    const int r0 = uniform_int((int)(((unsigned long long)tile * (unsigned)a.N) / (unsigned)a.n_tiles));
+    const int r1 = uniform_int((int)(((unsigned long long)(tile + 1) * (unsigned)a.N) / (unsigned)a.n_tiles));
+    const int n0 = r0 + 16 * rt;
+    const int rows_valid = uniform_int(max(0, min(16, r1 - n0)));
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
+    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
+                                (unsigned)rows_valid * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
+    const int iters = (a.K8 + XW - 1) / XW;
+    u32x4 *wl = sm + wave * 16 * PITCH;
+    u32x4 *xl = sm + NW * 16 * PITCH;
+    const int wrow = lane >> 5, wcol = lane & 31;
+    const int i16 = lane & 15, g = lane >> 4;
+
+    int issued = 0;
+    auto load = [&](u32x4(&wv)[8], u32x4(&xv)[XL]) {
+        const int j = issued++;
+        const int lim = j < iters ? a.K8 : 0;
+        const int c = j * XW + ks * KW + wcol;     // this lane's weight chunk
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            wv[q] = load_w(wres, lane_off(c < lim, (unsigned)(2 * q + wrow) * row_bytes + (unsigned)c * 16u), 0);
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            const int e = tid + 64 * NW * i;
+            const int tok = e / XW, cc = j * XW + (e % XW);
+            xv[i] = load_x(xres, lane_off(cc < lim, (unsigned)tok * x_pitch + (unsigned)cc * 16u), 0);
+        }
+    };
+
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto stage = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
+        u32x4 *xw = xl + (j & 1) * MT * XP;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            wl[(2 * q + wrow) * PITCH + wcol] = wv[q];
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            const int e = tid + 64 * NW * i;
+            xw[(e / XW) * XP + (e % XW)] = xv[i];
+        }
+        load(wv, xv);                          // iteration j + U (past the end: no memory access)
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        if (j >= iters)
+            return;
+#pragma unroll
+        for (int h = 0; h < KW / 16; ++h) {
+            u32x4 av[4], bv[4][T];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                av[s] = wl[i16 * PITCH + 4 * (4 * h + s) + g];
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    bv[s][t] = xw[(16 * t + i16) * XP + ks * KW + 4 * (4 * h + s) + g];
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    acc[t] = mma16<H>(av[s], bv[s][t], acc[t]);
+        }
+    };
+
+    u32x4 w0[8], x0[XL], w1[8], x1[XL], w2[8], x2[XL], w3[8], x3[XL];
+    load(w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (U >= 3) {
+        load(w2, x2);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (U >= 4) {
+        load(w3, x3);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // whole rounds of U iterations (see the MFMAS kernel)
+    for (int j = 0; j < iters; j += U) {
+        stage(w0, x0, j);
+        stage(w1, x1, j + 1);
+        if constexpr (U >= 3)
+            stage(w2, x2, j + 2);
+        if constexpr (U >= 4)
+            stage(w3, x3, j + 3);
+    }
+
+    // add the KS partial sums of each row group, in ks order, through LDS
+    // (the tiles are free: every wave is past its last fragment read)
+    float *red = reinterpret_cast<float *>(sm);
+    __syncthreads();
+    if constexpr (KS > 1) {
+        if (ks > 0) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    red[((wave * T + t) * 4 + q) * 64 + lane] = acc[t][q];
+        }
+        __syncthreads();
+        if (ks > 0)
+            return;
+#pragma unroll
+        for (int s = 1; s < KS; ++s)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[t][q] += red[(((s * RT + rt) * T + t) * 4 + q) * 64 + lane];
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int tok = 16 * t + i16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + 4 * g + q;
+            if (tok < a.M && n < r1)
+                store_out(a, tok, n, acc[t][q]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Measurement probes: a plain streaming read of a buffer (what the weight
 // stream could reach with no arithmetic around it) and an empty launch.
 // ---------------------------------------------------------------------------
@@ -1441,6 +1601,8 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
 #define SK_MFMAX(T, NW) SK_PAIR(SKINNY_PATH_MFMAX, 16 * T, NW, 1, k_mfmax, T, NW)
 #define SK_MFMAD(T, NW, D) SK_PAIR(SKINNY_PATH_MFMAD, 16 * T, NW, D, k_mfmad, T, NW, D)
 #define SK_MFMAS(T, NW, D) SK_PAIR(SKINNY_PATH_MFMAS, 16 * T, NW, D, k_mfmas, T, NW, D)
+// MFMAK: rows field = 100 * KS + RT (row groups and K groups), unroll = iterations in flight
+#define SK_MFMAK(T, RT, KS, U) SK_PAIR(SKINNY_PATH_MFMAK, 16 * T, 100 * KS + RT, U, k_mfmak, T, RT, KS, U)
 
 // Instances whose double-buffered loads, accumulators and offsets fit in 256
 // VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
@@ -1485,6 +1647,8 @@ static const KernelInfo kKernels[] = {
     // MFMAS: rows field = waves, unroll field = pipeline depth; stream-K grid
     SK_MFMAS(1, 2, 3), SK_MFMAS(1, 4, 2), SK_MFMAS(1, 4, 3), SK_MFMAS(1, 4, 4), SK_MFMAS(1, 8, 2),
     SK_MFMAS(2, 4, 2), SK_MFMAS(2, 4, 3), SK_MFMAS(2, 8, 2),
+    SK_MFMAK(1, 1, 4, 2), SK_MFMAK(1, 2, 2, 2), SK_MFMAK(1, 2, 2, 3), SK_MFMAK(1, 2, 4, 2), SK_MFMAK(1, 2, 4, 3),
+    SK_MFMAK(2, 2, 2, 2),
 };
 
 const KernelInfo *kernel_table(int *count)

@@ -133,8 +133,12 @@ Entry make_entry(const skinny_tactic &t, int N, int K, int half)
         // equal row ranges, at least as many (x split) as there are CUs
         const int want = (device_cus() + t.split - 1) / t.split;
         en.n_tiles = std::min(N, std::max(en.n_tiles, want));
+    } else if (t.path == SKINNY_PATH_MFMAK) {
+        // equal row ranges, split per CU; K stays inside the workgroup
+        en.n_tiles = std::min(N, std::max(en.n_tiles, device_cus() * t.split));
+        en.grid = (unsigned)en.n_tiles;
     }
-    en.grid = (unsigned)(en.n_tiles * t.split);
+    en.grid = t.path == SKINNY_PATH_MFMAK ? (unsigned)en.n_tiles : (unsigned)(en.n_tiles * t.split);
     en.block = (unsigned)(64 * t.waves);
     en.lds = (unsigned)tactic_lds_bytes(t, K / 8);
     en.t = t;
@@ -158,7 +162,8 @@ void raise_lds_limits()
         const KernelInfo *ks = kernel_table(&nk);
         for (int i = 0; i < nk; ++i)
             if (ks[i].path == SKINNY_PATH_DOT2X || ks[i].path == SKINNY_PATH_MFMAX ||
-                ks[i].path == SKINNY_PATH_MFMAD || ks[i].path == SKINNY_PATH_MFMAS)
+                ks[i].path == SKINNY_PATH_MFMAD || ks[i].path == SKINNY_PATH_MFMAS ||
+                ks[i].path == SKINNY_PATH_MFMAK)
                 (void)hipFuncSetAttribute(ks[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         (void)hipGetLastError();
     });
@@ -168,6 +173,8 @@ size_t ws_floats(const Entry &en)
 {
     if (en.t.path == SKINNY_PATH_MFMAS || en.t.path == SKINNY_PATH_MFMAR)
         return en.sk_parts > 1 ? (size_t)en.n_tiles * en.sk_parts * en.t.mt * en.t.rows : 0;
+    if (en.t.path == SKINNY_PATH_MFMAK)
+        return 0;
     return en.t.split > 1 ? (size_t)en.n_tiles * en.t.split * en.t.mt * en.t.rows : 0;
 }
 
@@ -175,7 +182,7 @@ bool uses_counters(const Entry &en)
 {
     if (en.t.path == SKINNY_PATH_MFMAS || en.t.path == SKINNY_PATH_MFMAR)
         return en.sk_parts > 1;
-    return en.t.split > 1;
+    return en.t.split > 1 && en.t.path != SKINNY_PATH_MFMAK;
 }
 
 // Static LDS of a kernel plus the device's per-workgroup limit, looked up
@@ -740,9 +747,9 @@ skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len
     }
     const Entry &en = p->e[M];
     static const char *const kNames[] = {"dot2", "mfma16x16x32", "dot2x", "mfmax16x16x32", "mfmad16x16x32",
-                                         "mfmas16x16x32", "mfmar16x16x32"};
+                                         "mfmas16x16x32", "mfmar16x16x32", "mfmak16x16x32"};
     snprintf(buf, len, "%s mt=%d rows=%d waves=%d unroll=%d split=%d grid=%u block=%u lds=%u",
-             (t.path >= 0 && t.path <= 6) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
+             (t.path >= 0 && t.path <= 7) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
              en.grid, en.block, en.lds);
     return SKINNY_OK;
 }

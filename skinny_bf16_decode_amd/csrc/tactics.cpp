@@ -32,6 +32,8 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
         return mfmax_lds_bytes(t.waves, t.mt);
     case SKINNY_PATH_MFMAD:
         return mfmad_lds_bytes(t.waves, t.mt, t.unroll);
+    case SKINNY_PATH_MFMAK:
+        return t.rows >= 16 ? mfmak_lds_bytes(t.waves, t.mt, t.waves / (t.rows / 16)) : 0;
     default:
         return 0;
     }
@@ -60,6 +62,12 @@ const KernelInfo *tactic_kernel(const skinny_tactic &t, int half)
         if (t.rows != 16 * t.waves)
             return nullptr;
         return find_kernel(SKINNY_PATH_MFMAS, t.mt, t.waves, t.unroll, half);
+    case SKINNY_PATH_MFMAK: {                  // KernelInfo.rows = 100 KS + RT
+        if (t.rows < 16 || t.rows % 16 || t.waves % (t.rows / 16))
+            return nullptr;
+        const int rt = t.rows / 16, ks = t.waves / rt;
+        return find_kernel(t.path, t.mt, 100 * ks + rt, t.unroll, half);
+    }
     default:
         return nullptr;
     }
@@ -119,6 +127,11 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             set_error("split=%d exceeds the %d 16-byte chunks of a row", t->split, k8);
             return SKINNY_ERR_INVALID_ARG;
         }
+    } else if (t->path == SKINNY_PATH_MFMAK) {
+        if (t->split > 2) {
+            set_error("split=%d: for MFMAK split is row ranges per CU, 1 or 2", t->split);
+            return SKINNY_ERR_INVALID_ARG;
+        }
     } else if (t->path == SKINNY_PATH_MFMAR) {
         const int stages = (k8 + kMfmaxChunks - 1) / kMfmaxChunks;
         if (t->split > stages) {
@@ -132,7 +145,7 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             return SKINNY_ERR_INVALID_ARG;
         }
     } else {
-        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD), 5 (MFMAS) or 6 (MFMAR)", t->path);
+        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD), 5 (MFMAS), 6 (MFMAR) or 7 (MFMAK)", t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
     const size_t lds_limit = (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
@@ -178,12 +191,18 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                             continue;
                         t.rows = 16 * w;
                     }
+                    if (path == SKINNY_PATH_MFMAK) {     // k.rows = 100 KS + RT
+                        const int rt = k.rows % 100, ks = k.rows / 100;
+                        if (w != rt * ks || s > 2)
+                            continue;
+                        t.rows = 16 * rt;
+                    }
                     if (path == SKINNY_PATH_MFMAS && s > 3)
                         continue;                        // split: workgroups per CU
                     if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                         continue;
                     const int tiles = (N + t.rows - 1) / t.rows;
-                    if (s > 1 && tiles * w >= 8 * 256 && path != SKINNY_PATH_MFMAS)
+                    if (s > 1 && tiles * w >= 8 * 256 && path != SKINNY_PATH_MFMAS && path != SKINNY_PATH_MFMAK)
                         continue;   // enough waves already; a K split only adds traffic
                     if (path == SKINNY_PATH_DOT2) {
                         // each lane of the workgroup should own at least one chunk per
@@ -195,7 +214,7 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                         // every wave streams the whole split: one full pipeline stage at least
                         if (k8 / s < 64 * k.unroll)
                             continue;
-                    } else if (path == SKINNY_PATH_MFMAS) {
+                    } else if (path == SKINNY_PATH_MFMAS || path == SKINNY_PATH_MFMAK) {
                         if (k8 < 2 * kMfmaxChunks)
                             continue;
                     } else if (path == SKINNY_PATH_MFMAX || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAR) {
