@@ -848,19 +848,25 @@ __device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, const float *
 // The weight is loaded row-contiguously -- each wave-wide load covers two
 // rows x 512 bytes, full 128-byte lines -- into registers, one stage (32
 // chunks = 8 K-steps of 32) ahead, and re-laid out through a wave-private LDS
-// tile [16 rows][32 chunks] (row pitch 528 bytes, so the 16 rows of a column
-// fall on distinct banks) from which each lane reads its A fragment (row i,
+// tile [16 rows][32 chunks] from which each lane reads its A fragment (row i,
 // chunk 4 step + g).  The x window [MT tokens][32 chunks] of the same stage is
 // loaded cooperatively by the workgroup into a double-buffered LDS tile and
 // read as B fragments.  Loading W with the 16-row MFMA pattern directly would
 // split every request into 64-byte halves of lines.
+//
+// Row pitch of both tiles: 34 chunks (544 bytes).  With 16 lanes reading 16
+// rows of one 16-byte column, gfx950's LDS served the 128-bit reads without a
+// bank conflict only for row pitches of 2 mod 4 chunks (34, 66, 70, 130 ...);
+// a pitch of 33 chunks cost 4 conflict cycles per read and 32 chunks 28
+// (SQ_LDS_BANK_CONFLICT per SQ_INSTS_LDS, measured).  Writes of whole rows
+// were conflict-free at every pitch tried.
 // ---------------------------------------------------------------------------
 template <int T, int NW, bool H>
 __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
 {
     constexpr int MT = 16 * T;
     constexpr int KW = kMfmaxChunks;           // chunks per stage
-    constexpr int PITCH = KW + 1;              // row pitch in 16-byte chunks
+    constexpr int PITCH = KW + 2;              // row pitch in 16-byte chunks (see k_mfmax)
     constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
     static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
     extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [2][MT][PITCH]
@@ -1159,7 +1165,7 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
 // A stage is 32 K-chunks (512 bytes of each row).  The weight is loaded
 // row-contiguously (each wave-wide load is two rows x 512 bytes) into
 // registers U stages ahead, and re-laid out through a wave-private LDS tile
-// [16 rows][33 chunks] from which lane (g, i) reads its A fragment (row i,
+// [16 rows][34 chunks] from which lane (g, i) reads its A fragment (row i,
 // chunk 4 step + g); the x window [MT tokens][32 chunks] of a stage is
 // loaded by the whole workgroup into a double-buffered LDS tile and read as
 // B fragments, so x is fetched once per tile, not once per wave.
@@ -1185,7 +1191,7 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
 {
     constexpr int MT = 16 * T;
     constexpr int KW = kMfmaxChunks;           // chunks per stage
-    constexpr int PITCH = KW + 1;              // row pitch in 16-byte chunks
+    constexpr int PITCH = KW + 2;              // row pitch in 16-byte chunks (see k_mfmax)
     constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
     static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
     static_assert(U >= 2 && U <= 4, "two to four stages in flight");
@@ -1415,9 +1421,9 @@ __global__ __launch_bounds__(512) void k_mfmak(KArgs a)
     constexpr int MT = 16 * T;
     constexpr int NW = RT * KS;
     constexpr int KW = kMfmaxChunks;           // chunks per wave per iteration
-    constexpr int PITCH = KW + 1;
+    constexpr int PITCH = KW + 2;
     constexpr int XW = KS * KW;                // x window width, chunks
-    constexpr int XP = XW + 1;                 // its row pitch
+    constexpr int XP = XW + 2;                 // its row pitch, 2 mod 4 chunks (see k_mfmax)
     constexpr int XL = (MT * XW) / (64 * NW);  // x chunks per thread per iteration
     static_assert(XL >= 1 && XL * 64 * NW == MT * XW, "x window must split evenly over the waves");
     static_assert(U >= 2 && U <= 4, "two to four iterations in flight");

@@ -77,13 +77,13 @@ constexpr size_t kMaxLds = 60 * 1024;          // in-WG split-K paths (DOT2, MFM
 constexpr size_t kStaticLdsReserve = 1024;
 constexpr size_t kMaxLdsStaged = 160 * 1024 - kStaticLdsReserve;
 constexpr int kMfmaxChunks = 32;               // K chunks per MFMAX stage
-inline size_t mfmax_lds_bytes(int waves, int mt) { return (size_t)(16 * waves + 2 * mt) * (kMfmaxChunks + 1) * 16; }
+inline size_t mfmax_lds_bytes(int waves, int mt) { return (size_t)(16 * waves + 2 * mt) * (kMfmaxChunks + 2) * 16; }
 // MFMAD: per wave `depth` weight slots of 16 rows x 32 chunks, plus `depth` x slots of mt x 32 chunks
 inline size_t mfmad_lds_bytes(int waves, int mt, int depth) { return (size_t)depth * (16 * waves + mt) * 32 * 16; }
-// MFMAK: wave tiles [waves][16][33] and two x windows [mt][32 ks + 1]
+// MFMAK: wave tiles [waves][16][34] and two x windows [mt][32 ks + 2]
 inline size_t mfmak_lds_bytes(int waves, int mt, int ks)
 {
-    return ((size_t)waves * 16 * (kMfmaxChunks + 1) + 2 * (size_t)mt * (kMfmaxChunks * ks + 1)) * 16;
+    return ((size_t)waves * 16 * (kMfmaxChunks + 2) + 2 * (size_t)mt * (kMfmaxChunks * ks + 2)) * 16;
 }
 
 }  // namespace skinny
