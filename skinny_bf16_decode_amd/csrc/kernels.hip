@@ -225,57 +225,89 @@ __device__ __forceinline__ void wave_reduce_transpose(float *v, int lane)
 // agent-scope atomic loads; on gfx950 these are the write-through / coherent
 // forms of the plain access (sc1), so no L2 writeback is needed to publish
 // them.  An agent-scope release fence would add one (buffer_wbl2), and those
-// writebacks serialise per XCD.  A workgroup publishes its partial, waits
-// until its own stores have completed (s_waitcnt vmcnt(0): the part of a
-// release that orders prior coherent stores), then bumps the tile's arrival
-// counter with an agent-scope atomic.  The workgroup that sees split - 1
-// arrivals before its own reads every partial in split order, so the sum is
-// deterministic, and resets the counter to zero for the next launch.
+// writebacks serialise per XCD.
+//
+// Every slot of the workspace holds kSlotEmpty, a signalling-NaN pattern that
+// no fp32 arithmetic produces, except while a partial is in it.  A workgroup
+// publishes its partial and bumps the tile's arrival counter with an
+// agent-scope atomic straight away, without waiting for its stores to
+// complete: the workgroup that sees split - 1 arrivals before its own knows
+// that every partial has been issued, and reads each slot until it no longer
+// holds kSlotEmpty (a store in flight always lands; the re-read is bounded
+// all the same).  It sums the partials in split order, so the sum is
+// deterministic, then empties the slots and resets the counter for the next
+// launch.  Against waiting for the stores before the atomic this takes one
+// memory round trip off the end of every split launch.
 // ---------------------------------------------------------------------------
+constexpr unsigned kSlotEmpty = kSlotEmptyBits;
+constexpr int kSlotSpinLimit = 1 << 16;
+
 __device__ __forceinline__ void publish_partial(float *p, float v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float read_partial(const float *p)
+__device__ __forceinline__ unsigned read_slot(const float *p)
 {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(reinterpret_cast<const unsigned *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void empty_slot(float *p)
+{
+    __hip_atomic_store(reinterpret_cast<unsigned *>(p), kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The last arriver's sum of a thread's N output values over the partial
 // slots: v[i] = sum over p < parts, in slot order from 0, of slot p at
-// offset off[i] (slots `stride` floats apart).  The loads of four slots are
-// all issued before the first add, so the reduction costs ceil(parts / 4)
-// memory round trips instead of parts x N.
+// offset off[i] (slots `stride` floats apart); off[i] < 0 is no value.  The
+// loads of four slots are all issued before the first add, so the reduction
+// costs ceil(parts / 4) memory round trips instead of parts x N.  Each slot
+// is emptied once read; no two threads may name the same offset.
 template <int N>
-__device__ __forceinline__ void sum_partials(const float *wsp, long stride, int parts, const int (&off)[N],
+__device__ __forceinline__ void sum_partials(float *wsp, long stride, int parts, const int (&off)[N],
                                              float (&v)[N])
 {
 #pragma unroll
     for (int i = 0; i < N; ++i)
         v[i] = 0.f;
     for (int p0 = 0; p0 < parts; p0 += 4) {
-        float r[4][N];
+        unsigned r[4][N];
+        bool empty = false;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int i = 0; i < N; ++i)
-                r[k][i] = p0 + k < parts ? read_partial(wsp + (long)(p0 + k) * stride + off[i]) : 0.f;
+            for (int i = 0; i < N; ++i) {
+                r[k][i] = p0 + k < parts && off[i] >= 0 ? read_slot(wsp + (long)(p0 + k) * stride + off[i]) : 0u;
+                empty |= r[k][i] == kSlotEmpty;
+            }
+        // a store still in flight: read the empty slots again, with one
+        // bounded budget for the whole batch (past it the sum is a NaN)
+        for (int spin = 0; empty && spin < kSlotSpinLimit; ++spin) {
+            empty = false;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    if (r[k][i] == kSlotEmpty) {
+                        r[k][i] = read_slot(wsp + (long)(p0 + k) * stride + off[i]);
+                        empty |= r[k][i] == kSlotEmpty;
+                    }
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (p0 + k < parts)
 #pragma unroll
-                for (int i = 0; i < N; ++i)
-                    v[i] += r[k][i];
+                for (int i = 0; i < N; ++i) {
+                    v[i] += __builtin_bit_cast(float, r[k][i]);
+                    if (off[i] >= 0)
+                        empty_slot(wsp + (long)(p0 + k) * stride + off[i]);
+                }
     }
 }
 
-__device__ __forceinline__ void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Called by every thread of the workgroup after it published its partials.
+// Called by every thread of the workgroup after it issued its partial's stores.
 __device__ __forceinline__ bool split_arrive_last(const KArgs &a, int tile, unsigned *flag_lds)
 {
-    wait_own_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned prev =
@@ -466,9 +498,8 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
     // Only wave 0 is left and it holds the whole partial, so the arrival is a
     // wave-level one (no workgroup barrier once the other waves have exited).
     float *wsp = a.ws + (long)tile * a.split * V;
-    if (tid < V)
+    if (live)                                  // exactly the slots the finaliser reads
         publish_partial(wsp + (long)s * V + tid, total);
-    wait_own_stores();
     unsigned prev = 0;
     if (lane == 0)
         prev = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -640,8 +671,10 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
         int off[4];
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            off[i] = min(e0 + i * nthr, E - 1);
+        for (int i = 0; i < 4; ++i) {             // the published values: tokens < mlim
+            const int e = e0 + i * nthr;
+            off[i] = e < E && e / NT < mlim ? e : -1;
+        }
         sum_partials<4>(wsp, E, a.split, off, v);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -802,7 +835,7 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
         float v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            off[k] = min(e0 + k * nthr, E - 1);
+            off[k] = e0 + k * nthr < E ? e0 + k * nthr : -1;
         sum_partials<4>(wsp, E, a.split, off, v);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -821,7 +854,7 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
 // n_wg + 16 wave + 4 (lane / 16) + q) sums the slots and stores the rows
 // below n_end.
 template <int T, int NW>
-__device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, const float *wsp, int E, int parts, int n_wg,
+__device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, float *wsp, int E, int parts, int n_wg,
                                                    int n_end)
 {
     constexpr int EPT = 4 * T;                 // values per thread: E = 64 NW EPT
@@ -1371,8 +1404,7 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
         publish(first_cut, acc_first);
     if (last_cut >= 0)
         publish(last_cut, acc);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // partials published
-    __syncthreads();
+    __syncthreads();                           // every wave has issued its partial stores
     auto arrive = [&](int t) -> unsigned {
         if (t < 0)
             return 0u;

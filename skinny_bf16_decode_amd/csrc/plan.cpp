@@ -334,6 +334,7 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
                                  hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemsetAsync(xbuf.p, 0, (size_t)SKINNY_MAX_M * K * 2, st));
     HIP_TRY(hipMemsetAsync(ctrbuf.p, 0, std::max<size_t>(max_tiles, 1) * 4, st));
+    HIP_TRY(hipMemsetD32Async((hipDeviceptr_t)wsbuf.p, (int)kSlotEmptyBits, std::max<size_t>(max_ws, 1), st));
     hipEvent_t e0, e1;
     HIP_TRY(hipEventCreate(&e0));
     HIP_TRY(hipEventCreate(&e1));
@@ -522,6 +523,10 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
         }
         if ((e = hipMemset(p->ctr, 0, max_tiles * 4)) != hipSuccess) {
             hip_fail(e, "hipMemset(split-K counters)");
+            return fail(SKINNY_ERR_HIP);
+        }
+        if ((e = hipMemsetD32((hipDeviceptr_t)p->ws, (int)kSlotEmptyBits, max_ws)) != hipSuccess) {
+            hip_fail(e, "hipMemsetD32(split-K workspace)");
             return fail(SKINNY_ERR_HIP);
         }
     }

@@ -69,6 +69,10 @@ void set_error(const char *fmt, ...);
 inline int tiles_for(const skinny_tactic &t, int N) { return (N + t.rows - 1) / t.rows; }
 
 constexpr int kMaxWaves = 8;
+// Bits of an empty split-K workspace slot (a signalling NaN no arithmetic
+// produces); the workspace is filled with it when allocated, and every
+// launch leaves it so.
+constexpr unsigned kSlotEmptyBits = 0x7FB55AA5u;
 constexpr size_t kMaxLds = 60 * 1024;          // in-WG split-K paths (DOT2, MFMA)
 // LDS-staged paths (DOT2X, MFMAX, MFMAD) may use a CU's whole 160 KiB, less a
 // reserve for the kernels' own static __shared__ variables: a dispatch whose
