@@ -74,7 +74,9 @@ typedef enum {
     SKINNY_PATH_MFMA = 1,  /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; waves split K */
     SKINNY_PATH_DOT2X = 2, /* v_dot2_f32_bf16, tiles 1/2/4/8; waves own rows, x staged in LDS */
     SKINNY_PATH_MFMAX = 3, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
-                              W re-laid out and x staged through LDS via registers */
+                              W re-laid out and x staged through LDS via registers;
+                              unroll = 2: equal row ranges (at least CUs / split of them)
+                              instead of aligned 16 * waves row tiles */
     SKINNY_PATH_MFMAD = 4, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
                               W and x streamed straight into LDS rings (direct-to-LDS loads) */
     SKINNY_PATH_MFMAS = 5, /* MFMAX's register-to-LDS pipeline under a stream-K schedule: one
@@ -106,7 +108,8 @@ typedef struct {
                    groups of 16), with waves a multiple of rows / 16 */
     int waves;  /* wavefronts per workgroup: 1,2,4,8 */
     int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
-                   (MFMAX: 1, its stage is fixed at 32 chunks; MFMAD: the depth of
+                   (MFMAX: 1 = row tiles of 16 * waves rows, 2 = equal row ranges, its
+                   stage is fixed at 32 chunks; MFMAD: the depth of
                    its LDS rings, 2..4 stages of 32 chunks; MFMAS, MFMAR, MFMAK:
                    weight stages of 32 chunks in flight in registers, 2..4) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16; MFMAS: the

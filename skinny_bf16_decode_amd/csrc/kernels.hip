@@ -909,13 +909,19 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int tile, s;
     block_coords(a, tile, s);
-    const int n_wg = tile * NW * 16;
+    // row tile: 16 NW aligned rows, or (ranges) the equal range
+    // [tile N / n_tiles, (tile + 1) N / n_tiles) of at most 16 NW rows
+    const auto range_row = [&](int t) {
+        return uniform_int((int)(((unsigned long long)(unsigned)t * (unsigned)a.N) / (unsigned)a.n_tiles));
+    };
+    const int n_wg = a.ranges ? range_row(tile) : tile * NW * 16;
+    const int n_end = a.ranges ? range_row(tile + 1) : a.N;
     const int n0 = n_wg + wave * 16;
     const int kb = (int)(((long)s * a.K8) / a.split);
     const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
     const int stages = (ke - kb + KW - 1) / KW;
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
-    const int rows_valid = uniform_int(max(0, min(16, a.N - n0)));
+    const int rows_valid = uniform_int(max(0, min(16, n_end - n0)));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
     const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
@@ -1012,7 +1018,7 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = n0 + 4 * g + q;
-                if (n < a.N)
+                if (n < n_end)
                     store_out(a, tok, n, acc[t][q]);
             }
         }
@@ -1027,7 +1033,7 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
             publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
     if (!split_arrive_last(a, tile, &flag))
         return;
-    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg, a.N);
+    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg, n_end);
     split_reset(a, tile);
 }
 

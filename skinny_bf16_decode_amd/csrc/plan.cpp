@@ -133,6 +133,10 @@ Entry make_entry(const skinny_tactic &t, int N, int K, int half)
         // equal row ranges, at least as many (x split) as there are CUs
         const int want = (device_cus() + t.split - 1) / t.split;
         en.n_tiles = std::min(N, std::max(en.n_tiles, want));
+    } else if (t.path == SKINNY_PATH_MFMAX && t.unroll == 2) {
+        // equal row ranges, enough of them (x split) for every CU
+        const int want = (device_cus() + t.split - 1) / t.split;
+        en.n_tiles = std::min(N, std::max(en.n_tiles, want));
     } else if (t.path == SKINNY_PATH_MFMAK) {
         // equal row ranges, split per CU; K stays inside the workgroup
         en.n_tiles = std::min(N, std::max(en.n_tiles, device_cus() * t.split));
@@ -216,6 +220,7 @@ hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
     a.remap = (en.t.split > 1 && a.nxcd > 1) ? 1 : 0;
     a.sk_spt = en.sk_spt;
     a.sk_parts = en.sk_parts;
+    a.ranges = en.t.path == SKINNY_PATH_MFMAX && en.t.unroll == 2;
     void *params[] = {&a};
     return hipLaunchKernel(en.fn, dim3(en.grid), dim3(en.block), params, en.lds, stream);
 }

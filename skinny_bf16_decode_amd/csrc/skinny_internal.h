@@ -31,6 +31,7 @@ struct KArgs {
     // dealt evenly over gridDim.x workgroups; sk_parts partial slots per tile
     int sk_spt;
     int sk_parts;
+    int ranges;         // MFMAX: row tile t is [t N / n_tiles, (t + 1) N / n_tiles)
     unsigned w_pitch;   // bytes between rows of W (multiple of 16)
     unsigned x_pitch;   // bytes between rows of x (multiple of 16)
     int ldo;            // elements between rows of out

@@ -50,9 +50,9 @@ const KernelInfo *tactic_kernel(const skinny_tactic &t, int half)
             return nullptr;
         return find_kernel(t.path, t.mt, t.rows / t.waves, t.unroll, half);
     case SKINNY_PATH_MFMAX:
-        if (t.rows != 16 * t.waves || t.unroll != 1)
+        if (t.rows != 16 * t.waves || (t.unroll != 1 && t.unroll != 2))
             return nullptr;
-        return find_kernel(t.path, t.mt, t.waves, 1, half);
+        return find_kernel(t.path, t.mt, t.waves, 1, half);   // unroll 2: same kernel, equal row ranges
     case SKINNY_PATH_MFMAD:
     case SKINNY_PATH_MFMAS:
         if (t.rows != 16 * t.waves)
@@ -228,6 +228,12 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                     if (count < cap)
                         buf[count] = t;
                     ++count;
+                    if (path == SKINNY_PATH_MFMAX) {     // the same kernel over equal row ranges
+                        t.unroll = 2;
+                        if (count < cap)
+                            buf[count] = t;
+                        ++count;
+                    }
                 }
             }
         }
