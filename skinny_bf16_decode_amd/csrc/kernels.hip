@@ -899,10 +899,11 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
 {
     constexpr int MT = 16 * T;
     constexpr int KW = kMfmaxChunks;           // chunks per stage
-    constexpr int PITCH = KW + 2;              // row pitch in 16-byte chunks (see k_mfmax)
+    constexpr int PITCH = KW + 2;              // row pitch in 16-byte chunks (see above)
     constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
+    constexpr int NX = mfmax_x_windows(MT);    // x windows in LDS: 4 (a barrier per 2 stages) or 2
     static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
-    extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [2][MT][PITCH]
+    extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [NX][MT][PITCH]
     __shared__ unsigned flag;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -940,12 +941,14 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
     // Two register buffers: while stage j is written to LDS and multiplied,
     // the loads of stages j + 1 and j + 2 are in flight.
     u32x4 wa[8], xa[XL], wb[8], xb[XL];
-    auto load = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
+    auto load_wt = [&](u32x4(&wv)[8], int j) {
         const int c = kb + j * KW + wcol;      // this lane's weight chunk
         const bool wok = j < stages && c < ke;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             wv[q] = load_w(wres, wok ? (unsigned)(2 * q + wrow) * row_bytes + (unsigned)c * 16u : kOffOob, 0);
+    };
+    auto load_xw = [&](u32x4(&xv)[XL], int j) {
 #pragma unroll
         for (int i = 0; i < XL; ++i) {
             const int e = tid + 64 * NW * i;
@@ -954,19 +957,22 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
             xv[i] = load_x(xres, xok ? (unsigned)tok * x_pitch + (unsigned)cc * 16u : kOffOob, 0);
         }
     };
-    auto stage = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
-        u32x4 *xw = xl + (j & 1) * MT * PITCH;
+    auto put_w = [&](const u32x4(&wv)[8]) {
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             wl[(2 * q + wrow) * PITCH + wcol] = wv[q];
+    };
+    auto put_x = [&](const u32x4(&xv)[XL], int j) {
+        u32x4 *xw = xl + (j % NX) * MT * PITCH;
 #pragma unroll
         for (int i = 0; i < XL; ++i) {
             const int e = tid + 64 * NW * i;
             xw[(e / KW) * PITCH + (e % KW)] = xv[i];
         }
-        load(wv, xv, j + 2);                   // past the last stage: out of range, no access
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
+    };
+    // multiply stage j: A fragments from the wave's W tile, B from x window j
+    auto compute = [&](int j) {
+        const u32x4 *xw = xl + (j % NX) * MT * PITCH;
         if constexpr (T <= 2) {
             // fragments are read four K-steps at a time, so one LDS round
             // trip feeds 4 T MFMAs
@@ -998,15 +1004,63 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
             }
         }
     };
-    load(wa, xa, 0);
-    load(wb, xb, 1);
-    int j = 0;
-    for (; j + 1 < stages; j += 2) {
-        stage(wa, xa, j);
-        stage(wb, xb, j + 1);
+    if constexpr (NX == 4) {
+        // loads in the loop's own order: the x of two stages, then the
+        // weights of the first, then of the second
+        load_xw(xa, 0);
+        load_xw(xb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_wt(wa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_wt(wb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // One barrier per pair of stages: the x windows of stages j and j + 1
+        // are written, then the barrier, then both stages are multiplied.
+        // Window j % 4 is rewritten two stages later, after every wave has
+        // passed the next barrier, i.e. finished multiplying stage j.  The
+        // weight tile is private to the wave and needs no barrier.
+        for (int j = 0; j < stages; j += 2) {
+            put_x(xa, j);
+            put_x(xb, j + 1);
+            load_xw(xa, j + 2);                // past the last stage: out of range, no access
+            load_xw(xb, j + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            put_w(wa);
+            load_wt(wa, j + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(j);
+            // the second half runs its loads even past the last stage (no
+            // memory access then), so that every pass through the loop
+            // issues the same loads and the waits stay partial
+            put_w(wb);
+            load_wt(wb, j + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j + 1 < stages)
+                compute(j + 1);
+        }
+    } else {
+        load_wt(wa, 0);
+        load_xw(xa, 0);
+        load_wt(wb, 1);
+        load_xw(xb, 1);
+        auto stage = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
+            put_w(wv);
+            put_x(xv, j);
+            load_wt(wv, j + 2);                // past the last stage: out of range, no access
+            load_xw(xv, j + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            compute(j);
+        };
+        int j = 0;
+        for (; j + 1 < stages; j += 2) {
+            stage(wa, xa, j);
+            stage(wb, xb, j + 1);
+        }
+        if (j < stages)
+            stage(wa, xa, j);
     }
-    if (j < stages)
-        stage(wa, xa, j);
 
     // lane (g, i) holds rows 4g .. 4g+3 (of this wave's 16) of token 16 t + i
     if (a.split == 1) {

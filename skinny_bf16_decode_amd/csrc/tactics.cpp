@@ -27,6 +27,7 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
     case SKINNY_PATH_DOT2X:
         return (size_t)t.mt * ((K8 + t.split - 1) / t.split) * 16;
     case SKINNY_PATH_MFMAX:
+        return mfmax_own_lds_bytes(t.waves, t.mt);
     case SKINNY_PATH_MFMAS:
     case SKINNY_PATH_MFMAR:
         return mfmax_lds_bytes(t.waves, t.mt);
