@@ -901,7 +901,8 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
     constexpr int KW = kMfmaxChunks;           // chunks per stage
     constexpr int PITCH = KW + 2;              // row pitch in 16-byte chunks (see above)
     constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
-    constexpr int NX = mfmax_x_windows(MT);    // x windows in LDS: 4 (a barrier per 2 stages) or 2
+    constexpr int NX = mfmax_x_windows(MT, NW);   // x windows in LDS: a barrier per NX / 2 stages
+    constexpr int PB = NX / 2;                 // stages per barrier
     static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
     extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [NX][MT][PITCH]
     __shared__ unsigned flag;
@@ -938,9 +939,10 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
     for (int t = 0; t < T; ++t)
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Two register buffers: while stage j is written to LDS and multiplied,
-    // the loads of stages j + 1 and j + 2 are in flight.
-    u32x4 wa[8], xa[XL], wb[8], xb[XL];
+    // Two weight register buffers: while stage j is written to LDS and
+    // multiplied, the weight loads of stages j + 1 and j + 2 are in flight;
+    // the x of the next PB stages is in flight in xr.
+    u32x4 wa[8], wb[8], xr[PB][XL];
     auto load_wt = [&](u32x4(&wv)[8], int j) {
         const int c = kb + j * KW + wcol;      // this lane's weight chunk
         const bool wok = j < stages && c < ke;
@@ -1004,42 +1006,50 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
             }
         }
     };
-    if constexpr (NX == 4) {
-        // loads in the loop's own order: the x of two stages, then the
-        // weights of the first, then of the second
-        load_xw(xa, 0);
-        load_xw(xb, 1);
+    if constexpr (PB >= 2) {
+        // One barrier per PB stages: the x windows of stages j .. j + PB - 1
+        // are written, then the barrier, then the PB stages are multiplied.
+        // Window j % NX is rewritten PB stages later, after every wave has
+        // passed the next barrier, i.e. finished multiplying stage j.  The
+        // weight tile is private to the wave and needs no barrier.  Loads are
+        // issued in the loop's own order from the start -- the x of PB stages,
+        // then the weights stage by stage -- and every pass issues all of
+        // them (past the last stage they touch no memory), so every wait in
+        // the loop stays partial.
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+            load_xw(xr[p], p);
         __builtin_amdgcn_sched_barrier(0);
         load_wt(wa, 0);
         __builtin_amdgcn_sched_barrier(0);
         load_wt(wb, 1);
         __builtin_amdgcn_sched_barrier(0);
-        // One barrier per pair of stages: the x windows of stages j and j + 1
-        // are written, then the barrier, then both stages are multiplied.
-        // Window j % 4 is rewritten two stages later, after every wave has
-        // passed the next barrier, i.e. finished multiplying stage j.  The
-        // weight tile is private to the wave and needs no barrier.
-        for (int j = 0; j < stages; j += 2) {
-            put_x(xa, j);
-            put_x(xb, j + 1);
-            load_xw(xa, j + 2);                // past the last stage: out of range, no access
-            load_xw(xb, j + 3);
+        for (int j = 0; j < stages; j += PB) {
+#pragma unroll
+            for (int p = 0; p < PB; ++p)
+                put_x(xr[p], j + p);
+#pragma unroll
+            for (int p = 0; p < PB; ++p)
+                load_xw(xr[p], j + PB + p);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
-            put_w(wa);
-            load_wt(wa, j + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(j);
-            // the second half runs its loads even past the last stage (no
-            // memory access then), so that every pass through the loop
-            // issues the same loads and the waits stay partial
-            put_w(wb);
-            load_wt(wb, j + 3);
-            __builtin_amdgcn_sched_barrier(0);
-            if (j + 1 < stages)
-                compute(j + 1);
+#pragma unroll
+            for (int p = 0; p < PB; p += 2) {
+                put_w(wa);
+                load_wt(wa, j + p + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + p < stages)
+                    compute(j + p);
+                put_w(wb);
+                load_wt(wb, j + p + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + p + 1 < stages)
+                    compute(j + p + 1);
+            }
         }
     } else {
+        u32x4(&xa)[XL] = xr[0];
+        u32x4 xb[XL];
         load_wt(wa, 0);
         load_xw(xa, 0);
         load_wt(wb, 1);
