@@ -365,9 +365,36 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     a.ldo = a.ldr = N;
 
     const int iters = std::max(1, env_int("SKINNY_TUNE_ITERS", 2 * copies > 8 ? 2 * copies : 8));
+    // mean time per launch of `iters` launches over the rotated copies, or -1
+    auto time_once = [&](const Entry &en, double &us) -> hipError_t {
+        us = -1.0;
+        hipError_t e = hipEventRecord(e0, st);
+        if (e != hipSuccess)
+            return e;
+        bool ok = true;
+        for (int j = 0; j < iters && ok; ++j) {
+            a.W = (const char *)wcopies.p + wbytes * ((j + 1) % copies);
+            ok = launch(en, a, st) == hipSuccess;
+        }
+        if ((e = hipEventRecord(e1, st)) != hipSuccess || (e = hipEventSynchronize(e1)) != hipSuccess)
+            return e;
+        if (!ok) {
+            (void)hipGetLastError();
+            return hipSuccess;
+        }
+        float ms = 0.f;
+        if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess)
+            return e;
+        us = 1000.0 * ms / iters;
+        return hipSuccess;
+    };
+
+    // First pass: every candidate at its full token tile, best of two.
     std::vector<double> times(count, -1.0);
+    std::vector<Entry> entries(count);
     for (int i = 0; i < count; ++i) {
-        const Entry en = make_entry(cand[i], N, K, half);
+        entries[i] = make_entry(cand[i], N, K, half);
+        const Entry &en = entries[i];
         if (!en.fn || !lds_fits(en.fn, en.lds))
             continue;
         a.M = cand[i].mt;
@@ -378,22 +405,12 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
         }
         double best = -1.0;
         for (int rep = 0; rep < 2; ++rep) {
-            HIP_TRY(hipEventRecord(e0, st));
-            bool ok = true;
-            for (int j = 0; j < iters && ok; ++j) {
-                a.W = (const char *)wcopies.p + wbytes * ((j + 1) % copies);
-                ok = launch(en, a, st) == hipSuccess;
-            }
-            HIP_TRY(hipEventRecord(e1, st));
-            HIP_TRY(hipEventSynchronize(e1));
-            if (!ok) {
-                (void)hipGetLastError();
+            double us;
+            HIP_TRY(time_once(en, us));
+            if (us < 0) {
                 best = -1.0;
                 break;
             }
-            float ms = 0.f;
-            HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
-            const double us = 1000.0 * ms / iters;
             if (best < 0 || us < best)
                 best = us;
         }
@@ -401,6 +418,39 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     }
     HIP_TRY(hipStreamSynchronize(st));
     skinny_status s = skinny_select_table(cand.data(), times.data(), count, table.data());
+
+    // Second pass: for each M, the few fastest candidates of the first pass
+    // whose tile serves M are timed again at M itself (x and out of M rows),
+    // round-robin over three rounds, and the fastest is kept.  First-pass
+    // times at the full tile overstate a large tile at small M, and single
+    // timings differ by a few per cent from run to run.
+    const int refine = env_int("SKINNY_TUNE_REFINE", 4);
+    for (int m = 1; s == SKINNY_OK && refine > 1 && m <= SKINNY_MAX_M; ++m) {
+        std::vector<int> top;
+        for (int i = 0; i < count; ++i)
+            if (times[i] >= 0 && cand[i].mt >= m)
+                top.push_back(i);
+        std::sort(top.begin(), top.end(), [&](int x, int y) { return times[x] < times[y]; });
+        if ((int)top.size() > refine)
+            top.resize(refine);
+        if (top.size() < 2)
+            continue;
+        std::vector<double> best(top.size(), -1.0);
+        a.M = m;
+        for (int round = 0; round < 3; ++round)
+            for (size_t c = 0; c < top.size(); ++c) {
+                double us;
+                HIP_TRY(time_once(entries[top[c]], us));
+                if (us >= 0 && (best[c] < 0 || us < best[c]))
+                    best[c] = us;
+            }
+        int pick = -1;
+        for (size_t c = 0; c < top.size(); ++c)
+            if (best[c] >= 0 && (pick < 0 || best[c] < best[pick]))
+                pick = (int)c;
+        if (pick >= 0)
+            table[m - 1] = cand[top[pick]];
+    }
     if (env_int("SKINNY_LOG", 0) >= 2) {
         for (int i = 0; i < count; ++i)
             fprintf(stderr, "[skinny] cand N=%d K=%d path=%d mt=%d rows=%d waves=%d unroll=%d split=%d : %.3f us\n",
