@@ -75,8 +75,8 @@ typedef enum {
     SKINNY_PATH_DOT2X = 2, /* v_dot2_f32_bf16, tiles 1/2/4/8; waves own rows, x staged in LDS */
     SKINNY_PATH_MFMAX = 3, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
                               W re-laid out and x staged through LDS via registers;
-                              unroll = 2: equal row ranges (at least CUs / split of them)
-                              instead of aligned 16 * waves row tiles */
+                              unroll = 2: equal row ranges (a whole multiple of CUs / split
+                              of them) instead of aligned 16 * waves row tiles */
     SKINNY_PATH_MFMAD = 4, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
                               W and x streamed straight into LDS rings (direct-to-LDS loads) */
     SKINNY_PATH_MFMAS = 5, /* MFMAX's register-to-LDS pipeline under a stream-K schedule: one

@@ -134,9 +134,11 @@ Entry make_entry(const skinny_tactic &t, int N, int K, int half)
         const int want = (device_cus() + t.split - 1) / t.split;
         en.n_tiles = std::min(N, std::max(en.n_tiles, want));
     } else if (t.path == SKINNY_PATH_MFMAX && t.unroll == 2) {
-        // equal row ranges, enough of them (x split) for every CU
-        const int want = (device_cus() + t.split - 1) / t.split;
-        en.n_tiles = std::min(N, std::max(en.n_tiles, want));
+        // equal row ranges, a whole multiple of CUs / split of them, so that
+        // every CU gets the same number of (range, K part) workgroups
+        const int per_round = (device_cus() + t.split - 1) / t.split;
+        const int rounds = (en.n_tiles + per_round - 1) / per_round;
+        en.n_tiles = std::min(N, rounds * per_round);
     } else if (t.path == SKINNY_PATH_MFMAK) {
         // equal row ranges, split per CU; K stays inside the workgroup
         en.n_tiles = std::min(N, std::max(en.n_tiles, device_cus() * t.split));
