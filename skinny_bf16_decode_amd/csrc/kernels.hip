@@ -21,7 +21,8 @@
 //    in a fixed order and writes the output (the split-K GEMM of the page
 //    "vllm.models.glm5next.nvidia.specialized_decode.gemm", which reduces its
 //    split-K partials across a thread-block cluster; here the exchange goes
-//    through memory with agent-scope release/acquire).
+//    through memory with agent-scope atomic stores and loads and an
+//    arrival counter).
 //
 // DOT2 (token tiles 1..8): v_dot2_f32_bf16, two BF16 products into an fp32
 // accumulator per instruction.  MFMA (token tiles 16..64): W rows are the
