@@ -85,10 +85,13 @@ typedef enum {
     SKINNY_PATH_MFMAR = 6, /* the MFMAS kernel on a data-parallel grid: one workgroup per
                               (row range, K split), with at least CUs / split equal row
                               ranges of at most 16 * waves rows; split = 1: no exchange */
-    SKINNY_PATH_MFMAK = 7  /* tiles 16/32: one workgroup per equal row range (at least
+    SKINNY_PATH_MFMAK = 7, /* tiles 16/32: one workgroup per equal row range (at least
                               split x CUs ranges of at most `rows` rows) over all of K;
                               waves = rows / 16 row groups x K groups, whose partial sums
                               are added in LDS: no exchange between workgroups */
+    SKINNY_PATH_DOT2R = 8  /* the DOT2 kernels over equal row ranges of at most `rows` rows,
+                              a whole multiple of CUs / split of them, so that every CU gets
+                              the same number of (range, K split) workgroups */
 } skinny_path;
 
 /*

@@ -36,7 +36,9 @@ PATH_MFMAD = 4
 PATH_MFMAS = 5
 PATH_MFMAR = 6
 PATH_MFMAK = 7
-PATH_NAMES = {0: "dot2", 1: "mfma", 2: "dot2x", 3: "mfmax", 4: "mfmad", 5: "mfmas", 6: "mfmar", 7: "mfmak"}
+PATH_DOT2R = 8
+PATH_NAMES = {0: "dot2", 1: "mfma", 2: "dot2x", 3: "mfmax", 4: "mfmad", 5: "mfmas", 6: "mfmar", 7: "mfmak",
+              8: "dot2r"}
 
 STATUS = {
     0: "SKINNY_OK",

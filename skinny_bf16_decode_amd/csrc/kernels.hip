@@ -393,11 +393,17 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
     const int nthr = blockDim.x, nwaves = nthr >> 6;
     int tile, s;
     block_coords(a, tile, s);
-    const int n0 = tile * R;
+    // row tile: R aligned rows, or (ranges) the equal range
+    // [tile N / n_tiles, (tile + 1) N / n_tiles) of at most R rows
+    const auto range_row = [&](int t) {
+        return uniform_int((int)(((unsigned long long)(unsigned)t * (unsigned)a.N) / (unsigned)a.n_tiles));
+    };
+    const int n0 = a.ranges ? range_row(tile) : tile * R;
+    const int n_end = a.ranges ? range_row(tile + 1) : a.N;
     const int kb = (int)(((long)s * a.K8) / a.split);
     const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
-    const int rows_valid = uniform_int(min(R, a.N - n0));
+    const int rows_valid = uniform_int(max(0, min(R, n_end - n0)));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)n0 * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
     const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
             total += red[w][tid];
     }
     const int m = tid / R, r = tid - (tid / R) * R, n = n0 + r;
-    const bool live = tid < V && m < a.M && n < a.N;
+    const bool live = tid < V && m < a.M && n < n_end;
     if (a.split == 1) {
         if (live)
             store_out(a, m, n, total);

@@ -46,6 +46,8 @@ const KernelInfo *tactic_kernel(const skinny_tactic &t, int half)
     case SKINNY_PATH_DOT2:
     case SKINNY_PATH_MFMA:
         return find_kernel(t.path, t.mt, t.rows, t.unroll, half);
+    case SKINNY_PATH_DOT2R:                    // the DOT2 kernels, another grid
+        return find_kernel(SKINNY_PATH_DOT2, t.mt, t.rows, t.unroll, half);
     case SKINNY_PATH_DOT2X:
         if (t.waves < 1 || t.rows % t.waves)
             return nullptr;
@@ -123,7 +125,7 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
         return SKINNY_ERR_INVALID_ARG;
     }
     if (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_DOT2X || t->path == SKINNY_PATH_MFMAX ||
-        t->path == SKINNY_PATH_MFMAD || t->path == SKINNY_PATH_MFMAS) {
+        t->path == SKINNY_PATH_MFMAD || t->path == SKINNY_PATH_MFMAS || t->path == SKINNY_PATH_DOT2R) {
         if (t->split > k8) {
             set_error("split=%d exceeds the %d 16-byte chunks of a row", t->split, k8);
             return SKINNY_ERR_INVALID_ARG;
@@ -146,7 +148,8 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             return SKINNY_ERR_INVALID_ARG;
         }
     } else {
-        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD), 5 (MFMAS), 6 (MFMAR) or 7 (MFMAK)", t->path);
+        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD), 5 (MFMAS), 6 (MFMAR), "
+                  "7 (MFMAK) or 8 (DOT2R)", t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
     const size_t lds_limit = (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
@@ -176,8 +179,11 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
         const KernelInfo &k = ks[i];
         if (k.half)
             continue;                                    // the same tactics as the BF16 twin
-        // the stream-K kernels also run on a data-parallel grid (MFMAR)
-        const int paths[2] = {k.path, k.path == SKINNY_PATH_MFMAS ? SKINNY_PATH_MFMAR : -1};
+        // the stream-K kernels also run on a data-parallel grid (MFMAR), the
+        // DOT2 kernels over equal row ranges (DOT2R)
+        const int paths[2] = {k.path, k.path == SKINNY_PATH_MFMAS ? SKINNY_PATH_MFMAR
+                                      : k.path == SKINNY_PATH_DOT2 ? SKINNY_PATH_DOT2R
+                                                                    : -1};
         for (int path : paths) {
             if (path < 0)
                 continue;
@@ -205,6 +211,8 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                     const int tiles = (N + t.rows - 1) / t.rows;
                     if (s > 1 && tiles * w >= 8 * 256 && path != SKINNY_PATH_MFMAS && path != SKINNY_PATH_MFMAK)
                         continue;   // enough waves already; a K split only adds traffic
+                    if (path == SKINNY_PATH_DOT2R && tiles * s > 8 * 256)
+                        continue;   // many workgroups per CU balance themselves
                     if (path == SKINNY_PATH_DOT2) {
                         // each lane of the workgroup should own at least one chunk per
                         // split, and the unrolled loop should run at least once
