@@ -140,6 +140,29 @@ def test_enumeration_is_legal_and_covers_every_tile():
     assert sk.load_library().skinny_enumerate_tactics(0, 64, None, 0) == -1
 
 
+def test_row_range_tactics():
+    """The equal-row-range forms: MFMAX with unroll 2 and DOT2R (path 8, the
+    DOT2 kernels) are enumerated and legal; MFMAX takes unroll 1 or 2 only, and
+    DOT2R follows DOT2's rules on rows and unroll."""
+    cands = sk.enumerate_tactics(6288, 7168)
+    assert any(t.path == 3 and t.unroll == 2 for t in cands)
+    assert any(t.path == 3 and t.unroll == 1 for t in cands)
+    assert any(t.path == sk.PATH_DOT2R for t in cands)
+    sk.tactic_check(T(3, 16, 32, 2, 2, 1), 6288, 7168)
+    sk.tactic_check(T(sk.PATH_DOT2R, 2, 4, 1, 2, 1), 6288, 7168)
+    with pytest.raises(ValueError):
+        sk.tactic_check(T(3, 16, 32, 2, 3, 1), 6288, 7168)        # MFMAX unroll 3
+    with pytest.raises(ValueError):
+        sk.tactic_check(T(sk.PATH_DOT2R, 2, 3, 1, 1, 1), 6288, 7168)   # no DOT2 kernel with 3 rows
+    with pytest.raises(ValueError):
+        sk.tactic_check(T(10, 16, 16, 1, 1, 1), 6288, 7168)       # no such path
+    # many workgroups per CU balance themselves: no DOT2R with more than
+    # eight per CU of a 256-CU part
+    for t in cands:
+        if t.path == sk.PATH_DOT2R:
+            assert -(-6288 // t.rows) * t.split <= 8 * 256
+
+
 def test_table_rule_with_a_fake_timer():
     """table[M] = fastest candidate whose token tile >= M; ties to the
     smaller tile, then the lower index; failed candidates are skipped."""
