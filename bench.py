@@ -170,9 +170,27 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "skinny_projection_packed_qkvg_6
 
 
 def kernel_name(t):
-    if t.path == 1:
-        return f"k_mfma<{t.mt // 16}, {t.rows // 16}, {t.unroll}>"
-    return f"k_dot2<{t.mt}, {t.rows}, {t.unroll}>"
+    """The kernel instance a BF16 tactic launches, spelled as rocprofv3 lists it."""
+    T, w = t.mt // 16, t.waves
+    if t.path in (0, 8):                     # DOT2, DOT2R
+        args = (t.mt, t.rows, t.unroll)
+        name = "k_dot2"
+    elif t.path == 1:                        # MFMA
+        args, name = (T, t.rows // 16, t.unroll), "k_mfma"
+    elif t.path == 2:                        # DOT2X: rows per wave
+        args, name = (t.mt, t.rows // w, t.unroll), "k_dot2x"
+    elif t.path == 3:                        # MFMAX: unroll picks the grid, not the kernel
+        args, name = (T, w), "k_mfmax"
+    elif t.path == 4:                        # MFMAD
+        args, name = (T, w, t.unroll), "k_mfmad"
+    elif t.path in (5, 6):                   # MFMAS, MFMAR
+        args, name = (T, w, t.unroll), "k_mfmas"
+    elif t.path == 7:                        # MFMAK: row groups and K groups
+        rt = t.rows // 16
+        args, name = (T, rt, w // rt, t.unroll), "k_mfmak"
+    else:
+        return None
+    return f"{name}<{', '.join(str(a) for a in args)}, false>"
 
 
 def counted_traffic(setup):
@@ -189,7 +207,8 @@ def counted_traffic(setup):
         return None
     total = 0.0
     for m in M_SWEEP:
-        k = rec["kernels"].get(kernel_name(setup.plans[0].tactic(m)))
+        name = kernel_name(setup.plans[0].tactic(m))
+        k = rec["kernels"].get(name) if name else None
         if k is None:
             return None
         total += (k["fetch_kib"] + k["write_kib"]) * 1024.0
@@ -336,7 +355,7 @@ def main():
         "parity_last_call": "ok",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "skinny projection launches (k_dot2 / k_mfma instances of the step)",
+                     "kernel": "skinny projection launches of the step (the per-M table's kernels)",
                      "bytes_per_launch": round(algo_per_launch), "us_per_launch": round(us_per_launch, 3)},
         "cpu_baseline": cpu,
     }

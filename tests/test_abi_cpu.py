@@ -5,6 +5,7 @@ No kernel is launched here."""
 from __future__ import annotations
 
 import ctypes
+import sys
 import os
 import re
 import subprocess
@@ -205,3 +206,15 @@ def test_python_binding_has_no_fallback(tmp_path):
             mod.load_library(str(tmp_path / "libskinny.so"))
     finally:
         mod._lib = saved
+
+
+def test_bench_names_the_kernel_of_every_tactic():
+    """bench.py matches launches to the rocprofv3 traffic record by kernel
+    name; every enumerated tactic must map to its BF16 instance."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    for t in sk.enumerate_tactics(6288, 7168):
+        name = bench.kernel_name(t)
+        assert name and re.fullmatch(r"k_(dot2|dot2x|mfma|mfmax|mfmad|mfmas|mfmak)<(\d+, )+false>", name), (t, name)
+    assert bench.kernel_name(T(3, 32, 64, 4, 2, 2)) == "k_mfmax<2, 4, false>"
+    assert bench.kernel_name(T(sk.PATH_DOT2R, 2, 4, 1, 2, 1)) == "k_dot2<2, 4, 2, false>"
