@@ -105,9 +105,10 @@ typedef enum {
  */
 typedef struct {
     int path;   /* skinny_path */
-    int mt;     /* token tile: DOT2/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD/MFMAS/MFMAR/MFMAK 16,32,64 */
-    int rows;   /* weight rows per workgroup.  DOT2: 1..16 (mt*rows <= 64);
-                   MFMA: 16,32,64; DOT2X: waves * (1, 2 or 4); MFMAX, MFMAD, MFMAS, MFMAR: 16 * waves; MFMAK: 16 or 32 (row
+    int mt;     /* token tile: DOT2/DOT2R/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD/MFMAS/MFMAR/MFMAK 16,32,64 */
+    int rows;   /* weight rows per workgroup.  DOT2, DOT2R: 1..16 (mt*rows <= 64; for
+                   DOT2R the most rows of a range); MFMA: 16,32,64; DOT2X: waves * (1, 2
+                   or 4); MFMAX, MFMAD, MFMAS, MFMAR: 16 * waves; MFMAK: 16 or 32 (row
                    groups of 16), with waves a multiple of rows / 16 */
     int waves;  /* wavefronts per workgroup: 1,2,4,8 */
     int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
