@@ -265,6 +265,65 @@ def test_deterministic_and_graph_replay(sk):
     plan.close()
 
 
+def test_decode_kernels_repeat_and_graph_replay(sk):
+    """The kernels the packed 6288x7168 decode weight runs with -- DOT2 at
+    M = 1, DOT2 over equal row ranges at M = 2, the ranged 16-token MFMAX at
+    M = 16 and the ranged 32-token MFMAX with a two-way K split at M = 32 --
+    forced, at full size: bitwise identical over repeats and over graph
+    replays with eager work between them, and within the bound on 4096
+    sampled outputs per M."""
+    import torch
+    wl = si.WORKLOADS[3]
+    w_bits, x_bits = si.weight(3, 0), si.activations(3)
+    n = wl.n
+    w = gu.dev_bf16(w_bits)
+    x = gu.dev_bf16(x_bits)
+    forced = {1: sk.Tactic(0, 1, 2, 8, 1, 1), 2: sk.Tactic(sk.PATH_DOT2R, 2, 4, 1, 2, 1),
+              16: sk.Tactic(3, 16, 32, 2, 2, 1), 32: sk.Tactic(3, 32, 64, 4, 2, 2)}
+    table = []
+    for m in range(1, 65):
+        fits = [t for mm, t in sorted(forced.items()) if mm >= m]
+        table.append(fits[0] if fits else sk.Tactic(3, 64, 128, 8, 1, 4))
+    plan = sk.Prepared(w, torch.bfloat16, table=table)
+    for m, t in forced.items():
+        assert plan.tactic(m) == t, (m, plan.tactic(m))
+    rng = np.random.default_rng(606)
+    ref = {}
+    for m in forced:
+        out = gu.out_buffer(n, torch.bfloat16)
+        plan.run(x[:m], out[:m])
+        torch.cuda.synchronize()
+        assert gu.sentinel_intact(out, m), f"M={m}: rows >= M were written"
+        ref[m] = gu.host_bits(out).copy()
+        for _ in range(10):
+            out2 = gu.out_buffer(n, torch.bfloat16)
+            plan.run(x[:m], out2[:m])
+            torch.cuda.synchronize()
+            assert np.array_equal(gu.host_bits(out2), ref[m]), f"M={m}: repeat differs"
+        mi = rng.integers(0, m, size=4096)
+        ni = rng.integers(0, n, size=4096)
+        o, sv = oracle.gemm_sampled(x_bits[:m], w_bits, mi, ni)
+        got = si.bf16_bits_to_f32(ref[m][mi, ni]).astype(np.float64)
+        _bound_check(got, o, sv, "bf16", f"decode kernel M={m} {forced[m]}")
+    outs = {m: gu.out_buffer(n, torch.bfloat16) for m in forced}
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for m in forced:
+                plan.run(x[:m], outs[m][:m])
+    for rep in range(5):
+        for m in forced:
+            outs[m][:m].fill_(0)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for m in forced:
+            assert np.array_equal(gu.host_bits(outs[m]), ref[m]), (rep, m)
+    plan.close()
+
+
 def test_run_errors(sk):
     import torch
     n, k = 64, 256
