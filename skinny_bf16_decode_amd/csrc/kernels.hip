@@ -908,7 +908,7 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
     constexpr int KW = kMfmaxChunks;           // chunks per stage
     constexpr int PITCH = KW + 2;              // row pitch in 16-byte chunks (see above)
     constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
-    constexpr int NX = mfmax_x_windows(MT, NW);   // x windows in LDS: a barrier per NX / 2 stages
+    constexpr int NX = mfmax_x_windows(MT);    // x windows in LDS: a barrier per NX / 2 stages
     constexpr int PB = NX / 2;                 // stages per barrier
     static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
     extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [NX][MT][PITCH]

@@ -86,10 +86,10 @@ inline size_t mfmax_lds_bytes(int waves, int mt) { return (size_t)(16 * waves + 
 // MFMAX proper keeps 2 PB x windows, for a barrier per PB stages: PB = 2 for
 // token tiles up to 32, 1 for 64 (a barrier per 4 stages measured slower at
 // the 16-token tile: 17.6 against 16.3 us on 6288x7168)
-constexpr int mfmax_x_windows(int mt, int waves) { return (void)waves, mt <= 32 ? 4 : 2; }
+constexpr int mfmax_x_windows(int mt) { return mt <= 32 ? 4 : 2; }
 inline size_t mfmax_own_lds_bytes(int waves, int mt)
 {
-    return (size_t)(16 * waves + mfmax_x_windows(mt, waves) * mt) * (kMfmaxChunks + 2) * 16;
+    return (size_t)(16 * waves + mfmax_x_windows(mt) * mt) * (kMfmaxChunks + 2) * 16;
 }
 // MFMAD: per wave `depth` weight slots of 16 rows x 32 chunks, plus `depth` x slots of mt x 32 chunks
 inline size_t mfmad_lds_bytes(int waves, int mt, int depth) { return (size_t)depth * (16 * waves + mt) * 32 * 16; }
