@@ -89,9 +89,14 @@ typedef enum {
                               split x CUs ranges of at most `rows` rows) over all of K;
                               waves = rows / 16 row groups x K groups, whose partial sums
                               are added in LDS: no exchange between workgroups */
-    SKINNY_PATH_DOT2R = 8  /* the DOT2 kernels over equal row ranges of at most `rows` rows,
+    SKINNY_PATH_DOT2R = 8, /* the DOT2 kernels over equal row ranges of at most `rows` rows,
                               a whole multiple of CUs / split of them, so that every CU gets
                               the same number of (range, K split) workgroups */
+    SKINNY_PATH_MFMAW = 9  /* tiles 16/32/64: equal row ranges of at most `rows` rows (a whole
+                              multiple of CUs / split of them); every wave multiplies all
+                              rows / 16 row groups of the range over every waves-th K stage,
+                              W and x re-laid out through the wave's own LDS tiles, with no
+                              barrier until the waves' partial sums are added in LDS */
 } skinny_path;
 
 /*
@@ -105,17 +110,19 @@ typedef enum {
  */
 typedef struct {
     int path;   /* skinny_path */
-    int mt;     /* token tile: DOT2/DOT2R/DOT2X 1,2,4,8; MFMA/MFMAX/MFMAD/MFMAS/MFMAR/MFMAK 16,32,64 */
+    int mt;     /* token tile: DOT2/DOT2R/DOT2X 1,2,4,8; the MFMA paths 16,32,64 */
     int rows;   /* weight rows per workgroup.  DOT2, DOT2R: 1..16 (mt*rows <= 64; for
                    DOT2R the most rows of a range); MFMA: 16,32,64; DOT2X: waves * (1, 2
                    or 4); MFMAX, MFMAD, MFMAS, MFMAR: 16 * waves; MFMAK: 16 or 32 (row
-                   groups of 16), with waves a multiple of rows / 16 */
+                   groups of 16), with waves a multiple of rows / 16; MFMAW: 16, 32 or
+                   64 (the most rows of a range) */
     int waves;  /* wavefronts per workgroup: 1,2,4,8 */
     int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
                    (MFMAX: 1 = row tiles of 16 * waves rows, 2 = equal row ranges, its
                    stage is fixed at 32 chunks; MFMAD: the depth of
                    its LDS rings, 2..4 stages of 32 chunks; MFMAS, MFMAR, MFMAK:
-                   weight stages of 32 chunks in flight in registers, 2..4) */
+                   weight stages of 32 chunks in flight in registers, 2..4; MFMAW: 2
+                   stages of 16 chunks in flight) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16; MFMAS: the
                    stream-K grid, in workgroups per CU (1..4, capped at what fits);
                    MFMAK: row ranges per CU (1 or 2), K is never split between

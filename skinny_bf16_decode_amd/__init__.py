@@ -37,8 +37,9 @@ PATH_MFMAS = 5
 PATH_MFMAR = 6
 PATH_MFMAK = 7
 PATH_DOT2R = 8
+PATH_MFMAW = 9
 PATH_NAMES = {0: "dot2", 1: "mfma", 2: "dot2x", 3: "mfmax", 4: "mfmad", 5: "mfmas", 6: "mfmar", 7: "mfmak",
-              8: "dot2r"}
+              8: "dot2r", 9: "mfmaw"}
 
 STATUS = {
     0: "SKINNY_OK",

@@ -1304,7 +1304,6 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
     constexpr int PITCH = KW + 2;              // row pitch in 16-byte chunks (see k_mfmax)
     constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
     static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
-    static_assert(U >= 2 && U <= 4, "two to four stages in flight");
     constexpr int E = NW * T * 4 * 64;         // partial values of a tile
     extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [2][MT][PITCH]
     __shared__ unsigned last_flag[2];
@@ -1669,6 +1668,192 @@ __global__ __launch_bounds__(512) void k_mfmak(KArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// MFMAW kernel: token tile MT = 16 T; a workgroup owns one equal row range of
+// at most 16 RG rows and one K part (of `split`), with NW waves that each
+// multiply EVERY row group of the range over every NW-th K stage of 16 chunks
+// (4 MFMA K-steps).  No wave waits for another until the end:
+//
+//  * the weight and the x of a stage are loaded row-contiguously -- each
+//    wave-wide load is four rows (or tokens) x 256 bytes -- two stages ahead
+//    in registers, and re-laid out through the wave's own LDS tiles [16 RG][18]
+//    and [MT][18] (chunks) into A and B fragments.  A stage's weight
+//    registers are refilled as soon as they are in LDS, its x registers only
+//    after its MFMAs: x comes from L2, and issuing it with the weight (or
+//    three stages ahead) measured slower;
+//  * each B fragment feeds the MFMAs of all RG row groups, and the waves take
+//    disjoint K stages, so x is read once per workgroup and K stage however
+//    many rows the range has, with no x shared between waves;
+//  * the NW partial sums are added in LDS once, in wave order, after the
+//    stream; with split > 1 the sum goes through the split-K exchange.
+//
+// A and B take the same chunk (4 st + g) for K-group g of K-step st, so every
+// product W[n][k] x[m][k] is formed exactly once.  Row pitch 18 chunks (2 mod
+// 4): the fragment reads of 16 rows of one column are conflict-free (see
+// k_mfmax).  Unlike MFMAX, whose waves share each x window and meet at a
+// barrier every two stages, no wave here waits on another's loads.
+// ---------------------------------------------------------------------------
+template <int T, int RG, int NW, bool H>
+__global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
+{
+    constexpr int SC = kMfmawStageChunks;     // K chunks per stage
+    constexpr int PITCH = SC + 2;
+    constexpr int ROWS = 16 * RG;
+    constexpr int MT = 16 * T;
+    constexpr int E = RG * T * 4 * 64;         // partial values of one wave (and of the workgroup)
+    constexpr int EPT = E / (64 * NW);         // of them per thread in the final sum
+    static_assert(EPT >= 1 && EPT * 64 * NW == E, "the final sum must split evenly over the threads");
+    static_assert(E * 4 <= (ROWS + MT) * PITCH * 16, "the wave's LDS tiles must hold its partial sums");
+    extern __shared__ u32x4 sm[];              // [NW][ROWS + MT][PITCH]; at the end float [NW][E]
+    __shared__ unsigned flag;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tile, s;
+    block_coords(a, tile, s);
+    const auto range_row = [&](int t) {
+        return uniform_int((int)(((unsigned long long)(unsigned)t * (unsigned)a.N) / (unsigned)a.n_tiles));
+    };
+    const int n_wg = range_row(tile), n_end = range_row(tile + 1);
+    const int kb = (int)(((long)s * a.K8) / a.split);
+    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int stages = (ke - kb + SC - 1) / SC;
+    const int mine = stages > wave ? (stages - wave + NW - 1) / NW : 0;   // stages wave, wave + NW, ...
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
+    const int rows_valid = uniform_int(max(0, min(ROWS, n_end - n_wg)));
+    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n_wg : 0) * row_bytes,
+                                (unsigned)rows_valid * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
+    u32x4 *wl = sm + wave * (ROWS + MT) * PITCH;
+    u32x4 *xl = wl + ROWS * PITCH;
+    const int i16 = lane & 15, g = lane >> 4;
+
+    f32x4 acc[RG][T];
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Load q of a stage covers weight rows 4 q + g (x: tokens 4 q + g), chunk
+    // i16 of the wave's j-th stage; past the wave's last stage, or past the
+    // end of its K part, the offset is out of range and nothing is read.
+    const auto lane_chunk = [&](int j, unsigned &off) {
+        const int c = kb + (wave + NW * j) * SC + i16;
+        off = (unsigned)c * 16u;
+        return j < mine && c < ke;
+    };
+    auto load_wt = [&](u32x4(&wv)[4 * RG], int j) {
+        unsigned co;
+        const bool ok = lane_chunk(j, co);
+#pragma unroll
+        for (int q = 0; q < 4 * RG; ++q)
+            wv[q] = load_w(wres, lane_off(ok, (unsigned)(4 * q + g) * row_bytes + co), 0);
+    };
+    auto load_xt = [&](u32x4(&xv)[4 * T], int j) {
+        unsigned co;
+        const bool ok = lane_chunk(j, co);
+#pragma unroll
+        for (int q = 0; q < 4 * T; ++q)
+            xv[q] = load_x(xres, lane_off(ok, (unsigned)(4 * q + g) * x_pitch + co), 0);
+    };
+    // Stage j.  The tiles are rewritten by the next stage only after these
+    // fragment reads, in the wave's own program order.
+    auto step = [&](u32x4(&wv)[4 * RG], u32x4(&xv)[4 * T], int j) {
+#pragma unroll
+        for (int q = 0; q < 4 * RG; ++q)
+            wl[(4 * q + g) * PITCH + i16] = wv[q];
+        load_wt(wv, j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j < mine) {
+#pragma unroll
+            for (int q = 0; q < 4 * T; ++q)
+                xl[(4 * q + g) * PITCH + i16] = xv[q];
+            u32x4 bv[4][T];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    bv[st][t] = xl[(16 * t + i16) * PITCH + 4 * st + g];
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                u32x4 av[4];
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    av[st] = wl[(16 * r + i16) * PITCH + 4 * st + g];
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        acc[r][t] = mma16<H>(av[st], bv[st][t], acc[r][t]);
+            }
+        }
+        load_xt(xv, j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Two stages in flight; every pass issues all of its loads (past the
+    // wave's last stage they touch no memory), so the waits stay partial.
+    u32x4 wa[4 * RG], xa[4 * T], wb[4 * RG], xb[4 * T];
+    load_wt(wa, 0);
+    load_xt(xa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_wt(wb, 1);
+    load_xt(xb, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < mine; j += 2) {
+        step(wa, xa, j);
+        step(wb, xb, j + 1);
+    }
+
+    // add the NW partial sums in wave order: value e = ((r T + t) 4 + q) 64 + lane
+    float *red = reinterpret_cast<float *>(sm);
+    __syncthreads();                           // every wave is past its last fragment read
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                red[wave * E + ((r * T + t) * 4 + q) * 64 + lane] = acc[r][t][q];
+    __syncthreads();
+    float v[EPT];
+    int off[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        off[i] = tid + 64 * NW * i;
+        v[i] = red[off[i]];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            v[i] += red[w * E + off[i]];
+    }
+    // value e: token 16 t + (e % 16), row n_wg + 16 r + 4 ((e / 16) % 4) + q
+    auto store_all = [&](const float(&vals)[EPT]) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = off[i], ln = e & 63, q = (e >> 6) & 3, rt = e >> 8;
+            const int r = rt / T, t = rt - (rt / T) * T;
+            const int tok = 16 * t + (ln & 15), n = n_wg + 16 * r + 4 * (ln >> 4) + q;
+            if (tok < a.M && n < n_end)
+                store_out(a, tok, n, vals[i]);
+        }
+    };
+    if (a.split == 1) {
+        store_all(v);
+        return;
+    }
+    float *wsp = a.ws + (long)tile * a.split * E;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+        publish_partial(wsp + (long)s * E + off[i], v[i]);
+    if (!split_arrive_last(a, tile, &flag))
+        return;
+    float sum[EPT];
+    sum_partials<EPT>(wsp, E, a.split, off, sum);
+    store_all(sum);
+    split_reset(a, tile);
+}
+
+// ---------------------------------------------------------------------------
 // Measurement probes: a plain streaming read of a buffer (what the weight
 // stream could reach with no arithmetic around it) and an empty launch.
 // ---------------------------------------------------------------------------
@@ -1718,6 +1903,8 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
 #define SK_MFMAS(T, NW, D) SK_PAIR(SKINNY_PATH_MFMAS, 16 * T, NW, D, k_mfmas, T, NW, D)
 // MFMAK: rows field = 100 * KS + RT (row groups and K groups), unroll = iterations in flight
 #define SK_MFMAK(T, RT, KS, U) SK_PAIR(SKINNY_PATH_MFMAK, 16 * T, 100 * KS + RT, U, k_mfmak, T, RT, KS, U)
+// MFMAW: rows field = 100 * NW + RG (waves and row groups), two stages in flight
+#define SK_MFMAW(T, RG, NW) SK_PAIR(SKINNY_PATH_MFMAW, 16 * T, 100 * NW + RG, 2, k_mfmaw, T, RG, NW)
 
 // Instances whose double-buffered loads, accumulators and offsets fit in 256
 // VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
@@ -1764,6 +1951,9 @@ static const KernelInfo kKernels[] = {
     SK_MFMAS(2, 4, 2), SK_MFMAS(2, 4, 3), SK_MFMAS(2, 8, 2),
     SK_MFMAK(1, 1, 4, 2), SK_MFMAK(1, 2, 2, 2), SK_MFMAK(1, 2, 2, 3), SK_MFMAK(1, 2, 4, 2), SK_MFMAK(1, 2, 4, 3),
     SK_MFMAK(2, 2, 2, 2),
+    SK_MFMAW(1, 1, 4), SK_MFMAW(1, 2, 2), SK_MFMAW(1, 2, 4), SK_MFMAW(1, 4, 4),
+    SK_MFMAW(2, 1, 4), SK_MFMAW(2, 2, 2), SK_MFMAW(2, 2, 4), SK_MFMAW(2, 2, 8), SK_MFMAW(2, 4, 4),
+    SK_MFMAW(4, 1, 4), SK_MFMAW(4, 2, 2), SK_MFMAW(4, 2, 4),
 };
 
 const KernelInfo *kernel_table(int *count)

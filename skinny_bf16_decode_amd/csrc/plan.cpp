@@ -133,7 +133,8 @@ Entry make_entry(const skinny_tactic &t, int N, int K, int half)
         // equal row ranges, at least as many (x split) as there are CUs
         const int want = (device_cus() + t.split - 1) / t.split;
         en.n_tiles = std::min(N, std::max(en.n_tiles, want));
-    } else if ((t.path == SKINNY_PATH_MFMAX && t.unroll == 2) || t.path == SKINNY_PATH_DOT2R) {
+    } else if ((t.path == SKINNY_PATH_MFMAX && t.unroll == 2) || t.path == SKINNY_PATH_DOT2R ||
+               t.path == SKINNY_PATH_MFMAW) {
         // equal row ranges, a whole multiple of CUs / split of them, so that
         // every CU gets the same number of (range, K part) workgroups
         const int per_round = (device_cus() + t.split - 1) / t.split;
@@ -169,7 +170,7 @@ void raise_lds_limits()
         for (int i = 0; i < nk; ++i)
             if (ks[i].path == SKINNY_PATH_DOT2X || ks[i].path == SKINNY_PATH_MFMAX ||
                 ks[i].path == SKINNY_PATH_MFMAD || ks[i].path == SKINNY_PATH_MFMAS ||
-                ks[i].path == SKINNY_PATH_MFMAK)
+                ks[i].path == SKINNY_PATH_MFMAK || ks[i].path == SKINNY_PATH_MFMAW)
                 (void)hipFuncSetAttribute(ks[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         (void)hipGetLastError();
     });
@@ -222,7 +223,8 @@ hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
     a.remap = (en.t.split > 1 && a.nxcd > 1) ? 1 : 0;
     a.sk_spt = en.sk_spt;
     a.sk_parts = en.sk_parts;
-    a.ranges = (en.t.path == SKINNY_PATH_MFMAX && en.t.unroll == 2) || en.t.path == SKINNY_PATH_DOT2R;
+    a.ranges = (en.t.path == SKINNY_PATH_MFMAX && en.t.unroll == 2) || en.t.path == SKINNY_PATH_DOT2R ||
+               en.t.path == SKINNY_PATH_MFMAW;
     void *params[] = {&a};
     return hipLaunchKernel(en.fn, dim3(en.grid), dim3(en.block), params, en.lds, stream);
 }
@@ -809,9 +811,10 @@ skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len
     }
     const Entry &en = p->e[M];
     static const char *const kNames[] = {"dot2", "mfma16x16x32", "dot2x", "mfmax16x16x32", "mfmad16x16x32",
-                                         "mfmas16x16x32", "mfmar16x16x32", "mfmak16x16x32", "dot2r"};
+                                         "mfmas16x16x32", "mfmar16x16x32", "mfmak16x16x32", "dot2r",
+                                         "mfmaw16x16x32"};
     snprintf(buf, len, "%s mt=%d rows=%d waves=%d unroll=%d split=%d grid=%u block=%u lds=%u",
-             (t.path >= 0 && t.path <= 8) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
+             (t.path >= 0 && t.path <= 9) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
              en.grid, en.block, en.lds);
     return SKINNY_OK;
 }

@@ -35,6 +35,8 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
         return mfmad_lds_bytes(t.waves, t.mt, t.unroll);
     case SKINNY_PATH_MFMAK:
         return t.rows >= 16 ? mfmak_lds_bytes(t.waves, t.mt, t.waves / (t.rows / 16)) : 0;
+    case SKINNY_PATH_MFMAW:
+        return mfmaw_lds_bytes(t.waves, t.rows, t.mt);
     default:
         return 0;
     }
@@ -71,6 +73,10 @@ const KernelInfo *tactic_kernel(const skinny_tactic &t, int half)
         const int rt = t.rows / 16, ks = t.waves / rt;
         return find_kernel(t.path, t.mt, 100 * ks + rt, t.unroll, half);
     }
+    case SKINNY_PATH_MFMAW:                    // KernelInfo.rows = 100 waves + row groups
+        if (t.rows < 16 || t.rows % 16)
+            return nullptr;
+        return find_kernel(t.path, t.mt, 100 * t.waves + t.rows / 16, t.unroll, half);
     default:
         return nullptr;
     }
@@ -135,6 +141,12 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             set_error("split=%d: for MFMAK split is row ranges per CU, 1 or 2", t->split);
             return SKINNY_ERR_INVALID_ARG;
         }
+    } else if (t->path == SKINNY_PATH_MFMAW) {
+        const int stages = (k8 + kMfmawStageChunks - 1) / kMfmawStageChunks;
+        if (t->split > stages) {
+            set_error("split=%d exceeds the %d K stages of %d chunks", t->split, stages, kMfmawStageChunks);
+            return SKINNY_ERR_INVALID_ARG;
+        }
     } else if (t->path == SKINNY_PATH_MFMAR) {
         const int stages = (k8 + kMfmaxChunks - 1) / kMfmaxChunks;
         if (t->split > stages) {
@@ -149,7 +161,7 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
         }
     } else {
         set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD), 5 (MFMAS), 6 (MFMAR), "
-                  "7 (MFMAK) or 8 (DOT2R)", t->path);
+                  "7 (MFMAK), 8 (DOT2R) or 9 (MFMAW)", t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
     const size_t lds_limit = (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
@@ -204,12 +216,18 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                             continue;
                         t.rows = 16 * rt;
                     }
+                    if (path == SKINNY_PATH_MFMAW) {     // k.rows = 100 waves + row groups
+                        if (w != k.rows / 100 || s > 4)
+                            continue;
+                        t.rows = 16 * (k.rows % 100);
+                    }
                     if (path == SKINNY_PATH_MFMAS && s > 3)
                         continue;                        // split: workgroups per CU
                     if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                         continue;
                     const int tiles = (N + t.rows - 1) / t.rows;
-                    if (s > 1 && tiles * w >= 8 * 256 && path != SKINNY_PATH_MFMAS && path != SKINNY_PATH_MFMAK)
+                    if (s > 1 && tiles * w >= 8 * 256 && path != SKINNY_PATH_MFMAS && path != SKINNY_PATH_MFMAK &&
+                        path != SKINNY_PATH_MFMAW)
                         continue;   // enough waves already; a K split only adds traffic
                     if (path == SKINNY_PATH_DOT2R && tiles * s > 8 * 256)
                         continue;   // many workgroups per CU balance themselves
@@ -225,6 +243,10 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                             continue;
                     } else if (path == SKINNY_PATH_MFMAS || path == SKINNY_PATH_MFMAK) {
                         if (k8 < 2 * kMfmaxChunks)
+                            continue;
+                    } else if (path == SKINNY_PATH_MFMAW) {
+                        // every wave should own two stages of its K part at least
+                        if (k8 / s < 2 * w * kMfmawStageChunks)
                             continue;
                     } else if (path == SKINNY_PATH_MFMAX || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAR) {
                         if (k8 / s < 2 * kMfmaxChunks)
