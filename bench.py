@@ -20,14 +20,23 @@ Diagnostics (per-M times, the plain read ceiling over the same rotated
 weights, the empty-launch floor, parity of the last outputs) go to the JSON's
 extra fields and to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--extra] [--no-cpu]
+The per-M tactic table is the one this library's tuner measured on an MI355X
+(256 CUs) when the committed profiles were taken, shipped in
+skinny_bf16_decode_amd/tables/ the way the pages ship measured per-part
+tables; it is loaded through a temporary copy of that file.  A GPU with
+another CU count finds no matching line and is tuned on the spot, and so is
+every run with --retune.  SKINNY_TABLE_CACHE, when set, takes precedence.
+
+  python bench.py [--steps K] [--warmup W] [--extra] [--no-cpu] [--retune]
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import shutil
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -36,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0
+SHIPPED_TABLES = os.path.join(ROOT, "skinny_bf16_decode_amd", "tables", "mi355x_tuned.txt")
 WORKLOAD = 3
 M_SWEEP = (1, 2, 4, 8, 16, 32)
 STEPS_PER_GRAPH = 16
@@ -232,6 +242,25 @@ def parity_of_last(setup, last_copy, m, samples=4096):
     return rep
 
 
+def use_tables(retune, cus):
+    """Point SKINNY_TABLE_CACHE at a temporary copy of the shipped tables
+    (unless the caller set it, or asked to retune); say where the headline
+    shape's table comes from."""
+    if os.environ.get("SKINNY_TABLE_CACHE"):
+        return f"SKINNY_TABLE_CACHE={os.environ['SKINNY_TABLE_CACHE']}"
+    if retune:
+        return "tuned on this GPU (--retune)"
+    fd, path = tempfile.mkstemp(prefix="skinny_tables_", suffix=".txt")
+    os.close(fd)
+    shutil.copyfile(SHIPPED_TABLES, path)
+    os.environ["SKINNY_TABLE_CACHE"] = path
+    with open(SHIPPED_TABLES) as f:
+        key = ["skinny-table", "v2", "gfx950", str(cus), "6288", "7168", "bf16", "bf16"]
+        if any(line.split()[:8] == key for line in f):
+            return f"shipped ({os.path.relpath(SHIPPED_TABLES, ROOT)}, {cus} CUs)"
+    return f"tuned on this GPU (no shipped table for {cus} CUs)"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +272,8 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="also launch a plain read of one weight copy and a 64 MiB device copy, "
                          "whose known byte counts scale the HBM traffic counters")
+    ap.add_argument("--retune", action="store_true",
+                    help="tune the tactic tables on this GPU instead of loading the shipped ones")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -259,6 +290,8 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count} "
         f"torch={torch.__version__} hip={torch.version.hip}")
+    table_source = use_tables(args.retune, props.multi_processor_count)
+    log(f"tactic table: {table_source}")
 
     setup = Setup(WORKLOAD)
     wl = setup.wl
@@ -371,6 +404,7 @@ def main():
         "read_ceiling_gbps": round(ceil_gb, 1),
         "empty_launch_us": round(floor_us, 3),
         "parity_last_call": "ok",
+        "tactic_table": table_source,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "skinny projection launches of the step (the per-M table's kernels)",

@@ -242,3 +242,33 @@ def test_bench_names_the_kernel_of_every_tactic():
     assert bench.kernel_name(T(3, 32, 64, 4, 2, 2)) == "k_mfmax<2, 4, false>"
     assert bench.kernel_name(T(sk.PATH_DOT2R, 2, 4, 1, 2, 1)) == "k_dot2<2, 4, 2, false>"
     assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2)) == "k_mfmaw<2, 4, 4, false>"
+
+
+def test_shipped_table_is_legal_and_profiled():
+    """The tactic table bench.py loads by default: one line per (chip, shape),
+    every entry legal for its shape with a token tile >= M (the library
+    ignores a line that fails this, and tunes instead), and the committed
+    HBM traffic record names the kernel of every token count the benchmark
+    step runs."""
+    import json
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    with open(bench.SHIPPED_TABLES) as f:
+        lines = [ln.split() for ln in f if ln.strip()]
+    assert lines
+    heads = set()
+    for ln in lines:
+        assert ln[:3] == ["skinny-table", "v2", "gfx950"] and len(ln) == 8 + 64
+        n, k = int(ln[4]), int(ln[5])
+        heads.add(tuple(ln[:8]))
+        for m, field in enumerate(ln[8:], start=1):
+            t = T(*map(int, field.split(".")))
+            sk.tactic_check(t, n, k)
+            assert t.mt >= m
+    assert len(heads) == len(lines)
+    head = next(ln for ln in lines if ln[4:8] == ["6288", "7168", "bf16", "bf16"])
+    with open(bench.TRAFFIC_RECORD) as f:
+        rec = json.load(f)
+    for m in bench.M_SWEEP:
+        name = bench.kernel_name(T(*map(int, head[8 + m - 1].split("."))))
+        assert name in rec["kernels"], (m, name)

@@ -265,21 +265,31 @@ def test_deterministic_and_graph_replay(sk):
     plan.close()
 
 
-def test_decode_kernels_repeat_and_graph_replay(sk):
-    """The kernels the packed 6288x7168 decode weight runs with -- DOT2 at
-    M = 1, DOT2 over equal row ranges at M = 2, the ranged 16-token MFMAX at
-    M = 16 and the ranged 32-token MFMAX with a two-way K split at M = 32 --
-    forced, at full size: bitwise identical over repeats and over graph
-    replays with eager work between them, and within the bound on 4096
-    sampled outputs per M."""
+# Kernels the tuner picks for the packed 6288x7168 decode weight, by token
+# count: DOT2 at M = 1, DOT2 over equal row ranges at M = 2, the ranged MFMAX
+# at 16 tokens and at 32 with a two-way K split; and the barrier-free MFMAW at
+# 4, 8 (with a two-way K split), 32 and 64 tokens.
+DECODE_KERNEL_SETS = {
+    "dot2_mfmax": lambda sk: {1: sk.Tactic(0, 1, 2, 8, 1, 1), 2: sk.Tactic(sk.PATH_DOT2R, 2, 4, 1, 2, 1),
+                              16: sk.Tactic(3, 16, 32, 2, 2, 1), 32: sk.Tactic(3, 32, 64, 4, 2, 2)},
+    "mfmaw": lambda sk: {4: sk.Tactic(sk.PATH_MFMAW, 16, 32, 2, 2, 1), 8: sk.Tactic(sk.PATH_MFMAW, 16, 32, 2, 2, 2),
+                         32: sk.Tactic(sk.PATH_MFMAW, 32, 32, 2, 2, 1), 64: sk.Tactic(sk.PATH_MFMAW, 64, 32, 4, 2, 1)},
+}
+
+
+@pytest.mark.parametrize("kernels", sorted(DECODE_KERNEL_SETS))
+def test_decode_kernels_repeat_and_graph_replay(sk, kernels):
+    """The kernels of the packed 6288x7168 decode weight, forced, at full
+    size: bitwise identical over repeats and over graph replays with eager
+    work between them, and within the bound on 4096 sampled outputs per M."""
     import torch
     wl = si.WORKLOADS[3]
     w_bits, x_bits = si.weight(3, 0), si.activations(3)
     n = wl.n
     w = gu.dev_bf16(w_bits)
     x = gu.dev_bf16(x_bits)
-    forced = {1: sk.Tactic(0, 1, 2, 8, 1, 1), 2: sk.Tactic(sk.PATH_DOT2R, 2, 4, 1, 2, 1),
-              16: sk.Tactic(3, 16, 32, 2, 2, 1), 32: sk.Tactic(3, 32, 64, 4, 2, 2)}
+    forced = DECODE_KERNEL_SETS[kernels](sk)
+    _say(f"[decode kernels {kernels}] {forced}")
     table = []
     for m in range(1, 65):
         fits = [t for mm, t in sorted(forced.items()) if mm >= m]
