@@ -202,8 +202,8 @@ def kernel_name(t):
     elif t.path == 7:                        # MFMAK: row groups and K groups
         rt = t.rows // 16
         args, name = (T, rt, w // rt, t.unroll), "k_mfmak"
-    elif t.path == 9:                        # MFMAW: row groups and waves
-        args, name = (T, t.rows // 16, w), "k_mfmaw"
+    elif t.path == 9:                        # MFMAW: row groups, waves, stage chunks
+        args, name = (T, t.rows // 16, w, 8 * t.unroll), "k_mfmaw"
     else:
         return None
     return f"{name}<{', '.join(str(a) for a in args)}, false>"

@@ -121,8 +121,8 @@ typedef struct {
                    (MFMAX: 1 = row tiles of 16 * waves rows, 2 = equal row ranges, its
                    stage is fixed at 32 chunks; MFMAD: the depth of
                    its LDS rings, 2..4 stages of 32 chunks; MFMAS, MFMAR, MFMAK:
-                   weight stages of 32 chunks in flight in registers, 2..4; MFMAW: 2
-                   stages of 16 chunks in flight) */
+                   weight stages of 32 chunks in flight in registers, 2..4; MFMAW:
+                   the stage width in 8-chunk units, 1 or 2, two stages in flight) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16; MFMAS: the
                    stream-K grid, in workgroups per CU (1..4, capped at what fits);
                    MFMAK: row ranges per CU (1 or 2), K is never split between

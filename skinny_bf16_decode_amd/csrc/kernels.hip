@@ -1670,13 +1670,14 @@ __global__ __launch_bounds__(512) void k_mfmak(KArgs a)
 // ---------------------------------------------------------------------------
 // MFMAW kernel: token tile MT = 16 T; a workgroup owns one equal row range of
 // at most 16 RG rows and one K part (of `split`), with NW waves that each
-// multiply EVERY row group of the range over every NW-th K stage of 16 chunks
-// (4 MFMA K-steps).  No wave waits for another until the end:
+// multiply EVERY row group of the range over every NW-th K stage of SC = 8 or
+// 16 chunks (SC / 4 MFMA K-steps).  No wave waits for another until the end:
 //
 //  * the weight and the x of a stage are loaded row-contiguously -- each
-//    wave-wide load is four rows (or tokens) x 256 bytes -- two stages ahead
-//    in registers, and re-laid out through the wave's own LDS tiles [16 RG][18]
-//    and [MT][18] (chunks) into A and B fragments.  A stage's weight
+//    wave-wide load is 64 / SC rows (or tokens) x 16 SC bytes -- two stages
+//    ahead in registers, and re-laid out through the wave's own LDS tiles
+//    [16 RG][SC + 2] and [MT][SC + 2] (chunks) into A and B fragments.  The
+//    stage width sets the bytes a wave keeps in flight.  A stage's weight
 //    registers are refilled as soon as they are in LDS, its x registers only
 //    after its MFMAs: x comes from L2, and issuing it with the weight (or
 //    three stages ahead) measured slower;
@@ -1687,15 +1688,18 @@ __global__ __launch_bounds__(512) void k_mfmak(KArgs a)
 //    stream; with split > 1 the sum goes through the split-K exchange.
 //
 // A and B take the same chunk (4 st + g) for K-group g of K-step st, so every
-// product W[n][k] x[m][k] is formed exactly once.  Row pitch 18 chunks (2 mod
-// 4): the fragment reads of 16 rows of one column are conflict-free (see
+// product W[n][k] x[m][k] is formed exactly once.  Row pitch SC + 2 chunks (2
+// mod 4): the fragment reads of 16 rows of one column are conflict-free (see
 // k_mfmax).  Unlike MFMAX, whose waves share each x window and meet at a
 // barrier every two stages, no wave here waits on another's loads.
 // ---------------------------------------------------------------------------
-template <int T, int RG, int NW, bool H>
+template <int T, int RG, int NW, int SC, bool H>
 __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
 {
-    constexpr int SC = kMfmawStageChunks;     // K chunks per stage
+    static_assert(SC == 8 || SC == 16, "stages of 8 or 16 chunks");
+    constexpr int RPL = 64 / SC;               // rows (tokens) per wave-wide load
+    constexpr int NL = 16 / RPL;               // loads per 16 rows (tokens)
+    constexpr int KS = SC / 4;                 // MFMA K-steps per stage
     constexpr int PITCH = SC + 2;
     constexpr int ROWS = 16 * RG;
     constexpr int MT = 16 * T;
@@ -1726,6 +1730,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
     u32x4 *wl = sm + wave * (ROWS + MT) * PITCH;
     u32x4 *xl = wl + ROWS * PITCH;
     const int i16 = lane & 15, g = lane >> 4;
+    const int lr = lane / SC, lc = lane % SC;  // row within a load, chunk within the stage
 
     f32x4 acc[RG][T];
 #pragma unroll
@@ -1734,54 +1739,54 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
         for (int t = 0; t < T; ++t)
             acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Load q of a stage covers weight rows 4 q + g (x: tokens 4 q + g), chunk
-    // i16 of the wave's j-th stage; past the wave's last stage, or past the
-    // end of its K part, the offset is out of range and nothing is read.
+    // Load q of a stage covers weight rows RPL q + lr (x: tokens RPL q + lr),
+    // chunk lc of the wave's j-th stage; past the wave's last stage, or past
+    // the end of its K part, the offset is out of range and nothing is read.
     const auto lane_chunk = [&](int j, unsigned &off) {
-        const int c = kb + (wave + NW * j) * SC + i16;
+        const int c = kb + (wave + NW * j) * SC + lc;
         off = (unsigned)c * 16u;
         return j < mine && c < ke;
     };
-    auto load_wt = [&](u32x4(&wv)[4 * RG], int j) {
+    auto load_wt = [&](u32x4(&wv)[NL * RG], int j) {
         unsigned co;
         const bool ok = lane_chunk(j, co);
 #pragma unroll
-        for (int q = 0; q < 4 * RG; ++q)
-            wv[q] = load_w(wres, lane_off(ok, (unsigned)(4 * q + g) * row_bytes + co), 0);
+        for (int q = 0; q < NL * RG; ++q)
+            wv[q] = load_w(wres, lane_off(ok, (unsigned)(RPL * q + lr) * row_bytes + co), 0);
     };
-    auto load_xt = [&](u32x4(&xv)[4 * T], int j) {
+    auto load_xt = [&](u32x4(&xv)[NL * T], int j) {
         unsigned co;
         const bool ok = lane_chunk(j, co);
 #pragma unroll
-        for (int q = 0; q < 4 * T; ++q)
-            xv[q] = load_x(xres, lane_off(ok, (unsigned)(4 * q + g) * x_pitch + co), 0);
+        for (int q = 0; q < NL * T; ++q)
+            xv[q] = load_x(xres, lane_off(ok, (unsigned)(RPL * q + lr) * x_pitch + co), 0);
     };
     // Stage j.  The tiles are rewritten by the next stage only after these
     // fragment reads, in the wave's own program order.
-    auto step = [&](u32x4(&wv)[4 * RG], u32x4(&xv)[4 * T], int j) {
+    auto step = [&](u32x4(&wv)[NL * RG], u32x4(&xv)[NL * T], int j) {
 #pragma unroll
-        for (int q = 0; q < 4 * RG; ++q)
-            wl[(4 * q + g) * PITCH + i16] = wv[q];
+        for (int q = 0; q < NL * RG; ++q)
+            wl[(RPL * q + lr) * PITCH + lc] = wv[q];
         load_wt(wv, j + 2);
         __builtin_amdgcn_sched_barrier(0);
         if (j < mine) {
 #pragma unroll
-            for (int q = 0; q < 4 * T; ++q)
-                xl[(4 * q + g) * PITCH + i16] = xv[q];
-            u32x4 bv[4][T];
+            for (int q = 0; q < NL * T; ++q)
+                xl[(RPL * q + lr) * PITCH + lc] = xv[q];
+            u32x4 bv[KS][T];
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
+            for (int st = 0; st < KS; ++st)
 #pragma unroll
                 for (int t = 0; t < T; ++t)
                     bv[st][t] = xl[(16 * t + i16) * PITCH + 4 * st + g];
 #pragma unroll
             for (int r = 0; r < RG; ++r) {
-                u32x4 av[4];
+                u32x4 av[KS];
 #pragma unroll
-                for (int st = 0; st < 4; ++st)
+                for (int st = 0; st < KS; ++st)
                     av[st] = wl[(16 * r + i16) * PITCH + 4 * st + g];
 #pragma unroll
-                for (int st = 0; st < 4; ++st)
+                for (int st = 0; st < KS; ++st)
 #pragma unroll
                     for (int t = 0; t < T; ++t)
                         acc[r][t] = mma16<H>(av[st], bv[st][t], acc[r][t]);
@@ -1793,7 +1798,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
 
     // Two stages in flight; every pass issues all of its loads (past the
     // wave's last stage they touch no memory), so the waits stay partial.
-    u32x4 wa[4 * RG], xa[4 * T], wb[4 * RG], xb[4 * T];
+    u32x4 wa[NL * RG], xa[NL * T], wb[NL * RG], xb[NL * T];
     load_wt(wa, 0);
     load_xt(xa, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -1903,8 +1908,9 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
 #define SK_MFMAS(T, NW, D) SK_PAIR(SKINNY_PATH_MFMAS, 16 * T, NW, D, k_mfmas, T, NW, D)
 // MFMAK: rows field = 100 * KS + RT (row groups and K groups), unroll = iterations in flight
 #define SK_MFMAK(T, RT, KS, U) SK_PAIR(SKINNY_PATH_MFMAK, 16 * T, 100 * KS + RT, U, k_mfmak, T, RT, KS, U)
-// MFMAW: rows field = 100 * NW + RG (waves and row groups), two stages in flight
-#define SK_MFMAW(T, RG, NW) SK_PAIR(SKINNY_PATH_MFMAW, 16 * T, 100 * NW + RG, 2, k_mfmaw, T, RG, NW)
+// MFMAW: rows field = 100 * NW + RG (waves and row groups), unroll = stage
+// width in 8-chunk units (1: 8 chunks, 2: 16)
+#define SK_MFMAW(T, RG, NW, U) SK_PAIR(SKINNY_PATH_MFMAW, 16 * T, 100 * NW + RG, U, k_mfmaw, T, RG, NW, 8 * U)
 
 // Instances whose double-buffered loads, accumulators and offsets fit in 256
 // VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
@@ -1951,9 +1957,12 @@ static const KernelInfo kKernels[] = {
     SK_MFMAS(2, 4, 2), SK_MFMAS(2, 4, 3), SK_MFMAS(2, 8, 2),
     SK_MFMAK(1, 1, 4, 2), SK_MFMAK(1, 2, 2, 2), SK_MFMAK(1, 2, 2, 3), SK_MFMAK(1, 2, 4, 2), SK_MFMAK(1, 2, 4, 3),
     SK_MFMAK(2, 2, 2, 2),
-    SK_MFMAW(1, 1, 4), SK_MFMAW(1, 2, 2), SK_MFMAW(1, 2, 4), SK_MFMAW(1, 4, 4),
-    SK_MFMAW(2, 1, 4), SK_MFMAW(2, 2, 2), SK_MFMAW(2, 2, 4), SK_MFMAW(2, 2, 8), SK_MFMAW(2, 4, 4),
-    SK_MFMAW(4, 1, 4), SK_MFMAW(4, 2, 2), SK_MFMAW(4, 2, 4),
+    SK_MFMAW(1, 1, 4, 2), SK_MFMAW(1, 2, 1, 2), SK_MFMAW(1, 2, 2, 2), SK_MFMAW(1, 2, 4, 2), SK_MFMAW(1, 4, 4, 2),
+    SK_MFMAW(2, 1, 4, 2), SK_MFMAW(2, 2, 1, 2), SK_MFMAW(2, 2, 2, 2), SK_MFMAW(2, 2, 4, 2), SK_MFMAW(2, 2, 8, 2),
+    SK_MFMAW(2, 4, 4, 2), SK_MFMAW(4, 1, 4, 2), SK_MFMAW(4, 2, 2, 2), SK_MFMAW(4, 2, 4, 2),
+    SK_MFMAW(1, 1, 4, 1), SK_MFMAW(1, 2, 2, 1), SK_MFMAW(1, 2, 4, 1), SK_MFMAW(1, 2, 8, 1), SK_MFMAW(1, 4, 4, 1),
+    SK_MFMAW(2, 2, 2, 1), SK_MFMAW(2, 2, 4, 1), SK_MFMAW(2, 2, 8, 1), SK_MFMAW(2, 4, 4, 1),
+    SK_MFMAW(4, 2, 2, 1), SK_MFMAW(4, 2, 4, 1),
 };
 
 const KernelInfo *kernel_table(int *count)

@@ -93,12 +93,12 @@ inline size_t mfmax_own_lds_bytes(int waves, int mt)
 }
 // MFMAD: per wave `depth` weight slots of 16 rows x 32 chunks, plus `depth` x slots of mt x 32 chunks
 inline size_t mfmad_lds_bytes(int waves, int mt, int depth) { return (size_t)depth * (16 * waves + mt) * 32 * 16; }
-// MFMAW: wave tiles [waves][rows + mt][18 chunks] for stages of 16 chunks; the
-// waves' partial sums reuse them at the end
-constexpr int kMfmawStageChunks = 16;
-inline size_t mfmaw_lds_bytes(int waves, int rows, int mt)
+// MFMAW: stages of 8 unroll chunks (8 or 16); wave tiles [waves][rows + mt]
+// [stage + 2 chunks], which the waves' partial sums reuse at the end
+inline int mfmaw_stage_chunks(int unroll) { return 8 * unroll; }
+inline size_t mfmaw_lds_bytes(int waves, int rows, int mt, int unroll)
 {
-    return (size_t)waves * (rows + mt) * (kMfmawStageChunks + 2) * 16;
+    return (size_t)waves * (rows + mt) * (mfmaw_stage_chunks(unroll) + 2) * 16;
 }
 // MFMAK: wave tiles [waves][16][34] and two x windows [mt][32 ks + 2]
 inline size_t mfmak_lds_bytes(int waves, int mt, int ks)

@@ -36,7 +36,7 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
     case SKINNY_PATH_MFMAK:
         return t.rows >= 16 ? mfmak_lds_bytes(t.waves, t.mt, t.waves / (t.rows / 16)) : 0;
     case SKINNY_PATH_MFMAW:
-        return mfmaw_lds_bytes(t.waves, t.rows, t.mt);
+        return mfmaw_lds_bytes(t.waves, t.rows, t.mt, t.unroll);
     default:
         return 0;
     }
@@ -142,9 +142,13 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             return SKINNY_ERR_INVALID_ARG;
         }
     } else if (t->path == SKINNY_PATH_MFMAW) {
-        const int stages = (k8 + kMfmawStageChunks - 1) / kMfmawStageChunks;
+        if (t->unroll != 1 && t->unroll != 2) {
+            set_error("unroll=%d: for MFMAW the stage width in 8-chunk units, 1 or 2", t->unroll);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+        const int sc = mfmaw_stage_chunks(t->unroll), stages = (k8 + sc - 1) / sc;
         if (t->split > stages) {
-            set_error("split=%d exceeds the %d K stages of %d chunks", t->split, stages, kMfmawStageChunks);
+            set_error("split=%d exceeds the %d K stages of %d chunks", t->split, stages, sc);
             return SKINNY_ERR_INVALID_ARG;
         }
     } else if (t->path == SKINNY_PATH_MFMAR) {
@@ -246,7 +250,7 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                             continue;
                     } else if (path == SKINNY_PATH_MFMAW) {
                         // every wave should own two stages of its K part at least
-                        if (k8 / s < 2 * w * kMfmawStageChunks)
+                        if (k8 / s < 2 * w * mfmaw_stage_chunks(k.unroll))
                             continue;
                     } else if (path == SKINNY_PATH_MFMAX || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAR) {
                         if (k8 / s < 2 * kMfmaxChunks)

@@ -166,22 +166,24 @@ def test_row_range_tactics():
 
 def test_barrier_free_row_range_tactics():
     """MFMAW (path 9): ranges of at most 16, 32 or 64 rows (row groups of
-    16), with its compiled wave counts only, two stages in flight (unroll 2),
-    and a K split no larger than its 16-chunk stages; every wave of every
-    candidate owns at least two stages of its K part."""
+    16), with its compiled wave counts only, stages of 8 (unroll 1) or 16
+    chunks (unroll 2), and a K split no larger than its stage count; every
+    wave of every candidate owns at least two stages of its K part."""
     cands = [t for t in sk.enumerate_tactics(6288, 7168) if t.path == sk.PATH_MFMAW]
     assert {t.mt for t in cands} == {16, 32, 64}
+    assert {t.unroll for t in cands} == {1, 2}
     assert {t.rows for t in cands} == {16, 32, 64}
     for t in cands:
-        assert t.unroll == 2 and t.rows % 16 == 0
-        assert (7168 // 8) // t.split >= 2 * t.waves * 16
+        assert t.unroll in (1, 2) and t.rows % 16 == 0
+        assert (7168 // 8) // t.split >= 2 * t.waves * 8 * t.unroll
     sk.tactic_check(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2), 6288, 7168)
     sk.tactic_check(T(sk.PATH_MFMAW, 16, 32, 2, 2, 1), 6288, 7168)
     for bad in (T(sk.PATH_MFMAW, 32, 64, 8, 2, 1),    # spills: not compiled
                 T(sk.PATH_MFMAW, 16, 48, 4, 2, 1),    # no 3-group instance
                 T(sk.PATH_MFMAW, 16, 24, 4, 2, 1),    # not whole row groups
-                T(sk.PATH_MFMAW, 16, 32, 4, 3, 1),    # two stages in flight only
-                T(sk.PATH_MFMAW, 16, 32, 4, 2, 9)):   # 128 chunks: 8 stages of 16
+                T(sk.PATH_MFMAW, 16, 32, 4, 3, 1),    # stages of 8 or 16 chunks only
+                T(sk.PATH_MFMAW, 16, 32, 4, 2, 9),    # 128 chunks: 8 stages of 16
+                T(sk.PATH_MFMAW, 16, 32, 4, 1, 17)):  # 16 stages of 8
         with pytest.raises(ValueError):
             sk.tactic_check(bad, 6288, 1024)
 
@@ -241,7 +243,8 @@ def test_bench_names_the_kernel_of_every_tactic():
             (t, name)
     assert bench.kernel_name(T(3, 32, 64, 4, 2, 2)) == "k_mfmax<2, 4, false>"
     assert bench.kernel_name(T(sk.PATH_DOT2R, 2, 4, 1, 2, 1)) == "k_dot2<2, 4, 2, false>"
-    assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2)) == "k_mfmaw<2, 4, 4, false>"
+    assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2)) == "k_mfmaw<2, 4, 4, 16, false>"
+    assert bench.kernel_name(T(sk.PATH_MFMAW, 16, 32, 2, 1, 1)) == "k_mfmaw<1, 2, 2, 8, false>"
 
 
 def test_shipped_table_is_legal_and_profiled():
