@@ -100,17 +100,48 @@ __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c)
 // workgroup ids round-robin over the XCDs; with `remap`, ids are renumbered
 // so that consecutive logical indices -- the `split` workgroups of one row
 // tile -- sit on the same XCD (a bijection of [0, gridDim.x)).
+// A value the caller knows is the same in every lane, made provably so.  The
+// row counts in the kernels come from HIP's min/max, whose results this compiler treats
+// as divergent; a buffer resource built from a "divergent" size is then
+// re-materialised lane by lane around every load.
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// x / d for the divisor whose FastDiv the host made (values shared by every
+// lane: scalar multiply-high, add and shifts)
+__device__ __forceinline__ unsigned fdiv(unsigned x, const FastDiv &f)
+{
+    const unsigned t = __umulhi(x, f.mul);
+    return (t + ((x - t) >> f.s1)) >> f.s2;
+}
+
 __device__ __forceinline__ void block_coords(const KArgs &a, int &tile, int &s)
 {
-    int idx = blockIdx.x;
+    unsigned idx = blockIdx.x;
     if (a.remap) {
-        const int g = gridDim.x, nx = a.nxcd;
-        const int xcd = idx % nx, j = idx / nx;
-        const int q = g / nx, r = g % nx;
-        idx = xcd * q + (xcd < r ? xcd : r) + j;
+        // gridDim.x = grid_q nxcd + grid_r: XCD x holds grid_q (+ 1 if x < grid_r) ids
+        const unsigned j = fdiv(idx, a.fd_nxcd), xcd = idx - j * (unsigned)a.nxcd;
+        idx = xcd * (unsigned)a.grid_q + (xcd < (unsigned)a.grid_r ? xcd : (unsigned)a.grid_r) + j;
     }
-    tile = idx / a.split;
-    s = idx - tile * a.split;
+    const unsigned t = fdiv(idx, a.fd_split);
+    tile = (int)t;
+    s = (int)(idx - t * (unsigned)a.split);
+}
+
+// First row of equal row range t, floor(t N / n_tiles), t <= n_tiles.  With
+// N = rows_q n_tiles + rows_r it is t rows_q + floor(t rows_r / n_tiles), in
+// 32 bits while n_tiles < 2^16; otherwise the plain 64-bit form.
+__device__ __forceinline__ int tile_row(const KArgs &a, int t)
+{
+    if (a.rows_fast)
+        return uniform_int((int)((unsigned)t * a.rows_q + fdiv((unsigned)t * a.rows_r, a.fd_tiles)));
+    return uniform_int((int)(((unsigned long long)(unsigned)t * (unsigned)a.N) / (unsigned)a.n_tiles));
+}
+
+// First unit of K part s of `split` over `total` units, floor(s total /
+// split), s <= split <= 16: s total < 2^32 because K / 8 < 2^28.
+__device__ __forceinline__ int split_point(const KArgs &a, int s, int total)
+{
+    return (int)fdiv((unsigned)s * (unsigned)total, a.fd_split);
 }
 
 // out[m][n] = v (+ res[m][n], added in fp32 before the one rounding to BF16)
@@ -339,11 +370,6 @@ __device__ __forceinline__ void split_reset(const KArgs &a, int tile)
 constexpr unsigned kOffOob = 0x7FFFFFF0u;
 constexpr int kCpolNt = 2;   // nontemporal
 
-// A value the caller knows is the same in every lane, made provably so.  The
-// row counts below come from HIP's min/max, whose results this compiler treats
-// as divergent; a buffer resource built from a "divergent" size is then
-// re-materialised lane by lane around every load.
-__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // A per-lane offset that is either a real offset or kOffOob.  Passing it
 // through an empty asm keeps it a plain select: otherwise this compiler may
@@ -395,13 +421,10 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
     block_coords(a, tile, s);
     // row tile: R aligned rows, or (ranges) the equal range
     // [tile N / n_tiles, (tile + 1) N / n_tiles) of at most R rows
-    const auto range_row = [&](int t) {
-        return uniform_int((int)(((unsigned long long)(unsigned)t * (unsigned)a.N) / (unsigned)a.n_tiles));
-    };
-    const int n0 = a.ranges ? range_row(tile) : tile * R;
-    const int n_end = a.ranges ? range_row(tile + 1) : a.N;
-    const int kb = (int)(((long)s * a.K8) / a.split);
-    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int n0 = a.ranges ? tile_row(a, tile) : tile * R;
+    const int n_end = a.ranges ? tile_row(a, tile + 1) : a.N;
+    const int kb = split_point(a, s, a.K8);
+    const int ke = split_point(a, s + 1, a.K8);
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(max(0, min(R, n_end - n0)));
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)n0 * row_bytes,
@@ -555,8 +578,8 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
 
     const int steps_full = a.K8 >> 2;              // steps with all 4 chunks in range
     const int steps = (a.K8 + 3) >> 2;
-    const int sb = (int)(((long)s * steps) / a.split);
-    const int se = (int)(((long)(s + 1) * steps) / a.split);
+    const int sb = split_point(a, s, steps);
+    const int se = split_point(a, s + 1, steps);
     const int se_full = se < steps_full ? se : steps_full;
 
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
@@ -721,8 +744,8 @@ __global__ __launch_bounds__(512) void k_dot2x(KArgs a)
     block_coords(a, tile, s);
     const int n_wg = tile * nwaves * R;        // first row of the workgroup
     const int n0 = n_wg + wave * R;            // first row of this wave
-    const int kb = (int)(((long)s * a.K8) / a.split);
-    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int kb = split_point(a, s, a.K8);
+    const int ke = split_point(a, s + 1, a.K8);
     const int kr = ke - kb;
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(max(0, min(R, a.N - n0)));
@@ -920,14 +943,11 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
     block_coords(a, tile, s);
     // row tile: 16 NW aligned rows, or (ranges) the equal range
     // [tile N / n_tiles, (tile + 1) N / n_tiles) of at most 16 NW rows
-    const auto range_row = [&](int t) {
-        return uniform_int((int)(((unsigned long long)(unsigned)t * (unsigned)a.N) / (unsigned)a.n_tiles));
-    };
-    const int n_wg = a.ranges ? range_row(tile) : tile * NW * 16;
-    const int n_end = a.ranges ? range_row(tile + 1) : a.N;
+    const int n_wg = a.ranges ? tile_row(a, tile) : tile * NW * 16;
+    const int n_end = a.ranges ? tile_row(a, tile + 1) : a.N;
     const int n0 = n_wg + wave * 16;
-    const int kb = (int)(((long)s * a.K8) / a.split);
-    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int kb = split_point(a, s, a.K8);
+    const int ke = split_point(a, s + 1, a.K8);
     const int stages = (ke - kb + KW - 1) / KW;
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(max(0, min(16, n_end - n0)));
@@ -1151,8 +1171,8 @@ __global__ __launch_bounds__(512) void k_mfmad(KArgs a)
     block_coords(a, tile, s);
     const int n_wg = tile * NW * 16;
     const int n0 = n_wg + wave * 16;
-    const int kb = (int)(((long)s * a.K8) / a.split);
-    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int kb = split_point(a, s, a.K8);
+    const int ke = split_point(a, s + 1, a.K8);
     const int stages = (ke - kb + KW - 1) / KW;
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
     const int rows_valid = uniform_int(max(0, min(16, a.N - n0)));
@@ -1325,7 +1345,7 @@ __global__ __launch_bounds__(512) void k_mfmas(KArgs a)
     // tile t is the row range [t N / n_tiles, (t + 1) N / n_tiles), at most
     // 16 NW rows; wave w multiplies its rows 16 w .. 16 w + 15
     auto tile_row = [&](unsigned t) {
-        return uniform_int((int)(((unsigned long long)t * (unsigned)a.N) / (unsigned)a.n_tiles));
+        return skinny::tile_row(a, (int)t);
     };
 
     // loads: stage j of the range is unit u0 + j
@@ -1541,8 +1561,8 @@ __global__ __launch_bounds__(512) void k_mfmak(KArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rt = wave % RT, ks = wave / RT;
     const unsigned tile = blockIdx.x;
-    const int r0 = uniform_int((int)(((unsigned long long)tile * (unsigned)a.N) / (unsigned)a.n_tiles));
-    const int r1 = uniform_int((int)(((unsigned long long)(tile + 1) * (unsigned)a.N) / (unsigned)a.n_tiles));
+    const int r0 = tile_row(a, (int)tile);
+    const int r1 = tile_row(a, (int)tile + 1);
     const int n0 = r0 + 16 * rt;
     const int rows_valid = uniform_int(max(0, min(16, r1 - n0)));
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
@@ -1714,12 +1734,9 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int tile, s;
     block_coords(a, tile, s);
-    const auto range_row = [&](int t) {
-        return uniform_int((int)(((unsigned long long)(unsigned)t * (unsigned)a.N) / (unsigned)a.n_tiles));
-    };
-    const int n_wg = range_row(tile), n_end = range_row(tile + 1);
-    const int kb = (int)(((long)s * a.K8) / a.split);
-    const int ke = (int)(((long)(s + 1) * a.K8) / a.split);
+    const int n_wg = tile_row(a, tile), n_end = tile_row(a, tile + 1);
+    const int kb = split_point(a, s, a.K8);
+    const int ke = split_point(a, s + 1, a.K8);
     const int stages = (ke - kb + SC - 1) / SC;
     const int mine = stages > wave ? (stages - wave + NW - 1) / NW : 0;   // stages wave, wave + NW, ...
     const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;

@@ -33,6 +33,8 @@ struct Entry {
     const void *fn = nullptr;
     unsigned grid = 0, block = 0, lds = 0;
     int n_tiles = 0;
+    FastDiv fd_tiles{}, fd_split{};  // see KArgs
+    unsigned rows_q = 0, rows_r = 0;
     int sk_spt = 0, sk_parts = 0;   // stream-K: stages per tile, partial slots per tile
     skinny_tactic t{};
 };
@@ -149,6 +151,10 @@ Entry make_entry(const skinny_tactic &t, int N, int K, int half)
     en.block = (unsigned)(64 * t.waves);
     en.lds = (unsigned)tactic_lds_bytes(t, K / 8);
     en.t = t;
+    en.fd_tiles = make_fastdiv((uint32_t)en.n_tiles);
+    en.fd_split = make_fastdiv((uint32_t)t.split);
+    en.rows_q = (unsigned)(N / en.n_tiles);
+    en.rows_r = (unsigned)(N % en.n_tiles);
     if (t.path == SKINNY_PATH_MFMAS || t.path == SKINNY_PATH_MFMAR)
         stream_k_shape(en, K);
     return en;
@@ -225,6 +231,15 @@ hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
     a.sk_parts = en.sk_parts;
     a.ranges = (en.t.path == SKINNY_PATH_MFMAX && en.t.unroll == 2) || en.t.path == SKINNY_PATH_DOT2R ||
                en.t.path == SKINNY_PATH_MFMAW;
+    const int nx = a.nxcd > 1 ? a.nxcd : 1;
+    a.fd_tiles = en.fd_tiles;
+    a.fd_split = en.fd_split;
+    a.fd_nxcd = make_fastdiv((uint32_t)nx);
+    a.rows_q = en.rows_q;
+    a.rows_r = en.rows_r;
+    a.rows_fast = en.n_tiles < (1 << 16);
+    a.grid_q = (int)en.grid / nx;
+    a.grid_r = (int)en.grid % nx;
     void *params[] = {&a};
     return hipLaunchKernel(en.fn, dim3(en.grid), dim3(en.block), params, en.lds, stream);
 }

@@ -9,6 +9,37 @@
 
 namespace skinny {
 
+// Division of 32-bit unsigned values by a divisor fixed for a launch, as a
+// multiply-high, an add and two shifts (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994, section 4): with
+// t = (x * mul) >> 32,  x / d = (t + ((x - t) >> s1)) >> s2  for every 32-bit
+// x.  The kernels evaluate it on values every lane shares, where a general
+// 32- or 64-bit division is a long scalar instruction sequence that would
+// delay each workgroup's first load.
+struct FastDiv {
+    uint32_t mul;
+    uint32_t s1;
+    uint32_t s2;
+};
+
+// d >= 1.  d = 1: t = 0 and x / 1 = x.  Otherwise l = ceil(log2 d) >= 1,
+// mul = floor(2^32 (2^l - d) / d) + 1 < 2^32, s1 = 1, s2 = l - 1.
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    if (d <= 1)
+        return FastDiv{0u, 0u, 0u};
+    const uint32_t l = 32u - (uint32_t)__builtin_clz(d - 1u);
+    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, 1u, l - 1u};
+}
+
+// The same formula on the host, for tests.
+inline uint32_t fastdiv_eval(uint32_t x, const FastDiv &f)
+{
+    const uint32_t t = (uint32_t)(((uint64_t)x * f.mul) >> 32);
+    return (t + ((x - t) >> f.s1)) >> f.s2;
+}
+
 // Arguments of every kernel, passed by value.  W, x are viewed as rows of
 // 16-byte chunks (8 BF16 or FP16 values); K8 = K / 8 chunks per row, rows
 // w_pitch / x_pitch bytes apart.
@@ -36,6 +67,14 @@ struct KArgs {
     unsigned x_pitch;   // bytes between rows of x (multiple of 16)
     int ldo;            // elements between rows of out
     int ldr;            // elements between rows of res
+    // launch constants for divisions (see FastDiv): by n_tiles, split and
+    // nxcd; N = rows_q n_tiles + rows_r, so that with rows_fast (n_tiles <
+    // 2^16) t N / n_tiles = t rows_q + (t rows_r) / n_tiles in 32 bits; and
+    // gridDim.x = grid_q nxcd + grid_r
+    FastDiv fd_tiles, fd_split, fd_nxcd;
+    unsigned rows_q, rows_r;
+    int rows_fast;
+    int grid_q, grid_r;
 };
 
 // A compiled kernel instance.

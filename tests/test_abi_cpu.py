@@ -275,3 +275,15 @@ def test_shipped_table_is_legal_and_profiled():
     for m in bench.M_SWEEP:
         name = bench.kernel_name(T(*map(int, head[8 + m - 1].split("."))))
         assert name in rec["kernels"], (m, name)
+
+
+def test_launch_constant_division_is_exact(tmp_path):
+    """The kernels divide by n_tiles, split and the XCD count through
+    host-made multipliers (Granlund-Montgomery); the host form of the same
+    formula equals plain unsigned division on every divisor below 2^17 at
+    the quotient boundaries and extremes, and on random 32-bit pairs."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    exe = str(tmp_path / "fastdiv_check")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-o", exe, os.path.join(here, "fastdiv_check.cpp")], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.startswith("ok "), r.stdout + r.stderr
