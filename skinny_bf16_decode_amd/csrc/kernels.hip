@@ -438,7 +438,8 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
     for (int i = 0; i < V; ++i)
         acc[i] = 0.f;
 
-    const int passes = (ke - kb) / nthr;   // passes in which every lane has a chunk
+    // passes in which every lane has a chunk; nthr = 64 waves is a power of two
+    const int passes = (ke - kb) >> __builtin_ctz((unsigned)nthr);
     const int stages = passes / U;
 
     u32x4 wa[U][R], xa[U][MT], wb[U][R], xb[U][MT];
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
 
     // this wave's steps: sb + wave + nwaves * q, q = 0 .. qn - 1 (all full)
     const int first = sb + wave;
-    const int qn = first < se_full ? (se_full - first + nwaves - 1) / nwaves : 0;
+    const int qn = first < se_full ? (se_full - first + nwaves - 1) >> __builtin_ctz((unsigned)nwaves) : 0;
     const int stages = qn / U;
 
     u32x4 aa[U][RT], ba[U][T], ab[U][RT], bb[U][T];
