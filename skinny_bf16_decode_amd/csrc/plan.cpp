@@ -439,19 +439,27 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     skinny_status s = skinny_select_table(cand.data(), times.data(), count, table.data());
 
     // Second pass: for each M, the few fastest candidates of the first pass
-    // whose tile serves M are timed again at M itself (x and out of M rows),
-    // round-robin over three rounds, and the fastest is kept.  First-pass
-    // times at the full tile overstate a large tile at small M, and single
-    // timings differ by a few per cent from run to run.
+    // whose tile serves M, and the two fastest of every token tile >= M, are
+    // timed again at M itself (x and out of M rows), round-robin over three
+    // rounds, and the fastest is kept.  First-pass times at the full tile
+    // overstate a large tile at small M -- the best 16-token kernel at M = 4
+    // need not be among the fastest at M = 16 -- and single timings differ by
+    // a few per cent from run to run.
     const int refine = env_int("SKINNY_TUNE_REFINE", 4);
     for (int m = 1; s == SKINNY_OK && refine > 1 && m <= SKINNY_MAX_M; ++m) {
-        std::vector<int> top;
+        std::vector<int> order;
         for (int i = 0; i < count; ++i)
             if (times[i] >= 0 && cand[i].mt >= m)
+                order.push_back(i);
+        std::sort(order.begin(), order.end(), [&](int x, int y) { return times[x] < times[y]; });
+        std::vector<int> top;
+        std::map<int, int> per_tile;
+        for (size_t k = 0; k < order.size(); ++k) {
+            const int i = order[k];
+            if ((int)k < refine || per_tile[cand[i].mt] < 2)
                 top.push_back(i);
-        std::sort(top.begin(), top.end(), [&](int x, int y) { return times[x] < times[y]; });
-        if ((int)top.size() > refine)
-            top.resize(refine);
+            ++per_tile[cand[i].mt];
+        }
         if (top.size() < 2)
             continue;
         std::vector<double> best(top.size(), -1.0);
