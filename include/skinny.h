@@ -135,9 +135,9 @@ typedef struct {
  * Validates the arguments, then looks up the process-wide tactic table for
  * (device, N, K, out_dtype); on a miss it times every legal tactic on the
  * device with cache-cold weight copies at its full token tile, then times the
- * few fastest whose tile is >= M again at M itself (SKINNY_TUNE_REFINE of
- * them, default 4; 0 or 1 skips this pass) and keeps, for each M in 1..64,
- * the fastest.  Every tactic the table uses is
+ * few fastest whose tile is >= M (SKINNY_TUNE_REFINE of them, default 4; 0 or
+ * 1 skips this pass), and the two fastest of every tile >= M, again at M
+ * itself and keeps, for each M in 1..64, the fastest.  Every tactic the table uses is
  * launched once (warm-up) so that nothing loads lazily under graph capture.
  * The split-K workspace and arrival counters are allocated here.
  *
