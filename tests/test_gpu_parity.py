@@ -446,3 +446,22 @@ def test_stream_k_repeats_and_graph_replays(sk):
                 assert np.array_equal(gu.host_bits(outs[m]), ref[m]), (t, rep, m)
         del g
         plan.close()
+
+
+@pytest.mark.parametrize("n", [65535, 70001])
+def test_row_ranges_around_2_16_tiles(sk, n):
+    """Equal row ranges of one row each: 65535 ranges take the kernels' 32-bit
+    row-range arithmetic, 70001 its 64-bit form.  DOT2R with and without a
+    two-way K split (XCD remap and one arrival counter per range), exact on
+    integer inputs."""
+    import torch
+    k = 64
+    x_bits, w_bits = si.small_int_case(7000 + n, 64, n, k)
+    o, _ = oracle.gemm(x_bits, w_bits)
+    w = gu.dev_bf16(w_bits)
+    for t in (sk.Tactic(sk.PATH_DOT2R, 1, 1, 1, 1, 1), sk.Tactic(sk.PATH_DOT2R, 2, 1, 1, 1, 2)):
+        _say(f"[ranges {n}] {t}")
+        plan = sk.Prepared(w, torch.float32, table=gu.forced_table(t))
+        for m in sorted({1, t.mt}):
+            _check_exact(sk, plan, x_bits, o, m, f"{t} N={n} M={m}")
+        plan.close()
