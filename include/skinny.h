@@ -137,7 +137,9 @@ typedef struct {
  * device with cache-cold weight copies at its full token tile, then times the
  * few fastest whose tile is >= M (SKINNY_TUNE_REFINE of them, default 4; 0 or
  * 1 skips this pass), and the two fastest of every tile >= M, again at M
- * itself and keeps, for each M in 1..64, the fastest.  Every tactic the table uses is
+ * itself and keeps, for each M in 1..64, the fastest; then every tactic the
+ * table uses is timed again at each M its tile serves, and the fastest kept.
+ * Every tactic the table uses is
  * launched once (warm-up) so that nothing loads lazily under graph capture.
  * The split-K workspace and arrival counters are allocated here.
  *

@@ -446,6 +446,28 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     // need not be among the fastest at M = 16 -- and single timings differ by
     // a few per cent from run to run.
     const int refine = env_int("SKINNY_TUNE_REFINE", 4);
+    // The fastest of candidates `top` at M = m, each timed three times
+    // round-robin (best of three); -1 if none ran.
+    auto fastest_at = [&](int m, const std::vector<int> &top, int &pick) -> hipError_t {
+        std::vector<double> best(top.size(), -1.0);
+        a.M = m;
+        for (int round = 0; round < 3; ++round)
+            for (size_t c = 0; c < top.size(); ++c) {
+                double us;
+                hipError_t e = time_once(entries[top[c]], us);
+                if (e != hipSuccess)
+                    return e;
+                if (us >= 0 && (best[c] < 0 || us < best[c]))
+                    best[c] = us;
+            }
+        pick = -1;
+        for (size_t c = 0; c < top.size(); ++c)
+            if (best[c] >= 0 && (pick < 0 || best[c] < best[(size_t)pick]))
+                pick = (int)c;
+        pick = pick >= 0 ? top[(size_t)pick] : -1;
+        return hipSuccess;
+    };
+    std::vector<int> chosen(SKINNY_MAX_M, -1);   // candidate index of table[m - 1], once re-timed
     for (int m = 1; s == SKINNY_OK && refine > 1 && m <= SKINNY_MAX_M; ++m) {
         std::vector<int> order;
         for (int i = 0; i < count; ++i)
@@ -462,21 +484,36 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
         }
         if (top.size() < 2)
             continue;
-        std::vector<double> best(top.size(), -1.0);
-        a.M = m;
-        for (int round = 0; round < 3; ++round)
-            for (size_t c = 0; c < top.size(); ++c) {
-                double us;
-                HIP_TRY(time_once(entries[top[c]], us));
-                if (us >= 0 && (best[c] < 0 || us < best[c]))
-                    best[c] = us;
-            }
         int pick = -1;
-        for (size_t c = 0; c < top.size(); ++c)
-            if (best[c] >= 0 && (pick < 0 || best[c] < best[pick]))
-                pick = (int)c;
-        if (pick >= 0)
-            table[m - 1] = cand[top[pick]];
+        HIP_TRY(fastest_at(m, top, pick));
+        if (pick >= 0) {
+            table[m - 1] = cand[pick];
+            chosen[m - 1] = pick;
+        }
+    }
+    // Third pass: every kernel the table now uses for some M is timed again
+    // at each M its tile serves, and the fastest is kept.  The kernel that
+    // wins at M = 8 is often the fastest at M = 4 as well without being among
+    // the fastest candidates at its own full tile.
+    if (s == SKINNY_OK && refine > 1) {
+        std::vector<int> used;
+        for (int i : chosen)
+            if (i >= 0 && std::find(used.begin(), used.end(), i) == used.end())
+                used.push_back(i);
+        for (int m = 1; m <= SKINNY_MAX_M; ++m) {
+            if (chosen[m - 1] < 0)
+                continue;                          // its entry was not re-timed: keep it
+            std::vector<int> top;                  // includes chosen[m - 1]
+            for (int i : used)
+                if (cand[i].mt >= m)
+                    top.push_back(i);
+            if (top.size() < 2)
+                continue;
+            int pick = -1;
+            HIP_TRY(fastest_at(m, top, pick));
+            if (pick >= 0)
+                table[m - 1] = cand[pick];
+        }
     }
     if (env_int("SKINNY_LOG", 0) >= 2) {
         for (int i = 0; i < count; ++i)
