@@ -5,7 +5,8 @@
 
 Reads the kernel-trace statistics (``*_kernel_stats.csv``) and the per-dispatch
 counter collections of a FETCH_SIZE run and a WRITE_SIZE run (KiB per
-dispatch).  Counter values are scaled by the ratio of the known bytes of a
+dispatch), and optionally of a MfmaUtil run and an SQ_INSTS_VALU_MFMA_MOPS_BF16
+run (MFMA busy percent and MFMA operations per dispatch).  Counter values are scaled by the ratio of the known bytes of a
 calibration kernel to what the counter reports for it: ``k_probe_read``
 streams exactly 2*N*K bytes of one weight copy (FETCH_SIZE), and a 64 MiB
 device-to-device copy writes exactly 64 MiB (WRITE_SIZE).  Writes a short
@@ -82,6 +83,8 @@ def main():
     ap.add_argument("--weight-bytes", type=int, default=2 * 6288 * 7168)
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--title", default="skinny projection, 6288x7168 M sweep")
+    ap.add_argument("--mfma-util", help="counter collection of a --pmc MfmaUtil run")
+    ap.add_argument("--mfma-mops", help="counter collection of a --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 run")
     args = ap.parse_args()
     stats, kernels, fs, ws = summarize(args.trace_dir, args.fetch_csv, args.write_csv, args.weight_bytes)
     lines = [f"# {args.title}", "", "Commands (run from the repository root):", ""]
@@ -99,6 +102,17 @@ def main():
               "| kernel | dispatches | fetch KiB (scaled) | write KiB (scaled) |", "|---|---|---|---|"]
     for n, v in sorted(kernels.items()):
         lines.append(f"| `{n}` | {v['dispatches']} | {v['fetch_kib']:.1f} | {v['write_kib']:.1f} |")
+    if args.mfma_util and args.mfma_mops:
+        util, mops = load_counters(args.mfma_util), load_counters(args.mfma_mops)
+        lines += ["", "## MFMA use (rocprofv3 --pmc MfmaUtil, then --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
+                  "MfmaUtil = 100 x sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs); "
+                  "MFMA flops = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 (rows of a row group past N and "
+                  "token columns past M are multiplied too).", "",
+                  "| kernel | dispatches | MFMA busy % | MFMA flops per dispatch |", "|---|---|---|---|"]
+        for k in sorted(util, key=_short):
+            if "k_mfma" in k or "k_dot2" in k:
+                lines.append(f"| `{_short(k)}` | {len(util[k])} | {statistics.mean(util[k]):.2f} | "
+                             f"{statistics.mean(mops.get(k, [0.0])) * 512:.3e} |")
     os.makedirs(os.path.dirname(os.path.abspath(args.out_md)), exist_ok=True)
     with open(args.out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
