@@ -7,6 +7,7 @@ the stated bound |g - O| <= 1e-3 S + 1e-6 (+ 2^-8 |O| for BF16 output).
 """
 from __future__ import annotations
 
+import os
 import sys
 import time
 
@@ -277,23 +278,42 @@ DECODE_KERNEL_SETS = {
 }
 
 
-@pytest.mark.parametrize("kernels", sorted(DECODE_KERNEL_SETS))
+def shipped_decode_table(sk):
+    """The 64-entry table the benchmark loads for the packed 6288x7168 weight
+    (BF16 in and out), from the file shipped with the package."""
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "skinny_bf16_decode_amd", "tables", "mi355x_tuned.txt")
+    with open(path) as f:
+        for line in f:
+            p = line.split()
+            if p[4:8] == ["6288", "7168", "bf16", "bf16"]:
+                return [sk.Tactic(*map(int, e.split("."))) for e in p[8:]]
+    raise AssertionError("no shipped table for 6288x7168")
+
+
+@pytest.mark.parametrize("kernels", sorted(DECODE_KERNEL_SETS) + ["shipped"])
 def test_decode_kernels_repeat_and_graph_replay(sk, kernels):
     """The kernels of the packed 6288x7168 decode weight, forced, at full
     size: bitwise identical over repeats and over graph replays with eager
-    work between them, and within the bound on 4096 sampled outputs per M."""
+    work between them, and within the bound on 4096 sampled outputs per M.
+    "shipped" runs the benchmark's own table at the benchmark's token counts
+    (the launch configuration the benchmark times)."""
     import torch
     wl = si.WORKLOADS[3]
     w_bits, x_bits = si.weight(3, 0), si.activations(3)
     n = wl.n
     w = gu.dev_bf16(w_bits)
     x = gu.dev_bf16(x_bits)
-    forced = DECODE_KERNEL_SETS[kernels](sk)
+    if kernels == "shipped":
+        table = shipped_decode_table(sk)
+        forced = {m: table[m - 1] for m in (1, 2, 4, 8, 16, 32)}
+    else:
+        forced = DECODE_KERNEL_SETS[kernels](sk)
+        table = []
+        for m in range(1, 65):
+            fits = [t for mm, t in sorted(forced.items()) if mm >= m]
+            table.append(fits[0] if fits else sk.Tactic(3, 64, 128, 8, 1, 4))
     _say(f"[decode kernels {kernels}] {forced}")
-    table = []
-    for m in range(1, 65):
-        fits = [t for mm, t in sorted(forced.items()) if mm >= m]
-        table.append(fits[0] if fits else sk.Tactic(3, 64, 128, 8, 1, 4))
     plan = sk.Prepared(w, torch.bfloat16, table=table)
     for m, t in forced.items():
         assert plan.tactic(m) == t, (m, plan.tactic(m))
