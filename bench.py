@@ -371,6 +371,7 @@ def main():
         calibration_kernels(setup, stream)
     if args.extra:
         extra_workloads(stream)
+        oracle_small_workloads()
 
     cpu = None
     if not args.no_cpu:
@@ -488,6 +489,33 @@ def extra_workloads(stream):
         del s
         import torch
         torch.cuda.empty_cache()
+
+
+def oracle_small_workloads():
+    """The CPU oracle on the tiny and short-K workloads at each timed M, with
+    all of the host's threads and with one (min of 3 runs after 5 untimed
+    ones): baselines only, printed next to the GPU lines."""
+    import oracle
+    import skinny_inputs as si
+    all_threads = oracle.threads()
+    for cid in (1, 4):
+        wl = si.WORKLOADS[cid]
+        w_bits, x_bits = si.weight(cid), si.activations(cid)
+        for m in wl.m_values:
+            res = []
+            for t in (all_threads, 1):
+                oracle.set_threads(t)
+                for _ in range(5):             # untimed: the first calls after a team change start threads
+                    oracle.gemm(x_bits[:m], w_bits)
+                best = None
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    oracle.gemm(x_bits[:m], w_bits)
+                    dt = time.perf_counter() - t0
+                    best = dt if best is None else min(best, dt)
+                res.append(f"{t} thread(s) {best * 1e3:8.3f} ms/call {wl.weight_bytes / best / 1e9:7.3f} GB/s")
+            log(f"[oracle {wl.name}] M={m:2d}: " + ", ".join(res))
+    oracle.set_threads(all_threads)
 
 
 if __name__ == "__main__":

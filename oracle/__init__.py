@@ -78,6 +78,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_decode_bf16.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
     return lib
 
 
@@ -183,6 +185,11 @@ def decode_f16(bits, lib=None) -> np.ndarray:
 
 def threads(lib=None) -> int:
     return (lib or _get()).oracle_threads()
+
+
+def set_threads(n: int, lib=None) -> None:
+    """Threads the oracle's later calls use (timing only; results do not depend on it)."""
+    (lib or _get()).oracle_set_threads(int(n))
 
 
 # ----------------------------------------------------------------------------

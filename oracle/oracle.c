@@ -232,6 +232,19 @@ void oracle_decode_f16(const uint16_t *bits, long count, double *out)
         out[i] = f16_to_double(bits[i]);
 }
 
+/* Threads later parallel regions use (n >= 1), for timing the oracle on one
+ * core next to all of them; without OpenMP there is only one. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads an OpenMP parallel region uses here (for reporting). */
 int oracle_threads(void)
 {

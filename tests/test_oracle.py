@@ -166,3 +166,20 @@ def test_generator_fingerprints_match_golden():
     for cid in (1, 4):
         assert si.fingerprint(si.weight(cid)) == golden[str(cid)]["weight0"]
         assert si.fingerprint(si.activations(cid)) == golden[str(cid)]["x"]
+
+
+def test_thread_count_changes_nothing_but_speed():
+    """set_threads only changes how many threads later calls use: the
+    product and the magnitude sums are identical with one thread and with
+    all of them."""
+    all_threads = oracle.threads()
+    w_bits, x_bits = si.weight(4), si.activations(4)
+    try:
+        oracle.set_threads(1)
+        assert oracle.threads() == 1
+        o1, s1 = oracle.gemm(x_bits[:8], w_bits)
+    finally:
+        oracle.set_threads(all_threads)
+    assert oracle.threads() == all_threads
+    o, s = oracle.gemm(x_bits[:8], w_bits)
+    assert np.array_equal(o, o1) and np.array_equal(s, s1)
