@@ -221,8 +221,9 @@ def test_long_k_split_workload_sampled(sk):
 
 
 def test_deterministic_and_graph_replay(sk):
-    """Bitwise-identical results across repeated runs and across replays of a
-    captured graph (split-K counters must return to zero after every call)."""
+    """Bitwise-identical results across repeated runs and across 100 replays
+    of a captured graph (split-K counters must return to zero after every
+    call)."""
     import torch
     n, k = 1024, 4096
     x_bits, w_bits = si.random_case(77, 64, n, k)
@@ -255,7 +256,7 @@ def test_deterministic_and_graph_replay(sk):
         with torch.cuda.graph(g, stream=stream):
             for m in ref:
                 plan.run(x[:m], outs[m][:m])
-    for rep in range(10):
+    for rep in range(100):
         for m in ref:
             outs[m][:m].fill_(0)          # eager work between replays
         torch.cuda.synchronize()
