@@ -27,7 +27,11 @@ tables; it is loaded through a temporary copy of that file.  A GPU with
 another CU count finds no matching line and is tuned on the spot, and so is
 every run with --retune.  SKINNY_TABLE_CACHE, when set, takes precedence.
 
-  python bench.py [--steps K] [--warmup W] [--extra] [--no-cpu] [--retune]
+  python bench.py [--steps K] [--warmup W] [--extra] [--no-cpu] [--retune] [--workload 2|3|5]
+
+--workload times the M sweep of another decode weight instead (2: the square
+[3584, 7168], 5: the long-K [7168, 18432]), with its own metric line and
+counter record; 3, the packed [6288, 7168], is the headline.
 """
 from __future__ import annotations
 
@@ -180,6 +184,11 @@ def cpu_baseline(setup):
                       f"{step_s:.2f} s per step"}
 
 
+def traffic_record_path(wl):
+    """The committed HBM traffic record of a workload's M sweep."""
+    return os.path.join(ROOT, "profiles", f"skinny_projection_{wl.name}_msweep.traffic.json")
+
+
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "skinny_projection_packed_qkvg_6288x7168_msweep.traffic.json")
 
 
@@ -215,9 +224,10 @@ def counted_traffic(setup):
     kernel the step uses; otherwise None."""
     import json as _json
     from skinny_bf16_decode_amd import profiling
-    if not os.path.exists(TRAFFIC_RECORD):
+    record = traffic_record_path(setup.wl)
+    if not os.path.exists(record):
         return None
-    with open(TRAFFIC_RECORD) as f:
+    with open(record) as f:
         rec = _json.load(f)
     if rec.get("kernel_source_sha256") != profiling.kernel_source_sha():
         return None
@@ -242,9 +252,9 @@ def parity_of_last(setup, last_copy, m, samples=4096):
     return rep
 
 
-def use_tables(retune, cus):
+def use_tables(retune, cus, wl):
     """Point SKINNY_TABLE_CACHE at a temporary copy of the shipped tables
-    (unless the caller set it, or asked to retune); say where the headline
+    (unless the caller set it, or asked to retune); say where the timed
     shape's table comes from."""
     if os.environ.get("SKINNY_TABLE_CACHE"):
         return f"SKINNY_TABLE_CACHE={os.environ['SKINNY_TABLE_CACHE']}"
@@ -255,7 +265,7 @@ def use_tables(retune, cus):
     shutil.copyfile(SHIPPED_TABLES, path)
     os.environ["SKINNY_TABLE_CACHE"] = path
     with open(SHIPPED_TABLES) as f:
-        key = ["skinny-table", "v2", "gfx950", str(cus), "6288", "7168", "bf16", "bf16"]
+        key = ["skinny-table", "v2", "gfx950", str(cus), str(wl.n), str(wl.k), "bf16", "bf16"]
         if any(line.split()[:8] == key for line in f):
             return f"shipped ({os.path.relpath(SHIPPED_TABLES, ROOT)}, {cus} CUs)"
     return f"tuned on this GPU (no shipped table for {cus} CUs)"
@@ -274,6 +284,8 @@ def main():
                          "whose known byte counts scale the HBM traffic counters")
     ap.add_argument("--retune", action="store_true",
                     help="tune the tactic tables on this GPU instead of loading the shipped ones")
+    ap.add_argument("--workload", type=int, default=WORKLOAD, choices=(2, 3, 5),
+                    help="the decode weight whose M sweep is timed (3, the packed 6288x7168, is the headline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -290,10 +302,13 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count} "
         f"torch={torch.__version__} hip={torch.version.hip}")
-    table_source = use_tables(args.retune, props.multi_processor_count)
+    import skinny_inputs as si
+    global M_SWEEP
+    M_SWEEP = tuple(si.WORKLOADS[args.workload].m_values)
+    table_source = use_tables(args.retune, props.multi_processor_count, si.WORKLOADS[args.workload])
     log(f"tactic table: {table_source}")
 
-    setup = Setup(WORKLOAD)
+    setup = Setup(args.workload)
     wl = setup.wl
     log(f"workload {wl.name}: prepare {setup.prepare_s:.2f}s")
     for m in M_SWEEP:
@@ -383,7 +398,9 @@ def main():
         traffic = round(traffic)
         log(f"counted HBM traffic per launch: {traffic} B (algorithmic {round(algo_per_launch)} B)")
     line = {
-        "metric": "µs/call and weight-stream HBM GB/s (% of peak), 6288x7168 at M=1..32",
+        "metric": ("µs/call and weight-stream HBM GB/s (% of peak), 6288x7168 at M=1..32"
+                   if args.workload == WORKLOAD else
+                   f"µs/call and weight-stream HBM GB/s (% of peak), {wl.n}x{wl.k} at M={M_SWEEP[0]}..{M_SWEEP[-1]}"),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -248,11 +248,11 @@ def test_bench_names_the_kernel_of_every_tactic():
 
 
 def test_shipped_table_is_legal_and_profiled():
-    """The tactic table bench.py loads by default: one line per (chip, shape),
-    every entry legal for its shape with a token tile >= M (the library
-    ignores a line that fails this, and tunes instead), and the committed
-    HBM traffic record names the kernel of every token count the benchmark
-    step runs."""
+    """The tactic tables bench.py loads by default: one line per (chip,
+    shape), every entry legal for its shape with a token tile >= M (the
+    library ignores a line that fails this, and tunes instead), and the
+    shape's committed HBM traffic record names the kernel of every token
+    count its benchmark step runs."""
     import json
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     import bench
@@ -269,12 +269,15 @@ def test_shipped_table_is_legal_and_profiled():
             sk.tactic_check(t, n, k)
             assert t.mt >= m
     assert len(heads) == len(lines)
-    head = next(ln for ln in lines if ln[4:8] == ["6288", "7168", "bf16", "bf16"])
-    with open(bench.TRAFFIC_RECORD) as f:
-        rec = json.load(f)
-    for m in bench.M_SWEEP:
-        name = bench.kernel_name(T(*map(int, head[8 + m - 1].split("."))))
-        assert name in rec["kernels"], (m, name)
+    assert any(ln[4:8] == ["6288", "7168", "bf16", "bf16"] for ln in lines)
+    import skinny_inputs as si
+    for ln in lines:
+        wl = next(w for w in si.WORKLOADS.values() if [str(w.n), str(w.k)] == ln[4:6])
+        with open(bench.traffic_record_path(wl)) as f:
+            rec = json.load(f)
+        for m in wl.m_values:
+            name = bench.kernel_name(T(*map(int, ln[8 + m - 1].split("."))))
+            assert name in rec["kernels"], (wl.name, m, name)
 
 
 def test_launch_constant_division_is_exact(tmp_path):
