@@ -51,7 +51,7 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0
 SHIPPED_TABLES = os.path.join(ROOT, "skinny_bf16_decode_amd", "tables", "mi355x_tuned.txt")
 WORKLOAD = 3
-M_SWEEP = (1, 2, 4, 8, 16, 32)
+M_SWEEP = (1, 2, 4, 8, 16, 32)   # the headline step (packed 6288x7168)
 STEPS_PER_GRAPH = 16
 
 
@@ -163,23 +163,24 @@ def empty_floor(stream, reps=20):
 
 
 def cpu_baseline(setup):
-    """The oracle on one step of the workload (the six token counts on one
+    """The oracle on one step of the workload (its timed token counts on one
     weight copy), repeated until about 10 s of CPU time (at least 3 steps);
     GB/s of weight processed."""
+    sweep = tuple(setup.wl.m_values)
     import oracle
     x = setup.x_bits
     w = setup.w_bits[0]
     reps, t_total = 0, 0.0
     while reps < 3 or (t_total < 10.0 and reps < 1000):
         t0 = time.perf_counter()
-        for m in M_SWEEP:
+        for m in sweep:
             oracle.gemm(x[:m], w)
         t_total += time.perf_counter() - t0
         reps += 1
     step_s = t_total / reps
-    gbps = len(M_SWEEP) * setup.wl.weight_bytes / step_s / 1e9
+    gbps = len(sweep) * setup.wl.weight_bytes / step_s / 1e9
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"one full step ({len(M_SWEEP)} calls, M={list(M_SWEEP)}, one "
+            "sample": f"one full step ({len(sweep)} calls, M={list(sweep)}, one "
                       f"[{setup.wl.n},{setup.wl.k}] weight copy), {reps} rep(s), "
                       f"{step_s:.2f} s per step"}
 
@@ -222,6 +223,7 @@ def counted_traffic(setup):
     """HBM bytes per launch over the step, from the committed rocprofv3 counter
     record -- only if it was taken on this exact kernel source and covers every
     kernel the step uses; otherwise None."""
+    sweep = tuple(setup.wl.m_values)
     import json as _json
     from skinny_bf16_decode_amd import profiling
     record = traffic_record_path(setup.wl)
@@ -232,13 +234,13 @@ def counted_traffic(setup):
     if rec.get("kernel_source_sha256") != profiling.kernel_source_sha():
         return None
     total = 0.0
-    for m in M_SWEEP:
+    for m in sweep:
         name = kernel_name(setup.plans[0].tactic(m))
         k = rec["kernels"].get(name) if name else None
         if k is None:
             return None
         total += (k["fetch_kib"] + k["write_kib"]) * 1024.0
-    return total / len(M_SWEEP)
+    return total / len(sweep)
 
 
 def parity_of_last(setup, last_copy, m, samples=4096):
@@ -303,15 +305,14 @@ def main():
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count} "
         f"torch={torch.__version__} hip={torch.version.hip}")
     import skinny_inputs as si
-    global M_SWEEP
-    M_SWEEP = tuple(si.WORKLOADS[args.workload].m_values)
+    sweep = tuple(si.WORKLOADS[args.workload].m_values)
     table_source = use_tables(args.retune, props.multi_processor_count, si.WORKLOADS[args.workload])
     log(f"tactic table: {table_source}")
 
     setup = Setup(args.workload)
     wl = setup.wl
     log(f"workload {wl.name}: prepare {setup.prepare_s:.2f}s")
-    for m in M_SWEEP:
+    for m in sweep:
         log(f"  M={m:2d}: {setup.plans[0].describe(m)}")
     stream = torch.cuda.Stream()
 
@@ -320,13 +321,13 @@ def main():
     # forward pass holds many projections in one graph, so the time between
     # graph launches is spread over 16 steps rather than paid by every step.
     # Each step is the same six calls either way; K steps are exactly K steps.
-    calls = len(M_SWEEP)
+    calls = len(sweep)
     offsets = sorted({(calls * s) % setup.copies for s in range(setup.copies)})
     graphs, big = {}, {}
     for off in offsets:
-        graphs[off] = capture(lambda off=off: [setup.run(off + j, m) for j, m in enumerate(M_SWEEP)],
+        graphs[off] = capture(lambda off=off: [setup.run(off + j, m) for j, m in enumerate(sweep)],
                               stream)
-        big[off] = capture(lambda off=off: [setup.run(off + j, M_SWEEP[j % calls])
+        big[off] = capture(lambda off=off: [setup.run(off + j, sweep[j % calls])
                                             for j in range(calls * STEPS_PER_GRAPH)], stream)
 
     def replay_steps(first, count):
@@ -357,21 +358,21 @@ def main():
     value = weight_bytes_step * args.steps / elapsed / 1e9
     launches = calls * args.steps
     us_per_launch = 1e6 * elapsed / launches
-    algo_per_launch = sum(algorithmic_bytes(wl.n, wl.k, m) for m in M_SWEEP) / calls
+    algo_per_launch = sum(algorithmic_bytes(wl.n, wl.k, m) for m in sweep) / calls
     achieved = algo_per_launch / us_per_launch / 1e3
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {us_per_launch:.2f} us/call, "
         f"{value:.1f} GB/s weight stream ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s); host wall {wall:.3f}s")
 
     # the last call of the last step
     last_copy = (calls * (args.warmup + args.steps) - 1) % setup.copies
-    rep = parity_of_last(setup, last_copy, M_SWEEP[-1])
-    log(f"parity of the last call (M={M_SWEEP[-1]}, copy {last_copy}): {rep}")
+    rep = parity_of_last(setup, last_copy, sweep[-1])
+    log(f"parity of the last call (M={sweep[-1]}, copy {last_copy}): {rep}")
     if not rep.ok:
         print(f"parity failure: {rep}", file=sys.stderr)
         sys.exit(3)
 
     per_m = {}
-    for m in M_SWEEP:
+    for m in sweep:
         us = setup.per_m(stream, m, reps=args.per_m_reps)
         gb = wl.weight_bytes / us / 1e3
         per_m[str(m)] = {"us_per_call": round(us, 3), "weight_gbps": round(gb, 1),
@@ -400,7 +401,7 @@ def main():
     line = {
         "metric": ("µs/call and weight-stream HBM GB/s (% of peak), 6288x7168 at M=1..32"
                    if args.workload == WORKLOAD else
-                   f"µs/call and weight-stream HBM GB/s (% of peak), {wl.n}x{wl.k} at M={M_SWEEP[0]}..{M_SWEEP[-1]}"),
+                   f"µs/call and weight-stream HBM GB/s (% of peak), {wl.n}x{wl.k} at M={sweep[0]}..{sweep[-1]}"),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -413,9 +414,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: out[M,N] = x[M,K] @ W[N,K]^T, N={wl.n}, K={wl.k}, "
-                               f"one step = M in {list(M_SWEEP)}, BF16 in/out, fp32 accumulate, "
+                               f"one step = M in {list(sweep)}, BF16 in/out, fp32 accumulate, "
                                f"{setup.copies} rotated weight copies, hipGraph replay",
-                   "N": wl.n, "K": wl.k, "m_values": list(M_SWEEP), "weight_copies": setup.copies},
+                   "N": wl.n, "K": wl.k, "m_values": list(sweep), "weight_copies": setup.copies},
         "us_per_call": round(us_per_launch, 3),
         "pct_of_peak": round(100 * value / PEAK_GBPS, 1),
         "per_m": per_m,
