@@ -201,19 +201,14 @@ def kernel_name(t):
         name = "k_dot2"
     elif t.path == 1:                        # MFMA
         args, name = (T, t.rows // 16, t.unroll), "k_mfma"
-    elif t.path == 2:                        # DOT2X: rows per wave
-        args, name = (t.mt, t.rows // w, t.unroll), "k_dot2x"
     elif t.path == 3:                        # MFMAX: unroll picks the grid, not the kernel
         args, name = (T, w), "k_mfmax"
-    elif t.path == 4:                        # MFMAD
-        args, name = (T, w, t.unroll), "k_mfmad"
-    elif t.path in (5, 6):                   # MFMAS, MFMAR
-        args, name = (T, w, t.unroll), "k_mfmas"
-    elif t.path == 7:                        # MFMAK: row groups and K groups
-        rt = t.rows // 16
-        args, name = (T, rt, w // rt, t.unroll), "k_mfmak"
     elif t.path == 9:                        # MFMAW: row groups, waves, stage chunks
         args, name = (T, t.rows // 16, w, 8 * t.unroll), "k_mfmaw"
+    elif t.path == 10:                       # MFMA4: token groups and row groups of 4, stages in flight
+        args, name = ("true", t.mt // 4, t.rows // 4, t.unroll), "k_rgs"
+    elif t.path == 11:                       # DOT2W: tokens, row groups of 4, stages in flight
+        args, name = ("false", t.mt, t.rows // 4, t.unroll), "k_rgs"
     else:
         return None
     return f"{name}<{', '.join(str(a) for a in args)}, false>"

@@ -72,31 +72,34 @@ typedef enum {
 typedef enum {
     SKINNY_PATH_DOT2 = 0,  /* v_dot2_f32_bf16, token tiles 1/2/4/8; waves split K */
     SKINNY_PATH_MFMA = 1,  /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; waves split K */
-    SKINNY_PATH_DOT2X = 2, /* v_dot2_f32_bf16, tiles 1/2/4/8; waves own rows, x staged in LDS */
+    SKINNY_PATH_DOT2X = 2, /* retired (never the fastest on any measured shape); reserved */
     SKINNY_PATH_MFMAX = 3, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
                               W re-laid out and x staged through LDS via registers;
                               unroll = 2: equal row ranges (a whole multiple of CUs / split
                               of them) instead of aligned 16 * waves row tiles */
-    SKINNY_PATH_MFMAD = 4, /* v_mfma_f32_16x16x32_bf16, tiles 16/32/64; 16 rows per wave,
-                              W and x streamed straight into LDS rings (direct-to-LDS loads) */
-    SKINNY_PATH_MFMAS = 5, /* MFMAX's register-to-LDS pipeline under a stream-K schedule: one
-                              workgroup per slot the chip holds at once, each taking an equal
-                              share of (row tile, K stage) units */
-    SKINNY_PATH_MFMAR = 6, /* the MFMAS kernel on a data-parallel grid: one workgroup per
-                              (row range, K split), with at least CUs / split equal row
-                              ranges of at most 16 * waves rows; split = 1: no exchange */
-    SKINNY_PATH_MFMAK = 7, /* tiles 16/32: one workgroup per equal row range (at least
-                              split x CUs ranges of at most `rows` rows) over all of K;
-                              waves = rows / 16 row groups x K groups, whose partial sums
-                              are added in LDS: no exchange between workgroups */
+    SKINNY_PATH_MFMAD = 4, /* retired (direct-to-LDS rings; slower than MFMAX/MFMAW); reserved */
+    SKINNY_PATH_MFMAS = 5, /* retired (stream-K grid; slower than equal row ranges); reserved */
+    SKINNY_PATH_MFMAR = 6, /* retired (the stream-K kernel on a data-parallel grid); reserved */
+    SKINNY_PATH_MFMAK = 7, /* retired (in-workgroup K groups; overtaken by MFMAX/MFMAW); reserved */
     SKINNY_PATH_DOT2R = 8, /* the DOT2 kernels over equal row ranges of at most `rows` rows,
                               a whole multiple of CUs / split of them, so that every CU gets
                               the same number of (range, K split) workgroups */
-    SKINNY_PATH_MFMAW = 9  /* tiles 16/32/64: equal row ranges of at most `rows` rows (a whole
+    SKINNY_PATH_MFMAW = 9, /* tiles 16/32/64: equal row ranges of at most `rows` rows (a whole
                               multiple of CUs / split of them); every wave multiplies all
                               rows / 16 row groups of the range over every waves-th K stage,
                               W and x re-laid out through the wave's own LDS tiles, with no
                               barrier until the waves' partial sums are added in LDS */
+    SKINNY_PATH_MFMA4 = 10,/* v_mfma_f32_4x4x4_16b_bf16, tiles 4/8/16/32: equal row ranges of at
+                              most `rows` rows (a whole multiple of CUs / split of them); each of
+                              the 16 blocks of the MFMA takes one 16-byte K chunk, so a plain
+                              row-contiguous load of 4 rows (tokens) x 256 bytes becomes an
+                              operand after one lane permutation -- no LDS in the K loop; waves
+                              take every waves-th stage of 16 chunks; K parts meet in an
+                              atomic-swap exchange */
+    SKINNY_PATH_DOT2W = 11 /* v_dot2_f32_bf16, tiles 1/2/4/8: the MFMA4 kernel's stream (equal
+                              row ranges of 4-row groups, waves on every waves-th 16-chunk
+                              stage, row-contiguous loads straight into registers, each x load
+                              serving every row group) with dot2 arithmetic per lane */
 } skinny_path;
 
 /*
@@ -110,23 +113,23 @@ typedef enum {
  */
 typedef struct {
     int path;   /* skinny_path */
-    int mt;     /* token tile: DOT2/DOT2R/DOT2X 1,2,4,8; the MFMA paths 16,32,64 */
+    int mt;     /* token tile: DOT2/DOT2R/DOT2X/DOT2W 1,2,4,8; MFMA4 4,8,16,32; the other
+                   MFMA paths 16,32,64 */
     int rows;   /* weight rows per workgroup.  DOT2, DOT2R: 1..16 (mt*rows <= 64; for
-                   DOT2R the most rows of a range); MFMA: 16,32,64; DOT2X: waves * (1, 2
-                   or 4); MFMAX, MFMAD, MFMAS, MFMAR: 16 * waves; MFMAK: 16 or 32 (row
-                   groups of 16), with waves a multiple of rows / 16; MFMAW: 16, 32 or
-                   64 (the most rows of a range) */
+                   DOT2R the most rows of a range); MFMA: 16,32,64; MFMAX: 16 * waves;
+                   MFMAW: 16, 32 or
+                   64 (the most rows of a range); MFMA4, DOT2W: 4 x (1, 2, 4, 7, 13 or
+                   14), the most rows of a range (fewer row groups for the largest
+                   token tiles) */
     int waves;  /* wavefronts per workgroup: 1,2,4,8 */
     int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
                    (MFMAX: 1 = row tiles of 16 * waves rows, 2 = equal row ranges, its
-                   stage is fixed at 32 chunks; MFMAD: the depth of
-                   its LDS rings, 2..4 stages of 32 chunks; MFMAS, MFMAR, MFMAK:
-                   weight stages of 32 chunks in flight in registers, 2..4; MFMAW:
-                   the stage width in 8-chunk units, 1 or 2, two stages in flight) */
-    int split;  /* workgroups splitting K per row tile (1 = none), 1..16; MFMAS: the
-                   stream-K grid, in workgroups per CU (1..4, capped at what fits);
-                   MFMAK: row ranges per CU (1 or 2), K is never split between
-                   workgroups */
+                   stage is fixed at 32 chunks; MFMAW: the stage width in 8-chunk units,
+                   1 or 2, two stages in flight; MFMA4, DOT2W: stages of 16 chunks in
+                   flight, 2 or 3) */
+    int split;  /* workgroups splitting K per row tile (1 = none), 1..16 (MFMAW 1..4,
+                   MFMA4 and DOT2W 1..8); their fp32 partials meet in the plan's
+                   workspace, one agent-scope atomic swap per value and level */
 } skinny_tactic;
 
 /*
@@ -252,6 +255,15 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K);
  * is 0) and returns the total count, or -1 on bad arguments.  Host only.
  */
 int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap);
+
+/*
+ * skinny_enumerate_tactics_ex -- the same for a device with `cus` compute
+ * units (>= 1): the launch-shape rules (how many workgroups fill the chip,
+ * how many equal row ranges a K split needs) depend on it.
+ * skinny_enumerate_tactics is this with cus = 256 (an MI355X); the tuner
+ * inside skinny_prepare uses the current device's count.  Host only.
+ */
+int skinny_enumerate_tactics_ex(int N, int K, int cus, skinny_tactic *buf, int cap);
 
 /*
  * skinny_select_table -- the table rule.  Given `count` candidate tactics and

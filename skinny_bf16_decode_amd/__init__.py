@@ -30,16 +30,13 @@ IN_BF16 = 0
 IN_F16 = 1
 PATH_DOT2 = 0
 PATH_MFMA = 1
-PATH_DOT2X = 2
 PATH_MFMAX = 3
-PATH_MFMAD = 4
-PATH_MFMAS = 5
-PATH_MFMAR = 6
-PATH_MFMAK = 7
 PATH_DOT2R = 8
 PATH_MFMAW = 9
+PATH_MFMA4 = 10
+PATH_DOT2W = 11
 PATH_NAMES = {0: "dot2", 1: "mfma", 2: "dot2x", 3: "mfmax", 4: "mfmad", 5: "mfmas", 6: "mfmar", 7: "mfmak",
-              8: "dot2r", 9: "mfmaw"}
+              8: "dot2r", 9: "mfmaw", 10: "mfma4", 11: "dot2w"}
 
 STATUS = {
     0: "SKINNY_OK",
@@ -113,6 +110,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "skinny_last_error": (ctypes.c_char_p, []),
         "skinny_tactic_check": (i, [tp, i, i]),
         "skinny_enumerate_tactics": (i, [i, i, tp, i]),
+        "skinny_enumerate_tactics_ex": (i, [i, i, i, tp, i]),
         "skinny_select_table": (i, [tp, ctypes.POINTER(ctypes.c_double), i, tp]),
         "skinny_probe_read": (i, [vp, sz, vp, vp]),
         "skinny_probe_read_blocks": (i, []),
@@ -145,13 +143,14 @@ def tactic_check(t: Tactic, n: int, k: int) -> None:
     _raise(load_library().skinny_tactic_check(ctypes.byref(t), n, k))
 
 
-def enumerate_tactics(n: int, k: int) -> list:
+def enumerate_tactics(n: int, k: int, cus: int = 256) -> list:
+    """The candidates the tuner times for an [n, k] weight on a device with `cus` CUs."""
     lib = load_library()
-    count = lib.skinny_enumerate_tactics(n, k, None, 0)
+    count = lib.skinny_enumerate_tactics_ex(n, k, cus, None, 0)
     if count < 0:
-        raise ValueError(f"bad shape N={n} K={k}")
+        raise ValueError(f"bad shape N={n} K={k} or CU count {cus}")
     buf = (Tactic * count)()
-    lib.skinny_enumerate_tactics(n, k, buf, count)
+    lib.skinny_enumerate_tactics_ex(n, k, cus, buf, count)
     return [Tactic(*t.astuple()) for t in buf]
 
 

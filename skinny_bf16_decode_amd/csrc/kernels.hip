@@ -5,30 +5,32 @@
 // the decode-step product "out[M, N] = x[M, K] @ weight[N, K]^T" of class
 // PreparedWarpSplitK on the page "vllm.models.kimi_k3.nvidia.specialized_decode.
 // cutedsl.gemm.warp_splitk".  At decode sizes the whole cost is streaming W
-// once from HBM, so both kernels are organised around the weight stream:
+// once from HBM, so every kernel is organised around the weight stream:
 //
 //  * Each lane loads 16 bytes (8 BF16 of one row) per load, with the
-//    nontemporal bit, so one wave's load is a contiguous 1 KiB run (DOT2) or
-//    sixteen 64-byte runs (MFMA).  W is touched once and must not evict x or
-//    out from L2 -- the role the page's evict_first L2 policy plays there.
+//    nontemporal bit, and a wave's load covers whole runs of one or a few
+//    rows.  W is touched once and must not evict x or out from L2 -- the role
+//    the page's evict_first L2 policy plays there.
 //  * Workgroups own few rows (the page's small 16/32-row output tiles that let
-//    many blocks co-reside per SM), and split K across their waves: every
-//    wave holds fp32 partials of the same outputs over a different K range
-//    (the page's four compute warps that each own a K quarter), reduced at
-//    the end through DPP / lane swaps inside the wave and LDS across waves.
-//  * Optionally `split` workgroups share one row tile along K; each writes
-//    its fp32 partial to a workspace and the last to arrive sums the partials
-//    in a fixed order and writes the output (the split-K GEMM of the page
+//    many blocks co-reside per SM, here equal row ranges sized to the CU
+//    count), and split K across their waves: every wave holds fp32 partials
+//    of the same outputs over a different K range (the page's four compute
+//    warps that each own a K quarter), reduced at the end through DPP / lane
+//    swaps inside the wave and LDS across waves.
+//  * Optionally `split` workgroups share one row tile along K and exchange
+//    their fp32 partials through a workspace (the split-K GEMM of the page
 //    "vllm.models.glm5next.nvidia.specialized_decode.gemm", which reduces its
-//    split-K partials across a thread-block cluster; here the exchange goes
-//    through memory with agent-scope atomic stores and loads and an
-//    arrival counter).
+//    split-K partials across a thread-block cluster): here every partial
+//    travels inside an agent-scope atomic swap, and whichever part completes
+//    a pair adds it (swap_exchange).
 //
 // DOT2 (token tiles 1..8): v_dot2_f32_bf16, two BF16 products into an fp32
 // accumulator per instruction.  MFMA (token tiles 16..64): W rows are the
 // 16-row A operand and tokens the 16-column B operand of
 // v_mfma_f32_16x16x32_bf16 (the warp split-K page also puts the weight on the
-// MMA's row side and the tokens on its column side).
+// MMA's row side and the tokens on its column side).  MFMA4 (token tiles
+// 4..32): the 16-block v_mfma_f32_4x4x4_16b, whose blocks take sixteen K
+// chunks of four rows and four tokens.
 //
 // Accumulation is fp32 throughout; BF16 output is rounded to nearest even
 // once, from the final fp32 sum.
@@ -250,110 +252,137 @@ __device__ __forceinline__ void wave_reduce_transpose(float *v, int lane)
     step_dpp<V5, kDppQuadXor1, 1>(v, lane);
 }
 
-// ---------------------------------------------------------------------------
-// Cross-workgroup split-K exchange.
-//
-// Partials are written with agent-scope atomic stores and read back with
-// agent-scope atomic loads; on gfx950 these are the write-through / coherent
-// forms of the plain access (sc1), so no L2 writeback is needed to publish
-// them.  An agent-scope release fence would add one (buffer_wbl2), and those
-// writebacks serialise per XCD.
-//
-// Every slot of the workspace holds kSlotEmpty, a signalling-NaN pattern that
-// no fp32 arithmetic produces, except while a partial is in it.  A workgroup
-// publishes its partial and bumps the tile's arrival counter with an
-// agent-scope atomic straight away, without waiting for its stores to
-// complete: the workgroup that sees split - 1 arrivals before its own knows
-// that every partial has been issued, and reads each slot until it no longer
-// holds kSlotEmpty (a store in flight always lands; the re-read is bounded
-// all the same).  It sums the partials in split order, so the sum is
-// deterministic, then empties the slots and resets the counter for the next
-// launch.  Against waiting for the stores before the atomic this takes one
-// memory round trip off the end of every split launch.
-// ---------------------------------------------------------------------------
 constexpr unsigned kSlotEmpty = kSlotEmptyBits;
-constexpr int kSlotSpinLimit = 1 << 16;
-
-__device__ __forceinline__ void publish_partial(float *p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ unsigned read_slot(const float *p)
-{
-    return __hip_atomic_load(reinterpret_cast<const unsigned *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ void empty_slot(float *p)
 {
     __hip_atomic_store(reinterpret_cast<unsigned *>(p), kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The last arriver's sum of a thread's N output values over the partial
-// slots: v[i] = sum over p < parts, in slot order from 0, of slot p at
-// offset off[i] (slots `stride` floats apart); off[i] < 0 is no value.  The
-// loads of four slots are all issued before the first add, so the reduction
-// costs ceil(parts / 4) memory round trips instead of parts x N.  Each slot
-// is emptied once read; no two threads may name the same offset.
-template <int N>
-__device__ __forceinline__ void sum_partials(float *wsp, long stride, int parts, const int (&off)[N],
-                                             float (&v)[N])
+// ---------------------------------------------------------------------------
+// Cross-workgroup split-K exchange by atomic swaps.
+//
+// The `parts` K parts of a row tile meet in a fixed binary tree: at level 0
+// parts (0, 1), (2, 3), ... pair up in one node each, an odd part out moves
+// up unpaired, and so on until one value is left; a tile has parts - 1 nodes
+// of E values, each holding kSlotEmpty between launches.  A part swaps its
+// value into its node with one agent-scope atomic exchange and gets back what
+// was there: kSlotEmpty means the partner has not arrived and will carry the
+// pair on, so this value is done; anything else is the partner's value, and
+// this part empties the node, adds the two and moves up a level.  Whoever
+// completes the root holds the whole sum.
+//
+// Each node adds exactly its two children, and fp32 addition is commutative,
+// so the sum is the same bits whatever the arrival order: ((p0 + p1) +
+// (p2 + p3)) for four parts.  The value travels inside the atomic itself, so
+// nothing is fenced, nothing waits for another workgroup and no counter is
+// needed: one memory round trip per level, and a late partner can never be
+// missed (the second of two swaps on a node always sees the first).  Every
+// node is used by exactly two swaps per launch and left empty, so the next
+// launch (graph replays included) finds the workspace as the first did.
+// Values no part holds (outputs past N or M) are never swapped, by any part.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned swap_slot(float *p, float v)
 {
+    return __hip_atomic_exchange(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// v[i] (at value offset off[i] >= 0 of this tile; off[i] < 0: none) is this
+// part's partial; on return done[i] says whether this thread now holds the
+// whole sum of value i in v[i].  wsp is the tile's node array [parts - 1][E].
+template <int N>
+__device__ __forceinline__ void swap_exchange(float *wsp, int E, int parts, int part, const int (&off)[N],
+                                              float (&v)[N], bool (&done)[N])
+{
+    bool live[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-        v[i] = 0.f;
-    for (int p0 = 0; p0 < parts; p0 += 4) {
-        unsigned r[4][N];
-        bool empty = false;
+    for (int i = 0; i < N; ++i) {
+        live[i] = off[i] >= 0;
+        done[i] = false;
+    }
+    int pos = part, n = parts, node0 = 0;
+    while (n > 1) {
+        const int pairs = n >> 1;
+        if (pos < 2 * pairs) {
+            float *node = wsp + (long)(node0 + (pos >> 1)) * E;
+            unsigned old[N];
+            // all swaps of the level in flight before the first is looked at
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+            for (int i = 0; i < N; ++i)
+                old[i] = live[i] ? swap_slot(node + off[i], v[i]) : kSlotEmpty;
 #pragma unroll
             for (int i = 0; i < N; ++i) {
-                r[k][i] = p0 + k < parts && off[i] >= 0 ? read_slot(wsp + (long)(p0 + k) * stride + off[i]) : 0u;
-                empty |= r[k][i] == kSlotEmpty;
-            }
-        // a store still in flight: read the empty slots again, with one
-        // bounded budget for the whole batch (past it the sum is a NaN)
-        for (int spin = 0; empty && spin < kSlotSpinLimit; ++spin) {
-            empty = false;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int i = 0; i < N; ++i)
-                    if (r[k][i] == kSlotEmpty) {
-                        r[k][i] = read_slot(wsp + (long)(p0 + k) * stride + off[i]);
-                        empty |= r[k][i] == kSlotEmpty;
-                    }
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (p0 + k < parts)
-#pragma unroll
-                for (int i = 0; i < N; ++i) {
-                    v[i] += __builtin_bit_cast(float, r[k][i]);
-                    if (off[i] >= 0)
-                        empty_slot(wsp + (long)(p0 + k) * stride + off[i]);
+                if (!live[i])
+                    continue;
+                if (old[i] == kSlotEmpty) {
+                    live[i] = false;           // the partner carries the pair on
+                } else {
+                    empty_slot(node + off[i]);
+                    v[i] += __uint_as_float(old[i]);
                 }
+            }
+        }
+        node0 += pairs;
+        pos >>= 1;
+        n = (n + 1) >> 1;
     }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        done[i] = live[i];
 }
 
-// Called by every thread of the workgroup after it issued its partial's stores.
-__device__ __forceinline__ bool split_arrive_last(const KArgs &a, int tile, unsigned *flag_lds)
-{
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev =
-            __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *flag_lds = (prev == (unsigned)(a.split - 1)) ? 1u : 0u;
-    }
-    __syncthreads();
-    return *flag_lds != 0;
-}
+// The same exchange on value pairs: values 2p and 2p + 1 of a thread travel
+// in one 64-bit swap, halving the atomics.  Pair p sits at the 64-bit slot
+// pair_off[p] of every node (E / 2 slots); a pair is swapped when either of
+// its values is live in this tile -- the same pairs in every K part -- and a
+// value that is not live just rides along.
+constexpr unsigned long long kPairEmpty = ((unsigned long long)kSlotEmpty << 32) | kSlotEmpty;
 
-__device__ __forceinline__ void split_reset(const KArgs &a, int tile)
+template <int N>
+__device__ __forceinline__ void swap_exchange_pairs(float *wsp, int E, int parts, int part, const int (&off)[N],
+                                                    const int (&pair_off)[N / 2], float (&v)[N], bool (&done)[N])
 {
-    if (threadIdx.x == 0)
-        __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    static_assert(N % 2 == 0, "values go in pairs");
+    bool live[N / 2];
+#pragma unroll
+    for (int p = 0; p < N / 2; ++p)
+        live[p] = off[2 * p] >= 0 || off[2 * p + 1] >= 0;
+    int pos = part, n = parts, node0 = 0;
+    while (n > 1) {
+        const int pairs = n >> 1;
+        if (pos < 2 * pairs) {
+            unsigned long long *node =
+                reinterpret_cast<unsigned long long *>(wsp + (long)(node0 + (pos >> 1)) * E);
+            unsigned long long old[N / 2];
+#pragma unroll
+            for (int p = 0; p < N / 2; ++p) {
+                const unsigned long long mine = ((unsigned long long)__float_as_uint(v[2 * p + 1]) << 32) |
+                                                __float_as_uint(v[2 * p]);
+                old[p] = live[p] ? __hip_atomic_exchange(node + pair_off[p], mine, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)
+                                 : kPairEmpty;
+            }
+#pragma unroll
+            for (int p = 0; p < N / 2; ++p) {
+                if (!live[p])
+                    continue;
+                if (old[p] == kPairEmpty) {
+                    live[p] = false;           // the partner carries the pair on
+                } else {
+                    __hip_atomic_store(node + pair_off[p], kPairEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v[2 * p] += __uint_as_float((unsigned)old[p]);
+                    v[2 * p + 1] += __uint_as_float((unsigned)(old[p] >> 32));
+                }
+            }
+        }
+        node0 += pairs;
+        pos >>= 1;
+        n = (n + 1) >> 1;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        done[i] = off[i] >= 0 && live[i / 2];
 }
 
 // ---------------------------------------------------------------------------
@@ -367,7 +396,6 @@ __device__ __forceinline__ void split_reset(const KArgs &a, int tile)
 // past the end of its K range uses kOffOob, which is out of range for any
 // resource here (tiles are far below 2 GiB).
 // ---------------------------------------------------------------------------
-constexpr unsigned kOffOob = 0x7FFFFFF0u;
 constexpr int kCpolNt = 2;   // nontemporal
 
 
@@ -525,26 +553,14 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
             store_out(a, m, n, total);
         return;
     }
-    // split-K: publish this workgroup's partial, the last arriver finalises.
-    // Only wave 0 is left and it holds the whole partial, so the arrival is a
-    // wave-level one (no workgroup barrier once the other waves have exited).
-    float *wsp = a.ws + (long)tile * a.split * V;
-    if (live)                                  // exactly the slots the finaliser reads
-        publish_partial(wsp + (long)s * V + tid, total);
-    unsigned prev = 0;
-    if (lane == 0)
-        prev = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != (unsigned)(a.split - 1))
-        return;
-    if (live) {
-        const int off[1] = {tid};
-        float sum[1];
-        sum_partials<1>(wsp, V, a.split, off, sum);
+    // split-K: wave 0 holds the workgroup's whole partial; it meets the other
+    // K parts' in the swap exchange, and whoever completes a value stores it
+    const int off[1] = {live ? tid : -1};
+    float sum[1] = {total};
+    bool done[1];
+    swap_exchange<1>(a.ws + (long)tile * (a.split - 1) * V, V, a.split, s, off, sum, done);
+    if (done[0])
         store_out(a, m, n, sum[0]);
-    }
-    if (lane == 0)
-        __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -567,7 +583,6 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
 {
     constexpr int MT = 16 * T, NT = 16 * RT, NTP = NT + 1;
     extern __shared__ float lds[];   // [waves][MT][NTP]
-    __shared__ unsigned flag;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -686,223 +701,29 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
         }
         return;
     }
-    float *wsp = a.ws + (long)tile * a.split * E;
-    for (int e = tid; e < E; e += nthr) {
-        const int tok = e / NT, row = e - (e / NT) * NT;
-        if (tok >= mlim)
-            continue;
-        float v = 0.f;
-        for (int w = 0; w < nwaves; ++w)
-            v += lds[((long)w * MT + tok) * NTP + row];
-        publish_partial(wsp + (long)s * E + e, v);
-    }
-    if (!split_arrive_last(a, tile, &flag))
-        return;
+    float *wsp = a.ws + (long)tile * (a.split - 1) * E;
     for (int e0 = tid; e0 < E; e0 += 4 * nthr) {
         int off[4];
         float v[4];
+        bool done[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {             // the published values: tokens < mlim
+        for (int i = 0; i < 4; ++i) {             // the values every K part holds
             const int e = e0 + i * nthr;
-            off[i] = e < E && e / NT < mlim ? e : -1;
+            const int tok = e / NT, row = e - (e / NT) * NT;
+            const bool live = e < E && tok < mlim && n0 + row < a.N;
+            off[i] = live ? e : -1;
+            v[i] = 0.f;
+            if (live)
+                for (int w = 0; w < nwaves; ++w)
+                    v[i] += lds[((long)w * MT + tok) * NTP + row];
         }
-        sum_partials<4>(wsp, E, a.split, off, v);
+        swap_exchange<4>(wsp, E, a.split, s, off, v, done);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = e0 + i * nthr;
-            const int tok = e / NT, row = e - (e / NT) * NT;
-            if (e < E && tok < mlim && n0 + row < a.N)
-                store_out(a, tok, n0 + row, v[i]);
+            if (done[i])
+                store_out(a, e / NT, n0 + e - (e / NT) * NT, v[i]);
         }
-    }
-    split_reset(a, tile);
-}
-
-// ---------------------------------------------------------------------------
-// DOT2X kernel: token tile MT <= 8; each wave owns R rows of the workgroup's
-// row tile (waves * R rows), and the x slice of the workgroup's K range is
-// staged once in LDS, shared by all rows of the workgroup.
-//
-// Every wave streams its own rows over the whole K range of the split: lane
-// l takes chunks kb + l, kb + l + 64, ... of each of its R rows, so a
-// wave-wide load is 1 KiB of one row and U loads per row form U KiB
-// contiguous runs.  The x operands come from LDS (one ds_read per token and
-// chunk, reused over the R rows), which takes them off the vector-memory
-// path: only W flows through it.  No cross-wave reduction is needed; the
-// in-wave transposing reduction finishes each wave's R x MT outputs.
-// ---------------------------------------------------------------------------
-template <int MT, int R, int U, bool H>
-__global__ __launch_bounds__(512) void k_dot2x(KArgs a)
-{
-    constexpr int V = MT * R;
-    extern __shared__ u32x4 xs[];   // [MT][kr] chunks of x[0..MT)[kb..ke)
-    __shared__ unsigned flag;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nthr = blockDim.x, nwaves = nthr >> 6;
-    int tile, s;
-    block_coords(a, tile, s);
-    const int n_wg = tile * nwaves * R;        // first row of the workgroup
-    const int n0 = n_wg + wave * R;            // first row of this wave
-    const int kb = split_point(a, s, a.K8);
-    const int ke = split_point(a, s + 1, a.K8);
-    const int kr = ke - kb;
-    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
-    const int rows_valid = uniform_int(max(0, min(R, a.N - n0)));
-    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
-                                (unsigned)rows_valid * row_bytes);
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
-    const unsigned lane_off = (unsigned)(kb + lane) * 16u;
-    constexpr unsigned kPass = 64u * 16u;      // one wave-wide pass: 64 chunks
-
-    float acc[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-        acc[i] = 0.f;
-
-    const int passes = kr / 64;
-    const int stages = passes / U;
-    u32x4 wa[U][R], wb[U][R];
-    auto load = [&](u32x4(&w)[U][R], int j) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const unsigned so = (unsigned)(j * U + u) * kPass;
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                w[u][r] = load_w(wres, (unsigned)r * row_bytes + lane_off, so);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto compute = [&](const u32x4(&w)[U][R], int j) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = lane + 64 * (j * U + u);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const u32x4 xv = xs[m * kr + c];
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    acc[m * R + r] = dot8<H>(w[u][r], xv, acc[m * R + r]);
-            }
-        }
-    };
-
-    // First weight stage in flight before the activations are staged.
-    if (stages > 0)
-        load(wa, 0);
-    {
-        const int total = MT * kr;
-        for (int q0 = tid; q0 < total; q0 += 8 * nthr) {
-            u32x4 v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = q0 + i * nthr;
-                const int m = q / kr, c = q - (q / kr) * kr;
-                v[i] = load_x(xres, q < total ? (unsigned)m * x_pitch + (unsigned)(kb + c) * 16u : kOffOob, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = q0 + i * nthr;
-                if (q < total)
-                    xs[q] = v[i];
-            }
-        }
-    }
-    __syncthreads();
-
-    if (stages > 0) {
-        int j = 0;
-        for (; j + 2 < stages; j += 2) {
-            load(wb, j + 1);
-            compute(wa, j);
-            load(wa, j + 2);
-            compute(wb, j + 1);
-        }
-        if (j + 1 < stages) {
-            load(wb, j + 1);
-            compute(wa, j);
-            compute(wb, j + 1);
-        } else {
-            compute(wa, j);
-        }
-    }
-    for (int p = stages * U; p * 64 < kr; ++p) {
-        const int c = lane + 64 * p;
-        const bool ok = c < kr;
-        const unsigned so = (unsigned)p * kPass;
-        u32x4 w[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            w[r] = load_w(wres, ok ? (unsigned)r * row_bytes + lane_off : kOffOob, so);
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const u32x4 xv = ok ? xs[m * kr + (ok ? c : 0)] : zero;   // index kept in range
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                acc[m * R + r] = dot8<H>(w[r], xv, acc[m * R + r]);
-        }
-    }
-
-    wave_reduce_transpose<V>(acc, lane);
-    constexpr int kLanesPerValue = 64 / V;
-    const bool holder = (lane & (kLanesPerValue - 1)) == 0;
-    const int idx = lane / kLanesPerValue;     // value index m * R + r
-    const int m = idx / R, r = idx - (idx / R) * R;
-    if (a.split == 1) {
-        if (holder && m < a.M && n0 + r < a.N)
-            store_out(a, m, n0 + r, acc[0]);
-        return;
-    }
-    const int E = nwaves * V;                  // partial values of the workgroup
-    float *wsp = a.ws + (long)tile * a.split * E;
-    if (holder)
-        publish_partial(wsp + (long)s * E + wave * V + idx, acc[0]);
-    if (!split_arrive_last(a, tile, &flag))
-        return;
-    for (int e0 = tid; e0 < E; e0 += 4 * nthr) {
-        int off[4];
-        float v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            off[k] = e0 + k * nthr < E ? e0 + k * nthr : -1;
-        sum_partials<4>(wsp, E, a.split, off, v);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int e = e0 + k * nthr;
-            const int w = e / V, i = e - (e / V) * V;
-            const int mm = i / R, rr = i - (i / R) * R, n = n_wg + w * R + rr;
-            if (e < E && mm < a.M && n < a.N)
-                store_out(a, mm, n, v[k]);
-        }
-    }
-    split_reset(a, tile);
-}
-
-// The last arriver of a tile whose partials are MFMA accumulator fragments
-// (value e = ((wave T + t) 4 + q) 64 + lane: token 16 t + lane % 16, row
-// n_wg + 16 wave + 4 (lane / 16) + q) sums the slots and stores the rows
-// below n_end.
-template <int T, int NW>
-__device__ __forceinline__ void finalize_mfma_tile(const KArgs &a, float *wsp, int E, int parts, int n_wg,
-                                                   int n_end)
-{
-    constexpr int EPT = 4 * T;                 // values per thread: E = 64 NW EPT
-    int off[EPT];
-    float v[EPT];
-#pragma unroll
-    for (int i = 0; i < EPT; ++i)
-        off[i] = (int)threadIdx.x + 64 * NW * i;
-    sum_partials<EPT>(wsp, E, parts, off, v);
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int e = off[i];
-        const int ln = e & 63, q = (e >> 6) & 3, wt = e >> 8;
-        const int w = wt / T, t = wt - (wt / T) * T;
-        const int tok = 16 * t + (ln & 15), n = n_wg + 16 * w + 4 * (ln >> 4) + q;
-        if (tok < a.M && n < n_end)
-            store_out(a, tok, n, v[i]);
     }
 }
 
@@ -936,7 +757,6 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
     constexpr int PB = NX / 2;                 // stages per barrier
     static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
     extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [NX][MT][PITCH]
-    __shared__ unsigned flag;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1116,576 +936,31 @@ __global__ __launch_bounds__(512) void k_mfmax(KArgs a)
         }
         return;
     }
+    // split-K: this wave's values ((wave T + t) 4 + q) 64 + lane of the
+    // workgroup's partial meet the other K parts' in the swap exchange
     constexpr int E = NW * T * 4 * 64;         // partial values of the workgroup
-    float *wsp = a.ws + (long)tile * a.split * E;
+    int off[4 * T];
+    float v[4 * T];
+    bool done[4 * T];
 #pragma unroll
     for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
-    if (!split_arrive_last(a, tile, &flag))
-        return;
-    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg, n_end);
-    split_reset(a, tile);
-}
-
-// ---------------------------------------------------------------------------
-// MFMAD kernel: token tile MT = 16 T; NW waves each own 16 weight rows; the
-// weight and activation tiles stream straight into LDS rings D stages deep.
-//
-// A stage is 32 K-chunks (512 bytes of a row, 8 MFMA K-steps).  Loads use the
-// direct-to-LDS form of the 16-byte buffer load: lane l of a load writes LDS
-// bytes [16 l, 16 l + 16) of the load's destination, while its global address
-// is free.  Each load covers two rows: lanes 0-31 fill row 2q, lanes 32-63 row
-// 2q + 1, and the lane at LDS position p of row r fetches chunk p ^ r (r < 16),
-// so that the 16 rows of one K column sit in 16 different bank groups when
-// the MFMA fragments are read back (lane (g, i) reads row i, chunk 4 step + g,
-// at position (4 step + g) ^ i).  Loads past the end of a row range, of the
-// weight (rows >= N) or of x (tokens >= M) are out of the buffer resource and
-// write zeros.  The weight ring is private to each wave; the x ring is filled
-// cooperatively and shared, so one barrier per stage orders both its fill
-// and the reuse of its slots.  The loads of D - 1 stages are in flight while a
-// stage is multiplied, and none of it passes through registers.
-// ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, u32x4 *lds_dst, unsigned voff)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, voff, 0, 0, kCpolNt);
-}
-
-template <int T, int NW, int D, bool H>
-__global__ __launch_bounds__(512) void k_mfmad(KArgs a)
-{
-    constexpr int MT = 16 * T;
-    constexpr int KW = 32;                       // chunks per stage
-    constexpr int XI = MT / (2 * NW);            // x loads per wave per stage
-    static_assert(XI >= 1 && XI * 2 * NW == MT, "x tile must split evenly over the waves");
-    constexpr int WSLOT = 16 * KW;               // u32x4 per weight slot (8 KiB)
-    constexpr int XSLOT = MT * KW;               // u32x4 per x slot
-    extern __shared__ u32x4 sm[];                // [NW][D][WSLOT] then [D][XSLOT]
-    __shared__ unsigned flag;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int tile, s;
-    block_coords(a, tile, s);
-    const int n_wg = tile * NW * 16;
-    const int n0 = n_wg + wave * 16;
-    const int kb = split_point(a, s, a.K8);
-    const int ke = split_point(a, s + 1, a.K8);
-    const int stages = (ke - kb + KW - 1) / KW;
-    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
-    const int rows_valid = uniform_int(max(0, min(16, a.N - n0)));
-    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
-                                (unsigned)rows_valid * row_bytes);
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
-    u32x4 *wring = sm + wave * D * WSLOT;
-    u32x4 *xring = sm + NW * D * WSLOT;
-
-    // DMA lane mapping: row (or token) parity from lane >> 5, LDS position from lane & 31
-    const int half = lane >> 5, pos = lane & 31;
-    const int i16 = lane & 15, g = lane >> 4;
-
-    // Stage j into slot j % D; chunks past the split (or stages past the last)
-    // get an out-of-range offset and land as zeros.  Every call issues exactly
-    // 8 + XI loads on every lane -- the waits below count on it -- so the
-    // validity test is a per-lane select, never a branch.
-    auto issue = [&](int j) {
-        const int slot = j % D;
-        const int cbase = kb + j * KW;
-        const int lim = j < stages ? ke : kb;    // no chunk is valid past the last stage
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int r = 2 * q + half;
-            const int c = cbase + (pos ^ r);
-            const unsigned off = c < lim ? (unsigned)r * row_bytes + (unsigned)c * 16u : kOffOob;
-            dma16(wres, wring + slot * WSLOT + 2 * q * KW, off);
-        }
-#pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            const int pair = wave + NW * i;        // tokens 2 pair, 2 pair + 1
-            const int tok = 2 * pair + half;
-            const int c = cbase + (pos ^ (tok & 15));
-            const unsigned off = c < lim ? (unsigned)tok * x_pitch + (unsigned)c * 16u : kOffOob;
-            dma16(xres, xring + slot * XSLOT + 2 * pair * KW, off);
-        }
-    };
-
-    f32x4 acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int j = 0; j < D - 1; ++j)
-        issue(j);
-    for (int j = 0; j < stages; ++j) {
-        // this wave's loads of stage j are done once at most D - 2 stages remain outstanding
-        if constexpr (D == 2)
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if constexpr (D == 3)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 + XI) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (8 + XI)) : "memory");
-        // Every wave's share of stage j has landed once all waves pass here.
-        // A bare barrier: __syncthreads would also wait for every load in
-        // flight (its release fence), draining the ring.  The asm is a
-        // compiler barrier too, so no LDS read moves above it.
-        asm volatile("s_barrier" ::: "memory");
-        issue(j + D - 1);                        // refills the slot stage j - 1 used
-        const u32x4 *wsl = wring + (j % D) * WSLOT;
-        const u32x4 *xsl = xring + (j % D) * XSLOT;
-#pragma unroll
-        for (int st = 0; st < KW / 4; ++st) {
-            const int p = (4 * st + g) ^ i16;
-            const u32x4 av = wsl[i16 * KW + p];
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const u32x4 bv = xsl[(16 * t + i16) * KW + p];
-                acc[t] = mma16<H>(av, bv, acc[t]);
-            }
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may land after the wave ends
-
-    // lane (g, i) holds rows 4g .. 4g+3 (of this wave's 16) of token 16 t + i
-    if (a.split == 1) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int tok = 16 * t + i16;
-            if (tok >= a.M)
-                continue;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + 4 * g + q;
-                if (n < a.N)
-                    store_out(a, tok, n, acc[t][q]);
-            }
-        }
-        return;
-    }
-    constexpr int E = NW * T * 4 * 64;           // partial values of the workgroup
-    float *wsp = a.ws + (long)tile * a.split * E;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            publish_partial(wsp + (long)s * E + ((wave * T + t) * 4 + q) * 64 + lane, acc[t][q]);
-    if (!split_arrive_last(a, tile, &flag))
-        return;
-    finalize_mfma_tile<T, NW>(a, wsp, E, a.split, n_wg, a.N);
-    split_reset(a, tile);
-}
-
-// ---------------------------------------------------------------------------
-// MFMAS kernel: token tile MT = 16 T, NW waves each own 16 rows of a row
-// tile of at most 16 NW rows, under a stream-K schedule, with U weight
-// stages in flight in registers.
-//
-// The work is the flat list of units (row tile t, K stage k), t < n_tiles,
-// k < spt = ceil(K / 256), and workgroup g of G takes units [g U / G,
-// (g + 1) U / G).  Tile t is the row range [t N / n_tiles, (t + 1) N /
-// n_tiles), so tiles differ by at most one row.  With G = the workgroups
-// that fit on the chip at once (MFMAS), every workgroup streams the same
-// amount of weight and none waits for a second round; with G = n_tiles
-// (MFMAR, split 1) each workgroup owns one whole tile, and n_tiles may be
-// raised to the CU count so that every CU gets one equal row range and no
-// partial sums are exchanged.
-//
-// A stage is 32 K-chunks (512 bytes of each row).  The weight is loaded
-// row-contiguously (each wave-wide load is two rows x 512 bytes) into
-// registers U stages ahead, and re-laid out through a wave-private LDS tile
-// [16 rows][34 chunks] from which lane (g, i) reads its A fragment (row i,
-// chunk 4 step + g); the x window [MT tokens][32 chunks] of a stage is
-// loaded by the whole workgroup into a double-buffered LDS tile and read as
-// B fragments, so x is fetched once per tile, not once per wave.
-//
-// A range meets at most two cut tiles: the tile it starts in (unless it
-// starts at the tile's first stage) and the tile it ends in (unless it ends
-// at the tile's last stage); the tiles between are whole and stored as they
-// complete.  A cut tile is shared by consecutive workgroups: each publishes
-// its fp32 partial in slot (g - first workgroup of the tile), arrives on the
-// tile's counter, and the last to arrive sums the slots in order
-// (deterministic) and stores.  The partial of the first cut tile is kept in
-// registers until the loop is over, so that every exchange store is issued
-// after the last weight load.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int sk_owner(unsigned u, unsigned units, unsigned G)
-{
-    // the workgroup whose range [g U / G, (g + 1) U / G) contains unit u
-    return (int)((((unsigned long long)u + 1) * G - 1) / units);
-}
-
-template <int T, int NW, int U, bool H>
-__global__ __launch_bounds__(512) void k_mfmas(KArgs a)
-{
-    constexpr int MT = 16 * T;
-    constexpr int KW = kMfmaxChunks;           // chunks per stage
-    constexpr int PITCH = KW + 2;              // row pitch in 16-byte chunks (see k_mfmax)
-    constexpr int XL = (MT * KW) / (64 * NW);  // x chunks per thread per stage
-    static_assert(XL >= 1 && XL * 64 * NW == MT * KW, "x window must split evenly over the waves");
-    constexpr int E = NW * T * 4 * 64;         // partial values of a tile
-    extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [2][MT][PITCH]
-    __shared__ unsigned last_flag[2];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const unsigned G = gridDim.x, gi = blockIdx.x;
-    const unsigned spt = (unsigned)a.sk_spt;
-    const unsigned units = (unsigned)a.n_tiles * spt;
-    const unsigned u0 = (unsigned)(((unsigned long long)gi * units) / G);
-    const unsigned u1 = (unsigned)(((unsigned long long)(gi + 1) * units) / G);
-    const int count = (int)(u1 - u0);
-    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
-    u32x4 *wl = sm + wave * 16 * PITCH;
-    u32x4 *xl = sm + NW * 16 * PITCH;
-    const int wrow = lane >> 5, wcol = lane & 31;
-    const int i16 = lane & 15, g = lane >> 4;
-    // tile t is the row range [t N / n_tiles, (t + 1) N / n_tiles), at most
-    // 16 NW rows; wave w multiplies its rows 16 w .. 16 w + 15
-    auto tile_row = [&](unsigned t) {
-        return skinny::tile_row(a, (int)t);
-    };
-
-    // loads: stage j of the range is unit u0 + j
-    unsigned ld_tile = u0 / spt, ld_step = u0 - ld_tile * spt;
-    int issued = 0;
-    auto load = [&](u32x4(&wv)[8], u32x4(&xv)[XL]) {
-        const bool live = issued++ < count;
-        const int n0 = tile_row(ld_tile) + wave * 16;
-        const int rows_valid = uniform_int(live ? max(0, min(16, tile_row(ld_tile + 1) - n0)) : 0);
-        const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
-                                    (unsigned)rows_valid * row_bytes);
-        const int cbase = (int)ld_step * KW;
-        const int lim = live ? a.K8 : 0;
-        const int c = cbase + wcol;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            wv[q] = load_w(wres, lane_off(c < lim, (unsigned)(2 * q + wrow) * row_bytes + (unsigned)c * 16u), 0);
-#pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            const int e = tid + 64 * NW * i;
-            const int tok = e / KW, cc = cbase + (e % KW);
-            xv[i] = load_x(xres, lane_off(cc < lim, (unsigned)tok * x_pitch + (unsigned)cc * 16u), 0);
-        }
-        const bool wrap = ld_step + 1 == spt;
-        ld_step = wrap ? 0u : ld_step + 1;
-        ld_tile = wrap ? ld_tile + 1 : ld_tile;
-    };
-
-    f32x4 acc[T], acc_first[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc_first[t] = acc[t];
-    }
-    unsigned c_tile = ld_tile, c_step = ld_step;   // the unit multiplied next
-    bool seg_whole_start = c_step == 0;            // current segment starts at stage 0
-    int first_cut = -1;                            // cut tile met first, partial in acc_first
-
-    auto store_tile = [&](int tile, const f32x4(&v)[T]) {
-        const int n0 = tile_row((unsigned)tile) + wave * 16, n_end = tile_row((unsigned)tile + 1);
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int tok = 16 * t + i16;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + 4 * g + q;
-                if (tok < a.M && n < n_end)
-                    store_out(a, tok, n, v[t][q]);
-            }
-        }
-    };
-    auto publish = [&](int tile, const f32x4(&v)[T]) {
-        const int part = (int)gi - sk_owner((unsigned)tile * spt, units, G);
-        float *wsp = a.ws + ((long)tile * a.sk_parts + part) * E;
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                publish_partial(wsp + ((wave * T + t) * 4 + q) * 64 + lane, v[t][q]);
-    };
-
-    auto stage = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
-        u32x4 *xw = xl + (j & 1) * MT * PITCH;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            wl[(2 * q + wrow) * PITCH + wcol] = wv[q];
-#pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            const int e = tid + 64 * NW * i;
-            xw[(e / KW) * PITCH + (e % KW)] = xv[i];
-        }
-        load(wv, xv);                          // stage j + U (past the range: no memory access)
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        if (j >= count)
-            return;
-        // fragments are read four K-steps at a time, so one LDS round trip
-        // feeds 4 T MFMAs
-#pragma unroll
-        for (int h = 0; h < KW / 16; ++h) {
-            u32x4 av[4], bv[4][T];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                av[s] = wl[i16 * PITCH + 4 * (4 * h + s) + g];
-#pragma unroll
-                for (int t = 0; t < T; ++t)
-                    bv[s][t] = xw[(16 * t + i16) * PITCH + 4 * (4 * h + s) + g];
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int t = 0; t < T; ++t)
-                    acc[t] = mma16<H>(av[s], bv[s][t], acc[t]);
-        }
-        // a segment ends at its tile's last stage or at the range's last
-        // stage; the segment of the range's last stage is handled after the
-        // loop
-        if (j < count - 1 && c_step == spt - 1) {
-            if (seg_whole_start) {
-                store_tile((int)c_tile, acc);
-            } else {                           // the range's first segment, cut
-                first_cut = (int)c_tile;
-#pragma unroll
-                for (int t = 0; t < T; ++t)
-                    acc_first[t] = acc[t];
-            }
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-                acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            seg_whole_start = true;
-        }
-        if (j < count - 1) {
-            const bool wrap = c_step + 1 == spt;
-            c_step = wrap ? 0u : c_step + 1;
-            c_tile = wrap ? c_tile + 1 : c_tile;
-        }
-    };
-
-    // the prologue loads stay in stage order (sched_barrier), so that the
-    // loads of the stage multiplied first are the oldest in flight
-    u32x4 w0[8], x0[XL], w1[8], x1[XL], w2[8], x2[XL], w3[8], x3[XL];
-    load(w0, x0);
-    __builtin_amdgcn_sched_barrier(0);
-    load(w1, x1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (U >= 3) {
-        load(w2, x2);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (U >= 4) {
-        load(w3, x3);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // Whole rounds of U stages, the stages past `count` idle: an exit from
-    // the middle of a round would give the loop a path on which the newest
-    // loads are not the ones the next round waits for, and every round would
-    // then wait for all of its loads.
-    for (int j = 0; j < count; j += U) {
-        stage(w0, x0, j);
-        stage(w1, x1, j + 1);
-        if constexpr (U >= 3)
-            stage(w2, x2, j + 2);
-        if constexpr (U >= 4)
-            stage(w3, x3, j + 3);
-    }
-
-    // The last segment (c_tile, stages up to c_step) is whole if it started
-    // at stage 0 and reached the tile's last stage.
-    const bool last_whole = seg_whole_start && c_step == spt - 1;
-    const int last_cut = last_whole ? -1 : (int)c_tile;
-    if (first_cut >= 0)
-        publish(first_cut, acc_first);
-    if (last_cut >= 0)
-        publish(last_cut, acc);
-    __syncthreads();                           // every wave has issued its partial stores
-    auto arrive = [&](int t) -> unsigned {
-        if (t < 0)
-            return 0u;
-        const int parts = sk_owner((unsigned)(t + 1) * spt - 1, units, G) - sk_owner((unsigned)t * spt, units, G) + 1;
-        const unsigned prev = __hip_atomic_fetch_add(a.ctr + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return prev == (unsigned)(parts - 1) ? (unsigned)parts : 0u;
-    };
-    if (tid == 0) {
-        last_flag[0] = arrive(first_cut);
-        last_flag[1] = arrive(last_cut);
-    }
-    if (last_whole)
-        store_tile((int)c_tile, acc);
-    __syncthreads();
-    auto finalize = [&](int t, int parts) {
-        if (!parts)
-            return;
-        finalize_mfma_tile<T, NW>(a, a.ws + (long)t * a.sk_parts * E, E, parts, tile_row((unsigned)t),
-                                  tile_row((unsigned)t + 1));
-        if (tid == 0)
-            __hip_atomic_store(a.ctr + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    finalize(first_cut, (int)last_flag[0]);
-    finalize(last_cut, (int)last_flag[1]);
-}
-
-// ---------------------------------------------------------------------------
-// MFMAK kernel: token tile MT = 16 T; a workgroup owns one row range of at
-// most 16 RT rows and the whole of K, with RT x KS waves: wave (rt, ks)
-// multiplies rows 16 rt .. 16 rt + 15 of the range over every KS-th K stage
-// starting at stage ks, and the KS partial sums of a row group are added in
-// LDS at the end (in ks order), so no partial sum leaves the workgroup.
-//
-// The grid has n_tiles = max(ceil(N / 16 RT), split x CUs) equal row ranges
-// [t N / n_tiles, (t + 1) N / n_tiles): with N / 16 RT below the CU count
-// every CU gets the same number of rows (6288 rows: 24 or 25 per CU), which
-// 16-row MFMA tiles alone cannot do without sharing tiles between
-// workgroups.  The weight path is MFMAS's: row-contiguous loads U iterations
-// ahead in registers, re-laid out through a wave-private LDS tile; the x
-// window of an iteration covers KS stages, [MT tokens][32 KS chunks], loaded
-// by the whole workgroup into a double-buffered LDS tile.
-// ---------------------------------------------------------------------------
-template <int T, int RT, int KS, int U, bool H>
-__global__ __launch_bounds__(512) void k_mfmak(KArgs a)
-{
-    constexpr int MT = 16 * T;
-    constexpr int NW = RT * KS;
-    constexpr int KW = kMfmaxChunks;           // chunks per wave per iteration
-    constexpr int PITCH = KW + 2;
-    constexpr int XW = KS * KW;                // x window width, chunks
-    constexpr int XP = XW + 2;                 // its row pitch, 2 mod 4 chunks (see k_mfmax)
-    constexpr int XL = (MT * XW) / (64 * NW);  // x chunks per thread per iteration
-    static_assert(XL >= 1 && XL * 64 * NW == MT * XW, "x window must split evenly over the waves");
-    static_assert(U >= 2 && U <= 4, "two to four iterations in flight");
-    extern __shared__ u32x4 sm[];              // [NW][16][PITCH] then [2][MT][XP]
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rt = wave % RT, ks = wave / RT;
-    const unsigned tile = blockIdx.x;
-    const int r0 = tile_row(a, (int)tile);
-    const int r1 = tile_row(a, (int)tile + 1);
-    const int n0 = r0 + 16 * rt;
-    const int rows_valid = uniform_int(max(0, min(16, r1 - n0)));
-    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
-    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n0 : 0) * row_bytes,
-                                (unsigned)rows_valid * row_bytes);
-    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
-    const int iters = (a.K8 + XW - 1) / XW;
-    u32x4 *wl = sm + wave * 16 * PITCH;
-    u32x4 *xl = sm + NW * 16 * PITCH;
-    const int wrow = lane >> 5, wcol = lane & 31;
-    const int i16 = lane & 15, g = lane >> 4;
-
-    int issued = 0;
-    auto load = [&](u32x4(&wv)[8], u32x4(&xv)[XL]) {
-        const int j = issued++;
-        const int lim = j < iters ? a.K8 : 0;
-        const int c = j * XW + ks * KW + wcol;     // this lane's weight chunk
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            wv[q] = load_w(wres, lane_off(c < lim, (unsigned)(2 * q + wrow) * row_bytes + (unsigned)c * 16u), 0);
-#pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            const int e = tid + 64 * NW * i;
-            const int tok = e / XW, cc = j * XW + (e % XW);
-            xv[i] = load_x(xres, lane_off(cc < lim, (unsigned)tok * x_pitch + (unsigned)cc * 16u), 0);
-        }
-    };
-
-    f32x4 acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto stage = [&](u32x4(&wv)[8], u32x4(&xv)[XL], int j) {
-        u32x4 *xw = xl + (j & 1) * MT * XP;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            wl[(2 * q + wrow) * PITCH + wcol] = wv[q];
-#pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            const int e = tid + 64 * NW * i;
-            xw[(e / XW) * XP + (e % XW)] = xv[i];
-        }
-        load(wv, xv);                          // iteration j + U (past the end: no memory access)
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        if (j >= iters)
-            return;
-#pragma unroll
-        for (int h = 0; h < KW / 16; ++h) {
-            u32x4 av[4], bv[4][T];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                av[s] = wl[i16 * PITCH + 4 * (4 * h + s) + g];
-#pragma unroll
-                for (int t = 0; t < T; ++t)
-                    bv[s][t] = xw[(16 * t + i16) * XP + ks * KW + 4 * (4 * h + s) + g];
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int t = 0; t < T; ++t)
-                    acc[t] = mma16<H>(av[s], bv[s][t], acc[t]);
-        }
-    };
-
-    u32x4 w0[8], x0[XL], w1[8], x1[XL], w2[8], x2[XL], w3[8], x3[XL];
-    load(w0, x0);
-    __builtin_amdgcn_sched_barrier(0);
-    load(w1, x1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (U >= 3) {
-        load(w2, x2);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (U >= 4) {
-        load(w3, x3);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // whole rounds of U iterations (see the MFMAS kernel)
-    for (int j = 0; j < iters; j += U) {
-        stage(w0, x0, j);
-        stage(w1, x1, j + 1);
-        if constexpr (U >= 3)
-            stage(w2, x2, j + 2);
-        if constexpr (U >= 4)
-            stage(w3, x3, j + 3);
-    }
-
-    // add the KS partial sums of each row group, in ks order, through LDS
-    // (the tiles are free: every wave is past its last fragment read)
-    float *red = reinterpret_cast<float *>(sm);
-    __syncthreads();
-    if constexpr (KS > 1) {
-        if (ks > 0) {
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    red[((wave * T + t) * 4 + q) * 64 + lane] = acc[t][q];
-        }
-        __syncthreads();
-        if (ks > 0)
-            return;
-#pragma unroll
-        for (int s = 1; s < KS; ++s)
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[t][q] += red[(((s * RT + rt) * T + t) * 4 + q) * 64 + lane];
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int tok = 16 * t + i16;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int n = n0 + 4 * g + q;
-            if (tok < a.M && n < r1)
-                store_out(a, tok, n, acc[t][q]);
+            const bool live = 16 * t + i16 < a.M && n0 + 4 * g + q < n_end;
+            off[t * 4 + q] = live ? ((wave * T + t) * 4 + q) * 64 + lane : -1;
+            v[t * 4 + q] = acc[t][q];
         }
-    }
+    int pair_off[2 * T];                       // the wave's pairs, slot (wave 2T + p) 64 + lane
+#pragma unroll
+    for (int p = 0; p < 2 * T; ++p)
+        pair_off[p] = (wave * 2 * T + p) * 64 + lane;
+    swap_exchange_pairs<4 * T>(a.ws + (long)tile * (a.split - 1) * E, E, a.split, s, off, pair_off, v, done);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (done[t * 4 + q])
+                store_out(a, 16 * t + i16, n0 + 4 * g + q, v[t * 4 + q]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1729,7 +1004,6 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
     static_assert(EPT >= 1 && EPT * 64 * NW == E, "the final sum must split evenly over the threads");
     static_assert(E * 4 <= (ROWS + MT) * PITCH * 16, "the wave's LDS tiles must hold its partial sums");
     extern __shared__ u32x4 sm[];              // [NW][ROWS + MT][PITCH]; at the end float [NW][E]
-    __shared__ unsigned flag;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1839,41 +1113,333 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
             for (int q = 0; q < 4; ++q)
                 red[wave * E + ((r * T + t) * 4 + q) * 64 + lane] = acc[r][t][q];
     __syncthreads();
+    // value e: token 16 t + (e % 16), row n_wg + 16 r + 4 ((e / 16) % 4) + q
+    auto locate = [&](int e, int &tok, int &n) {
+        const int ln = e & 63, q = (e >> 6) & 3, rt = e >> 8;
+        const int r = rt / T, t = rt - (rt / T) * T;
+        tok = 16 * t + (ln & 15);
+        n = n_wg + 16 * r + 4 * (ln >> 4) + q;
+    };
     float v[EPT];
     int off[EPT];
+    bool done[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
-        off[i] = tid + 64 * NW * i;
-        v[i] = red[off[i]];
+        const int e = tid + 64 * NW * i;
+        int tok, n;
+        locate(e, tok, n);
+        off[i] = tok < a.M && n < n_end ? e : -1;
+        v[i] = red[e];
 #pragma unroll
         for (int w = 1; w < NW; ++w)
-            v[i] += red[w * E + off[i]];
+            v[i] += red[w * E + e];
+        done[i] = off[i] >= 0;
     }
-    // value e: token 16 t + (e % 16), row n_wg + 16 r + 4 ((e / 16) % 4) + q
-    auto store_all = [&](const float(&vals)[EPT]) {
+    if (a.split > 1) {
+        float *wsp = a.ws + (long)tile * (a.split - 1) * E;
+        if constexpr (EPT % 2 == 0) {
+            int pair_off[EPT / 2];             // the thread's pairs, slot p 64 NW + tid
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int e = off[i], ln = e & 63, q = (e >> 6) & 3, rt = e >> 8;
-            const int r = rt / T, t = rt - (rt / T) * T;
-            const int tok = 16 * t + (ln & 15), n = n_wg + 16 * r + 4 * (ln >> 4) + q;
-            if (tok < a.M && n < n_end)
-                store_out(a, tok, n, vals[i]);
+            for (int p = 0; p < EPT / 2; ++p)
+                pair_off[p] = p * 64 * NW + tid;
+            swap_exchange_pairs<EPT>(wsp, E, a.split, s, off, pair_off, v, done);
+        } else {
+            swap_exchange<EPT>(wsp, E, a.split, s, off, v, done);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        if (!done[i])
+            continue;
+        int tok, n;
+        locate(tid + 64 * NW * i, tok, n);
+        store_out(a, tok, n, v[i]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-group stream kernels (MFMA4, DOT2W).  A workgroup owns one equal row
+// range of at most 4 RG rows and one K part (of `split`); its NW waves take
+// every NW-th stage of 16 K chunks, U stages in flight in registers, with
+// nothing shared between waves until their sums are added in LDS at the end.
+// Every wave-wide load is the row-contiguous kind: lane l reads chunk l & 15
+// of the stage from row (or token) l >> 4 of a 4-row group -- four runs of
+// 256 bytes -- so the weight goes HBM -> VGPR -> arithmetic with no LDS.
+//
+// MFMA4 (token groups T of 4 tokens): v_mfma_f32_4x4x4_16b (BF16, or FP16
+// with H) multiplies sixteen independent 4x4x4 blocks: lane 4 b + i gives
+// block b its A row i and its B column i (4 values each) and gets back
+// D_b[0..3][i].  Block b takes chunk b of the stage, A row i is weight row
+// 4 rg + i and B column i token 4 tg + i, so a loaded register becomes an
+// operand pair (its low and high 8 bytes) once lane 4 b + i holds what lane
+// 16 i + b loaded: one ds_bpermute per dword moves it there (the order the
+// operands need, four rows per quad of lanes, loads measurably slower than
+// the row-contiguous order).  Each x register serves all RG row groups.
+// The blocks hold partial sums over different chunks: after the stream they
+// are added by a transposing butterfly over lane bits 5..2.
+//
+// DOT2W (token tile T = 1, 2, 4 or 8): v_dot2_f32_bf16 (v_dot2_f32_f16),
+// lane l multiplies its weight chunk with the same chunk of each token's x,
+// loaded per lane (the four lanes of a chunk read the same 16 bytes, which a
+// load serves once); each x register serves all RG row groups.  After the
+// stream the 16 chunk lanes of a row are added over lane bits 3..0.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// c += a b on 4 BF16 (FP16) values per lane, one 4x4x4 block per 4 lanes
+template <bool H>
+__device__ __forceinline__ f32x4 mma4(unsigned a0, unsigned a1, unsigned b0, unsigned b1, f32x4 c)
+{
+    const u32x2 av = {a0, a1}, bv = {b0, b1};
+    if constexpr (H)
+        return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4, av), __builtin_bit_cast(f16x4, bv), c,
+                                                  0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, av), __builtin_bit_cast(s16x4, bv),
+                                                      c, 0, 0, 0);
+}
+
+// lane 4 b + i takes the 16 bytes lane 16 i + b holds (src_addr = 4 x that lane)
+__device__ __forceinline__ u32x4 to_block_order(u32x4 v, int src_addr)
+{
+    const unsigned v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+    return u32x4{(unsigned)__builtin_amdgcn_ds_bpermute(src_addr, (int)v0),
+                 (unsigned)__builtin_amdgcn_ds_bpermute(src_addr, (int)v1),
+                 (unsigned)__builtin_amdgcn_ds_bpermute(src_addr, (int)v2),
+                 (unsigned)__builtin_amdgcn_ds_bpermute(src_addr, (int)v3)};
+}
+
+// Transposing steps over single lane bits, exact pairings (lane i with
+// i ^ bit): as in wave_reduce_transpose, the lane with the bit clear keeps the
+// first half of its vector and adds its partner's copy of that half.
+//   bit 3: DPP row_ror:8 (lane i and i ^ 8 of a 16-lane row)
+//   bit 2: row_half_mirror (7 - i) then a quad reversal, which brings the
+//          partner back to the same quad position: i ^ 4
+//   bit 1: quad_perm [2,3,0,1]     bit 0: quad_perm [1,0,3,2]
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppQuadReverse = 0x1B;   // quad_perm [3,2,1,0]
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_xor4_read(float x)
+{
+    return dpp_read<kDppQuadReverse>(dpp_read<kDppRowHalfMirror>(x));
+}
+
+template <int V, int BIT>
+__device__ __forceinline__ void step_exact(float *v, int lane)
+{
+    const bool hi = (lane & BIT) != 0;
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+        const float send = hi ? v[i] : v[i + V / 2];
+        const float keep = hi ? v[i + V / 2] : v[i];
+        float got;
+        if constexpr (BIT == 8)
+            got = dpp_read<kDppRowRor8>(send);
+        else if constexpr (BIT == 4)
+            got = dpp_xor4_read<0>(send);
+        else if constexpr (BIT == 2)
+            got = dpp_read<kDppQuadXor2>(send);
+        else
+            got = dpp_read<kDppQuadXor1>(send);
+        v[i] = keep + got;
+    }
+}
+
+constexpr int pow2_at_least(int v, int lo) { return v <= lo ? lo : 2 * pow2_at_least((v + 1) / 2, lo); }
+
+template <bool MFMA, int T, int RG, int U, bool H>
+__global__ __launch_bounds__(256) void k_rgs(KArgs a)
+{
+    constexpr int MT = MFMA ? 4 * T : T;       // token tile
+    constexpr int XL = MFMA ? T : T;           // x loads per stage (token groups / tokens)
+    constexpr int ROWS = 4 * RG;
+    constexpr int V = MFMA ? 4 * RG * T : RG * T;   // sums per lane before the lane reduction
+    constexpr int P = pow2_at_least(V, 16);
+    constexpr int Q = P / 16;                  // per lane after it
+    static_assert(rgs_values_per_lane(MFMA, RG, T) == Q, "host and kernel must agree on the LDS size");
+    extern __shared__ float red[];             // [waves][Q][64]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = blockDim.x >> 6;
+    int tile, s;
+    block_coords(a, tile, s);
+    const int n_wg = tile_row(a, tile), n_end = tile_row(a, tile + 1);
+    const int kb = split_point(a, s, a.K8);
+    const int ke = split_point(a, s + 1, a.K8);
+    const int stages = (ke - kb + 15) >> 4;
+    const int mine = stages > wave ? (stages - wave + nw - 1) / nw : 0;   // stages wave, wave + nw, ...
+    const unsigned row_bytes = a.w_pitch, x_pitch = a.x_pitch;
+    const int rows_valid = uniform_int(max(0, min(ROWS, n_end - n_wg)));
+    const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n_wg : 0) * row_bytes,
+                                (unsigned)rows_valid * row_bytes);
+    const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
+    const int r4 = lane >> 4, c16 = lane & 15;
+    const int perm_src = 4 * (16 * (lane & 3) + (lane >> 2));   // lane 4 b + i <- lane 16 i + b
+
+    f32x4 macc[MFMA ? RG : 1][MFMA ? T : 1];
+    float dacc[MFMA ? 1 : RG][MFMA ? 1 : MT];
+    if constexpr (MFMA) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                macc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                dacc[r][m] = 0.f;
+    }
+
+    // this lane's chunk of the wave's j-th stage; past the wave's last stage,
+    // or past the end of its K part, the load is out of range (no memory read)
+    auto load = [&](u32x4(&wv)[RG], u32x4(&xv)[XL], int j) {
+        const int c = kb + (wave + nw * j) * 16 + c16;
+        const bool ok = j < mine && c < ke;
+        const unsigned co = (unsigned)c * 16u;
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+            wv[r] = load_w(wres, lane_off(ok, (unsigned)(4 * r + r4) * row_bytes + co), 0);
+#pragma unroll
+        for (int t = 0; t < XL; ++t)
+            xv[t] = load_x(xres, lane_off(ok, (unsigned)(MFMA ? 4 * t + r4 : t) * x_pitch + co), 0);
+        __builtin_amdgcn_sched_barrier(0);   // loads stay ahead of the arithmetic
+    };
+    auto compute = [&](const u32x4(&wv)[RG], const u32x4(&xv)[XL]) {
+        if constexpr (MFMA) {
+            u32x4 xb[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                xb[t] = to_block_order(xv[t], perm_src);
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const u32x4 wb = to_block_order(wv[r], perm_src);
+                const unsigned w0 = wb.x, w1 = wb.y, w2 = wb.z, w3 = wb.w;
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const unsigned x0 = xb[t].x, x1 = xb[t].y, x2 = xb[t].z, x3 = xb[t].w;
+                    macc[r][t] = mma4<H>(w0, w1, x0, x1, macc[r][t]);
+                    macc[r][t] = mma4<H>(w2, w3, x2, x3, macc[r][t]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    dacc[r][m] = dot8<H>(wv[r], xv[m], dacc[r][m]);
         }
     };
-    if (a.split == 1) {
-        store_all(v);
-        return;
-    }
-    float *wsp = a.ws + (long)tile * a.split * E;
+
+    // U stages in flight; every pass issues all of its loads (past the wave's
+    // last stage they read nothing), so the waits stay partial.
+    u32x4 wbuf[U][RG], xbuf[U][XL];
 #pragma unroll
-    for (int i = 0; i < EPT; ++i)
-        publish_partial(wsp + (long)s * E + off[i], v[i]);
-    if (!split_arrive_last(a, tile, &flag))
-        return;
-    float sum[EPT];
-    sum_partials<EPT>(wsp, E, a.split, off, sum);
-    store_all(sum);
-    split_reset(a, tile);
+    for (int u = 0; u < U; ++u)
+        load(wbuf[u], xbuf[u], u);
+    for (int j = 0; j < mine; j += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (j + u < mine)
+                compute(wbuf[u], xbuf[u]);
+            load(wbuf[u], xbuf[u], j + u + U);
+        }
+    }
+
+    // Lane reduction.  MFMA4: lane bits 5..2 index the block, bits 1..0 the
+    // token column; value index (rg T + tg) 4 + row.  DOT2W: lane bits 3..0
+    // index the chunk, bits 5..4 the row within a group; value index rg MT + m.
+    // Afterwards lane l holds, for q < Q, value (seg Q + q) summed over the
+    // reduced lanes, seg = (l >> 2) & 15 (MFMA4) or l & 15 (DOT2W).
+    float v[P];
+    if constexpr (MFMA) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    v[(r * T + t) * 4 + q] = macc[r][t][q];
+    } else {
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                v[r * MT + m] = dacc[r][m];
+    }
+#pragma unroll
+    for (int i = V; i < P; ++i)
+        v[i] = 0.f;
+    if constexpr (MFMA) {
+        step_swap32<P>(v);
+        step_swap16<P / 2>(v);
+        step_exact<P / 4, 8>(v, lane);
+        step_exact<P / 8, 4>(v, lane);
+    } else {
+        step_exact<P, 8>(v, lane);
+        step_exact<P / 2, 4>(v, lane);
+        step_exact<P / 4, 2>(v, lane);
+        step_exact<P / 8, 1>(v, lane);
+    }
+
+    // the waves' sums, added in LDS in wave order
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        red[(wave * Q + q) * 64 + lane] = v[q];
+    __syncthreads();
+    // value e of the workgroup: lane e & 63, q = e >> 6 -> (token, row) or none
+    auto locate = [&](int e, int &tok, int &row) {
+        const int ln = e & 63, q = e >> 6;
+        if constexpr (MFMA) {
+            const int idx = ((ln >> 2) & 15) * Q + q, rt = idx >> 2;
+            tok = 4 * (rt % T) + (ln & 3);
+            row = n_wg + 4 * (rt / T) + (idx & 3);
+            return idx < V;
+        } else {
+            const int idx = (ln & 15) * Q + q;
+            tok = idx % MT;
+            row = n_wg + 4 * (idx / MT) + (ln >> 4);
+            return idx < V;
+        }
+    };
+    float sum[Q];
+    int off[Q];
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        const int e = tid + 64 * nw * i;
+        off[i] = -1;
+        sum[i] = 0.f;
+        int tok, row;
+        if (e >= Q * 64 || !locate(e, tok, row) || row >= n_end || tok >= a.M)
+            continue;
+        off[i] = e;
+        const int ln = e & 63, q = e >> 6;
+        float t = red[q * 64 + ln];
+        for (int w = 1; w < nw; ++w)
+            t += red[(w * Q + q) * 64 + ln];
+        sum[i] = t;
+    }
+    bool ok[Q];
+    if (a.split == 1) {
+#pragma unroll
+        for (int i = 0; i < Q; ++i)
+            ok[i] = off[i] >= 0;
+    } else {
+        swap_exchange<Q>(a.ws + (long)tile * (a.split - 1) * (Q * 64), Q * 64, a.split, s, off, sum, ok);
+    }
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        if (!ok[i])
+            continue;
+        int tok, row;
+        locate(off[i], tok, row);
+        store_out(a, tok, row, sum[i]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1920,15 +1486,15 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
         {PATH, MT, ROWS, U, 1, (const void *)&KERNEL<__VA_ARGS__, true>}
 #define SK_DOT2(MT, R, U) SK_PAIR(SKINNY_PATH_DOT2, MT, R, U, k_dot2, MT, R, U)
 #define SK_MFMA(T, RT, U) SK_PAIR(SKINNY_PATH_MFMA, 16 * T, 16 * RT, U, k_mfma, T, RT, U)
-#define SK_DOT2X(MT, R, U) SK_PAIR(SKINNY_PATH_DOT2X, MT, R, U, k_dot2x, MT, R, U)
 #define SK_MFMAX(T, NW) SK_PAIR(SKINNY_PATH_MFMAX, 16 * T, NW, 1, k_mfmax, T, NW)
-#define SK_MFMAD(T, NW, D) SK_PAIR(SKINNY_PATH_MFMAD, 16 * T, NW, D, k_mfmad, T, NW, D)
-#define SK_MFMAS(T, NW, D) SK_PAIR(SKINNY_PATH_MFMAS, 16 * T, NW, D, k_mfmas, T, NW, D)
-// MFMAK: rows field = 100 * KS + RT (row groups and K groups), unroll = iterations in flight
-#define SK_MFMAK(T, RT, KS, U) SK_PAIR(SKINNY_PATH_MFMAK, 16 * T, 100 * KS + RT, U, k_mfmak, T, RT, KS, U)
 // MFMAW: rows field = 100 * NW + RG (waves and row groups), unroll = stage
 // width in 8-chunk units (1: 8 chunks, 2: 16)
 #define SK_MFMAW(T, RG, NW, U) SK_PAIR(SKINNY_PATH_MFMAW, 16 * T, 100 * NW + RG, U, k_mfmaw, T, RG, NW, 8 * U)
+// Row-group stream kernels, waves at run time: rows field = 4 RG (the most rows
+// of a range), unroll field = stages in flight.  MFMA4: token tile 4 TG.
+// DOT2W: token tile MT.
+#define SK_MFMA4(TG, RG, U) SK_PAIR(SKINNY_PATH_MFMA4, 4 * TG, 4 * RG, U, k_rgs, true, TG, RG, U)
+#define SK_DOT2W(MT, RG, U) SK_PAIR(SKINNY_PATH_DOT2W, MT, 4 * RG, U, k_rgs, false, MT, RG, U)
 
 // Instances whose double-buffered loads, accumulators and offsets fit in 256
 // VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
@@ -1957,30 +1523,26 @@ static const KernelInfo kKernels[] = {
     SK_MFMA(2, 4, 1), SK_MFMA(2, 4, 2),
     SK_MFMA(4, 1, 1), SK_MFMA(4, 1, 2),
     SK_MFMA(4, 2, 1), SK_MFMA(4, 2, 2),
-    // DOT2X: rows field = rows per wave
-    SK_DOT2X(1, 1, 2), SK_DOT2X(1, 1, 4), SK_DOT2X(1, 2, 2), SK_DOT2X(1, 2, 4), SK_DOT2X(1, 4, 2),
-    SK_DOT2X(2, 1, 2), SK_DOT2X(2, 1, 4), SK_DOT2X(2, 2, 2), SK_DOT2X(2, 2, 4), SK_DOT2X(2, 4, 2),
-    SK_DOT2X(4, 1, 2), SK_DOT2X(4, 1, 4), SK_DOT2X(4, 2, 2), SK_DOT2X(4, 2, 4), SK_DOT2X(4, 4, 2),
-    SK_DOT2X(8, 1, 2), SK_DOT2X(8, 1, 4), SK_DOT2X(8, 2, 2), SK_DOT2X(8, 2, 4), SK_DOT2X(8, 4, 2),
     // MFMAX: rows field = waves (16 rows each)
     SK_MFMAX(1, 1), SK_MFMAX(1, 2), SK_MFMAX(1, 4), SK_MFMAX(1, 8),
     SK_MFMAX(2, 2), SK_MFMAX(2, 4), SK_MFMAX(2, 8),
     SK_MFMAX(4, 4), SK_MFMAX(4, 8),
-    // MFMAD: rows field = waves (16 rows each), unroll field = pipeline depth
-    SK_MFMAD(1, 2, 4), SK_MFMAD(1, 4, 3), SK_MFMAD(1, 8, 2),
-    SK_MFMAD(2, 2, 4), SK_MFMAD(2, 4, 2), SK_MFMAD(2, 4, 3),
-    SK_MFMAD(4, 2, 3), SK_MFMAD(4, 4, 2),
-    // MFMAS: rows field = waves, unroll field = pipeline depth; stream-K grid
-    SK_MFMAS(1, 2, 3), SK_MFMAS(1, 4, 2), SK_MFMAS(1, 4, 3), SK_MFMAS(1, 4, 4), SK_MFMAS(1, 8, 2),
-    SK_MFMAS(2, 4, 2), SK_MFMAS(2, 4, 3), SK_MFMAS(2, 8, 2),
-    SK_MFMAK(1, 1, 4, 2), SK_MFMAK(1, 2, 2, 2), SK_MFMAK(1, 2, 2, 3), SK_MFMAK(1, 2, 4, 2), SK_MFMAK(1, 2, 4, 3),
-    SK_MFMAK(2, 2, 2, 2),
     SK_MFMAW(1, 1, 4, 2), SK_MFMAW(1, 2, 1, 2), SK_MFMAW(1, 2, 2, 2), SK_MFMAW(1, 2, 4, 2), SK_MFMAW(1, 4, 4, 2),
     SK_MFMAW(2, 1, 4, 2), SK_MFMAW(2, 2, 1, 2), SK_MFMAW(2, 2, 2, 2), SK_MFMAW(2, 2, 4, 2), SK_MFMAW(2, 2, 8, 2),
     SK_MFMAW(2, 4, 4, 2), SK_MFMAW(4, 1, 4, 2), SK_MFMAW(4, 2, 2, 2), SK_MFMAW(4, 2, 4, 2),
     SK_MFMAW(1, 1, 4, 1), SK_MFMAW(1, 2, 2, 1), SK_MFMAW(1, 2, 4, 1), SK_MFMAW(1, 2, 8, 1), SK_MFMAW(1, 4, 4, 1),
     SK_MFMAW(2, 2, 2, 1), SK_MFMAW(2, 2, 4, 1), SK_MFMAW(2, 2, 8, 1), SK_MFMAW(2, 4, 4, 1),
     SK_MFMAW(4, 2, 2, 1), SK_MFMAW(4, 2, 4, 1),
+#define SK_RGS_ROWS(X, T, U) X(T, 1, U), X(T, 2, U), X(T, 4, U), X(T, 7, U), X(T, 13, U), X(T, 14, U)
+    SK_RGS_ROWS(SK_MFMA4, 1, 2), SK_RGS_ROWS(SK_MFMA4, 2, 2), SK_RGS_ROWS(SK_MFMA4, 4, 2),
+    SK_RGS_ROWS(SK_MFMA4, 1, 3), SK_RGS_ROWS(SK_MFMA4, 2, 3), SK_RGS_ROWS(SK_MFMA4, 4, 3),
+    SK_MFMA4(8, 1, 2), SK_MFMA4(8, 2, 2), SK_MFMA4(8, 4, 2), SK_MFMA4(8, 7, 2),
+    SK_MFMA4(8, 1, 3), SK_MFMA4(8, 2, 3), SK_MFMA4(8, 4, 3), SK_MFMA4(8, 7, 3),
+    SK_RGS_ROWS(SK_DOT2W, 1, 2), SK_RGS_ROWS(SK_DOT2W, 2, 2), SK_RGS_ROWS(SK_DOT2W, 4, 2),
+    SK_RGS_ROWS(SK_DOT2W, 1, 3), SK_RGS_ROWS(SK_DOT2W, 2, 3), SK_RGS_ROWS(SK_DOT2W, 4, 3),
+    // 8 tokens x 13 or 14 row groups would not fit the 256 VGPRs dot2 operands live in
+    SK_DOT2W(8, 1, 2), SK_DOT2W(8, 2, 2), SK_DOT2W(8, 4, 2), SK_DOT2W(8, 7, 2),
+    SK_DOT2W(8, 1, 3), SK_DOT2W(8, 2, 3), SK_DOT2W(8, 4, 3), SK_DOT2W(8, 7, 3),
 };
 
 const KernelInfo *kernel_table(int *count)

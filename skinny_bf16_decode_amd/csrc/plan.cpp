@@ -35,7 +35,6 @@ struct Entry {
     int n_tiles = 0;
     FastDiv fd_tiles{}, fd_split{};  // see KArgs
     unsigned rows_q = 0, rows_r = 0;
-    int sk_spt = 0, sk_parts = 0;   // stream-K: stages per tile, partial slots per tile
     skinny_tactic t{};
 };
 
@@ -48,8 +47,7 @@ struct skinny_plan {
     int ldw = 0;                     // W row pitch, elements
     int half = 0;                    // 1: FP16 inputs
     skinny_out_dtype od = SKINNY_OUT_BF16;
-    float *ws = nullptr;
-    unsigned *ctr = nullptr;
+    float *ws = nullptr;             // split-K exchange nodes (kSlotEmptyBits between launches)
     KArgs base{};
     Entry e[SKINNY_MAX_M + 1];
 };
@@ -94,60 +92,21 @@ int device_cus()
     return cus;
 }
 
-// Stream-K grid and partial slots.  MFMAS: split workgroups per CU, or as
-// many as fit on a CU at once if fewer; MFMAR: one workgroup per (tile, K
-// split).  Either way at most one per unit, and for each tile the number of
-// workgroups whose unit range meets it -- the same owner formula the kernel
-// uses.
-void stream_k_shape(Entry &en, int K)
-{
-    const unsigned spt = (unsigned)((K / 8 + kMfmaxChunks - 1) / kMfmaxChunks);
-    const unsigned units = (unsigned)en.n_tiles * spt;
-    unsigned G;
-    if (en.t.path == SKINNY_PATH_MFMAR) {
-        G = (unsigned)en.n_tiles * (unsigned)en.t.split;
-    } else {
-        int per_cu = 0;
-        if (!en.fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, en.fn, (int)en.block, en.lds) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        (void)hipGetLastError();
-        G = (unsigned)(std::min(per_cu, en.t.split) * device_cus());
-    }
-    if (G > units)
-        G = units;
-    auto owner = [&](unsigned u) { return (int)((((unsigned long long)u + 1) * G - 1) / units); };
-    int parts = 1;
-    for (int t = 0; t < en.n_tiles; ++t)
-        parts = std::max(parts, owner((unsigned)(t + 1) * spt - 1) - owner((unsigned)t * spt) + 1);
-    en.grid = G;
-    en.sk_spt = (int)spt;
-    en.sk_parts = parts;
-}
-
 Entry make_entry(const skinny_tactic &t, int N, int K, int half)
 {
     Entry en;
     const KernelInfo *k = tactic_kernel(t, half);
     en.fn = k ? k->fn : nullptr;
     en.n_tiles = tiles_for(t, N);
-    if (t.path == SKINNY_PATH_MFMAR) {
-        // equal row ranges, at least as many (x split) as there are CUs
-        const int want = (device_cus() + t.split - 1) / t.split;
-        en.n_tiles = std::min(N, std::max(en.n_tiles, want));
-    } else if ((t.path == SKINNY_PATH_MFMAX && t.unroll == 2) || t.path == SKINNY_PATH_DOT2R ||
-               t.path == SKINNY_PATH_MFMAW) {
+    if ((t.path == SKINNY_PATH_MFMAX && t.unroll == 2) || t.path == SKINNY_PATH_DOT2R ||
+        t.path == SKINNY_PATH_MFMAW || is_rgs_path(t.path)) {
         // equal row ranges, a whole multiple of CUs / split of them, so that
         // every CU gets the same number of (range, K part) workgroups
         const int per_round = (device_cus() + t.split - 1) / t.split;
         const int rounds = (en.n_tiles + per_round - 1) / per_round;
         en.n_tiles = std::min(N, rounds * per_round);
-    } else if (t.path == SKINNY_PATH_MFMAK) {
-        // equal row ranges, split per CU; K stays inside the workgroup
-        en.n_tiles = std::min(N, std::max(en.n_tiles, device_cus() * t.split));
-        en.grid = (unsigned)en.n_tiles;
     }
-    en.grid = t.path == SKINNY_PATH_MFMAK ? (unsigned)en.n_tiles : (unsigned)(en.n_tiles * t.split);
+    en.grid = (unsigned)(en.n_tiles * t.split);
     en.block = (unsigned)(64 * t.waves);
     en.lds = (unsigned)tactic_lds_bytes(t, K / 8);
     en.t = t;
@@ -155,8 +114,6 @@ Entry make_entry(const skinny_tactic &t, int N, int K, int half)
     en.fd_split = make_fastdiv((uint32_t)t.split);
     en.rows_q = (unsigned)(N / en.n_tiles);
     en.rows_r = (unsigned)(N % en.n_tiles);
-    if (t.path == SKINNY_PATH_MFMAS || t.path == SKINNY_PATH_MFMAR)
-        stream_k_shape(en, K);
     return en;
 }
 
@@ -174,28 +131,17 @@ void raise_lds_limits()
         int nk = 0;
         const KernelInfo *ks = kernel_table(&nk);
         for (int i = 0; i < nk; ++i)
-            if (ks[i].path == SKINNY_PATH_DOT2X || ks[i].path == SKINNY_PATH_MFMAX ||
-                ks[i].path == SKINNY_PATH_MFMAD || ks[i].path == SKINNY_PATH_MFMAS ||
-                ks[i].path == SKINNY_PATH_MFMAK || ks[i].path == SKINNY_PATH_MFMAW)
+            if (ks[i].path == SKINNY_PATH_MFMAX || ks[i].path == SKINNY_PATH_MFMAW || is_rgs_path(ks[i].path))
                 (void)hipFuncSetAttribute(ks[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
         (void)hipGetLastError();
     });
 }
 
+// Floats of split-K exchange nodes a table entry needs: split - 1 nodes of
+// one tile's values per row tile (see swap_exchange in the kernels).
 size_t ws_floats(const Entry &en)
 {
-    if (en.t.path == SKINNY_PATH_MFMAS || en.t.path == SKINNY_PATH_MFMAR)
-        return en.sk_parts > 1 ? (size_t)en.n_tiles * en.sk_parts * en.t.mt * en.t.rows : 0;
-    if (en.t.path == SKINNY_PATH_MFMAK)
-        return 0;
-    return en.t.split > 1 ? (size_t)en.n_tiles * en.t.split * en.t.mt * en.t.rows : 0;
-}
-
-bool uses_counters(const Entry &en)
-{
-    if (en.t.path == SKINNY_PATH_MFMAS || en.t.path == SKINNY_PATH_MFMAR)
-        return en.sk_parts > 1;
-    return en.t.split > 1 && en.t.path != SKINNY_PATH_MFMAK;
+    return en.t.split > 1 ? (size_t)en.n_tiles * (en.t.split - 1) * tile_values(en.t) : 0;
 }
 
 // Static LDS of a kernel plus the device's per-workgroup limit, looked up
@@ -227,10 +173,8 @@ hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
     a.n_tiles = en.n_tiles;
     a.split = en.t.split;
     a.remap = (en.t.split > 1 && a.nxcd > 1) ? 1 : 0;
-    a.sk_spt = en.sk_spt;
-    a.sk_parts = en.sk_parts;
     a.ranges = (en.t.path == SKINNY_PATH_MFMAX && en.t.unroll == 2) || en.t.path == SKINNY_PATH_DOT2R ||
-               en.t.path == SKINNY_PATH_MFMAW;
+               en.t.path == SKINNY_PATH_MFMAW || is_rgs_path(en.t.path);
     const int nx = a.nxcd > 1 ? a.nxcd : 1;
     a.fd_tiles = en.fd_tiles;
     a.fd_split = en.fd_split;
@@ -277,8 +221,10 @@ skinny_status check_prepare_args(const void *W, int N, int K, int ldw, int in_dt
         set_error("ldw=%d must be >= K=%d and a multiple of 8 (a 16-byte row pitch)", ldw, K);
         return SKINNY_ERR_SHAPE;
     }
-    if ((long long)ldw * 16 * 2 >= (1LL << 31)) {
-        set_error("ldw=%d: 16 rows of W must span less than 2 GiB", ldw);
+    // every kernel builds its W buffer resource over at most kMaxTileRows rows
+    // and marks a skipped load with the offset kOffOob, which must lie past it
+    if ((long long)ldw * 2 * kMaxTileRows >= (long long)kOffOob) {
+        set_error("ldw=%d: %d rows of W must span less than %u bytes", ldw, kMaxTileRows, kOffOob);
         return SKINNY_ERR_SHAPE;
     }
     if ((long long)N * K >= (1LL << 31)) {
@@ -323,29 +269,26 @@ struct DevBuf {
 skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int nxcd,
                    std::array<skinny_tactic, SKINNY_MAX_M> &table)
 {
-    const int count = skinny_enumerate_tactics(N, K, nullptr, 0);
+    const int cus = device_cus();
+    const int count = skinny_enumerate_tactics_ex(N, K, cus, nullptr, 0);
     if (count <= 0) {
         set_error("no candidate tactics for N=%d K=%d", N, K);
         return SKINNY_ERR_SHAPE;
     }
     std::vector<skinny_tactic> cand(count);
-    skinny_enumerate_tactics(N, K, cand.data(), count);
+    skinny_enumerate_tactics_ex(N, K, cus, cand.data(), count);
 
     const size_t wbytes = (size_t)N * K * 2;
     const size_t cold = (size_t)768 << 20;   // well past the 256 MiB Infinity Cache
     int copies = (int)std::min<size_t>(16, std::max<size_t>(1, (cold + wbytes - 1) / wbytes));
-    size_t max_ws = 0, max_tiles = 0;
-    for (const skinny_tactic &t : cand) {
-        Entry en = make_entry(t, N, K, half);
-        max_ws = std::max(max_ws, ws_floats(en));
-        max_tiles = std::max(max_tiles, (size_t)en.n_tiles);
-    }
-    DevBuf wcopies, xbuf, obuf, wsbuf, ctrbuf;
+    size_t max_ws = 0;
+    for (const skinny_tactic &t : cand)
+        max_ws = std::max(max_ws, ws_floats(make_entry(t, N, K, half)));
+    DevBuf wcopies, xbuf, obuf, wsbuf;
     HIP_TRY(hipMalloc(&wcopies.p, wbytes * copies));
     HIP_TRY(hipMalloc(&xbuf.p, (size_t)SKINNY_MAX_M * K * 2));
     HIP_TRY(hipMalloc(&obuf.p, (size_t)SKINNY_MAX_M * N * 4));
     HIP_TRY(hipMalloc(&wsbuf.p, std::max<size_t>(max_ws, 1) * 4));
-    HIP_TRY(hipMalloc(&ctrbuf.p, std::max<size_t>(max_tiles, 1) * 4));
     hipStream_t st;
     HIP_TRY(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
     struct StreamGuard {
@@ -357,7 +300,6 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
         HIP_TRY(hipMemcpy2DAsync((char *)wcopies.p + wbytes * c, (size_t)K * 2, W, (size_t)ldw * 2, (size_t)K * 2, N,
                                  hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemsetAsync(xbuf.p, 0, (size_t)SKINNY_MAX_M * K * 2, st));
-    HIP_TRY(hipMemsetAsync(ctrbuf.p, 0, std::max<size_t>(max_tiles, 1) * 4, st));
     HIP_TRY(hipMemsetD32Async((hipDeviceptr_t)wsbuf.p, (int)kSlotEmptyBits, std::max<size_t>(max_ws, 1), st));
     hipEvent_t e0, e1;
     HIP_TRY(hipEventCreate(&e0));
@@ -375,7 +317,6 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     a.x = xbuf.p;
     a.out = obuf.p;
     a.ws = (float *)wsbuf.p;
-    a.ctr = (unsigned *)ctrbuf.p;
     a.N = N;
     a.K8 = K / 8;
     a.out_f32 = od == SKINNY_OUT_F32;
@@ -613,7 +554,7 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
     p->ldw = ldw;
     p->half = half;
     p->od = od;
-    size_t max_ws = 0, max_tiles = 0;
+    size_t max_ws = 0;
     for (int m = 1; m <= SKINNY_MAX_M; ++m) {
         p->e[m] = make_entry(table[m - 1], N, K, half);
         if (!p->e[m].fn || !lds_fits(p->e[m].fn, p->e[m].lds)) {
@@ -623,8 +564,6 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
             return SKINNY_ERR_INVALID_ARG;
         }
         max_ws = std::max(max_ws, ws_floats(p->e[m]));
-        if (uses_counters(p->e[m]))
-            max_tiles = std::max(max_tiles, (size_t)p->e[m].n_tiles);
     }
     auto fail = [&](skinny_status s) {
         skinny_destroy(p);
@@ -636,14 +575,6 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
             hip_fail(e, "hipMalloc(split-K workspace)");
             return fail(e == hipErrorOutOfMemory ? SKINNY_ERR_NOMEM : SKINNY_ERR_HIP);
         }
-        if ((e = hipMalloc(&p->ctr, max_tiles * 4)) != hipSuccess) {
-            hip_fail(e, "hipMalloc(split-K counters)");
-            return fail(e == hipErrorOutOfMemory ? SKINNY_ERR_NOMEM : SKINNY_ERR_HIP);
-        }
-        if ((e = hipMemset(p->ctr, 0, max_tiles * 4)) != hipSuccess) {
-            hip_fail(e, "hipMemset(split-K counters)");
-            return fail(SKINNY_ERR_HIP);
-        }
         if ((e = hipMemsetD32((hipDeviceptr_t)p->ws, (int)kSlotEmptyBits, max_ws)) != hipSuccess) {
             hip_fail(e, "hipMemsetD32(split-K workspace)");
             return fail(SKINNY_ERR_HIP);
@@ -652,7 +583,6 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
     KArgs &a = p->base;
     a.W = W;
     a.ws = p->ws;
-    a.ctr = p->ctr;
     a.N = N;
     a.K8 = K / 8;
     a.out_f32 = od == SKINNY_OUT_F32;
@@ -803,8 +733,8 @@ skinny_status skinny_run_ex(const skinny_plan *p, const void *x, int ldx, const 
         return SKINNY_ERR_SHAPE;
     }
     const size_t osz = p->od == SKINNY_OUT_F32 ? 4 : 2;
-    if ((long long)ldx * (SKINNY_MAX_M * 2) >= (1LL << 31)) {
-        set_error("ldx=%d: 64 rows of x must span less than 2 GiB", ldx);
+    if ((long long)ldx * (SKINNY_MAX_M * 2) >= (long long)kOffOob) {
+        set_error("ldx=%d: %d rows of x must span less than %u bytes", ldx, SKINNY_MAX_M, kOffOob);
         return SKINNY_ERR_SHAPE;
     }
     if (((uintptr_t)x & 15) || ((uintptr_t)out & (osz - 1)) || ((uintptr_t)residual & (osz - 1))) {
@@ -872,9 +802,9 @@ skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len
     const Entry &en = p->e[M];
     static const char *const kNames[] = {"dot2", "mfma16x16x32", "dot2x", "mfmax16x16x32", "mfmad16x16x32",
                                          "mfmas16x16x32", "mfmar16x16x32", "mfmak16x16x32", "dot2r",
-                                         "mfmaw16x16x32"};
+                                         "mfmaw16x16x32", "mfma4x4x4", "dot2w"};
     snprintf(buf, len, "%s mt=%d rows=%d waves=%d unroll=%d split=%d grid=%u block=%u lds=%u",
-             (t.path >= 0 && t.path <= 9) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
+             (t.path >= 0 && t.path <= 11) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
              en.grid, en.block, en.lds);
     return SKINNY_OK;
 }
@@ -883,16 +813,13 @@ void skinny_destroy(skinny_plan *p)
 {
     if (!p)
         return;
-    if (p->ws || p->ctr) {
+    if (p->ws) {
         int cur = -1;
         (void)hipGetDevice(&cur);
         if (cur != p->device)
             (void)hipSetDevice(p->device);
         (void)hipDeviceSynchronize();
-        if (p->ws)
-            (void)hipFree(p->ws);
-        if (p->ctr)
-            (void)hipFree(p->ctr);
+        (void)hipFree(p->ws);
         if (cur != p->device && cur >= 0)
             (void)hipSetDevice(cur);
     }

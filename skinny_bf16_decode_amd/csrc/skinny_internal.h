@@ -48,8 +48,7 @@ struct KArgs {
     const void *x;      // [M] rows of K8 chunks, x_pitch bytes apart
     void *out;          // [M][ldo] BF16 or fp32
     const void *res;    // [M][ldr], the out type, added before the store; or NULL
-    float *ws;          // split-K partials, [tile][split][mt][rows]
-    unsigned *ctr;      // split-K arrival counters, one per row tile
+    float *ws;          // split-K exchange nodes, [tile][split - 1][values of a tile]
     int N;
     int K8;
     int M;
@@ -58,11 +57,7 @@ struct KArgs {
     int out_f32;        // 1: fp32 output, 0: BF16
     int nxcd;           // XCDs the dispatcher deals workgroups over
     int remap;          // 1: place the split-K workgroups of a tile on one XCD
-    // stream-K schedule (MFMAS): units = n_tiles * sk_spt stages of 32 chunks,
-    // dealt evenly over gridDim.x workgroups; sk_parts partial slots per tile
-    int sk_spt;
-    int sk_parts;
-    int ranges;         // MFMAX: row tile t is [t N / n_tiles, (t + 1) N / n_tiles)
+    int ranges;         // row tile t is [t N / n_tiles, (t + 1) N / n_tiles)
     unsigned w_pitch;   // bytes between rows of W (multiple of 16)
     unsigned x_pitch;   // bytes between rows of x (multiple of 16)
     int ldo;            // elements between rows of out
@@ -89,8 +84,9 @@ const KernelInfo *kernel_table(int *count);
 const KernelInfo *find_kernel(int path, int mt, int rows, int unroll, int half);
 
 // The compiled instance a tactic runs for BF16 (half = 0) or FP16 inputs
-// (KernelInfo.rows is rows per workgroup for DOT2/MFMA, rows per wave for
-// DOT2X, waves for MFMAX/MFMAD/MFMAS), or nullptr.  Every instance exists for
+// (KernelInfo.rows is rows per workgroup for DOT2/MFMA, waves for MFMAX,
+// 100 waves + row groups for MFMAW, the most rows of a range for MFMA4 and
+// DOT2W), or nullptr.  Every instance exists for
 // both input types, so a tactic's legality does not depend on it.
 const KernelInfo *tactic_kernel(const skinny_tactic &t, int half = 0);
 
@@ -109,19 +105,24 @@ void set_error(const char *fmt, ...);
 inline int tiles_for(const skinny_tactic &t, int N) { return (N + t.rows - 1) / t.rows; }
 
 constexpr int kMaxWaves = 8;
-// Bits of an empty split-K workspace slot (a signalling NaN no arithmetic
+// A buffer load whose offset is at or past its resource's size reads zero and
+// touches no memory; kernels pass this offset for a load they skip, so every
+// resource (at most kMaxTileRows rows of W, SKINNY_MAX_M rows of x) must be
+// smaller than it.
+constexpr unsigned kOffOob = 0x7FFFFFF0u;
+constexpr int kMaxTileRows = 64;
+// Bits of an empty split-K exchange node (a signalling NaN no arithmetic
 // produces); the workspace is filled with it when allocated, and every
 // launch leaves it so.
 constexpr unsigned kSlotEmptyBits = 0x7FB55AA5u;
 constexpr size_t kMaxLds = 60 * 1024;          // in-WG split-K paths (DOT2, MFMA)
-// LDS-staged paths (DOT2X, MFMAX, MFMAD) may use a CU's whole 160 KiB, less a
+// LDS-staged paths (MFMAX, MFMAW) may use a CU's whole 160 KiB, less a
 // reserve for the kernels' own static __shared__ variables: a dispatch whose
 // static + dynamic LDS exceeds the device limit is not rejected at launch but
 // aborts the queue.  Launches are also checked against the exact static size.
 constexpr size_t kStaticLdsReserve = 1024;
 constexpr size_t kMaxLdsStaged = 160 * 1024 - kStaticLdsReserve;
 constexpr int kMfmaxChunks = 32;               // K chunks per MFMAX stage
-inline size_t mfmax_lds_bytes(int waves, int mt) { return (size_t)(16 * waves + 2 * mt) * (kMfmaxChunks + 2) * 16; }
 // MFMAX proper keeps 2 PB x windows, for a barrier per PB stages: PB = 2 for
 // token tiles up to 32, 1 for 64 (a barrier per 4 stages measured slower at
 // the 16-token tile: 17.6 against 16.3 us on 6288x7168)
@@ -130,8 +131,6 @@ inline size_t mfmax_own_lds_bytes(int waves, int mt)
 {
     return (size_t)(16 * waves + mfmax_x_windows(mt) * mt) * (kMfmaxChunks + 2) * 16;
 }
-// MFMAD: per wave `depth` weight slots of 16 rows x 32 chunks, plus `depth` x slots of mt x 32 chunks
-inline size_t mfmad_lds_bytes(int waves, int mt, int depth) { return (size_t)depth * (16 * waves + mt) * 32 * 16; }
 // MFMAW: stages of 8 unroll chunks (8 or 16); wave tiles [waves][rows + mt]
 // [stage + 2 chunks], which the waves' partial sums reuse at the end
 inline int mfmaw_stage_chunks(int unroll) { return 8 * unroll; }
@@ -139,10 +138,38 @@ inline size_t mfmaw_lds_bytes(int waves, int rows, int mt, int unroll)
 {
     return (size_t)waves * (rows + mt) * (mfmaw_stage_chunks(unroll) + 2) * 16;
 }
-// MFMAK: wave tiles [waves][16][34] and two x windows [mt][32 ks + 2]
-inline size_t mfmak_lds_bytes(int waves, int mt, int ks)
+// Row-group stream kernels (MFMA4, DOT2W): each lane ends with Q = max(16, V
+// rounded up to a power of two) / 16 sums, V = 4 RG T (MFMA4, T token groups)
+// or RG T (DOT2W, T tokens), added over the waves in LDS [waves][Q][64]
+constexpr int rgs_values_per_lane(bool mfma, int rg, int t)
 {
-    return ((size_t)waves * 16 * (kMfmaxChunks + 2) + 2 * (size_t)mt * (kMfmaxChunks * ks + 2)) * 16;
+    int p = 16;
+    while (p < (mfma ? 4 : 1) * rg * t)
+        p *= 2;
+    return p / 16;
+}
+inline int rgs_q(const skinny_tactic &t)
+{
+    const bool mfma = t.path == SKINNY_PATH_MFMA4;
+    return rgs_values_per_lane(mfma, t.rows / 4, mfma ? t.mt / 4 : t.mt);
+}
+inline size_t rgs_lds_bytes(const skinny_tactic &t) { return (size_t)t.waves * rgs_q(t) * 64 * sizeof(float); }
+// exchange nodes per tile: split - 1 of Q * 64 values
+inline size_t rgs_node_floats(const skinny_tactic &t) { return (size_t)rgs_q(t) * 64; }
+// K chunks per row-group stream stage (one per block of the 16-block MFMA)
+constexpr int kRgsChunks = 16;
+inline bool is_rgs_path(int path) { return path == SKINNY_PATH_MFMA4 || path == SKINNY_PATH_DOT2W; }
+// Kernel families measured and removed (their path numbers stay reserved, so a
+// stored table that names one is refused, not misread).
+inline bool is_retired_path(int path)
+{
+    return path == SKINNY_PATH_DOT2X || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAS ||
+           path == SKINNY_PATH_MFMAR || path == SKINNY_PATH_MFMAK;
+}
+// Values of one row tile's partial, the size of one exchange node
+inline size_t tile_values(const skinny_tactic &t)
+{
+    return is_rgs_path(t.path) ? rgs_node_floats(t) : (size_t)t.mt * t.rows;
 }
 
 }  // namespace skinny

@@ -2,6 +2,8 @@
 // table rule, status texts and the thread-local error text.  Nothing here
 // calls the HIP runtime, so all of it runs (and is tested) without a GPU.
 #include <stdarg.h>
+
+#include <algorithm>
 #include <stdio.h>
 #include <string.h>
 
@@ -21,22 +23,17 @@ void set_error(const char *fmt, ...)
 
 size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
 {
+    (void)K8;
     switch (t.path) {
     case SKINNY_PATH_MFMA:
         return (size_t)t.waves * t.mt * (t.rows + 1) * sizeof(float);
-    case SKINNY_PATH_DOT2X:
-        return (size_t)t.mt * ((K8 + t.split - 1) / t.split) * 16;
     case SKINNY_PATH_MFMAX:
         return mfmax_own_lds_bytes(t.waves, t.mt);
-    case SKINNY_PATH_MFMAS:
-    case SKINNY_PATH_MFMAR:
-        return mfmax_lds_bytes(t.waves, t.mt);
-    case SKINNY_PATH_MFMAD:
-        return mfmad_lds_bytes(t.waves, t.mt, t.unroll);
-    case SKINNY_PATH_MFMAK:
-        return t.rows >= 16 ? mfmak_lds_bytes(t.waves, t.mt, t.waves / (t.rows / 16)) : 0;
     case SKINNY_PATH_MFMAW:
         return mfmaw_lds_bytes(t.waves, t.rows, t.mt, t.unroll);
+    case SKINNY_PATH_MFMA4:
+    case SKINNY_PATH_DOT2W:
+        return rgs_lds_bytes(t);
     default:
         return 0;
     }
@@ -50,33 +47,17 @@ const KernelInfo *tactic_kernel(const skinny_tactic &t, int half)
         return find_kernel(t.path, t.mt, t.rows, t.unroll, half);
     case SKINNY_PATH_DOT2R:                    // the DOT2 kernels, another grid
         return find_kernel(SKINNY_PATH_DOT2, t.mt, t.rows, t.unroll, half);
-    case SKINNY_PATH_DOT2X:
-        if (t.waves < 1 || t.rows % t.waves)
-            return nullptr;
-        return find_kernel(t.path, t.mt, t.rows / t.waves, t.unroll, half);
     case SKINNY_PATH_MFMAX:
         if (t.rows != 16 * t.waves || (t.unroll != 1 && t.unroll != 2))
             return nullptr;
         return find_kernel(t.path, t.mt, t.waves, 1, half);   // unroll 2: same kernel, equal row ranges
-    case SKINNY_PATH_MFMAD:
-    case SKINNY_PATH_MFMAS:
-        if (t.rows != 16 * t.waves)
-            return nullptr;
-        return find_kernel(t.path, t.mt, t.waves, t.unroll, half);
-    case SKINNY_PATH_MFMAR:                    // the MFMAS kernels, another grid
-        if (t.rows != 16 * t.waves)
-            return nullptr;
-        return find_kernel(SKINNY_PATH_MFMAS, t.mt, t.waves, t.unroll, half);
-    case SKINNY_PATH_MFMAK: {                  // KernelInfo.rows = 100 KS + RT
-        if (t.rows < 16 || t.rows % 16 || t.waves % (t.rows / 16))
-            return nullptr;
-        const int rt = t.rows / 16, ks = t.waves / rt;
-        return find_kernel(t.path, t.mt, 100 * ks + rt, t.unroll, half);
-    }
     case SKINNY_PATH_MFMAW:                    // KernelInfo.rows = 100 waves + row groups
         if (t.rows < 16 || t.rows % 16)
             return nullptr;
         return find_kernel(t.path, t.mt, 100 * t.waves + t.rows / 16, t.unroll, half);
+    case SKINNY_PATH_MFMA4:                    // KernelInfo.rows = the most rows of a range
+    case SKINNY_PATH_DOT2W:
+        return find_kernel(t.path, t.mt, t.rows, t.unroll, half);
     default:
         return nullptr;
     }
@@ -126,19 +107,13 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
         set_error("split=%d: must be 1..16", t->split);
         return SKINNY_ERR_INVALID_ARG;
     }
-    if (t->path == SKINNY_PATH_MFMAS && t->split > 4) {
-        set_error("split=%d: for the stream-K path split is workgroups per CU, 1..4", t->split);
+    if (is_retired_path(t->path)) {
+        set_error("path=%d: this kernel family was measured and removed; its number stays reserved", t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
-    if (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_DOT2X || t->path == SKINNY_PATH_MFMAX ||
-        t->path == SKINNY_PATH_MFMAD || t->path == SKINNY_PATH_MFMAS || t->path == SKINNY_PATH_DOT2R) {
+    if (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_MFMAX || t->path == SKINNY_PATH_DOT2R) {
         if (t->split > k8) {
             set_error("split=%d exceeds the %d 16-byte chunks of a row", t->split, k8);
-            return SKINNY_ERR_INVALID_ARG;
-        }
-    } else if (t->path == SKINNY_PATH_MFMAK) {
-        if (t->split > 2) {
-            set_error("split=%d: for MFMAK split is row ranges per CU, 1 or 2", t->split);
             return SKINNY_ERR_INVALID_ARG;
         }
     } else if (t->path == SKINNY_PATH_MFMAW) {
@@ -151,10 +126,19 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             set_error("split=%d exceeds the %d K stages of %d chunks", t->split, stages, sc);
             return SKINNY_ERR_INVALID_ARG;
         }
-    } else if (t->path == SKINNY_PATH_MFMAR) {
-        const int stages = (k8 + kMfmaxChunks - 1) / kMfmaxChunks;
-        if (t->split > stages) {
-            set_error("split=%d exceeds the %d K stages of %d chunks", t->split, stages, kMfmaxChunks);
+    } else if (is_rgs_path(t->path)) {
+        if (t->unroll != 2 && t->unroll != 3) {
+            set_error("unroll=%d: stages of %d chunks in flight, 2 or 3", t->unroll, kRgsChunks);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+        if (t->waves > 4) {
+            set_error("waves=%d: MFMA4 and DOT2W workgroups hold at most 4 waves", t->waves);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+        const int stages = (k8 + kRgsChunks - 1) / kRgsChunks;
+        if (t->split > 8 || t->split > stages) {
+            set_error("split=%d: MFMA4 and DOT2W split K into at most 8 parts and at most their %d stages of %d "
+                      "chunks", t->split, stages, kRgsChunks);
             return SKINNY_ERR_INVALID_ARG;
         }
     } else if (t->path == SKINNY_PATH_MFMA) {
@@ -164,11 +148,11 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             return SKINNY_ERR_INVALID_ARG;
         }
     } else {
-        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 2 (DOT2X), 3 (MFMAX), 4 (MFMAD), 5 (MFMAS), 6 (MFMAR), "
-                  "7 (MFMAK), 8 (DOT2R) or 9 (MFMAW)", t->path);
+        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 3 (MFMAX), 8 (DOT2R), 9 (MFMAW), 10 (MFMA4) or 11 (DOT2W)",
+                  t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
-    const size_t lds_limit = (t->path == SKINNY_PATH_DOT2 || t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
+    const size_t lds_limit = (t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
     if (tactic_lds_bytes(*t, k8) > lds_limit) {
         set_error("tactic needs %zu bytes of LDS (limit %zu)", tactic_lds_bytes(*t, k8), lds_limit);
         return SKINNY_ERR_INVALID_ARG;
@@ -183,7 +167,12 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
 
 int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
 {
-    if (N < 1 || K < 8 || K % 8 || cap < 0 || (cap > 0 && !buf))
+    return skinny_enumerate_tactics_ex(N, K, 256, buf, cap);
+}
+
+int skinny_enumerate_tactics_ex(int N, int K, int cus, skinny_tactic *buf, int cap)
+{
+    if (N < 1 || K < 8 || K % 8 || cus < 1 || cap < 0 || (cap > 0 && !buf))
         return -1;
     const int k8 = K / 8;
     int count = 0;
@@ -195,45 +184,42 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
         const KernelInfo &k = ks[i];
         if (k.half)
             continue;                                    // the same tactics as the BF16 twin
-        // the stream-K kernels also run on a data-parallel grid (MFMAR), the
-        // DOT2 kernels over equal row ranges (DOT2R)
-        const int paths[2] = {k.path, k.path == SKINNY_PATH_MFMAS ? SKINNY_PATH_MFMAR
-                                      : k.path == SKINNY_PATH_DOT2 ? SKINNY_PATH_DOT2R
-                                                                    : -1};
+        // the DOT2 kernels also run over equal row ranges (DOT2R)
+        const int paths[2] = {k.path, k.path == SKINNY_PATH_DOT2 ? SKINNY_PATH_DOT2R : -1};
         for (int path : paths) {
             if (path < 0)
                 continue;
             for (int w : kWaves) {
                 for (int s : kSplits) {
                     skinny_tactic t = {path, k.mt, k.rows, w, k.unroll, s};
-                    if (path == SKINNY_PATH_DOT2X)
-                        t.rows = k.rows * w;             // k.rows is rows per wave
-                    if (path == SKINNY_PATH_MFMAX || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAS ||
-                        path == SKINNY_PATH_MFMAR) {
+                    if (path == SKINNY_PATH_MFMAX) {
                         if (w != k.rows)                 // k.rows is the wave count
                             continue;
                         t.rows = 16 * w;
-                    }
-                    if (path == SKINNY_PATH_MFMAK) {     // k.rows = 100 KS + RT
-                        const int rt = k.rows % 100, ks = k.rows / 100;
-                        if (w != rt * ks || s > 2)
-                            continue;
-                        t.rows = 16 * rt;
                     }
                     if (path == SKINNY_PATH_MFMAW) {     // k.rows = 100 waves + row groups
                         if (w != k.rows / 100 || s > 4)
                             continue;
                         t.rows = 16 * (k.rows % 100);
                     }
-                    if (path == SKINNY_PATH_MFMAS && s > 3)
-                        continue;                        // split: workgroups per CU
+                    if (is_rgs_path(path)) {
+                        // the instance whose row groups the equal ranges fill: a range of
+                        // ceil(N / ranges) rows leaves none of its 4-row groups empty
+                        if (w > 4 || s > 4)
+                            continue;
+                        const int per_round = (cus + s - 1) / s;
+                        const int ranges0 = (N + k.rows - 1) / k.rows;
+                        const int ranges = ((ranges0 + per_round - 1) / per_round) * per_round;
+                        const int most = (N + ranges - 1) / std::min(N, ranges);
+                        if (most <= k.rows - 4)
+                            continue;
+                    }
                     if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                         continue;
                     const int tiles = (N + t.rows - 1) / t.rows;
-                    if (s > 1 && tiles * w >= 8 * 256 && path != SKINNY_PATH_MFMAS && path != SKINNY_PATH_MFMAK &&
-                        path != SKINNY_PATH_MFMAW)
+                    if (s > 1 && tiles * w >= 8 * cus && path != SKINNY_PATH_MFMAW && !is_rgs_path(path))
                         continue;   // enough waves already; a K split only adds traffic
-                    if (path == SKINNY_PATH_DOT2R && tiles * s > 8 * 256)
+                    if (path == SKINNY_PATH_DOT2R && tiles * s > 8 * cus)
                         continue;   // many workgroups per CU balance themselves
                     if (path == SKINNY_PATH_DOT2) {
                         // each lane of the workgroup should own at least one chunk per
@@ -241,21 +227,18 @@ int skinny_enumerate_tactics(int N, int K, skinny_tactic *buf, int cap)
                         const int per_split = k8 / s;
                         if (per_split < 64 * w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
                             continue;
-                    } else if (path == SKINNY_PATH_DOT2X) {
-                        // every wave streams the whole split: one full pipeline stage at least
-                        if (k8 / s < 64 * k.unroll)
-                            continue;
-                    } else if (path == SKINNY_PATH_MFMAS || path == SKINNY_PATH_MFMAK) {
-                        if (k8 < 2 * kMfmaxChunks)
-                            continue;
                     } else if (path == SKINNY_PATH_MFMAW) {
                         // every wave should own two stages of its K part at least
                         if (k8 / s < 2 * w * mfmaw_stage_chunks(k.unroll))
                             continue;
-                    } else if (path == SKINNY_PATH_MFMAX || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAR) {
+                    } else if (is_rgs_path(path)) {
+                        // every wave should own a stage of its K part at least
+                        if (k8 / s < w * kRgsChunks && !(w == 1 && s == 1))
+                            continue;
+                    } else if (path == SKINNY_PATH_MFMAX) {
                         if (k8 / s < 2 * kMfmaxChunks)
                             continue;
-                    } else {
+                    } else if (path == SKINNY_PATH_MFMA) {
                         const int per_split = ((k8 + 3) / 4) / s;
                         if (per_split < w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
                             continue;

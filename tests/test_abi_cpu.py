@@ -66,6 +66,7 @@ def test_prepare_rejects_before_any_device_call(ptr, n, k, od, want):
     (256, 512, 512, 2, 0, 1),       # bad in dtype
     (256, 512, 512, -1, 1, 1),
     (256, 512, 1 << 26, 0, 0, 2),   # 16 rows of W past 2 GiB
+    (256, 512, 1 << 24, 0, 0, 2),   # 64 rows of W (the largest tile) reach the out-of-range load offset
 ])
 def test_prepare_ex_rejects_before_any_device_call(n, k, ldw, idt, od, want):
     lib = sk.load_library()
@@ -156,12 +157,73 @@ def test_row_range_tactics():
     with pytest.raises(ValueError):
         sk.tactic_check(T(sk.PATH_DOT2R, 2, 3, 1, 1, 1), 6288, 7168)   # no DOT2 kernel with 3 rows
     with pytest.raises(ValueError):
-        sk.tactic_check(T(11, 16, 16, 1, 1, 1), 6288, 7168)       # no such path
+        sk.tactic_check(T(12, 16, 16, 1, 1, 1), 6288, 7168)       # no such path
     # many workgroups per CU balance themselves: no DOT2R with more than
-    # eight per CU of a 256-CU part
+    # eight per CU of the part enumerated for (256 CUs unless told otherwise)
+    for cus in (256, 80):
+        for t in sk.enumerate_tactics(6288, 7168, cus=cus):
+            if t.path == sk.PATH_DOT2R:
+                assert -(-6288 // t.rows) * t.split <= 8 * cus
+
+
+@pytest.mark.parametrize("path", [2, 4, 5, 6, 7])
+def test_retired_paths_are_refused(path):
+    """Kernel families measured and removed keep their path numbers reserved:
+    a tactic naming one is refused (so a stored table that names one is
+    ignored and the shape tuned afresh), and none is enumerated."""
+    with pytest.raises(ValueError, match="removed"):
+        sk.tactic_check(T(path, 16, 32, 2, 1, 1), 6288, 7168)
+    assert all(t.path == 0 or t.path not in (2, 4, 5, 6, 7) for t in sk.enumerate_tactics(6288, 7168))
+
+
+def test_enumeration_follows_the_cu_count():
+    """The launch-shape rules take the device's CU count: a part with fewer
+    CUs gets fewer K-split DOT2R candidates (its rows already fill it) and
+    MFMA4 instances sized to its larger per-CU row ranges."""
+    full = sk.enumerate_tactics(6288, 7168)
+    assert full == sk.enumerate_tactics(6288, 7168, cus=256)
+    small = sk.enumerate_tactics(6288, 7168, cus=64)
+    for t in small:
+        sk.tactic_check(t, 6288, 7168)
+    m4 = lambda c: {t.rows for t in c if t.path == sk.PATH_MFMA4 and t.split == 1}
+    # one range per CU without a K split: 24-25 rows on 256 CUs, 49-50 on 64
+    assert 28 in m4(full) and 52 not in m4(full)
+    assert 52 in m4(small)
+    assert sk.load_library().skinny_enumerate_tactics_ex(6288, 7168, 0, None, 0) == -1
+
+
+@pytest.mark.parametrize("path,tiles", [(sk.PATH_MFMA4, {4, 8, 16, 32}), (sk.PATH_DOT2W, {1, 2, 4, 8})])
+def test_row_group_stream_tactics(path, tiles):
+    """MFMA4 (path 10) and DOT2W (path 11), the row-group stream kernels:
+    ranges of at most 4, 8, 16, 28, 52 or 56 rows, at most 4 waves, 2 or 3
+    stages of 16 chunks in flight, K split 1..8 and no more parts than
+    stages; the enumerator keeps the instance whose 4-row groups the equal
+    ranges fill (none left empty)."""
+    cands = [t for t in sk.enumerate_tactics(6288, 7168) if t.path == path]
+    assert {t.mt for t in cands} == tiles
+    assert {t.unroll for t in cands} == {2, 3}
     for t in cands:
-        if t.path == sk.PATH_DOT2R:
-            assert -(-6288 // t.rows) * t.split <= 8 * 256
+        per_round = -(-256 // t.split)
+        ranges = -(-(-(-6288 // t.rows)) // per_round) * per_round
+        most = -(-6288 // ranges)
+        assert t.rows - 4 < most <= t.rows, t
+        assert t.waves <= 4
+    assert any(t.rows == 28 and t.split == 1 for t in cands)      # 24-25 rows per CU
+    assert any(t.rows == 52 and t.split == 2 for t in cands)      # 49 rows, two K halves
+    big = max(tiles)
+    sk.tactic_check(T(path, big, 28, 4, 3, 1), 6288, 7168)
+    sk.tactic_check(T(path, big // 2, 56, 1, 2, 8), 6288, 7168)
+    for bad in (T(path, big, 52, 4, 2, 1),            # 13 row groups x the largest tile: not compiled
+                T(path, big // 2, 24, 4, 2, 1),       # no 6-group instance
+                T(path, big // 2, 28, 8, 2, 1),       # more than 4 waves
+                T(path, big // 2, 28, 4, 1, 1),       # 2 or 3 stages in flight
+                T(path, big // 2, 28, 4, 4, 1),
+                T(path, 3 * big // 8, 28, 4, 2, 1),   # not a compiled token tile
+                T(path, big // 2, 28, 4, 2, 9)):      # more than 8 K parts
+        with pytest.raises(ValueError):
+            sk.tactic_check(bad, 6288, 7168)
+    with pytest.raises(ValueError):
+        sk.tactic_check(T(path, big // 2, 28, 1, 2, 3), 64, 256)   # 2 stages of 16 chunks
 
 
 def test_barrier_free_row_range_tactics():
@@ -239,8 +301,11 @@ def test_bench_names_the_kernel_of_every_tactic():
     import bench
     for t in sk.enumerate_tactics(6288, 7168):
         name = bench.kernel_name(t)
-        assert name and re.fullmatch(r"k_(dot2|dot2x|mfma|mfmax|mfmad|mfmas|mfmak|mfmaw)<(\d+, )+false>", name), \
-            (t, name)
+        assert name and re.fullmatch(r"k_(dot2|mfma|mfmax|mfmaw|rgs)<((\d+|true|false), )+false>",
+                                     name), (t, name)
+    assert bench.kernel_name(T(sk.PATH_MFMA4, 16, 28, 4, 3, 1)) == "k_rgs<true, 4, 7, 3, false>"
+    assert bench.kernel_name(T(sk.PATH_MFMA4, 4, 52, 2, 2, 2)) == "k_rgs<true, 1, 13, 2, false>"
+    assert bench.kernel_name(T(sk.PATH_DOT2W, 8, 28, 4, 2, 1)) == "k_rgs<false, 8, 7, 2, false>"
     assert bench.kernel_name(T(3, 32, 64, 4, 2, 2)) == "k_mfmax<2, 4, false>"
     assert bench.kernel_name(T(sk.PATH_DOT2R, 2, 4, 1, 2, 1)) == "k_dot2<2, 4, 2, false>"
     assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2)) == "k_mfmaw<2, 4, 4, 16, false>"
