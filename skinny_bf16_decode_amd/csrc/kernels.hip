@@ -252,11 +252,15 @@ __device__ __forceinline__ void wave_reduce_transpose(float *v, int lane)
     step_dpp<V5, kDppQuadXor1, 1>(v, lane);
 }
 
-constexpr unsigned kSlotEmpty = kSlotEmptyBits;
+// A node holds a value v as bits(v) ^ kSlotEmptyBits, so an all-zero node
+// (zero-initialised memory, or a node some launch emptied) reads as empty:
+// decoding 0 gives the signalling-NaN pattern kSlotEmptyBits, which no fp32
+// arithmetic produces.
+constexpr unsigned kSlotKey = kSlotEmptyBits;
 
 __device__ __forceinline__ void empty_slot(float *p)
 {
-    __hip_atomic_store(reinterpret_cast<unsigned *>(p), kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<unsigned *>(p), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -265,10 +269,10 @@ __device__ __forceinline__ void empty_slot(float *p)
 // The `parts` K parts of a row tile meet in a fixed binary tree: at level 0
 // parts (0, 1), (2, 3), ... pair up in one node each, an odd part out moves
 // up unpaired, and so on until one value is left; a tile has parts - 1 nodes
-// of E values, each holding kSlotEmpty between launches.  A part swaps its
-// value into its node with one agent-scope atomic exchange and gets back what
-// was there: kSlotEmpty means the partner has not arrived and will carry the
-// pair on, so this value is done; anything else is the partner's value, and
+// of E values, each empty between launches.  A part swaps its value into its
+// node with one agent-scope atomic exchange and gets back what was there:
+// empty means the partner has not arrived and will carry the pair on, so
+// this value is done; anything else is the partner's value, and
 // this part empties the node, adds the two and moves up a level.  Whoever
 // completes the root holds the whole sum.
 //
@@ -279,12 +283,15 @@ __device__ __forceinline__ void empty_slot(float *p)
 // needed: one memory round trip per level, and a late partner can never be
 // missed (the second of two swaps on a node always sees the first).  Every
 // node is used by exactly two swaps per launch and left empty, so the next
-// launch (graph replays included) finds the workspace as the first did.
+// launch (graph replays included) finds the workspace as the first did: all
+// zero, the state a zeroed allocation and a static device array start in.
 // Values no part holds (outputs past N or M) are never swapped, by any part.
 // ---------------------------------------------------------------------------
+// swaps v into the node and returns what was there, both in the node's
+// encoding (bits ^ kSlotKey; 0 = empty)
 __device__ __forceinline__ unsigned swap_slot(float *p, float v)
 {
-    return __hip_atomic_exchange(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+    return __hip_atomic_exchange(reinterpret_cast<unsigned *>(p), __float_as_uint(v) ^ kSlotKey, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -310,16 +317,16 @@ __device__ __forceinline__ void swap_exchange(float *wsp, int E, int parts, int 
             // all swaps of the level in flight before the first is looked at
 #pragma unroll
             for (int i = 0; i < N; ++i)
-                old[i] = live[i] ? swap_slot(node + off[i], v[i]) : kSlotEmpty;
+                old[i] = live[i] ? swap_slot(node + off[i], v[i]) : 0u;
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 if (!live[i])
                     continue;
-                if (old[i] == kSlotEmpty) {
+                if (old[i] == 0u) {
                     live[i] = false;           // the partner carries the pair on
                 } else {
                     empty_slot(node + off[i]);
-                    v[i] += __uint_as_float(old[i]);
+                    v[i] += __uint_as_float(old[i] ^ kSlotKey);
                 }
             }
         }
@@ -337,7 +344,7 @@ __device__ __forceinline__ void swap_exchange(float *wsp, int E, int parts, int 
 // pair_off[p] of every node (E / 2 slots); a pair is swapped when either of
 // its values is live in this tile -- the same pairs in every K part -- and a
 // value that is not live just rides along.
-constexpr unsigned long long kPairEmpty = ((unsigned long long)kSlotEmpty << 32) | kSlotEmpty;
+constexpr unsigned long long kPairKey = ((unsigned long long)kSlotKey << 32) | kSlotKey;
 
 template <int N>
 __device__ __forceinline__ void swap_exchange_pairs(float *wsp, int E, int parts, int part, const int (&off)[N],
@@ -357,22 +364,23 @@ __device__ __forceinline__ void swap_exchange_pairs(float *wsp, int E, int parts
             unsigned long long old[N / 2];
 #pragma unroll
             for (int p = 0; p < N / 2; ++p) {
-                const unsigned long long mine = ((unsigned long long)__float_as_uint(v[2 * p + 1]) << 32) |
-                                                __float_as_uint(v[2 * p]);
+                const unsigned long long mine = (((unsigned long long)__float_as_uint(v[2 * p + 1]) << 32) |
+                                                 __float_as_uint(v[2 * p])) ^ kPairKey;
                 old[p] = live[p] ? __hip_atomic_exchange(node + pair_off[p], mine, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT)
-                                 : kPairEmpty;
+                                 : 0ull;
             }
 #pragma unroll
             for (int p = 0; p < N / 2; ++p) {
                 if (!live[p])
                     continue;
-                if (old[p] == kPairEmpty) {
+                if (old[p] == 0ull) {
                     live[p] = false;           // the partner carries the pair on
                 } else {
-                    __hip_atomic_store(node + pair_off[p], kPairEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    v[2 * p] += __uint_as_float((unsigned)old[p]);
-                    v[2 * p + 1] += __uint_as_float((unsigned)(old[p] >> 32));
+                    __hip_atomic_store(node + pair_off[p], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const unsigned long long theirs = old[p] ^ kPairKey;
+                    v[2 * p] += __uint_as_float((unsigned)theirs);
+                    v[2 * p + 1] += __uint_as_float((unsigned)(theirs >> 32));
                 }
             }
         }

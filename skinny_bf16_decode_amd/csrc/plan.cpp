@@ -47,7 +47,7 @@ struct skinny_plan {
     int ldw = 0;                     // W row pitch, elements
     int half = 0;                    // 1: FP16 inputs
     skinny_out_dtype od = SKINNY_OUT_BF16;
-    float *ws = nullptr;             // split-K exchange nodes (kSlotEmptyBits between launches)
+    float *ws = nullptr;             // split-K exchange nodes (all zero, i.e. empty, between launches)
     KArgs base{};
     Entry e[SKINNY_MAX_M + 1];
 };
@@ -238,6 +238,79 @@ skinny_status check_prepare_args(const void *W, int N, int K, int ldw, int in_dt
     return SKINNY_OK;
 }
 
+// Validation of a run's arguments (x, residual, out, M) for an [N][K]
+// weight; no HIP call.
+skinny_status check_run_args(int N, int K, skinny_out_dtype od, const void *x, int ldx, const void *residual,
+                             int ldr, const void *out, int ldo, int M)
+{
+    if (M < 1 || M > SKINNY_MAX_M) {
+        set_error("M=%d outside 1..%d", M, SKINNY_MAX_M);
+        return SKINNY_ERR_UNSUPPORTED_M;
+    }
+    if (!x || !out) {
+        set_error("x or out is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if (ldx < K || ldx % 8 || ldo < N || (residual && ldr < N)) {
+        set_error("ldx=%d (>= K=%d, multiple of 8), ldo=%d and ldr=%d (>= N=%d) out of range", ldx, K, ldo,
+                  ldr, N);
+        return SKINNY_ERR_SHAPE;
+    }
+    const size_t osz = od == SKINNY_OUT_F32 ? 4 : 2;
+    if ((long long)ldx * (SKINNY_MAX_M * 2) >= (long long)kOffOob) {
+        set_error("ldx=%d: %d rows of x must span less than %u bytes", ldx, SKINNY_MAX_M, kOffOob);
+        return SKINNY_ERR_SHAPE;
+    }
+    if (((uintptr_t)x & 15) || ((uintptr_t)out & (osz - 1)) || ((uintptr_t)residual & (osz - 1))) {
+        set_error("x=%p must be 16-byte aligned, out=%p and residual=%p element aligned", x, out, residual);
+        return SKINNY_ERR_ALIGN;
+    }
+    if (residual && residual != out) {
+        // the residual must be out itself or lie apart from it
+        const char *o0 = (const char *)out, *o1 = o0 + ((size_t)(M - 1) * ldo + N) * osz;
+        const char *r0 = (const char *)residual, *r1 = r0 + ((size_t)(M - 1) * ldr + N) * osz;
+        if (r0 < o1 && o0 < r1) {
+            set_error("residual=%p overlaps out=%p without being it", residual, out);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+    } else if (residual && ldr != ldo) {
+        set_error("residual is out but ldr=%d != ldo=%d", ldr, ldo);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    return SKINNY_OK;
+}
+
+// The weight-side kernel arguments of an [N][K] weight (pitch ldw) whose
+// split-K exchange nodes are at ws.
+KArgs weight_args(const void *W, int N, int K, int ldw, skinny_out_dtype od, int nxcd, float *ws)
+{
+    KArgs a{};
+    a.W = W;
+    a.ws = ws;
+    a.N = N;
+    a.K8 = K / 8;
+    a.out_f32 = od == SKINNY_OUT_F32;
+    a.w_pitch = (unsigned)ldw * 2u;
+    a.x_pitch = (unsigned)K * 2u;       // per call
+    a.ldo = a.ldr = N;                  // per call
+    // SKINNY_XCD_REMAP=0 turns off the placement of a tile's split-K
+    // workgroups on one XCD (then the partial exchange crosses XCDs).
+    a.nxcd = env_int("SKINNY_XCD_REMAP", 1) ? nxcd : 1;
+    return a;
+}
+
+// The per-call kernel arguments.
+void set_call_args(KArgs &a, const void *x, int ldx, const void *residual, int ldr, void *out, int ldo, int M)
+{
+    a.x = x;
+    a.out = out;
+    a.res = residual;
+    a.M = M;
+    a.x_pitch = (unsigned)ldx * 2u;
+    a.ldo = ldo;
+    a.ldr = residual ? ldr : ldo;
+}
+
 skinny_status current_gfx950(int *dev, int *cus)
 {
     int count = 0;
@@ -300,7 +373,7 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
         HIP_TRY(hipMemcpy2DAsync((char *)wcopies.p + wbytes * c, (size_t)K * 2, W, (size_t)ldw * 2, (size_t)K * 2, N,
                                  hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemsetAsync(xbuf.p, 0, (size_t)SKINNY_MAX_M * K * 2, st));
-    HIP_TRY(hipMemsetD32Async((hipDeviceptr_t)wsbuf.p, (int)kSlotEmptyBits, std::max<size_t>(max_ws, 1), st));
+    HIP_TRY(hipMemsetAsync(wsbuf.p, 0, std::max<size_t>(max_ws, 1) * 4, st));   // every exchange node empty
     hipEvent_t e0, e1;
     HIP_TRY(hipEventCreate(&e0));
     HIP_TRY(hipEventCreate(&e1));
@@ -575,23 +648,13 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
             hip_fail(e, "hipMalloc(split-K workspace)");
             return fail(e == hipErrorOutOfMemory ? SKINNY_ERR_NOMEM : SKINNY_ERR_HIP);
         }
-        if ((e = hipMemsetD32((hipDeviceptr_t)p->ws, (int)kSlotEmptyBits, max_ws)) != hipSuccess) {
-            hip_fail(e, "hipMemsetD32(split-K workspace)");
+        if ((e = hipMemset(p->ws, 0, max_ws * 4)) != hipSuccess) {   // every exchange node empty
+            hip_fail(e, "hipMemset(split-K workspace)");
             return fail(SKINNY_ERR_HIP);
         }
     }
+    p->base = weight_args(W, N, K, ldw, od, nxcd, p->ws);
     KArgs &a = p->base;
-    a.W = W;
-    a.ws = p->ws;
-    a.N = N;
-    a.K8 = K / 8;
-    a.out_f32 = od == SKINNY_OUT_F32;
-    a.w_pitch = (unsigned)ldw * 2u;
-    a.x_pitch = (unsigned)K * 2u;       // per call
-    a.ldo = a.ldr = N;                  // per call
-    // SKINNY_XCD_REMAP=0 turns off the placement of a tile's split-K
-    // workgroups on one XCD (then the partial exchange crosses XCDs).
-    a.nxcd = env_int("SKINNY_XCD_REMAP", 1) ? nxcd : 1;
 
     // Warm every distinct kernel the table uses, on scratch x/out, so that no
     // code object loads lazily inside a later graph capture.
@@ -719,50 +782,12 @@ skinny_status skinny_run_ex(const skinny_plan *p, const void *x, int ldx, const 
         set_error("plan is NULL");
         return SKINNY_ERR_INVALID_ARG;
     }
-    if (M < 1 || M > SKINNY_MAX_M) {
-        set_error("M=%d outside 1..%d", M, SKINNY_MAX_M);
-        return SKINNY_ERR_UNSUPPORTED_M;
-    }
-    if (!x || !out) {
-        set_error("x or out is NULL");
-        return SKINNY_ERR_INVALID_ARG;
-    }
-    if (ldx < p->K || ldx % 8 || ldo < p->N || (residual && ldr < p->N)) {
-        set_error("ldx=%d (>= K=%d, multiple of 8), ldo=%d and ldr=%d (>= N=%d) out of range", ldx, p->K, ldo,
-                  ldr, p->N);
-        return SKINNY_ERR_SHAPE;
-    }
-    const size_t osz = p->od == SKINNY_OUT_F32 ? 4 : 2;
-    if ((long long)ldx * (SKINNY_MAX_M * 2) >= (long long)kOffOob) {
-        set_error("ldx=%d: %d rows of x must span less than %u bytes", ldx, SKINNY_MAX_M, kOffOob);
-        return SKINNY_ERR_SHAPE;
-    }
-    if (((uintptr_t)x & 15) || ((uintptr_t)out & (osz - 1)) || ((uintptr_t)residual & (osz - 1))) {
-        set_error("x=%p must be 16-byte aligned, out=%p and residual=%p element aligned", x, out, residual);
-        return SKINNY_ERR_ALIGN;
-    }
-    if (residual && residual != out) {
-        // the residual must be out itself or lie apart from it
-        const char *o0 = (const char *)out, *o1 = o0 + ((size_t)(M - 1) * ldo + p->N) * osz;
-        const char *r0 = (const char *)residual, *r1 = r0 + ((size_t)(M - 1) * ldr + p->N) * osz;
-        if (r0 < o1 && o0 < r1) {
-            set_error("residual=%p overlaps out=%p without being it", residual, out);
-            return SKINNY_ERR_INVALID_ARG;
-        }
-    } else if (residual && ldr != ldo) {
-        set_error("residual is out but ldr=%d != ldo=%d", ldr, ldo);
-        return SKINNY_ERR_INVALID_ARG;
-    }
-    const Entry &en = p->e[M];
+    skinny_status s = check_run_args(p->N, p->K, p->od, x, ldx, residual, ldr, out, ldo, M);
+    if (s != SKINNY_OK)
+        return s;
     KArgs a = p->base;
-    a.x = x;
-    a.out = out;
-    a.res = residual;
-    a.M = M;
-    a.x_pitch = (unsigned)ldx * 2u;
-    a.ldo = ldo;
-    a.ldr = residual ? ldr : ldo;
-    hipError_t e = launch(en, a, (hipStream_t)stream);
+    set_call_args(a, x, ldx, residual, ldr, out, ldo, M);
+    hipError_t e = launch(p->e[M], a, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "hipLaunchKernel");
     return SKINNY_OK;

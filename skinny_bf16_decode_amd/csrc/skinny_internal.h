@@ -111,9 +111,9 @@ constexpr int kMaxWaves = 8;
 // smaller than it.
 constexpr unsigned kOffOob = 0x7FFFFFF0u;
 constexpr int kMaxTileRows = 64;
-// Bits of an empty split-K exchange node (a signalling NaN no arithmetic
-// produces); the workspace is filled with it when allocated, and every
-// launch leaves it so.
+// A split-K exchange node holds a value as its bits XOR this signalling-NaN
+// pattern (no fp32 arithmetic produces it), so an all-zero node is empty:
+// the workspace is zeroed when allocated, and every launch leaves it so.
 constexpr unsigned kSlotEmptyBits = 0x7FB55AA5u;
 constexpr size_t kMaxLds = 60 * 1024;          // in-WG split-K paths (DOT2, MFMA)
 // LDS-staged paths (MFMAX, MFMAW) may use a CU's whole 160 KiB, less a
