@@ -224,6 +224,31 @@ skinny_status skinny_run_ex(const skinny_plan *plan, const void *x, int ldx, con
  */
 skinny_status skinny_run(const skinny_plan *plan, const void *x, void *out, int M, void *stream);
 
+/*
+ * skinny_run_static -- one product out = x W^T (+ residual) with a given
+ * tactic and no plan, allocating nothing: for callers that cannot allocate
+ * device (or host) memory where they run it -- code under graph capture,
+ * tight serving loops, harnesses that forbid allocation.  The arguments are
+ * those of skinny_prepare_tactics_ex (W, N, K, ldw, in_dtype, out_dtype, one
+ * tactic whose token tile is >= M) and of skinny_run_ex (x ... stream), with
+ * the same checks and status codes; the result is bit-identical to a plan
+ * prepared with that tactic.
+ *
+ * A K-split tactic exchanges its partials through a device array the library
+ * holds per GPU for the life of the process (SKINNY_STATIC_SCRATCH_BYTES);
+ * a tactic that would need more returns SKINNY_ERR_SHAPE.  Every call on a
+ * GPU shares that GPU's array: calls that may overlap on one GPU (two
+ * streams, say) race and must not be issued; calls in stream order are fine.
+ * The first call on a device looks the array up (hipGetSymbolAddress) and
+ * the first launch of a kernel loads its code, so make one call before graph
+ * capture.  No warm-up, no tuning: the tactic is the caller's choice (for
+ * example skinny_plan_tactic of a plan prepared earlier).
+ */
+#define SKINNY_STATIC_SCRATCH_BYTES (4 << 20)
+skinny_status skinny_run_static(const void *W, int N, int K, int ldw, skinny_in_dtype in_dtype,
+                                skinny_out_dtype out_dtype, const skinny_tactic *tactic, const void *x, int ldx,
+                                const void *residual, int ldr, void *out, int ldo, int M, void *stream);
+
 /* 1 if the plan serves M tokens (1 <= M <= 64), else 0 (Projection.supports). */
 int skinny_supports(const skinny_plan *plan, int M);
 

@@ -112,6 +112,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "skinny_enumerate_tactics": (i, [i, i, tp, i]),
         "skinny_enumerate_tactics_ex": (i, [i, i, i, tp, i]),
         "skinny_select_table": (i, [tp, ctypes.POINTER(ctypes.c_double), i, tp]),
+        "skinny_run_static": (i, [vp, i, i, i, i, i, tp, vp, i, vp, i, vp, i, i, vp]),
         "skinny_probe_read": (i, [vp, sz, vp, vp]),
         "skinny_probe_read_blocks": (i, []),
         "skinny_probe_empty": (i, [vp]),
@@ -185,6 +186,31 @@ def probe_read_blocks() -> int:
 def probe_empty(stream=None) -> None:
     """Measurement only: one empty launch."""
     _raise(load_library().skinny_probe_empty(_stream_handle(stream)))
+
+
+STATIC_SCRATCH_BYTES = 4 << 20   # SKINNY_STATIC_SCRATCH_BYTES
+
+
+def run_static(weight, tactic: Tactic, x, out, stream=None, residual=None, out_dtype=None):
+    """out[:M] = x @ weight^T (+ residual[:M]) with one given tactic and no
+    plan: skinny_run_static, which allocates nothing (its split-K exchange
+    uses a device array the library holds per GPU).  Tensors as for
+    Prepared.run; out's dtype (BF16 or fp32) selects the output type."""
+    import torch
+    lib = load_library()
+    out_dtype = out.dtype if out_dtype is None else out_dtype
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    idt = IN_F16 if weight.dtype == torch.float16 else IN_BF16
+    n, k = weight.shape
+    m = x.shape[0]
+    ldx = x.stride(0) if m > 1 else k
+    ldo = out.stride(0) if out.shape[0] > 1 else n
+    ldr = (residual.stride(0) if residual.shape[0] > 1 else n) if residual is not None else 0
+    _raise(lib.skinny_run_static(ctypes.c_void_p(weight.data_ptr()), n, k, weight.stride(0), idt, od,
+                                 ctypes.byref(Tactic(*tactic.astuple())), ctypes.c_void_p(x.data_ptr()), ldx,
+                                 ctypes.c_void_p(residual.data_ptr()) if residual is not None else None, ldr,
+                                 ctypes.c_void_p(out.data_ptr()), ldo, m, _stream_handle(stream)))
+    return out
 
 
 class Prepared:

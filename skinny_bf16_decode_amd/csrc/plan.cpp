@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <array>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <stdio.h>
@@ -700,6 +701,52 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
     return SKINNY_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free runs (skinny_run_static): the split-K exchange nodes live in
+// a file-scope device array, one copy per device, zero at load and left zero
+// (empty) by every launch.  In host code `scratch` only names the symbol; its
+// device address is looked up once per device and kept in g_scratch.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[SKINNY_STATIC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, looked up on its first use.
+skinny_status scratch_of_device(int dev, float **ptr)
+{
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("device %d: the static scratch serves devices 0..%d", dev, kMaxDevices - 1);
+        return SKINNY_ERR_DEVICE;
+    }
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = static_cast<float *>(p);
+    return SKINNY_OK;
+}
+
+// The LDS limit check of lds_fits without its cache (which allocates).
+bool lds_fits_now(const void *fn, unsigned dynamic_bytes)
+{
+    int dev = 0, max_lds = 0;
+    hipFuncAttributes attr{};
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        hipFuncGetAttributes(&attr, fn) != hipSuccess)
+        return false;
+    return attr.sharedSizeBytes + dynamic_bytes <= (size_t)max_lds;
+}
+
 }  // namespace
 
 extern "C" {
@@ -796,6 +843,53 @@ skinny_status skinny_run_ex(const skinny_plan *p, const void *x, int ldx, const 
 skinny_status skinny_run(const skinny_plan *p, const void *x, void *out, int M, void *stream)
 {
     return skinny_run_ex(p, x, p ? p->K : 0, nullptr, 0, out, p ? p->N : 0, M, stream);
+}
+
+skinny_status skinny_run_static(const void *W, int N, int K, int ldw, skinny_in_dtype in_dtype,
+                                skinny_out_dtype out_dtype, const skinny_tactic *tactic, const void *x, int ldx,
+                                const void *residual, int ldr, void *out, int ldo, int M, void *stream)
+{
+    skinny_plan *unused = nullptr;           // check_prepare_args writes through it; nothing is built
+    skinny_status s = check_prepare_args(W, N, K, ldw, (int)in_dtype, out_dtype, &unused);
+    if (s != SKINNY_OK)
+        return s;
+    if (!tactic) {
+        set_error("tactic is NULL");
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    if ((s = check_run_args(N, K, out_dtype, x, ldx, residual, ldr, out, ldo, M)) != SKINNY_OK)
+        return s;
+    if ((s = skinny_tactic_check(tactic, N, K)) != SKINNY_OK)
+        return s;
+    if (tactic->mt < M) {
+        set_error("the tactic's token tile %d is smaller than M=%d", tactic->mt, M);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    int dev = 0, cus = 0;
+    if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)
+        return s;
+    raise_lds_limits();
+    const Entry en = make_entry(*tactic, N, K, in_dtype == SKINNY_IN_F16);
+    if (!en.fn || !lds_fits_now(en.fn, en.lds)) {
+        set_error("the tactic needs %u bytes of dynamic LDS, more than the device allows with the kernel's "
+                  "static LDS", en.lds);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    const size_t need = ws_floats(en) * sizeof(float);
+    if (need > SKINNY_STATIC_SCRATCH_BYTES) {
+        set_error("the tactic's split-K exchange needs %zu bytes of scratch; the static scratch holds %d",
+                  need, SKINNY_STATIC_SCRATCH_BYTES);
+        return SKINNY_ERR_SHAPE;
+    }
+    float *ws = nullptr;
+    if (need && (s = scratch_of_device(dev, &ws)) != SKINNY_OK)
+        return s;
+    KArgs a = weight_args(W, N, K, ldw, out_dtype, cus % 8 == 0 ? 8 : 1, ws);
+    set_call_args(a, x, ldx, residual, ldr, out, ldo, M);
+    hipError_t e = launch(en, a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipLaunchKernel");
+    return SKINNY_OK;
 }
 
 int skinny_supports(const skinny_plan *p, int M) { return p && M >= 1 && M <= SKINNY_MAX_M; }
