@@ -135,13 +135,25 @@ typedef struct {
 /*
  * skinny_prepare -- build a plan for weight W [N][K] (BF16 bits, device).
  *
+ * The install-time step of the pages: the module docstring of
+ * "vllm.models.kimi_k3.nvidia.low_latency_gemm" resolves the static part of
+ * the per-shape, per-token-count decision once into an {M: call} plan (and
+ * its autotune_kda_qkvg tunes before graph capture); PreparedWarpSplitK's
+ * constructor compiles one code per M and PreparedProjection.prepare one
+ * kernel per batch (pages "...cutedsl.gemm.warp_splitk" and
+ * "...cutedsl.gemm.projection") before any run.  Here the per-M choice is
+ * measured on the chip, and the kernels are compiled into the library and
+ * warmed.
+ *
  * Validates the arguments, then looks up the process-wide tactic table for
  * (device, N, K, out_dtype); on a miss it times every legal tactic on the
  * device with cache-cold weight copies at its full token tile, then times the
  * few fastest whose tile is >= M (SKINNY_TUNE_REFINE of them, default 4; 0 or
  * 1 skips this pass), and the two fastest of every tile >= M, again at M
  * itself and keeps, for each M in 1..64, the fastest; then every tactic the
- * table uses is timed again at each M its tile serves, and the fastest kept.
+ * table uses is timed again at each M its tile serves, and the fastest kept;
+ * finally, at M <= 8, the quickest v_dot2 tactic replaces the choice when it
+ * is within SKINNY_TUNE_DOT2_MARGIN (relative, default 0.01; negative: off).
  * Every tactic the table uses is
  * launched once (warm-up) so that nothing loads lazily under graph capture.
  * The split-K workspace and arrival counters are allocated here.
@@ -255,16 +267,40 @@ int skinny_supports(const skinny_plan *plan, int M);
 /* The tactic the plan uses for M tokens. */
 skinny_status skinny_plan_tactic(const skinny_plan *plan, int M, skinny_tactic *out);
 
-/* Human-readable name of the plan's kernel for M tokens, NUL-terminated in buf. */
+/*
+ * skinny_describe -- human-readable name of the plan's kernel for M tokens
+ * and its launch shape, NUL-terminated in buf (truncated to len - 1 chars):
+ * the entry of the {M: call} plan the low_latency_gemm module docstring
+ * describes, a ProjectionSpec's "winning backend per token count".
+ * SKINNY_ERR_INVALID_ARG for a NULL plan or buf or len = 0,
+ * SKINNY_ERR_UNSUPPORTED_M for M outside 1..64.
+ */
 skinny_status skinny_describe(const skinny_plan *plan, int M, char *buf, size_t len);
 
-/* Free the plan, its workspace and counters.  Synchronises the device.  NULL is a no-op. */
+/*
+ * skinny_destroy -- free the plan and its split-K workspace.  The plan owns
+ * its per-weight state as PreparedProjection owns its kernels and TMA maps
+ * (page "...cutedsl.gemm.projection"); the weight stays the caller's.
+ * Synchronises the plan's device first.  NULL is a no-op.
+ */
 void skinny_destroy(skinny_plan *plan);
 
-/* Static text for a status code. */
+/*
+ * skinny_status_string -- static text for a status code ("unknown status"
+ * for any other value).  The statuses stand for the pages' ValueErrors
+ * (PreparedWarpSplitK's packed-BF16 and 32 B alignment checks,
+ * PreparedProjection's dtype, pitch and prepared-batch checks) and for
+ * select_kimi_k3_backend returning None "to fall back"
+ * (SKINNY_ERR_UNSUPPORTED_M).
+ */
 const char *skinny_status_string(skinny_status s);
 
-/* Thread-local text of the last failure on this thread ("" if none). */
+/*
+ * skinny_last_error -- the text of the last failure on this thread ("" if
+ * none), naming the offending argument and value the way the pages'
+ * ValueError messages do.  Owned by the library; valid until the next
+ * failing call on the same thread.
+ */
 const char *skinny_last_error(void);
 
 /*

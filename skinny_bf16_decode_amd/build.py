@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libskinny.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "plan.cpp", "tactics.cpp"]
+SOURCES = ["kernels.hip", "plan.cpp", "tactics.cpp", "tables.cpp"]
 
 COMMON = [
     f"--offload-arch={ARCH}",

@@ -1492,66 +1492,12 @@ const void *probe_empty_fn() { return (const void *)&k_probe_empty; }
 #define SK_PAIR(PATH, MT, ROWS, U, KERNEL, ...)                                                        \
     {PATH, MT, ROWS, U, 0, (const void *)&KERNEL<__VA_ARGS__, false>},                               \
         {PATH, MT, ROWS, U, 1, (const void *)&KERNEL<__VA_ARGS__, true>}
-#define SK_DOT2(MT, R, U) SK_PAIR(SKINNY_PATH_DOT2, MT, R, U, k_dot2, MT, R, U)
-#define SK_MFMA(T, RT, U) SK_PAIR(SKINNY_PATH_MFMA, 16 * T, 16 * RT, U, k_mfma, T, RT, U)
-#define SK_MFMAX(T, NW) SK_PAIR(SKINNY_PATH_MFMAX, 16 * T, NW, 1, k_mfmax, T, NW)
-// MFMAW: rows field = 100 * NW + RG (waves and row groups), unroll = stage
-// width in 8-chunk units (1: 8 chunks, 2: 16)
-#define SK_MFMAW(T, RG, NW, U) SK_PAIR(SKINNY_PATH_MFMAW, 16 * T, 100 * NW + RG, U, k_mfmaw, T, RG, NW, 8 * U)
-// Row-group stream kernels, waves at run time: rows field = 4 RG (the most rows
-// of a range), unroll field = stages in flight.  MFMA4: token tile 4 TG.
-// DOT2W: token tile MT.
-#define SK_MFMA4(TG, RG, U) SK_PAIR(SKINNY_PATH_MFMA4, 4 * TG, 4 * RG, U, k_rgs, true, TG, RG, U)
-#define SK_DOT2W(MT, RG, U) SK_PAIR(SKINNY_PATH_DOT2W, MT, 4 * RG, U, k_rgs, false, MT, RG, U)
-
-// Instances whose double-buffered loads, accumulators and offsets fit in 256
-// VGPRs without spilling (roughly 8 U (R + MT) + R MT registers).
+// instances.def maps each family's parameters to the table fields through
+// SK_PAIR(path, mt, rows, unroll, kernel template, template arguments...)
 static const KernelInfo kKernels[] = {
-    SK_DOT2(1, 1, 1), SK_DOT2(1, 1, 2), SK_DOT2(1, 1, 4),
-    SK_DOT2(1, 2, 1), SK_DOT2(1, 2, 2), SK_DOT2(1, 2, 4),
-    SK_DOT2(1, 4, 1), SK_DOT2(1, 4, 2), SK_DOT2(1, 4, 4),
-    SK_DOT2(1, 8, 1), SK_DOT2(1, 8, 2),
-    SK_DOT2(1, 16, 1),
-    SK_DOT2(2, 1, 1), SK_DOT2(2, 1, 2), SK_DOT2(2, 1, 4),
-    SK_DOT2(2, 2, 1), SK_DOT2(2, 2, 2), SK_DOT2(2, 2, 4),
-    SK_DOT2(2, 4, 1), SK_DOT2(2, 4, 2),
-    SK_DOT2(2, 8, 1),
-    SK_DOT2(4, 1, 1), SK_DOT2(4, 1, 2), SK_DOT2(4, 1, 4),
-    SK_DOT2(4, 2, 1), SK_DOT2(4, 2, 2),
-    SK_DOT2(4, 4, 1), SK_DOT2(4, 4, 2),
-    SK_DOT2(4, 8, 1),
-    SK_DOT2(8, 1, 1), SK_DOT2(8, 1, 2),
-    SK_DOT2(8, 2, 1),
-    SK_DOT2(8, 4, 1),
-    SK_MFMA(1, 1, 1), SK_MFMA(1, 1, 2), SK_MFMA(1, 1, 4),
-    SK_MFMA(1, 2, 1), SK_MFMA(1, 2, 2), SK_MFMA(1, 2, 4),
-    SK_MFMA(1, 4, 1), SK_MFMA(1, 4, 2),
-    SK_MFMA(2, 1, 1), SK_MFMA(2, 1, 2), SK_MFMA(2, 1, 4),
-    SK_MFMA(2, 2, 1), SK_MFMA(2, 2, 2), SK_MFMA(2, 2, 4),
-    SK_MFMA(2, 4, 1), SK_MFMA(2, 4, 2),
-    SK_MFMA(4, 1, 1), SK_MFMA(4, 1, 2),
-    SK_MFMA(4, 2, 1), SK_MFMA(4, 2, 2),
-    // MFMAX: rows field = waves (16 rows each)
-    SK_MFMAX(1, 1), SK_MFMAX(1, 2), SK_MFMAX(1, 4), SK_MFMAX(1, 8),
-    SK_MFMAX(2, 2), SK_MFMAX(2, 4), SK_MFMAX(2, 8),
-    SK_MFMAX(4, 4), SK_MFMAX(4, 8),
-    SK_MFMAW(1, 1, 4, 2), SK_MFMAW(1, 2, 1, 2), SK_MFMAW(1, 2, 2, 2), SK_MFMAW(1, 2, 4, 2), SK_MFMAW(1, 4, 4, 2),
-    SK_MFMAW(2, 1, 4, 2), SK_MFMAW(2, 2, 1, 2), SK_MFMAW(2, 2, 2, 2), SK_MFMAW(2, 2, 4, 2), SK_MFMAW(2, 2, 8, 2),
-    SK_MFMAW(2, 4, 4, 2), SK_MFMAW(4, 1, 4, 2), SK_MFMAW(4, 2, 2, 2), SK_MFMAW(4, 2, 4, 2),
-    SK_MFMAW(1, 1, 4, 1), SK_MFMAW(1, 2, 2, 1), SK_MFMAW(1, 2, 4, 1), SK_MFMAW(1, 2, 8, 1), SK_MFMAW(1, 4, 4, 1),
-    SK_MFMAW(2, 2, 2, 1), SK_MFMAW(2, 2, 4, 1), SK_MFMAW(2, 2, 8, 1), SK_MFMAW(2, 4, 4, 1),
-    SK_MFMAW(4, 2, 2, 1), SK_MFMAW(4, 2, 4, 1),
-#define SK_RGS_ROWS(X, T, U) X(T, 1, U), X(T, 2, U), X(T, 4, U), X(T, 7, U), X(T, 13, U), X(T, 14, U)
-    SK_RGS_ROWS(SK_MFMA4, 1, 2), SK_RGS_ROWS(SK_MFMA4, 2, 2), SK_RGS_ROWS(SK_MFMA4, 4, 2),
-    SK_RGS_ROWS(SK_MFMA4, 1, 3), SK_RGS_ROWS(SK_MFMA4, 2, 3), SK_RGS_ROWS(SK_MFMA4, 4, 3),
-    SK_MFMA4(8, 1, 2), SK_MFMA4(8, 2, 2), SK_MFMA4(8, 4, 2), SK_MFMA4(8, 7, 2),
-    SK_MFMA4(8, 1, 3), SK_MFMA4(8, 2, 3), SK_MFMA4(8, 4, 3), SK_MFMA4(8, 7, 3),
-    SK_RGS_ROWS(SK_DOT2W, 1, 2), SK_RGS_ROWS(SK_DOT2W, 2, 2), SK_RGS_ROWS(SK_DOT2W, 4, 2),
-    SK_RGS_ROWS(SK_DOT2W, 1, 3), SK_RGS_ROWS(SK_DOT2W, 2, 3), SK_RGS_ROWS(SK_DOT2W, 4, 3),
-    // 8 tokens x 13 or 14 row groups would not fit the 256 VGPRs dot2 operands live in
-    SK_DOT2W(8, 1, 2), SK_DOT2W(8, 2, 2), SK_DOT2W(8, 4, 2), SK_DOT2W(8, 7, 2),
-    SK_DOT2W(8, 1, 3), SK_DOT2W(8, 2, 3), SK_DOT2W(8, 4, 3), SK_DOT2W(8, 7, 3),
+#include "instances.def"
 };
+#undef SK_PAIR
 
 const KernelInfo *kernel_table(int *count)
 {

@@ -71,6 +71,12 @@ int env_int(const char *name, int dflt)
     return (v && *v) ? atoi(v) : dflt;
 }
 
+double env_double(const char *name, double dflt)
+{
+    const char *v = getenv(name);
+    return (v && *v) ? strtod(v, nullptr) : dflt;
+}
+
 skinny_status hip_fail(hipError_t e, const char *what)
 {
     set_error("%s: %s", what, hipGetErrorString(e));
@@ -461,10 +467,10 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     // need not be among the fastest at M = 16 -- and single timings differ by
     // a few per cent from run to run.
     const int refine = env_int("SKINNY_TUNE_REFINE", 4);
-    // The fastest of candidates `top` at M = m, each timed three times
-    // round-robin (best of three); -1 if none ran.
-    auto fastest_at = [&](int m, const std::vector<int> &top, int &pick) -> hipError_t {
-        std::vector<double> best(top.size(), -1.0);
+    // Candidates `top` at M = m, each timed three times round-robin: best[c]
+    // is the best of three of top[c] (-1 if it did not run).
+    auto times_at = [&](int m, const std::vector<int> &top, std::vector<double> &best) -> hipError_t {
+        best.assign(top.size(), -1.0);
         a.M = m;
         for (int round = 0; round < 3; ++round)
             for (size_t c = 0; c < top.size(); ++c) {
@@ -475,6 +481,14 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
                 if (us >= 0 && (best[c] < 0 || us < best[c]))
                     best[c] = us;
             }
+        return hipSuccess;
+    };
+    // The fastest of candidates `top` at M = m; -1 if none ran.
+    auto fastest_at = [&](int m, const std::vector<int> &top, int &pick) -> hipError_t {
+        std::vector<double> best;
+        hipError_t e = times_at(m, top, best);
+        if (e != hipSuccess)
+            return e;
         pick = -1;
         for (size_t c = 0; c < top.size(); ++c)
             if (best[c] >= 0 && (pick < 0 || best[c] < best[(size_t)pick]))
@@ -530,6 +544,46 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
                 table[m - 1] = cand[pick];
         }
     }
+    // Fourth pass: the dot2 paths are the arithmetic meant for token counts
+    // up to 8, so at M <= 8 the fastest of the two quickest dot2 candidates
+    // (DOT2, DOT2R, DOT2W) that serve M replaces the table's choice when it
+    // is within SKINNY_TUNE_DOT2_MARGIN (relative, default 0.01) of it, both
+    // timed again at M.  A negative margin turns the preference off.
+    const double margin = env_double("SKINNY_TUNE_DOT2_MARGIN", 0.01);
+    if (s == SKINNY_OK && refine > 1 && margin >= 0) {
+        for (int m = 1; m <= 8 && m <= SKINNY_MAX_M; ++m) {
+            if (is_dot2_path(table[m - 1].path))
+                continue;
+            int cur = -1;
+            for (int i = 0; i < count && cur < 0; ++i)
+                if (memcmp(&cand[i], &table[m - 1], sizeof(skinny_tactic)) == 0)
+                    cur = i;
+            std::vector<int> dots;
+            for (int i = 0; i < count; ++i)
+                if (times[i] >= 0 && cand[i].mt >= m && is_dot2_path(cand[i].path))
+                    dots.push_back(i);
+            if (cur < 0 || dots.empty())
+                continue;
+            std::sort(dots.begin(), dots.end(), [&](int x, int y) { return times[x] < times[y]; });
+            std::vector<int> top{cur};
+            top.insert(top.end(), dots.begin(), dots.begin() + std::min<size_t>(2, dots.size()));
+            std::vector<double> t;
+            HIP_TRY(times_at(m, top, t));
+            int best = -1;
+            for (size_t c = 1; c < top.size(); ++c)
+                if (t[c] >= 0 && (best < 0 || t[c] < t[(size_t)best]))
+                    best = (int)c;
+            if (best < 0 || t[0] < 0)
+                continue;
+            const bool take = t[(size_t)best] <= (1.0 + margin) * t[0];
+            if (env_flag("SKINNY_LOG"))
+                fprintf(stderr, "[skinny] N=%d K=%d M=%d: dot2 path %d at %.3f us, path %d at %.3f us, gap %+.1f %%%s\n",
+                        N, K, m, cand[top[(size_t)best]].path, t[(size_t)best], table[m - 1].path, t[0],
+                        100.0 * (t[(size_t)best] / t[0] - 1.0), take ? ": dot2 taken" : "");
+            if (take)
+                table[m - 1] = cand[top[(size_t)best]];
+        }
+    }
     if (env_int("SKINNY_LOG", 0) >= 2) {
         for (int i = 0; i < count; ++i)
             fprintf(stderr, "[skinny] cand N=%d K=%d path=%d mt=%d rows=%d waves=%d unroll=%d split=%d : %.3f us\n",
@@ -541,66 +595,6 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
                 od == SKINNY_OUT_F32 ? "f32" : "bf16", count, copies);
     }
     return s;
-}
-
-// ---------------------------------------------------------------------------
-// Tuned tables persisted across processes (SKINNY_TABLE_CACHE=<file>), keyed
-// like the pages' per-part measured tables by the chip (arch, CU count) and
-// the shape.  One line per table:
-//   skinny-table v2 <arch> <cus> <N> <K> <bf16|f16 in> <bf16|f32 out> <64 x path.mt.rows.waves.unroll.split>
-// A line whose tactics fail validation is ignored.  Writers append.
-// ---------------------------------------------------------------------------
-const char *kTableTag = "skinny-table";
-
-bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
-                     std::array<skinny_tactic, SKINNY_MAX_M> &table)
-{
-    FILE *f = fopen(path, "r");
-    if (!f)
-        return false;
-    char line[8192];
-    bool found = false;
-    while (!found && fgets(line, sizeof line, f)) {
-        char tag[32], ver[8], arch[32], ins[8], ods[8];
-        int c, n, k, pos = 0;
-        if (sscanf(line, "%31s %7s %31s %d %d %d %7s %7s%n", tag, ver, arch, &c, &n, &k, ins, ods, &pos) != 8)
-            continue;
-        if (strcmp(tag, kTableTag) || strcmp(ver, "v2") || strcmp(arch, "gfx950") || c != cus ||
-            n != N || k != K || strcmp(ins, half ? "f16" : "bf16") ||
-            strcmp(ods, od == SKINNY_OUT_F32 ? "f32" : "bf16"))
-            continue;
-        std::array<skinny_tactic, SKINNY_MAX_M> t;
-        const char *q = line + pos;
-        bool ok = true;
-        for (int m = 1; m <= SKINNY_MAX_M && ok; ++m) {
-            skinny_tactic &e = t[m - 1];
-            int used = 0;
-            ok = sscanf(q, " %d.%d.%d.%d.%d.%d%n", &e.path, &e.mt, &e.rows, &e.waves, &e.unroll,
-                        &e.split, &used) == 6 &&
-                 skinny_tactic_check(&e, N, K) == SKINNY_OK && e.mt >= m;
-            q += used;
-        }
-        if (ok) {
-            table = t;
-            found = true;
-        }
-    }
-    fclose(f);
-    return found;
-}
-
-void save_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
-                     const std::array<skinny_tactic, SKINNY_MAX_M> &table)
-{
-    FILE *f = fopen(path, "a");
-    if (!f)
-        return;
-    fprintf(f, "%s v2 gfx950 %d %d %d %s %s", kTableTag, cus, N, K, half ? "f16" : "bf16",
-            od == SKINNY_OUT_F32 ? "f32" : "bf16");
-    for (const skinny_tactic &e : table)
-        fprintf(f, " %d.%d.%d.%d.%d.%d", e.path, e.mt, e.rows, e.waves, e.unroll, e.split);
-    fprintf(f, "\n");
-    fclose(f);
 }
 
 skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int dev, int nxcd,

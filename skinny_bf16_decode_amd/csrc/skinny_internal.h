@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <array>
+
 #include "../../include/skinny.h"
 
 namespace skinny {
@@ -101,8 +103,22 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8);
 // Thread-local error text.
 void set_error(const char *fmt, ...);
 
+// Stored tuned tables (tables.cpp): one text line per (chip, N, K, input and
+// output type).  parse_table_line fills `table` and returns true only for a
+// whole, valid line for this key; load_table_file returns the first such line
+// of a file; format_table_line writes one into buf (cap >= 8192 bytes holds
+// any table); save_table_file appends one.
+bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_out_dtype od,
+                      std::array<skinny_tactic, SKINNY_MAX_M> &table);
+bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
+                     std::array<skinny_tactic, SKINNY_MAX_M> &table);
+void format_table_line(int cus, int N, int K, int half, skinny_out_dtype od,
+                       const std::array<skinny_tactic, SKINNY_MAX_M> &table, char *buf, size_t cap);
+void save_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
+                     const std::array<skinny_tactic, SKINNY_MAX_M> &table);
+
 // Rows of W per tile and tile count for a tactic.
-inline int tiles_for(const skinny_tactic &t, int N) { return (N + t.rows - 1) / t.rows; }
+inline int tiles_for(const skinny_tactic &t, int N) { return (int)(((long long)N + t.rows - 1) / t.rows); }
 
 constexpr int kMaxWaves = 8;
 // A buffer load whose offset is at or past its resource's size reads zero and
@@ -159,6 +175,11 @@ inline size_t rgs_node_floats(const skinny_tactic &t) { return (size_t)rgs_q(t) 
 // K chunks per row-group stream stage (one per block of the 16-block MFMA)
 constexpr int kRgsChunks = 16;
 inline bool is_rgs_path(int path) { return path == SKINNY_PATH_MFMA4 || path == SKINNY_PATH_DOT2W; }
+// the v_dot2 kernels
+inline bool is_dot2_path(int path)
+{
+    return path == SKINNY_PATH_DOT2 || path == SKINNY_PATH_DOT2R || path == SKINNY_PATH_DOT2W;
+}
 // Kernel families measured and removed (their path numbers stay reserved, so a
 // stored table that names one is refused, not misread).
 inline bool is_retired_path(int path)

@@ -152,14 +152,16 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
                   t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
-    const size_t lds_limit = (t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
-    if (tactic_lds_bytes(*t, k8) > lds_limit) {
-        set_error("tactic needs %zu bytes of LDS (limit %zu)", tactic_lds_bytes(*t, k8), lds_limit);
-        return SKINNY_ERR_INVALID_ARG;
-    }
+    // the instance first: its fields are then small, so the LDS sizes below
+    // cannot overflow
     if (!tactic_kernel(*t)) {
         set_error("no compiled kernel for path=%d mt=%d rows=%d unroll=%d", t->path, t->mt, t->rows,
                   t->unroll);
+        return SKINNY_ERR_INVALID_ARG;
+    }
+    const size_t lds_limit = (t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
+    if (tactic_lds_bytes(*t, k8) > lds_limit) {
+        set_error("tactic needs %zu bytes of LDS (limit %zu)", tactic_lds_bytes(*t, k8), lds_limit);
         return SKINNY_ERR_INVALID_ARG;
     }
     return SKINNY_OK;
@@ -207,19 +209,19 @@ int skinny_enumerate_tactics_ex(int N, int K, int cus, skinny_tactic *buf, int c
                         // ceil(N / ranges) rows leaves none of its 4-row groups empty
                         if (w > 4 || s > 4)
                             continue;
-                        const int per_round = (cus + s - 1) / s;
-                        const int ranges0 = (N + k.rows - 1) / k.rows;
-                        const int ranges = ((ranges0 + per_round - 1) / per_round) * per_round;
-                        const int most = (N + ranges - 1) / std::min(N, ranges);
+                        const long long per_round = ((long long)cus + s - 1) / s;
+                        const long long ranges0 = ((long long)N + k.rows - 1) / k.rows;
+                        const long long ranges = ((ranges0 + per_round - 1) / per_round) * per_round;
+                        const long long most = ((long long)N + ranges - 1) / std::min<long long>(N, ranges);
                         if (most <= k.rows - 4)
                             continue;
                     }
                     if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                         continue;
-                    const int tiles = (N + t.rows - 1) / t.rows;
-                    if (s > 1 && tiles * w >= 8 * cus && path != SKINNY_PATH_MFMAW && !is_rgs_path(path))
+                    const long long tiles = ((long long)N + t.rows - 1) / t.rows, chip = 8LL * cus;
+                    if (s > 1 && tiles * w >= chip && path != SKINNY_PATH_MFMAW && !is_rgs_path(path))
                         continue;   // enough waves already; a K split only adds traffic
-                    if (path == SKINNY_PATH_DOT2R && tiles * s > 8 * cus)
+                    if (path == SKINNY_PATH_DOT2R && tiles * s > chip)
                         continue;   // many workgroups per CU balance themselves
                     if (path == SKINNY_PATH_DOT2) {
                         // each lane of the workgroup should own at least one chunk per
