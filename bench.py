@@ -253,19 +253,128 @@ def use_tables(retune, cus, wl):
     """Point SKINNY_TABLE_CACHE at a temporary copy of the shipped tables
     (unless the caller set it, or asked to retune); say where the timed
     shape's table comes from."""
-    if os.environ.get("SKINNY_TABLE_CACHE"):
+    global _OWN_TABLE_COPY
+    if os.environ.get("SKINNY_TABLE_CACHE") and not _OWN_TABLE_COPY:
         return f"SKINNY_TABLE_CACHE={os.environ['SKINNY_TABLE_CACHE']}"
     if retune:
         return "tuned on this GPU (--retune)"
-    fd, path = tempfile.mkstemp(prefix="skinny_tables_", suffix=".txt")
-    os.close(fd)
-    shutil.copyfile(SHIPPED_TABLES, path)
-    os.environ["SKINNY_TABLE_CACHE"] = path
+    if not _OWN_TABLE_COPY:
+        fd, path = tempfile.mkstemp(prefix="skinny_tables_", suffix=".txt")
+        os.close(fd)
+        shutil.copyfile(SHIPPED_TABLES, path)
+        os.environ["SKINNY_TABLE_CACHE"] = path
+        _OWN_TABLE_COPY = path
     with open(SHIPPED_TABLES) as f:
         key = ["skinny-table", "v2", "gfx950", str(cus), str(wl.n), str(wl.k), "bf16", "bf16"]
         if any(line.split()[:8] == key for line in f):
             return f"shipped ({os.path.relpath(SHIPPED_TABLES, ROOT)}, {cus} CUs)"
     return f"tuned on this GPU (no shipped table for {cus} CUs)"
+
+
+_OWN_TABLE_COPY = None
+
+
+def time_workload(setup, stream, steps, warmup, per_m_reps):
+    """Time `steps` steps of the workload's M sweep (graphs of STEPS_PER_GRAPH
+    steps, HIP events on `stream`), check the last call's output, and take
+    the per-M times, the read ceiling and the empty-launch floor."""
+    import torch
+    wl = setup.wl
+    sweep = tuple(wl.m_values)
+    for m in sweep:
+        log(f"  {wl.name} M={m:2d}: {setup.plans[0].describe(m)}")
+    # Graphs of one step and of STEPS_PER_GRAPH consecutive steps, one per
+    # starting copy offset: a captured decode forward pass holds many
+    # projections in one graph, so the time between graph launches is spread
+    # over 16 steps rather than paid by every step.  Each step is the same
+    # calls either way; `steps` steps are exactly that many steps.
+    calls = len(sweep)
+    offsets = sorted({(calls * s) % setup.copies for s in range(setup.copies)})
+    graphs, big = {}, {}
+    for off in offsets:
+        graphs[off] = capture(lambda off=off: [setup.run(off + j, m) for j, m in enumerate(sweep)], stream)
+        big[off] = capture(lambda off=off: [setup.run(off + j, sweep[j % calls])
+                                            for j in range(calls * STEPS_PER_GRAPH)], stream)
+
+    def replay_steps(first, count):
+        i = first
+        while i < first + count:
+            off = (calls * i) % setup.copies
+            if first + count - i >= STEPS_PER_GRAPH:
+                big[off].replay()
+                i += STEPS_PER_GRAPH
+            else:
+                graphs[off].replay()
+                i += 1
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):        # replays, and the events, on `stream`
+        replay_steps(0, warmup)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        t0 = time.perf_counter()
+        replay_steps(warmup, steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed = e0.elapsed_time(e1) / 1e3
+    ms_per_step = 1e3 * elapsed / steps
+    value = calls * wl.weight_bytes * steps / elapsed / 1e9
+    us_per_launch = 1e6 * elapsed / (calls * steps)
+    log(f"{wl.name}: timed {steps} steps: {ms_per_step * 1e3:.2f} us/step, {us_per_launch:.2f} us/call, "
+        f"{value:.1f} GB/s weight stream ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s); host wall {wall:.3f}s")
+    # the last call of the last step
+    last_copy = (calls * (warmup + steps) - 1) % setup.copies
+    rep = parity_of_last(setup, last_copy, sweep[-1])
+    log(f"parity of the last call (M={sweep[-1]}, copy {last_copy}): {rep}")
+    if not rep.ok:
+        print(f"parity failure ({wl.name}): {rep}", file=sys.stderr)
+        sys.exit(3)
+    per_m = {}
+    for m in sweep:
+        us = setup.per_m(stream, m, reps=per_m_reps)
+        gb = wl.weight_bytes / us / 1e3
+        per_m[str(m)] = {"us_per_call": round(us, 3), "weight_gbps": round(gb, 1),
+                         "pct_peak": round(100 * gb / PEAK_GBPS, 1)}
+        log(f"  {wl.name} M={m:2d}: {us:7.2f} us/call  {gb:7.1f} GB/s  {100 * gb / PEAK_GBPS:5.1f}%")
+    ceil_us, ceil_gb = read_ceiling(setup, stream)
+    floor_us = empty_floor(stream)
+    log(f"{wl.name}: read ceiling (plain nt stream of the same rotated weights): {ceil_us:.2f} us, "
+        f"{ceil_gb:.1f} GB/s; empty-launch floor {floor_us:.2f} us")
+    return {"value": value, "ms_per_step": ms_per_step, "us_per_launch": us_per_launch, "per_m": per_m,
+            "read_ceiling_gbps": ceil_gb, "read_ceiling_us": ceil_us, "empty_launch_us": floor_us}
+
+
+def summary(setup, res, table_source):
+    """The JSON fields of one timed workload: per-M times, the step's
+    roofline (algorithmic bytes per launch / average launch time against the
+    8 TB/s peak, and the counted HBM traffic per launch when the committed
+    record matches this kernel source), read ceiling and launch floor."""
+    wl = setup.wl
+    sweep = tuple(wl.m_values)
+    algo = sum(algorithmic_bytes(wl.n, wl.k, m) for m in sweep) / len(sweep)
+    achieved = algo / res["us_per_launch"] / 1e3
+    traffic = counted_traffic(setup)
+    if traffic is not None:
+        traffic = round(traffic)
+        log(f"{wl.name}: counted HBM traffic per launch: {traffic} B (algorithmic {round(algo)} B)")
+    return {
+        "workload": f"{wl.name} [{wl.n}, {wl.k}], M in {list(sweep)}, {setup.copies} rotated weight copies",
+        "us_per_call": round(res["us_per_launch"], 3),
+        "pct_of_peak": round(100 * res["value"] / PEAK_GBPS, 1),
+        "weight_gbps": round(res["value"], 1),
+        "per_m": res["per_m"],
+        "read_ceiling_gbps": round(res["read_ceiling_gbps"], 1),
+        "read_ceiling_us": round(res["read_ceiling_us"], 3),
+        "empty_launch_us": round(res["empty_launch_us"], 3),
+        "parity_last_call": "ok",
+        "tactic_table": table_source,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "skinny projection launches of the step (the per-M table's kernels)",
+                     "bytes_per_launch": round(algo), "us_per_launch": round(res["us_per_launch"], 3)},
+    }
 
 
 def main():
@@ -283,6 +392,8 @@ def main():
                     help="tune the tactic tables on this GPU instead of loading the shipped ones")
     ap.add_argument("--workload", type=int, default=WORKLOAD, choices=(2, 3, 5),
                     help="the decode weight whose M sweep is timed (3, the packed 6288x7168, is the headline)")
+    ap.add_argument("--no-second", action="store_true",
+                    help="skip the square 3584x7168 sweep reported beside the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -307,102 +418,40 @@ def main():
     setup = Setup(args.workload)
     wl = setup.wl
     log(f"workload {wl.name}: prepare {setup.prepare_s:.2f}s")
-    for m in sweep:
-        log(f"  M={m:2d}: {setup.plans[0].describe(m)}")
     stream = torch.cuda.Stream()
-
-    # Graphs of one step and of STEPS_PER_GRAPH consecutive steps, one per
-    # starting copy offset (6 calls per step over 4 copies): a captured decode
-    # forward pass holds many projections in one graph, so the time between
-    # graph launches is spread over 16 steps rather than paid by every step.
-    # Each step is the same six calls either way; K steps are exactly K steps.
-    calls = len(sweep)
-    offsets = sorted({(calls * s) % setup.copies for s in range(setup.copies)})
-    graphs, big = {}, {}
-    for off in offsets:
-        graphs[off] = capture(lambda off=off: [setup.run(off + j, m) for j, m in enumerate(sweep)],
-                              stream)
-        big[off] = capture(lambda off=off: [setup.run(off + j, sweep[j % calls])
-                                            for j in range(calls * STEPS_PER_GRAPH)], stream)
-
-    def replay_steps(first, count):
-        i = first
-        while i < first + count:
-            off = (calls * i) % setup.copies
-            if first + count - i >= STEPS_PER_GRAPH:
-                big[off].replay()
-                i += STEPS_PER_GRAPH
-            else:
-                graphs[off].replay()
-                i += 1
-
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):        # replays, and the events, on `stream`
-        replay_steps(0, args.warmup)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        t0 = time.perf_counter()
-        replay_steps(args.warmup, args.steps)
-        e1.record(stream)
-        torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    elapsed = e0.elapsed_time(e1) / 1e3
-    ms_per_step = 1e3 * elapsed / args.steps
-    weight_bytes_step = calls * wl.weight_bytes
-    value = weight_bytes_step * args.steps / elapsed / 1e9
-    launches = calls * args.steps
-    us_per_launch = 1e6 * elapsed / launches
-    algo_per_launch = sum(algorithmic_bytes(wl.n, wl.k, m) for m in sweep) / calls
-    achieved = algo_per_launch / us_per_launch / 1e3
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {us_per_launch:.2f} us/call, "
-        f"{value:.1f} GB/s weight stream ({100 * value / PEAK_GBPS:.1f}% of 8 TB/s); host wall {wall:.3f}s")
-
-    # the last call of the last step
-    last_copy = (calls * (args.warmup + args.steps) - 1) % setup.copies
-    rep = parity_of_last(setup, last_copy, sweep[-1])
-    log(f"parity of the last call (M={sweep[-1]}, copy {last_copy}): {rep}")
-    if not rep.ok:
-        print(f"parity failure: {rep}", file=sys.stderr)
-        sys.exit(3)
-
-    per_m = {}
-    for m in sweep:
-        us = setup.per_m(stream, m, reps=args.per_m_reps)
-        gb = wl.weight_bytes / us / 1e3
-        per_m[str(m)] = {"us_per_call": round(us, 3), "weight_gbps": round(gb, 1),
-                         "pct_peak": round(100 * gb / PEAK_GBPS, 1)}
-        log(f"  M={m:2d}: {us:7.2f} us/call  {gb:7.1f} GB/s  {100 * gb / PEAK_GBPS:5.1f}%")
-    ceil_us, ceil_gb = read_ceiling(setup, stream)
-    floor_us = empty_floor(stream)
-    log(f"read ceiling (plain nt stream of the same rotated weights): {ceil_us:.2f} us, "
-        f"{ceil_gb:.1f} GB/s; empty-launch floor {floor_us:.2f} us")
-
+    res = time_workload(setup, stream, args.steps, args.warmup, args.per_m_reps)
     if args.calibrate:
         calibration_kernels(setup, stream)
     if args.extra:
         extra_workloads(stream)
         oracle_small_workloads()
+    # the other target weight: the square [3584, 7168] sweep from its shipped
+    # table, reported beside the headline (not part of `value`)
+    other = None
+    if args.workload == WORKLOAD and not args.no_second:
+        table_source2 = use_tables(args.retune, props.multi_processor_count, si.WORKLOADS[2])
+        log(f"tactic table (square weight): {table_source2}")
+        setup2 = Setup(2)
+        res2 = time_workload(setup2, stream, max(1, args.steps // 2), max(1, args.warmup // 2), args.per_m_reps)
+        other = summary(setup2, res2, table_source2)
+        del setup2
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(setup)
         log(f"cpu baseline: {cpu}")
 
-    traffic = counted_traffic(setup)
-    if traffic is not None:
-        traffic = round(traffic)
-        log(f"counted HBM traffic per launch: {traffic} B (algorithmic {round(algo_per_launch)} B)")
     line = {
         "metric": ("µs/call and weight-stream HBM GB/s (% of peak), 6288x7168 at M=1..32"
                    if args.workload == WORKLOAD else
                    f"µs/call and weight-stream HBM GB/s (% of peak), {wl.n}x{wl.k} at M={sweep[0]}..{sweep[-1]}"),
-        "value": round(value, 1),
+        "value": round(res["value"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(res["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -412,19 +461,12 @@ def main():
                                f"one step = M in {list(sweep)}, BF16 in/out, fp32 accumulate, "
                                f"{setup.copies} rotated weight copies, hipGraph replay",
                    "N": wl.n, "K": wl.k, "m_values": list(sweep), "weight_copies": setup.copies},
-        "us_per_call": round(us_per_launch, 3),
-        "pct_of_peak": round(100 * value / PEAK_GBPS, 1),
-        "per_m": per_m,
-        "read_ceiling_gbps": round(ceil_gb, 1),
-        "empty_launch_us": round(floor_us, 3),
-        "parity_last_call": "ok",
-        "tactic_table": table_source,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "skinny projection launches of the step (the per-M table's kernels)",
-                     "bytes_per_launch": round(algo_per_launch), "us_per_launch": round(us_per_launch, 3)},
-        "cpu_baseline": cpu,
     }
+    main_summary = summary(setup, res, table_source)
+    line.update({k: v for k, v in main_summary.items() if k not in ("workload",)})
+    line["cpu_baseline"] = cpu
+    if other is not None:
+        line["square_3584x7168"] = other
     print(json.dumps(line), flush=True)
 
 

@@ -190,32 +190,31 @@ def test_decode_workloads(sk, cid):
     plan2.close()
 
 
-def test_long_k_split_workload_sampled(sk):
-    """[7168, 18432] at its timed token counts, checked on 4096 sampled outputs
-    per M, plus a forced cross-workgroup split-K tactic on both paths."""
+def test_long_k_split_workload(sk):
+    """[7168, 18432] at its timed token counts, tuned, and with a forced
+    four-way cross-workgroup K split on the DOT2 and MFMA paths: the whole
+    output against the oracle."""
     import torch
     cid = 5
     wl = si.WORKLOADS[cid]
     w_bits = si.weight(cid)
     x_bits = si.activations(cid)
-    rng = np.random.default_rng(55)
+    t0 = time.time()
+    o, sv = oracle.gemm(x_bits, w_bits)
+    _say(f"[cfg5] oracle {time.time() - t0:.1f}s")
     w = gu.dev_bf16(w_bits)
     plans = {"tuned": sk.Prepared(w, torch.bfloat16),
              "split4": sk.Prepared(w, torch.bfloat16, table=[
                  sk.Tactic(0, 8, 4, 4, 1, 4) if m <= 8 else sk.Tactic(1, 64, 16, 4, 2, 4)
                  for m in range(1, 65)])}
     for m in wl.m_values:
-        mi = rng.integers(0, m, size=4096)
-        ni = rng.integers(0, wl.n, size=4096)
-        o, s = oracle.gemm_sampled(x_bits, w_bits, mi, ni)
         for name, plan in plans.items():
             x = gu.dev_bf16(x_bits[:m])
             out = gu.out_buffer(wl.n, torch.bfloat16)
             plan.run(x, out[:m])
             torch.cuda.synchronize()
             assert gu.sentinel_intact(out, m)
-            got = gu.values(out)[mi, ni]
-            _bound_check(got, o, s, "bf16", f"cfg5 {name} M={m} {plan.describe(m)}")
+            _bound_check(gu.values(out)[:m], o[:m], sv[:m], "bf16", f"cfg5 {name} M={m} {plan.describe(m)}")
     for p in plans.values():
         p.close()
 
@@ -279,46 +278,119 @@ DECODE_KERNEL_SETS = {
 }
 
 
-def shipped_decode_table(sk):
-    """The 64-entry table the benchmark loads for the packed 6288x7168 weight
-    (BF16 in and out), from the file shipped with the package."""
+def shipped_table(sk, n, k):
+    """The 64-entry table the benchmark loads for an [n, k] weight (BF16 in
+    and out, 256 CUs), from the file shipped with the package."""
     path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                         "skinny_bf16_decode_amd", "tables", "mi355x_tuned.txt")
     with open(path) as f:
         for line in f:
             p = line.split()
-            if p[4:8] == ["6288", "7168", "bf16", "bf16"]:
+            if p[3:8] == ["256", str(n), str(k), "bf16", "bf16"]:
                 return [sk.Tactic(*map(int, e.split("."))) for e in p[8:]]
-    raise AssertionError("no shipped table for 6288x7168")
+    raise AssertionError(f"no shipped table for {n}x{k}")
 
 
-@pytest.mark.parametrize("kernels", sorted(DECODE_KERNEL_SETS) + ["shipped"])
+# the weights with a shipped table, by workload id
+SHIPPED = {2: (3584, 7168), 3: (6288, 7168), 5: (7168, 18432)}
+
+
+@pytest.mark.parametrize("cid", sorted(SHIPPED))
+def test_shipped_tables_exact_full_size(sk, cid):
+    """The shipped table of each decode weight, forced, on integer inputs at
+    the full shape (x, W in {-3..3}, so every partial sum is exact in fp32):
+    every M = 1..64 -- each kernel the table uses, at each M it serves --
+    bit for bit, fp32 out equal to the oracle and BF16 out to its nearest-even
+    rounding."""
+    import torch
+    n, k = SHIPPED[cid]
+    x_bits, w_bits = si.small_int_case(9000 + cid, 64, n, k)
+    t0 = time.time()
+    o, _ = oracle.gemm(x_bits, w_bits)
+    _say(f"[shipped exact {n}x{k}] oracle {time.time() - t0:.1f}s")
+    assert np.all(np.abs(o) < 2 ** 24)
+    table = shipped_table(sk, n, k)
+    w = gu.dev_bf16(w_bits)
+    for od in (torch.bfloat16, torch.float32):
+        plan = sk.Prepared(w, od, table=table)
+        for m in range(1, 65):
+            _check_exact(sk, plan, x_bits, o, m, f"{n}x{k} {od} M={m} {table[m - 1]}")
+        plan.close()
+
+
+@pytest.mark.parametrize("cid", sorted(SHIPPED))
+def test_shipped_tables_random_full_size(sk, cid):
+    """The shipped table of each decode weight on its seeded workload at the
+    full shape: the whole output within the stated bound at the benchmark's
+    token counts and at ragged ones, bit-identical over repeats and over graph
+    replays with eager work between them (the launch configuration
+    bench.py times)."""
+    import torch
+    wl = si.WORKLOADS[cid]
+    n, k = SHIPPED[cid]
+    w_bits, x_bits = si.weight(cid, 0), si.activations(cid)
+    t0 = time.time()
+    o, sv = oracle.gemm(x_bits, w_bits)
+    _say(f"[shipped random {n}x{k}] oracle {time.time() - t0:.1f}s")
+    w, x = gu.dev_bf16(w_bits), gu.dev_bf16(x_bits)
+    plan = sk.Prepared(w, torch.bfloat16, table=shipped_table(sk, n, k))
+    ms = sorted(set(wl.m_values) | {3, 7, 13, 31, 47, 64})
+    ref = {}
+    for m in ms:
+        out = gu.out_buffer(n, torch.bfloat16)
+        plan.run(x[:m], out[:m])
+        torch.cuda.synchronize()
+        assert gu.sentinel_intact(out, m), f"M={m}: rows >= M were written"
+        ref[m] = gu.host_bits(out).copy()
+        _bound_check(si.bf16_bits_to_f32(ref[m][:m]).astype(np.float64), o[:m], sv[:m], "bf16",
+                     f"shipped {n}x{k} M={m} {plan.describe(m)}")
+        for _ in range(3):
+            out2 = gu.out_buffer(n, torch.bfloat16)
+            plan.run(x[:m], out2[:m])
+            torch.cuda.synchronize()
+            assert np.array_equal(gu.host_bits(out2), ref[m]), f"M={m}: repeat differs"
+    timed = list(wl.m_values)
+    outs = {m: gu.out_buffer(n, torch.bfloat16) for m in timed}
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for m in timed:
+                plan.run(x[:m], outs[m][:m])
+    for rep in range(5):
+        for m in timed:
+            outs[m][:m].fill_(0)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for m in timed:
+            assert np.array_equal(gu.host_bits(outs[m]), ref[m]), (rep, m)
+    del g
+    plan.close()
+
+
+@pytest.mark.parametrize("kernels", sorted(DECODE_KERNEL_SETS))
 def test_decode_kernels_repeat_and_graph_replay(sk, kernels):
-    """The kernels of the packed 6288x7168 decode weight, forced, at full
+    """Kernel sets of the packed 6288x7168 decode weight, forced, at full
     size: bitwise identical over repeats and over graph replays with eager
-    work between them, and within the bound on 4096 sampled outputs per M.
-    "shipped" runs the benchmark's own table at the benchmark's token counts
-    (the launch configuration the benchmark times)."""
+    work between them, and the whole output within the bound."""
     import torch
     wl = si.WORKLOADS[3]
     w_bits, x_bits = si.weight(3, 0), si.activations(3)
     n = wl.n
     w = gu.dev_bf16(w_bits)
     x = gu.dev_bf16(x_bits)
-    if kernels == "shipped":
-        table = shipped_decode_table(sk)
-        forced = {m: table[m - 1] for m in (1, 2, 4, 8, 16, 32)}
-    else:
-        forced = DECODE_KERNEL_SETS[kernels](sk)
-        table = []
-        for m in range(1, 65):
-            fits = [t for mm, t in sorted(forced.items()) if mm >= m]
-            table.append(fits[0] if fits else sk.Tactic(3, 64, 128, 8, 1, 4))
+    o_all, s_all = oracle.gemm(x_bits, w_bits)
+    forced = DECODE_KERNEL_SETS[kernels](sk)
+    table = []
+    for m in range(1, 65):
+        fits = [t for mm, t in sorted(forced.items()) if mm >= m]
+        table.append(fits[0] if fits else sk.Tactic(3, 64, 128, 8, 1, 4))
     _say(f"[decode kernels {kernels}] {forced}")
     plan = sk.Prepared(w, torch.bfloat16, table=table)
     for m, t in forced.items():
         assert plan.tactic(m) == t, (m, plan.tactic(m))
-    rng = np.random.default_rng(606)
     ref = {}
     for m in forced:
         out = gu.out_buffer(n, torch.bfloat16)
@@ -331,11 +403,8 @@ def test_decode_kernels_repeat_and_graph_replay(sk, kernels):
             plan.run(x[:m], out2[:m])
             torch.cuda.synchronize()
             assert np.array_equal(gu.host_bits(out2), ref[m]), f"M={m}: repeat differs"
-        mi = rng.integers(0, m, size=4096)
-        ni = rng.integers(0, n, size=4096)
-        o, sv = oracle.gemm_sampled(x_bits[:m], w_bits, mi, ni)
-        got = si.bf16_bits_to_f32(ref[m][mi, ni]).astype(np.float64)
-        _bound_check(got, o, sv, "bf16", f"decode kernel M={m} {forced[m]}")
+        got = si.bf16_bits_to_f32(ref[m][:m]).astype(np.float64)
+        _bound_check(got, o_all[:m], s_all[:m], "bf16", f"decode kernel M={m} {forced[m]}")
     outs = {m: gu.out_buffer(n, torch.bfloat16) for m in forced}
     stream = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
