@@ -106,6 +106,7 @@ class Setup:
         import skinny_bf16_decode_amd as sk
         self.wl = si.WORKLOADS[cid]
         self.cid = cid
+        self.od = out_dtype
         self.copies = copies or self.wl.copies
         self.w_bits = [si.weight(cid, c) for c in range(self.copies)]
         self.x_bits = si.activations(cid)
@@ -185,9 +186,11 @@ def cpu_baseline(setup):
                       f"{step_s:.2f} s per step"}
 
 
-def traffic_record_path(wl):
-    """The committed HBM traffic record of a workload's M sweep."""
-    return os.path.join(ROOT, "profiles", f"skinny_projection_{wl.name}_msweep.traffic.json")
+def traffic_record_path(wl, od="bf16"):
+    """The committed HBM traffic record of a workload's M sweep (BF16 output,
+    or fp32 output with a _f32 suffix)."""
+    suffix = "_f32" if od == "f32" else ""
+    return os.path.join(ROOT, "profiles", f"skinny_projection_{wl.name}_msweep{suffix}.traffic.json")
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "skinny_projection_packed_qkvg_6288x7168_msweep.traffic.json")
@@ -221,7 +224,7 @@ def counted_traffic(setup):
     sweep = tuple(setup.wl.m_values)
     import json as _json
     from skinny_bf16_decode_amd import profiling
-    record = traffic_record_path(setup.wl)
+    record = traffic_record_path(setup.wl, setup.od)
     if not os.path.exists(record):
         return None
     with open(record) as f:
@@ -244,12 +247,15 @@ def parity_of_last(setup, last_copy, m, samples=4096):
     mi = rng.integers(0, m, size=samples)
     ni = rng.integers(0, setup.wl.n, size=samples)
     o, s = oracle.gemm_sampled(setup.x_bits, setup.w_bits[last_copy], mi, ni)
-    got = bf16_values(setup.out[last_copy])[mi, ni]
-    rep = oracle.check(got, o, s, "bf16")
+    if setup.od == "f32":
+        got = setup.out[last_copy].cpu().numpy().astype(np.float64)[mi, ni]
+    else:
+        got = bf16_values(setup.out[last_copy])[mi, ni]
+    rep = oracle.check(got, o, s, setup.od)
     return rep
 
 
-def use_tables(retune, cus, wl):
+def use_tables(retune, cus, wl, od="bf16"):
     """Point SKINNY_TABLE_CACHE at a temporary copy of the shipped tables
     (unless the caller set it, or asked to retune); say where the timed
     shape's table comes from."""
@@ -265,7 +271,7 @@ def use_tables(retune, cus, wl):
         os.environ["SKINNY_TABLE_CACHE"] = path
         _OWN_TABLE_COPY = path
     with open(SHIPPED_TABLES) as f:
-        key = ["skinny-table", "v2", "gfx950", str(cus), str(wl.n), str(wl.k), "bf16", "bf16"]
+        key = ["skinny-table", "v2", "gfx950", str(cus), str(wl.n), str(wl.k), "bf16", od]
         if any(line.split()[:8] == key for line in f):
             return f"shipped ({os.path.relpath(SHIPPED_TABLES, ROOT)}, {cus} CUs)"
     return f"tuned on this GPU (no shipped table for {cus} CUs)"
@@ -353,7 +359,8 @@ def summary(setup, res, table_source):
     record matches this kernel source), read ceiling and launch floor."""
     wl = setup.wl
     sweep = tuple(wl.m_values)
-    algo = sum(algorithmic_bytes(wl.n, wl.k, m) for m in sweep) / len(sweep)
+    out_bytes = 4 if setup.od == "f32" else 2
+    algo = sum(algorithmic_bytes(wl.n, wl.k, m, out_bytes) for m in sweep) / len(sweep)
     achieved = algo / res["us_per_launch"] / 1e3
     traffic = counted_traffic(setup)
     if traffic is not None:
@@ -390,8 +397,10 @@ def main():
                          "whose known byte counts scale the HBM traffic counters")
     ap.add_argument("--retune", action="store_true",
                     help="tune the tactic tables on this GPU instead of loading the shipped ones")
-    ap.add_argument("--workload", type=int, default=WORKLOAD, choices=(2, 3, 5),
-                    help="the decode weight whose M sweep is timed (3, the packed 6288x7168, is the headline)")
+    ap.add_argument("--workload", type=int, default=WORKLOAD, choices=(1, 2, 3, 4, 5),
+                    help="the weight whose M sweep is timed (3, the packed 6288x7168, is the headline)")
+    ap.add_argument("--out-dtype", choices=("bf16", "f32"), default="bf16",
+                    help="output type of the timed sweep (the headline is BF16)")
     ap.add_argument("--no-second", action="store_true",
                     help="skip the square 3584x7168 sweep reported beside the headline")
     args = ap.parse_args()
@@ -412,10 +421,11 @@ def main():
         f"torch={torch.__version__} hip={torch.version.hip}")
     import skinny_inputs as si
     sweep = tuple(si.WORKLOADS[args.workload].m_values)
-    table_source = use_tables(args.retune, props.multi_processor_count, si.WORKLOADS[args.workload])
+    table_source = use_tables(args.retune, props.multi_processor_count, si.WORKLOADS[args.workload],
+                              args.out_dtype)
     log(f"tactic table: {table_source}")
 
-    setup = Setup(args.workload)
+    setup = Setup(args.workload, out_dtype=args.out_dtype)
     wl = setup.wl
     log(f"workload {wl.name}: prepare {setup.prepare_s:.2f}s")
     stream = torch.cuda.Stream()
@@ -458,7 +468,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: out[M,N] = x[M,K] @ W[N,K]^T, N={wl.n}, K={wl.k}, "
-                               f"one step = M in {list(sweep)}, BF16 in/out, fp32 accumulate, "
+                               f"one step = M in {list(sweep)}, BF16 in, "
+                               f"{'fp32' if args.out_dtype == 'f32' else 'BF16'} out, fp32 accumulate, "
                                f"{setup.copies} rotated weight copies, hipGraph replay",
                    "N": wl.n, "K": wl.k, "m_values": list(sweep), "weight_copies": setup.copies},
     }

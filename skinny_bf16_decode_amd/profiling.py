@@ -54,18 +54,23 @@ def load_stats(trace_dir):
         return list(csv.DictReader(f))
 
 
-def summarize(trace_dir, fetch_csv, write_csv, weight_bytes, copy_bytes=64 << 20):
+def _ours(name: str) -> bool:
+    return "k_dot2" in name or "k_mfma" in name or "k_rgs" in name
+
+
+def summarize(trace_dir, fetch_csv, write_csv, weight_bytes, copy_bytes=64 << 20, fetch_scale=None):
     stats = load_stats(trace_dir)
     fetch = load_counters(fetch_csv)
     write = load_counters(write_csv)
     probe = [k for k in fetch if "k_probe_read" in k]
     copy = [k for k in write if "copyBuffer" in k or "copy" in k.lower()]
-    fetch_scale = weight_bytes / 1024.0 / statistics.mean(fetch[probe[0]]) if probe else None
+    if fetch_scale is None and probe:
+        fetch_scale = weight_bytes / 1024.0 / statistics.mean(fetch[probe[0]])
     big_copy = [k for k in copy if max(write[k]) >= copy_bytes / 1024 * 0.5]
     write_scale = (copy_bytes / 1024.0 / max(write[big_copy[0]])) if big_copy else None
     kernels = {}
     for k in fetch:
-        if "k_dot2" in k or "k_mfma" in k:
+        if _ours(k):
             f = statistics.mean(fetch[k]) * (fetch_scale or float("nan"))
             w = statistics.mean(write.get(k, [float("nan")])) * (write_scale or float("nan"))
             kernels[_short(k)] = {"fetch_kib": round(f, 1), "write_kib": round(w, 1),
@@ -85,19 +90,25 @@ def main():
     ap.add_argument("--title", default="skinny projection, 6288x7168 M sweep")
     ap.add_argument("--mfma-util", help="counter collection of a --pmc MfmaUtil run")
     ap.add_argument("--mfma-mops", help="counter collection of a --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 run")
+    ap.add_argument("--fetch-scale", type=float,
+                    help="FETCH_SIZE scale factor taken from a larger weight's calibration, for a weight "
+                         "that stays in L2 (its own plain read fetches next to nothing from HBM)")
     args = ap.parse_args()
-    stats, kernels, fs, ws = summarize(args.trace_dir, args.fetch_csv, args.write_csv, args.weight_bytes)
+    stats, kernels, fs, ws = summarize(args.trace_dir, args.fetch_csv, args.write_csv, args.weight_bytes,
+                                       fetch_scale=args.fetch_scale)
     lines = [f"# {args.title}", "", "Commands (run from the repository root):", ""]
     lines += [f"    {c}" for c in args.command]
     lines += ["", "## Kernel trace statistics (rocprofv3 --kernel-trace --stats)", "",
               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in stats:
         n = _short(r["Name"])
-        if "k_dot2" in n or "k_mfma" in n or "k_probe" in n:
+        if _ours(n) or "k_probe" in n:
             lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    calib = (f"given, from a larger weight's k_probe_read calibration" if args.fetch_scale is not None
+             else f"k_probe_read streams exactly {args.weight_bytes} B")
     lines += ["", "## HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
-              f"FETCH_SIZE scale factor {fs:.4f} (k_probe_read streams exactly {args.weight_bytes} B); "
+              f"FETCH_SIZE scale factor {fs:.4f} ({calib}); "
               f"WRITE_SIZE scale factor {ws:.4f} (64 MiB device copy).", "",
               "| kernel | dispatches | fetch KiB (scaled) | write KiB (scaled) |", "|---|---|---|---|"]
     for n, v in sorted(kernels.items()):
@@ -110,7 +121,7 @@ def main():
                   "token columns past M are multiplied too).", "",
                   "| kernel | dispatches | MFMA busy % | MFMA flops per dispatch |", "|---|---|---|---|"]
         for k in sorted(util, key=_short):
-            if "k_mfma" in k or "k_dot2" in k:
+            if _ours(k):
                 lines.append(f"| `{_short(k)}` | {len(util[k])} | {statistics.mean(util[k]):.2f} | "
                              f"{statistics.mean(mops.get(k, [0.0])) * 512:.3e} |")
     os.makedirs(os.path.dirname(os.path.abspath(args.out_md)), exist_ok=True)
