@@ -153,10 +153,11 @@ typedef struct {
  * itself and keeps, for each M in 1..64, the fastest; then every tactic the
  * table uses is timed again at each M its tile serves, and the fastest kept;
  * finally, at M <= 8, the quickest v_dot2 tactic replaces the choice when it
- * is within SKINNY_TUNE_DOT2_MARGIN (relative, default 0.01; negative: off).
- * Every tactic the table uses is
- * launched once (warm-up) so that nothing loads lazily under graph capture.
- * The split-K workspace and arrival counters are allocated here.
+ * is within SKINNY_TUNE_DOT2_MARGIN (relative, default 0.02, the run-to-run
+ * spread of one tactic's timing; negative: off).  Every tactic the table uses
+ * is launched once (warm-up) so that nothing loads lazily under graph capture.
+ * The split-K exchange workspace is allocated here (zeroed: zero is an empty
+ * exchange node).
  *
  * Tuned tables can persist across processes: when the environment variable
  * SKINNY_TABLE_CACHE names a file, a table for this chip (arch and CU count)

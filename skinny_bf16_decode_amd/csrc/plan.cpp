@@ -547,9 +547,10 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     // Fourth pass: the dot2 paths are the arithmetic meant for token counts
     // up to 8, so at M <= 8 the fastest of the two quickest dot2 candidates
     // (DOT2, DOT2R, DOT2W) that serve M replaces the table's choice when it
-    // is within SKINNY_TUNE_DOT2_MARGIN (relative, default 0.01) of it, both
-    // timed again at M.  A negative margin turns the preference off.
-    const double margin = env_double("SKINNY_TUNE_DOT2_MARGIN", 0.01);
+    // is within SKINNY_TUNE_DOT2_MARGIN (relative, default 0.02: two timings
+    // of one tactic differ by 1-2 % from run to run) of it, both timed again
+    // at M.  A negative margin turns the preference off.
+    const double margin = env_double("SKINNY_TUNE_DOT2_MARGIN", 0.02);
     if (s == SKINNY_OK && refine > 1 && margin >= 0) {
         for (int m = 1; m <= 8 && m <= SKINNY_MAX_M; ++m) {
             if (is_dot2_path(table[m - 1].path))
