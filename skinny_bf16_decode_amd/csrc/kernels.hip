@@ -1012,8 +1012,9 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
     constexpr int E = RG * T * 4 * 64;         // partial values of one wave (and of the workgroup)
     constexpr int EPT = E / (64 * NW);         // of them per thread in the final sum
     static_assert(EPT >= 1 && EPT * 64 * NW == E, "the final sum must split evenly over the threads");
-    static_assert(E * 4 <= (ROWS + MT) * PITCH * 16, "the wave's LDS tiles must hold its partial sums");
-    extern __shared__ u32x4 sm[];              // [NW][ROWS + MT][PITCH]; at the end float [NW][E]
+    constexpr int WAVE_LDS = (int)(mfmaw_wave_lds_bytes(ROWS, MT, SC) / 16);   // u32x4 per wave
+    static_assert(E * 4 <= WAVE_LDS * 16, "the wave's LDS share must hold its partial sums");
+    extern __shared__ u32x4 sm[];              // [NW][WAVE_LDS] (tiles [ROWS + MT][PITCH]); at the end float [NW][E]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1029,7 +1030,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
     const auto wres = make_rsrc(static_cast<const char *>(a.W) + (size_t)(rows_valid ? n_wg : 0) * row_bytes,
                                 (unsigned)rows_valid * row_bytes);
     const auto xres = make_rsrc(a.x, (unsigned)a.M * x_pitch);
-    u32x4 *wl = sm + wave * (ROWS + MT) * PITCH;
+    u32x4 *wl = sm + wave * WAVE_LDS;
     u32x4 *xl = wl + ROWS * PITCH;
     const int i16 = lane & 15, g = lane >> 4;
     const int lr = lane / SC, lc = lane % SC;  // row within a load, chunk within the stage

@@ -148,11 +148,18 @@ inline size_t mfmax_own_lds_bytes(int waves, int mt)
     return (size_t)(16 * waves + mfmax_x_windows(mt) * mt) * (kMfmaxChunks + 2) * 16;
 }
 // MFMAW: stages of 8 unroll chunks (8 or 16); wave tiles [waves][rows + mt]
-// [stage + 2 chunks], which the waves' partial sums reuse at the end
+// [stage + 2 chunks], which the waves' partial sums (rows x mt floats a wave)
+// reuse at the end -- the larger of the two per wave
 inline int mfmaw_stage_chunks(int unroll) { return 8 * unroll; }
+constexpr size_t mfmaw_wave_lds_bytes(int rows, int mt, int stage_chunks)
+{
+    return (size_t)(rows + mt) * (stage_chunks + 2) * 16 > (size_t)rows * mt * 4
+               ? (size_t)(rows + mt) * (stage_chunks + 2) * 16
+               : (size_t)rows * mt * 4;
+}
 inline size_t mfmaw_lds_bytes(int waves, int rows, int mt, int unroll)
 {
-    return (size_t)waves * (rows + mt) * (mfmaw_stage_chunks(unroll) + 2) * 16;
+    return (size_t)waves * mfmaw_wave_lds_bytes(rows, mt, mfmaw_stage_chunks(unroll));
 }
 // Row-group stream kernels (MFMA4, DOT2W): each lane ends with Q = max(16, V
 // rounded up to a power of two) / 16 sums, V = 4 RG T (MFMA4, T token groups)
