@@ -154,14 +154,22 @@ typedef struct {
  * table uses is timed again at each M its tile serves, and the fastest kept;
  * finally, at M <= 8, the quickest v_dot2 tactic replaces the choice when it
  * is within SKINNY_TUNE_DOT2_MARGIN (relative, default 0.02, the run-to-run
- * spread of one tactic's timing; negative: off).  Every tactic the table uses
- * is launched once (warm-up) so that nothing loads lazily under graph capture.
- * The split-K exchange workspace is allocated here (zeroed: zero is an empty
- * exchange node).
+ * spread of one tactic's timing; negative: off).
+ *
+ * A second table serves runs that add a residual, as select_kimi_k3_backend
+ * keys its choice on has_residual (page "vllm.models.kimi_k3.nvidia.
+ * low_latency_gemm"): the residual is read when a value is stored, after any
+ * split-K exchange, which changes the ranking at some M.  For each M every
+ * distinct tactic of the first table whose tile serves M is timed with a
+ * residual and the fastest kept (SKINNY_TUNE_RESIDUAL=0: the first table
+ * serves both).  Every tactic either table uses is launched once (warm-up) so
+ * that nothing loads lazily under graph capture.  The split-K exchange
+ * workspace is allocated here (zeroed: zero is an empty exchange node).
  *
  * Tuned tables can persist across processes: when the environment variable
- * SKINNY_TABLE_CACHE names a file, a table for this chip (arch and CU count)
- * and shape is loaded from it instead of tuning, and a freshly tuned table is
+ * SKINNY_TABLE_CACHE names a file, the tables for this chip (arch and CU
+ * count) and shape are loaded from it instead of tuning (one line each, the
+ * residual table's output type marked +res), and freshly tuned tables are
  * appended to it.  SKINNY_LOG=1 prints the chosen table, SKINNY_LOG=2 also
  * every candidate's time; SKINNY_TUNE_ITERS sets the timed launches per
  * candidate; SKINNY_XCD_REMAP=0 stops placing the split-K workgroups of a row
@@ -178,9 +186,10 @@ skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype out_d
 
 /*
  * skinny_prepare_tactics -- like skinny_prepare, but with the table given:
- * table[M - 1] is the tactic used for M tokens (M = 1..64) and must have a
- * token tile >= M.  No timing is done; tactics are validated and warmed.
- * Used to force a tactic (tests) or to load a table tuned earlier.
+ * table[M - 1] is the tactic used for M tokens (M = 1..64), with or without a
+ * residual, and must have a token tile >= M.  No timing is done; tactics are
+ * validated and warmed.  Used to force a tactic (tests) or to load a table
+ * tuned earlier.
  */
 skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dtype out_dtype,
                                      const skinny_tactic *table, skinny_plan **plan);
@@ -215,7 +224,9 @@ skinny_status skinny_prepare_tactics_ex(const void *W, int N, int K, int ldw, sk
  * (ldr >= N); it is added in fp32 to the fp32 sum before the one rounding to
  * BF16.  residual may be out itself (with ldr == ldo: out += x W^T) but must
  * not otherwise overlap out.  Elements of out outside rows < M and columns
- * < N are not touched.  Everything else as skinny_run, which is
+ * < N are not touched.  A run with a residual launches the plan's residual
+ * table entry for M (skinny_plan_tactic_ex), one without it the other table's.
+ * Everything else as skinny_run, which is
  * skinny_run_ex(plan, x, K, NULL, 0, out, N, M, stream).
  */
 skinny_status skinny_run_ex(const skinny_plan *plan, const void *x, int ldx, const void *residual, int ldr,
@@ -267,6 +278,14 @@ int skinny_supports(const skinny_plan *plan, int M);
 
 /* The tactic the plan uses for M tokens. */
 skinny_status skinny_plan_tactic(const skinny_plan *plan, int M, skinny_tactic *out);
+
+/*
+ * skinny_plan_tactic_ex -- the tactic the plan runs for M tokens with a
+ * residual (has_residual != 0) or without one (skinny_plan_tactic); the
+ * has_residual key of select_kimi_k3_backend on the low_latency_gemm page.
+ * Errors as skinny_plan_tactic.
+ */
+skinny_status skinny_plan_tactic_ex(const skinny_plan *plan, int M, int has_residual, skinny_tactic *out);
 
 /*
  * skinny_describe -- human-readable name of the plan's kernel for M tokens

@@ -257,9 +257,10 @@ class Prepared:
     def supports(self, tokens: int) -> bool:
         return bool(load_library().skinny_supports(self._plan, tokens))
 
-    def tactic(self, tokens: int) -> Tactic:
+    def tactic(self, tokens: int, residual: bool = False) -> Tactic:
+        """The tactic run for `tokens` tokens, with or without a residual."""
         t = Tactic()
-        _raise(load_library().skinny_plan_tactic(self._plan, tokens, ctypes.byref(t)))
+        _raise(load_library().skinny_plan_tactic_ex(self._plan, tokens, int(bool(residual)), ctypes.byref(t)))
         return t
 
     def describe(self, tokens: int) -> str:

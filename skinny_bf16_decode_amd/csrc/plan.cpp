@@ -50,14 +50,20 @@ struct skinny_plan {
     skinny_out_dtype od = SKINNY_OUT_BF16;
     float *ws = nullptr;             // split-K exchange nodes (all zero, i.e. empty, between launches)
     KArgs base{};
-    Entry e[SKINNY_MAX_M + 1];
+    Entry e[SKINNY_MAX_M + 1];       // runs without a residual
+    Entry er[SKINNY_MAX_M + 1];      // runs with a residual
 };
 
 namespace {
 
 using Key = std::tuple<int, int, int, int, int>;   // device, N, K, in dtype, out dtype
+using Table = std::array<skinny_tactic, SKINNY_MAX_M>;
+struct Tables {
+    Table plain;      // runs without a residual
+    Table residual;   // runs with a residual
+};
 std::mutex g_cache_mu;
-std::map<Key, std::array<skinny_tactic, SKINNY_MAX_M>> g_cache;
+std::map<Key, Tables> g_cache;
 
 bool env_flag(const char *name)
 {
@@ -346,67 +352,70 @@ struct DevBuf {
 };
 
 // Time every candidate on cache-cold copies of W and fill the table.
-skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int nxcd,
-                   std::array<skinny_tactic, SKINNY_MAX_M> &table)
-{
-    const int cus = device_cus();
-    const int count = skinny_enumerate_tactics_ex(N, K, cus, nullptr, 0);
-    if (count <= 0) {
-        set_error("no candidate tactics for N=%d K=%d", N, K);
-        return SKINNY_ERR_SHAPE;
-    }
-    std::vector<skinny_tactic> cand(count);
-    skinny_enumerate_tactics_ex(N, K, cus, cand.data(), count);
-
-    const size_t wbytes = (size_t)N * K * 2;
-    const size_t cold = (size_t)768 << 20;   // well past the 256 MiB Infinity Cache
-    int copies = (int)std::min<size_t>(16, std::max<size_t>(1, (cold + wbytes - 1) / wbytes));
-    size_t max_ws = 0;
-    for (const skinny_tactic &t : cand)
-        max_ws = std::max(max_ws, ws_floats(make_entry(t, N, K, half)));
-    DevBuf wcopies, xbuf, obuf, wsbuf;
-    HIP_TRY(hipMalloc(&wcopies.p, wbytes * copies));
-    HIP_TRY(hipMalloc(&xbuf.p, (size_t)SKINNY_MAX_M * K * 2));
-    HIP_TRY(hipMalloc(&obuf.p, (size_t)SKINNY_MAX_M * N * 4));
-    HIP_TRY(hipMalloc(&wsbuf.p, std::max<size_t>(max_ws, 1) * 4));
-    hipStream_t st;
-    HIP_TRY(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
-    struct StreamGuard {
-        hipStream_t s;
-        ~StreamGuard() { (void)hipStreamDestroy(s); }
-    } sg{st};
-    // packed copies of W (its pitch does not change the tactic)
-    for (int c = 0; c < copies; ++c)
-        HIP_TRY(hipMemcpy2DAsync((char *)wcopies.p + wbytes * c, (size_t)K * 2, W, (size_t)ldw * 2, (size_t)K * 2, N,
-                                 hipMemcpyDeviceToDevice, st));
-    HIP_TRY(hipMemsetAsync(xbuf.p, 0, (size_t)SKINNY_MAX_M * K * 2, st));
-    HIP_TRY(hipMemsetAsync(wsbuf.p, 0, std::max<size_t>(max_ws, 1) * 4, st));   // every exchange node empty
-    hipEvent_t e0, e1;
-    HIP_TRY(hipEventCreate(&e0));
-    HIP_TRY(hipEventCreate(&e1));
-    struct EventGuard {
-        hipEvent_t a, b;
-        ~EventGuard()
-        {
-            (void)hipEventDestroy(a);
-            (void)hipEventDestroy(b);
-        }
-    } eg{e0, e1};
-
+// Timing harness of the tuner: packed copies of W, rotated per launch so
+// that every launch reads its weight from HBM (their total is well past the
+// 256 MiB Infinity Cache), x, out and residual buffers of 64 rows, an
+// exchange workspace with every node empty, a private stream and two events.
+struct Harness {
+    DevBuf wcopies, xbuf, obuf, rbuf, wsbuf;
+    hipStream_t st = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    size_t wbytes = 0;
+    int copies = 1, iters = 8;
     KArgs a{};
-    a.x = xbuf.p;
-    a.out = obuf.p;
-    a.ws = (float *)wsbuf.p;
-    a.N = N;
-    a.K8 = K / 8;
-    a.out_f32 = od == SKINNY_OUT_F32;
-    a.nxcd = nxcd;
-    a.w_pitch = a.x_pitch = (unsigned)K * 2u;
-    a.ldo = a.ldr = N;
 
-    const int iters = std::max(1, env_int("SKINNY_TUNE_ITERS", 2 * copies > 8 ? 2 * copies : 8));
-    // mean time per launch of `iters` launches over the rotated copies, or -1
-    auto time_once = [&](const Entry &en, double &us) -> hipError_t {
+    Harness() = default;
+    Harness(const Harness &) = delete;
+    Harness &operator=(const Harness &) = delete;
+    ~Harness()
+    {
+        if (e0)
+            (void)hipEventDestroy(e0);
+        if (e1)
+            (void)hipEventDestroy(e1);
+        if (st)
+            (void)hipStreamDestroy(st);
+    }
+
+    hipError_t init(const void *W, int N, int K, int ldw, skinny_out_dtype od, int nxcd, size_t max_ws)
+    {
+        wbytes = (size_t)N * K * 2;
+        const size_t cold = (size_t)768 << 20;
+        copies = (int)std::min<size_t>(16, std::max<size_t>(1, (cold + wbytes - 1) / wbytes));
+        const size_t xb = (size_t)SKINNY_MAX_M * K * 2, ob = (size_t)SKINNY_MAX_M * N * 4;
+        const size_t wsb = std::max<size_t>(max_ws, 1) * 4;
+        hipError_t e;
+        if ((e = hipMalloc(&wcopies.p, wbytes * copies)) != hipSuccess || (e = hipMalloc(&xbuf.p, xb)) != hipSuccess ||
+            (e = hipMalloc(&obuf.p, ob)) != hipSuccess || (e = hipMalloc(&rbuf.p, ob)) != hipSuccess ||
+            (e = hipMalloc(&wsbuf.p, wsb)) != hipSuccess ||
+            (e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess ||
+            (e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess)
+            return e;
+        // packed copies of W (its pitch does not change the tactic)
+        for (int c = 0; c < copies; ++c)
+            if ((e = hipMemcpy2DAsync((char *)wcopies.p + wbytes * c, (size_t)K * 2, W, (size_t)ldw * 2,
+                                      (size_t)K * 2, N, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+                return e;
+        if ((e = hipMemsetAsync(xbuf.p, 0, xb, st)) != hipSuccess || (e = hipMemsetAsync(rbuf.p, 0, ob, st)) != hipSuccess ||
+            (e = hipMemsetAsync(wsbuf.p, 0, wsb, st)) != hipSuccess)   // every exchange node empty
+            return e;
+        a.x = xbuf.p;
+        a.out = obuf.p;
+        a.ws = (float *)wsbuf.p;
+        a.N = N;
+        a.K8 = K / 8;
+        a.out_f32 = od == SKINNY_OUT_F32;
+        a.nxcd = nxcd;
+        a.w_pitch = a.x_pitch = (unsigned)K * 2u;
+        a.ldo = a.ldr = N;
+        iters = std::max(1, env_int("SKINNY_TUNE_ITERS", 2 * copies > 8 ? 2 * copies : 8));
+        return hipStreamSynchronize(st);
+    }
+
+    // Mean time per launch of `iters` launches over the rotated copies at
+    // M = a.M; -1 if a launch failed.
+    hipError_t time_once(const Entry &en, double &us)
+    {
         us = -1.0;
         hipError_t e = hipEventRecord(e0, st);
         if (e != hipSuccess)
@@ -427,7 +436,46 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
             return e;
         us = 1000.0 * ms / iters;
         return hipSuccess;
-    };
+    }
+
+    // Entries `ens` at M = m, each timed three times round-robin: best[c] is
+    // the best of three of ens[c] (-1 if it did not run).
+    hipError_t times_at(int m, const std::vector<const Entry *> &ens, std::vector<double> &best)
+    {
+        best.assign(ens.size(), -1.0);
+        a.M = m;
+        for (int round = 0; round < 3; ++round)
+            for (size_t c = 0; c < ens.size(); ++c) {
+                double us;
+                hipError_t e = time_once(*ens[c], us);
+                if (e != hipSuccess)
+                    return e;
+                if (us >= 0 && (best[c] < 0 || us < best[c]))
+                    best[c] = us;
+            }
+        return hipSuccess;
+    }
+};
+
+skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int nxcd,
+                   std::array<skinny_tactic, SKINNY_MAX_M> &table)
+{
+    const int cus = device_cus();
+    const int count = skinny_enumerate_tactics_ex(N, K, cus, nullptr, 0);
+    if (count <= 0) {
+        set_error("no candidate tactics for N=%d K=%d", N, K);
+        return SKINNY_ERR_SHAPE;
+    }
+    std::vector<skinny_tactic> cand(count);
+    skinny_enumerate_tactics_ex(N, K, cus, cand.data(), count);
+    size_t max_ws = 0;
+    for (const skinny_tactic &t : cand)
+        max_ws = std::max(max_ws, ws_floats(make_entry(t, N, K, half)));
+    Harness h;
+    HIP_TRY(h.init(W, N, K, ldw, od, nxcd, max_ws));
+    KArgs &a = h.a;
+    const int copies = h.copies;
+    auto time_once = [&](const Entry &en, double &us) { return h.time_once(en, us); };
 
     // First pass: every candidate at its full token tile, best of two.
     std::vector<double> times(count, -1.0);
@@ -438,8 +486,8 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
         if (!en.fn || !lds_fits(en.fn, en.lds))
             continue;
         a.M = cand[i].mt;
-        a.W = wcopies.p;
-        if (launch(en, a, st) != hipSuccess) {
+        a.W = h.wcopies.p;
+        if (launch(en, a, h.st) != hipSuccess) {
             (void)hipGetLastError();
             continue;
         }
@@ -456,7 +504,7 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
         }
         times[i] = best;
     }
-    HIP_TRY(hipStreamSynchronize(st));
+    HIP_TRY(hipStreamSynchronize(h.st));
     skinny_status s = skinny_select_table(cand.data(), times.data(), count, table.data());
 
     // Second pass: for each M, the few fastest candidates of the first pass
@@ -470,18 +518,10 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     // Candidates `top` at M = m, each timed three times round-robin: best[c]
     // is the best of three of top[c] (-1 if it did not run).
     auto times_at = [&](int m, const std::vector<int> &top, std::vector<double> &best) -> hipError_t {
-        best.assign(top.size(), -1.0);
-        a.M = m;
-        for (int round = 0; round < 3; ++round)
-            for (size_t c = 0; c < top.size(); ++c) {
-                double us;
-                hipError_t e = time_once(entries[top[c]], us);
-                if (e != hipSuccess)
-                    return e;
-                if (us >= 0 && (best[c] < 0 || us < best[c]))
-                    best[c] = us;
-            }
-        return hipSuccess;
+        std::vector<const Entry *> ens;
+        for (int i : top)
+            ens.push_back(&entries[(size_t)i]);
+        return h.times_at(m, ens, best);
     };
     // The fastest of candidates `top` at M = m; -1 if none ran.
     auto fastest_at = [&](int m, const std::vector<int> &top, int &pick) -> hipError_t {
@@ -598,19 +638,82 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     return s;
 }
 
-skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int dev, int nxcd,
-                         const skinny_tactic *table, skinny_plan **out)
+// The table for runs with a residual.  The residual is read when a value is
+// stored, after the reductions and any split-K exchange, so it lengthens the
+// tails of the kernels unequally and can change which of them is fastest at
+// an M (the pages' backend choice is keyed on has_residual for the same
+// reason).  For each M, every distinct tactic of `table` whose token tile
+// serves M is timed at M with a residual, best of three rounds, and the
+// fastest is kept.
+skinny_status tune_residual(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int nxcd,
+                            const Table &table, Table &res_table)
 {
-    for (int m = 1; m <= SKINNY_MAX_M; ++m) {
-        const skinny_tactic &t = table[m - 1];
-        skinny_status s = skinny_tactic_check(&t, N, K);
-        if (s != SKINNY_OK)
-            return s;
-        if (t.mt < m) {
-            set_error("table entry for M=%d has token tile %d < M", m, t.mt);
-            return SKINNY_ERR_INVALID_ARG;
-        }
+    res_table = table;
+    std::vector<skinny_tactic> used;
+    for (const skinny_tactic &t : table)
+        if (std::none_of(used.begin(), used.end(),
+                         [&](const skinny_tactic &u) { return memcmp(&u, &t, sizeof t) == 0; }))
+            used.push_back(t);
+    if (used.size() < 2)
+        return SKINNY_OK;
+    std::vector<Entry> ens;
+    size_t max_ws = 0;
+    for (const skinny_tactic &t : used) {
+        ens.push_back(make_entry(t, N, K, half));
+        max_ws = std::max(max_ws, ws_floats(ens.back()));
     }
+    Harness h;
+    HIP_TRY(h.init(W, N, K, ldw, od, nxcd, max_ws));
+    h.a.res = h.rbuf.p;
+    for (size_t i = 0; i < ens.size(); ++i) {   // warm: load every code object before timing
+        if (!ens[i].fn || !lds_fits(ens[i].fn, ens[i].lds))
+            continue;
+        h.a.M = used[i].mt;
+        h.a.W = h.wcopies.p;
+        if (launch(ens[i], h.a, h.st) != hipSuccess)
+            (void)hipGetLastError();
+    }
+    HIP_TRY(hipStreamSynchronize(h.st));
+    for (int m = 1; m <= SKINNY_MAX_M; ++m) {
+        std::vector<const Entry *> top;
+        std::vector<size_t> idx;
+        for (size_t i = 0; i < used.size(); ++i)
+            if (used[i].mt >= m && ens[i].fn && lds_fits(ens[i].fn, ens[i].lds)) {
+                top.push_back(&ens[i]);
+                idx.push_back(i);
+            }
+        if (top.size() < 2)
+            continue;
+        std::vector<double> best;
+        HIP_TRY(h.times_at(m, top, best));
+        int pick = -1;
+        for (size_t c = 0; c < top.size(); ++c)
+            if (best[c] >= 0 && (pick < 0 || best[c] < best[(size_t)pick]))
+                pick = (int)c;
+        if (pick < 0)
+            continue;
+        res_table[m - 1] = used[idx[(size_t)pick]];
+        if (env_flag("SKINNY_LOG") && memcmp(&res_table[m - 1], &table[m - 1], sizeof(skinny_tactic)) != 0)
+            fprintf(stderr, "[skinny] N=%d K=%d M=%d with a residual: path %d mt %d split %d at %.3f us\n", N, K,
+                    m, res_table[m - 1].path, res_table[m - 1].mt, res_table[m - 1].split, best[(size_t)pick]);
+    }
+    return SKINNY_OK;
+}
+
+skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int dev, int nxcd,
+                         const skinny_tactic *table, const skinny_tactic *res_table, skinny_plan **out)
+{
+    for (const skinny_tactic *tb : {table, res_table})
+        for (int m = 1; m <= SKINNY_MAX_M; ++m) {
+            const skinny_tactic &t = tb[m - 1];
+            skinny_status s = skinny_tactic_check(&t, N, K);
+            if (s != SKINNY_OK)
+                return s;
+            if (t.mt < m) {
+                set_error("table entry for M=%d has token tile %d < M", m, t.mt);
+                return SKINNY_ERR_INVALID_ARG;
+            }
+        }
     skinny_plan *p = new (std::nothrow) skinny_plan;
     if (!p) {
         set_error("host allocation of the plan failed");
@@ -626,13 +729,16 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
     size_t max_ws = 0;
     for (int m = 1; m <= SKINNY_MAX_M; ++m) {
         p->e[m] = make_entry(table[m - 1], N, K, half);
-        if (!p->e[m].fn || !lds_fits(p->e[m].fn, p->e[m].lds)) {
-            set_error("table entry for M=%d needs %u bytes of dynamic LDS, more than the device allows "
-                      "with the kernel's static LDS", m, p->e[m].lds);
-            delete p;
-            return SKINNY_ERR_INVALID_ARG;
+        p->er[m] = make_entry(res_table[m - 1], N, K, half);
+        for (const Entry *en : {&p->e[m], &p->er[m]}) {
+            if (!en->fn || !lds_fits(en->fn, en->lds)) {
+                set_error("table entry for M=%d needs %u bytes of dynamic LDS, more than the device allows "
+                          "with the kernel's static LDS", m, en->lds);
+                delete p;
+                return SKINNY_ERR_INVALID_ARG;
+            }
+            max_ws = std::max(max_ws, ws_floats(*en));
         }
-        max_ws = std::max(max_ws, ws_floats(p->e[m]));
     }
     auto fail = [&](skinny_status s) {
         skinny_destroy(p);
@@ -652,7 +758,7 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
     p->base = weight_args(W, N, K, ldw, od, nxcd, p->ws);
     KArgs &a = p->base;
 
-    // Warm every distinct kernel the table uses, on scratch x/out, so that no
+    // Warm every distinct kernel the tables use, on scratch x/out, so that no
     // code object loads lazily inside a later graph capture.
     void *xs = nullptr, *os = nullptr;
     if ((e = hipMalloc(&xs, (size_t)SKINNY_MAX_M * K * 2)) != hipSuccess) {
@@ -665,18 +771,20 @@ skinny_status build_plan(const void *W, int N, int K, int ldw, int half, skinny_
         return fail(SKINNY_ERR_HIP);
     }
     e = hipMemset(xs, 0, (size_t)SKINNY_MAX_M * K * 2);
-    for (int m = 1; m <= SKINNY_MAX_M && e == hipSuccess; ++m) {
-        bool seen = false;
-        for (int j = 1; j < m; ++j)
-            seen |= memcmp(&p->e[j].t, &p->e[m].t, sizeof(skinny_tactic)) == 0;
-        if (seen)
-            continue;
-        KArgs w = a;
-        w.x = xs;
-        w.out = os;
-        w.M = m;
-        e = launch(p->e[m], w, nullptr);
-    }
+    std::vector<skinny_tactic> warmed;
+    for (int m = 1; m <= SKINNY_MAX_M && e == hipSuccess; ++m)
+        for (const Entry *en : {&p->e[m], &p->er[m]}) {
+            if (e != hipSuccess || std::any_of(warmed.begin(), warmed.end(), [&](const skinny_tactic &t) {
+                    return memcmp(&t, &en->t, sizeof t) == 0;
+                }))
+                continue;
+            warmed.push_back(en->t);
+            KArgs w = a;
+            w.x = xs;
+            w.out = os;
+            w.M = m;
+            e = launch(*en, w, nullptr);
+        }
     if (e == hipSuccess)
         e = hipDeviceSynchronize();
     (void)hipFree(xs);
@@ -758,27 +866,40 @@ skinny_status skinny_prepare_ex(const void *W, int N, int K, int ldw, skinny_in_
         return s;
     raise_lds_limits();
     const int nxcd = cus % 8 == 0 ? 8 : 1;
-    std::array<skinny_tactic, SKINNY_MAX_M> table;
+    Tables tb;
     {
         std::lock_guard<std::mutex> lock(g_cache_mu);
         const Key key{dev, N, K, half, (int)od};
         auto it = g_cache.find(key);
         const char *file = getenv("SKINNY_TABLE_CACHE");
+        const bool use_file = file && *file;
         if (it != g_cache.end()) {
-            table = it->second;
-        } else if (file && *file && load_table_file(file, cus, N, K, half, od, table)) {
-            if (env_flag("SKINNY_LOG"))
-                fprintf(stderr, "[skinny] N=%d K=%d: table loaded from %s\n", N, K, file);
-            g_cache[key] = table;
+            tb = it->second;
         } else {
-            if ((s = tune(W, N, K, ldw, half, od, nxcd, table)) != SKINNY_OK)
-                return s;
-            g_cache[key] = table;
-            if (file && *file)
-                save_table_file(file, cus, N, K, half, od, table);
+            if (use_file && load_table_file(file, cus, N, K, half, od, 0, tb.plain)) {
+                if (env_flag("SKINNY_LOG"))
+                    fprintf(stderr, "[skinny] N=%d K=%d: table loaded from %s\n", N, K, file);
+            } else {
+                if ((s = tune(W, N, K, ldw, half, od, nxcd, tb.plain)) != SKINNY_OK)
+                    return s;
+                if (use_file)
+                    save_table_file(file, cus, N, K, half, od, 0, tb.plain);
+            }
+            if (use_file && load_table_file(file, cus, N, K, half, od, 1, tb.residual)) {
+                if (env_flag("SKINNY_LOG"))
+                    fprintf(stderr, "[skinny] N=%d K=%d: residual table loaded from %s\n", N, K, file);
+            } else if (env_int("SKINNY_TUNE_RESIDUAL", 1) == 0) {
+                tb.residual = tb.plain;
+            } else {
+                if ((s = tune_residual(W, N, K, ldw, half, od, nxcd, tb.plain, tb.residual)) != SKINNY_OK)
+                    return s;
+                if (use_file)
+                    save_table_file(file, cus, N, K, half, od, 1, tb.residual);
+            }
+            g_cache[key] = tb;
         }
     }
-    return build_plan(W, N, K, ldw, half, od, dev, nxcd, table.data(), plan);
+    return build_plan(W, N, K, ldw, half, od, dev, nxcd, tb.plain.data(), tb.residual.data(), plan);
 }
 
 skinny_status skinny_prepare(const void *W, int N, int K, skinny_out_dtype od, skinny_plan **plan)
@@ -808,7 +929,8 @@ skinny_status skinny_prepare_tactics_ex(const void *W, int N, int K, int ldw, sk
     if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)
         return s;
     raise_lds_limits();
-    return build_plan(W, N, K, ldw, in_dtype == SKINNY_IN_F16, od, dev, cus % 8 == 0 ? 8 : 1, table, plan);
+    // the caller's table serves runs with and without a residual alike
+    return build_plan(W, N, K, ldw, in_dtype == SKINNY_IN_F16, od, dev, cus % 8 == 0 ? 8 : 1, table, table, plan);
 }
 
 skinny_status skinny_prepare_tactics(const void *W, int N, int K, skinny_out_dtype od,
@@ -829,7 +951,7 @@ skinny_status skinny_run_ex(const skinny_plan *p, const void *x, int ldx, const 
         return s;
     KArgs a = p->base;
     set_call_args(a, x, ldx, residual, ldr, out, ldo, M);
-    hipError_t e = launch(p->e[M], a, (hipStream_t)stream);
+    hipError_t e = launch(residual ? p->er[M] : p->e[M], a, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "hipLaunchKernel");
     return SKINNY_OK;
@@ -889,7 +1011,7 @@ skinny_status skinny_run_static(const void *W, int N, int K, int ldw, skinny_in_
 
 int skinny_supports(const skinny_plan *p, int M) { return p && M >= 1 && M <= SKINNY_MAX_M; }
 
-skinny_status skinny_plan_tactic(const skinny_plan *p, int M, skinny_tactic *out)
+skinny_status skinny_plan_tactic_ex(const skinny_plan *p, int M, int has_residual, skinny_tactic *out)
 {
     if (!p || !out) {
         set_error("plan or out is NULL");
@@ -899,8 +1021,13 @@ skinny_status skinny_plan_tactic(const skinny_plan *p, int M, skinny_tactic *out
         set_error("M=%d outside 1..%d", M, SKINNY_MAX_M);
         return SKINNY_ERR_UNSUPPORTED_M;
     }
-    *out = p->e[M].t;
+    *out = has_residual ? p->er[M].t : p->e[M].t;
     return SKINNY_OK;
+}
+
+skinny_status skinny_plan_tactic(const skinny_plan *p, int M, skinny_tactic *out)
+{
+    return skinny_plan_tactic_ex(p, M, 0, out);
 }
 
 skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len)

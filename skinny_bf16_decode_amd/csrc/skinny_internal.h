@@ -104,17 +104,18 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8);
 void set_error(const char *fmt, ...);
 
 // Stored tuned tables (tables.cpp): one text line per (chip, N, K, input and
-// output type).  parse_table_line fills `table` and returns true only for a
+// output type, residual or not: res = 1 for the table of runs that add a
+// residual).  parse_table_line fills `table` and returns true only for a
 // whole, valid line for this key; load_table_file returns the first such line
 // of a file; format_table_line writes one into buf (cap >= 8192 bytes holds
 // any table); save_table_file appends one.
-bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_out_dtype od,
+bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                       std::array<skinny_tactic, SKINNY_MAX_M> &table);
-bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
+bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                      std::array<skinny_tactic, SKINNY_MAX_M> &table);
-void format_table_line(int cus, int N, int K, int half, skinny_out_dtype od,
+void format_table_line(int cus, int N, int K, int half, skinny_out_dtype od, int res,
                        const std::array<skinny_tactic, SKINNY_MAX_M> &table, char *buf, size_t cap);
-void save_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
+void save_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                      const std::array<skinny_tactic, SKINNY_MAX_M> &table);
 
 // Rows of W per tile and tile count for a tactic.

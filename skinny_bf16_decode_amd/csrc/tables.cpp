@@ -1,8 +1,9 @@
 // Tuned tables stored in a text file (SKINNY_TABLE_CACHE=<file>), keyed like
 // the pages' per-part measured tables ("vllm.models.kimi_k3.nvidia.
 // low_latency_gemm", the measured {M: call} tables per part) by the chip (arch,
-// CU count) and the shape.  One line per table:
-//   skinny-table v2 <arch> <cus> <N> <K> <bf16|f16 in> <bf16|f32 out> <64 x path.mt.rows.waves.unroll.split>
+// CU count), the shape and whether the runs add a residual.  One line per table:
+//   skinny-table v2 <arch> <cus> <N> <K> <bf16|f16 in> <out> <64 x path.mt.rows.waves.unroll.split>
+// with <out> bf16 or f32, followed by +res for the table of runs with a residual.
 // The file is input from outside the library: a line is taken only when every
 // field parses as a whole decimal number in int range, there are exactly 64
 // tactics and nothing after them, every tactic passes skinny_tactic_check and
@@ -45,6 +46,13 @@ bool field_is(const char *s, const char *e, const char *word)
 {
     const size_t n = strlen(word);
     return (size_t)(e - s) == n && !memcmp(s, word, n);
+}
+
+const char *out_token(skinny_out_dtype od, int res)
+{
+    if (od == SKINNY_OUT_F32)
+        return res ? "f32+res" : "f32";
+    return res ? "bf16+res" : "bf16";
 }
 
 // A decimal int (optional '-', at least one digit, in int range) at the start
@@ -98,7 +106,7 @@ bool parse_tactic(const char *s, const char *e, skinny_tactic *t)
 
 }  // namespace
 
-bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_out_dtype od,
+bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                       std::array<skinny_tactic, SKINNY_MAX_M> &table)
 {
     const char *p = line, *s, *e;
@@ -115,7 +123,7 @@ bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_
             return false;
     if (!next_field(&p, &s, &e) || !field_is(s, e, half ? "f16" : "bf16"))
         return false;
-    if (!next_field(&p, &s, &e) || !field_is(s, e, od == SKINNY_OUT_F32 ? "f32" : "bf16"))
+    if (!next_field(&p, &s, &e) || !field_is(s, e, out_token(od, res)))
         return false;
     std::array<skinny_tactic, SKINNY_MAX_M> t;
     for (int m = 1; m <= SKINNY_MAX_M; ++m) {
@@ -131,7 +139,7 @@ bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_
     return true;
 }
 
-bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
+bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                      std::array<skinny_tactic, SKINNY_MAX_M> &table)
 {
     FILE *f = fopen(path, "r");
@@ -148,28 +156,28 @@ bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_o
             }
             continue;
         }
-        found = parse_table_line(line, cus, N, K, half, od, table);
+        found = parse_table_line(line, cus, N, K, half, od, res, table);
     }
     fclose(f);
     return found;
 }
 
-void format_table_line(int cus, int N, int K, int half, skinny_out_dtype od,
+void format_table_line(int cus, int N, int K, int half, skinny_out_dtype od, int res,
                        const std::array<skinny_tactic, SKINNY_MAX_M> &table, char *buf, size_t cap)
 {
     size_t n = (size_t)snprintf(buf, cap, "%s v2 gfx950 %d %d %d %s %s", kTableTag, cus, N, K,
-                                half ? "f16" : "bf16", od == SKINNY_OUT_F32 ? "f32" : "bf16");
+                                half ? "f16" : "bf16", out_token(od, res));
     for (const skinny_tactic &e : table)
         if (n < cap)
             n += (size_t)snprintf(buf + n, cap - n, " %d.%d.%d.%d.%d.%d", e.path, e.mt, e.rows, e.waves,
                                   e.unroll, e.split);
 }
 
-void save_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od,
+void save_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                      const std::array<skinny_tactic, SKINNY_MAX_M> &table)
 {
     char line[kMaxLine];
-    format_table_line(cus, N, K, half, od, table, line, sizeof line);
+    format_table_line(cus, N, K, half, od, res, table, line, sizeof line);
     FILE *f = fopen(path, "a");
     if (!f)
         return;

@@ -190,19 +190,20 @@ static Table a_table(int N, int K)
     return t;
 }
 
-static std::string line_of(int cus, int N, int K, int half, skinny_out_dtype od, const Table &t)
+static std::string line_of(int cus, int N, int K, int half, skinny_out_dtype od, const Table &t, int res = 0)
 {
     std::vector<char> buf(8192);
-    format_table_line(cus, N, K, half, od, t, buf.data(), buf.size());
+    format_table_line(cus, N, K, half, od, res, t, buf.data(), buf.size());
     return std::string(buf.data());
 }
 
 // parse a copy in a buffer of exactly its size, so ASan sees any read past it
-static bool parse_exact(const std::string &s, int cus, int N, int K, int half, skinny_out_dtype od, Table &out)
+static bool parse_exact(const std::string &s, int cus, int N, int K, int half, skinny_out_dtype od, Table &out,
+                        int res = 0)
 {
     std::vector<char> buf(s.begin(), s.end());
     buf.push_back(0);
-    return parse_table_line(buf.data(), cus, N, K, half, od, out);
+    return parse_table_line(buf.data(), cus, N, K, half, od, res, out);
 }
 
 static bool valid_table(const Table &t, int N, int K)
@@ -231,6 +232,14 @@ static void check_table_lines()
     CHECK(!parse_exact(good, cus, N, K + 8, 0, SKINNY_OUT_BF16, got), "other K");
     CHECK(!parse_exact(good, cus, N, K, 1, SKINNY_OUT_BF16, got), "other input type");
     CHECK(!parse_exact(good, cus, N, K, 0, SKINNY_OUT_F32, got), "other output type");
+    // the residual table's line: its own key, and never taken for the other
+    const std::string res_line = line_of(cus, N, K, 0, SKINNY_OUT_BF16, t, 1);
+    CHECK(res_line.find(" bf16+res ") != std::string::npos, "residual key %s", res_line.substr(0, 60).c_str());
+    CHECK(parse_exact(res_line, cus, N, K, 0, SKINNY_OUT_BF16, got, 1), "residual line parses as residual");
+    CHECK(!parse_exact(res_line, cus, N, K, 0, SKINNY_OUT_BF16, got, 0), "residual line is not the plain table");
+    CHECK(!parse_exact(good, cus, N, K, 0, SKINNY_OUT_BF16, got, 1), "plain line is not the residual table");
+    CHECK(!parse_exact(line_of(cus, N, K, 0, SKINNY_OUT_F32, t, 1), cus, N, K, 0, SKINNY_OUT_BF16, got, 1),
+          "f32+res is not bf16+res");
     // every prefix of the line is refused (the whole line less trailing blanks aside)
     for (size_t n = 0; n < good.size(); ++n)
         CHECK(!parse_exact(good.substr(0, n), cus, N, K, 0, SKINNY_OUT_BF16, got), "prefix of %zu chars", n);
@@ -288,7 +297,7 @@ static void check_table_lines()
     // format into short buffers stays inside them
     for (size_t cap : {(size_t)1, (size_t)10, (size_t)60, (size_t)61, (size_t)200, (size_t)4000}) {
         std::vector<char> buf(cap);
-        format_table_line(cus, N, K, 0, SKINNY_OUT_BF16, t, buf.data(), cap);
+        format_table_line(cus, N, K, 0, SKINNY_OUT_BF16, 0, t, buf.data(), cap);
         CHECK(strlen(buf.data()) < cap, "format cap %zu", cap);
     }
 }
@@ -301,7 +310,7 @@ static void check_table_files(const char *dir)
     const std::string path = std::string(dir) + "/tables.txt";
     Table got;
     // missing file
-    CHECK(!load_table_file((std::string(dir) + "/missing.txt").c_str(), cus, N, K, 0, SKINNY_OUT_F32, got),
+    CHECK(!load_table_file((std::string(dir) + "/missing.txt").c_str(), cus, N, K, 0, SKINNY_OUT_F32, 0, got),
           "missing file");
     // garbage around the line, an over-long line holding a valid table after the
     // read buffer (skipped), binary bytes, and the valid line last without a newline
@@ -317,7 +326,7 @@ static void check_table_files(const char *dir)
         fprintf(f, "\n%s", good.c_str());
         fclose(f);
     }
-    CHECK(load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_F32, got), "valid last line without newline");
+    CHECK(load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_F32, 0, got), "valid last line without newline");
     for (int m = 0; m < SKINNY_MAX_M; ++m)
         CHECK(same(got[(size_t)m], t[(size_t)m]), "loaded M=%d", m + 1);
     // a file of only malformed content
@@ -329,15 +338,23 @@ static void check_table_files(const char *dir)
         fprintf(f, "%s\n", tailonly.c_str());
         fclose(f);
     }
-    CHECK(!load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_F32, got), "malformed file");
+    CHECK(!load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_F32, 0, got), "malformed file");
     // save appends and load takes the first line for the key
     remove(path.c_str());
-    save_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_F32, t);
+    save_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_F32, 0, t);
     Table other = a_table(N, K);
     other[63] = t[63];
-    save_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_BF16, other);
-    CHECK(load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_F32, got), "saved table loads");
-    CHECK(load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_BF16, got), "second saved table loads");
+    save_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_BF16, 0, other);
+    CHECK(load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_F32, 0, got), "saved table loads");
+    CHECK(load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_BF16, 0, got), "second saved table loads");
+    CHECK(!load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_BF16, 1, got), "no residual table saved yet");
+    Table res = t;
+    res[0] = t[1].mt >= 1 ? t[1] : t[0];
+    save_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_BF16, 1, res);
+    CHECK(load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_BF16, 1, got) && same(got[0], res[0]),
+          "the residual table loads apart from the plain one");
+    CHECK(load_table_file(path.c_str(), cus, N, K, 0, SKINNY_OUT_BF16, 0, got) && same(got[0], other[0]),
+          "the plain table is unchanged by it");
     remove(path.c_str());
 }
 

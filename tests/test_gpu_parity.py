@@ -447,8 +447,9 @@ def test_run_errors(sk):
 
 
 def test_table_cache_file_round_trip(sk, tmp_path):
-    """SKINNY_TABLE_CACHE: a tuning process appends its table; a second
-    process loads it instead of tuning and chooses the same tactics."""
+    """SKINNY_TABLE_CACHE: a tuning process appends its two tables (without
+    and with a residual); a second process loads both instead of tuning and
+    chooses the same tactics."""
     import os
     import subprocess
     path = tmp_path / "tables.txt"
@@ -458,20 +459,51 @@ def test_table_cache_file_round_trip(sk, tmp_path):
         "from tests import gpu_util as gu\n"
         "x, w = si.random_case(9, 1, 640, 2048)\n"
         "plan = sk.Prepared(gu.dev_bf16(w), torch.bfloat16)\n"
-        "print('|'.join(repr(plan.tactic(m)) for m in range(1, 65)))\n"
+        "print('|'.join(repr(plan.tactic(m, r)) for r in (False, True) for m in range(1, 65)))\n"
     ) % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))),)
     env = dict(os.environ, SKINNY_TABLE_CACHE=str(path), SKINNY_LOG="1")
     first = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240)
     assert first.returncode == 0, first.stderr[-2000:]
     assert "tuned N=640 K=2048" in first.stderr
     lines = path.read_text().splitlines()
-    assert len(lines) == 1 and lines[0].startswith("skinny-table v2 gfx950 ")
-    assert lines[0].split()[4:8] == ["640", "2048", "bf16", "bf16"], lines[0][:80]
+    assert len(lines) == 2 and all(ln.startswith("skinny-table v2 gfx950 ") for ln in lines)
+    assert [ln.split()[4:8] for ln in lines] == [["640", "2048", "bf16", "bf16"],
+                                                 ["640", "2048", "bf16", "bf16+res"]], lines
     second = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240)
     assert second.returncode == 0, second.stderr[-2000:]
-    assert "table loaded from" in second.stderr and "tuned N=640" not in second.stderr
+    assert "table loaded from" in second.stderr and "residual table loaded from" in second.stderr
+    assert "tuned N=640" not in second.stderr
     assert first.stdout.strip().splitlines()[-1] == second.stdout.strip().splitlines()[-1]
-    assert len(path.read_text().splitlines()) == 1
+    assert len(path.read_text().splitlines()) == 2
+
+
+def test_residual_table(sk):
+    """Runs with a residual take the plan's residual table: at every M its
+    tactic is one of the plain table's tactics with a tile >= M, and the
+    residual runs are exact on integer inputs at every M (fp32 out equals
+    O + R bit for bit), in place and separate."""
+    import torch
+    n, k = 1000, 4096
+    x_bits, w_bits = si.small_int_case(33, 64, n, k)
+    o, _ = oracle.gemm(x_bits, w_bits)
+    rng = np.random.default_rng(5)
+    r = rng.integers(-8, 9, size=(64, n)).astype(np.float32)
+    plan = sk.Prepared(gu.dev_bf16(w_bits), torch.float32)
+    plain = {repr(plan.tactic(m)) for m in range(1, 65)}
+    x = gu.dev_bf16(x_bits)
+    res = torch.from_numpy(r).cuda()
+    for m in range(1, 65):
+        t = plan.tactic(m, residual=True)
+        assert repr(t) in plain and t.mt >= m, (m, t)
+        out = torch.full((64, n), float("nan"), dtype=torch.float32, device="cuda")
+        plan.run(x[:m], out[:m], residual=res[:m])
+        got = out.cpu().numpy()
+        assert np.array_equal(got[:m], (o[:m] + r[:m]).astype(np.float32)), m
+        assert np.isnan(got[m:]).all()
+        acc = res.clone()
+        plan.run(x[:m], acc[:m], residual=acc[:m])
+        assert np.array_equal(acc.cpu().numpy()[:m], (o[:m] + r[:m]).astype(np.float32)), m
+    plan.close()
 
 
 @pytest.mark.parametrize("remap", ["1", "0"])
