@@ -204,6 +204,8 @@ def kernel_name(t):
         name = "k_dot2"
     elif t.path == 1:                        # MFMA
         args, name = (T, t.rows // 16, t.unroll), "k_mfma"
+    elif t.path == 12:                       # MFMAT: the 16-token MFMA kernel over token groups
+        args, name = (1, t.rows // 16, t.unroll), "k_mfma"
     elif t.path == 3:                        # MFMAX: unroll picks the grid, not the kernel
         args, name = (T, w), "k_mfmax"
     elif t.path == 9:                        # MFMAW: row groups, waves, stage chunks

@@ -96,10 +96,16 @@ typedef enum {
                               operand after one lane permutation -- no LDS in the K loop; waves
                               take every waves-th stage of 16 chunks; K parts meet in an
                               atomic-swap exchange */
-    SKINNY_PATH_DOT2W = 11 /* v_dot2_f32_bf16, tiles 1/2/4/8: the MFMA4 kernel's stream (equal
+    SKINNY_PATH_DOT2W = 11,/* v_dot2_f32_bf16, tiles 1/2/4/8: the MFMA4 kernel's stream (equal
                               row ranges of 4-row groups, waves on every waves-th 16-chunk
                               stage, row-contiguous loads straight into registers, each x load
                               serving every row group) with dot2 arithmetic per lane */
+    SKINNY_PATH_MFMAT = 12 /* the 16-token MFMA kernel over token groups: mt = 32 or 64 is the
+                              most tokens served; a run launches ceil(M / 16) groups of 16
+                              tokens, each multiplying every row tile, so a weight too short
+                              to fill the chip with row tiles gets groups x tiles workgroups
+                              (it re-reads each tile from L2 once per group; enumerated only
+                              for weights of at most 16 MiB) */
 } skinny_path;
 
 /*
@@ -113,10 +119,10 @@ typedef enum {
  */
 typedef struct {
     int path;   /* skinny_path */
-    int mt;     /* token tile: DOT2/DOT2R/DOT2X/DOT2W 1,2,4,8; MFMA4 4,8,16,32; the other
-                   MFMA paths 16,32,64 */
+    int mt;     /* token tile: DOT2/DOT2R/DOT2X/DOT2W 1,2,4,8; MFMA4 4,8,16,32; MFMAT
+                   32,64 (tokens served, in groups of 16); the other MFMA paths 16,32,64 */
     int rows;   /* weight rows per workgroup.  DOT2, DOT2R: 1..16 (mt*rows <= 64; for
-                   DOT2R the most rows of a range); MFMA: 16,32,64; MFMAX: 16 * waves;
+                   DOT2R the most rows of a range); MFMA, MFMAT: 16,32,64; MFMAX: 16 * waves;
                    MFMAW: 16, 32 or
                    64 (the most rows of a range); MFMA4, DOT2W: 4 x (1, 2, 4, 7, 13 or
                    14), the most rows of a range (fewer row groups for the largest
@@ -147,7 +153,10 @@ typedef struct {
  *
  * Validates the arguments, then looks up the process-wide tactic table for
  * (device, N, K, out_dtype); on a miss it times every legal tactic on the
- * device with cache-cold weight copies at its full token tile, then times the
+ * device with cache-cold weight copies at its full token tile (each timing a
+ * replay of a captured graph of back-to-back launches, as decode steps run
+ * them, so that a kernel of a few microseconds is not timed at the host's
+ * launch rate), then times the
  * few fastest whose tile is >= M (SKINNY_TUNE_REFINE of them, default 4; 0 or
  * 1 skips this pass), and the two fastest of every tile >= M, again at M
  * itself and keeps, for each M in 1..64, the fastest; then every tactic the
@@ -161,8 +170,10 @@ typedef struct {
  * low_latency_gemm"): the residual is read when a value is stored, after any
  * split-K exchange, which changes the ranking at some M.  For each M every
  * distinct tactic of the first table whose tile serves M is timed with a
- * residual and the fastest kept (SKINNY_TUNE_RESIDUAL=0: the first table
- * serves both).  Every tactic either table uses is launched once (warm-up) so
+ * residual, and the fastest replaces the first table's entry if it is faster
+ * by more than SKINNY_TUNE_RESIDUAL_MARGIN (relative, default 0.01), or by
+ * more than the dot2 margin where that entry is a v_dot2 tactic at M <= 8
+ * (SKINNY_TUNE_RESIDUAL=0: the first table serves both).  Every tactic either table uses is launched once (warm-up) so
  * that nothing loads lazily under graph capture.  The split-K exchange
  * workspace is allocated here (zeroed: zero is an empty exchange node).
  *

@@ -35,8 +35,9 @@ PATH_DOT2R = 8
 PATH_MFMAW = 9
 PATH_MFMA4 = 10
 PATH_DOT2W = 11
+PATH_MFMAT = 12
 PATH_NAMES = {0: "dot2", 1: "mfma", 2: "dot2x", 3: "mfmax", 4: "mfmad", 5: "mfmas", 6: "mfmar", 7: "mfmak",
-              8: "dot2r", 9: "mfmaw", 10: "mfma4", 11: "dot2w"}
+              8: "dot2r", 9: "mfmaw", 10: "mfma4", 11: "dot2w", 12: "mfmat"}
 
 STATUS = {
     0: "SKINNY_OK",

@@ -585,6 +585,12 @@ __global__ __launch_bounds__(512) void k_dot2(KArgs a)
 // fp32 results (lane l holds rows 4 (l / 16) .. +3 of column l % 16) are
 // summed over waves in LDS, laid out [wave][token][row] so that the final
 // stores of out[token][n0 + row] are row-contiguous.
+//
+// Token groups (MFMAT): a launch with gridDim.y = ceil(M / MT) gives
+// workgroup row y tokens MT y .. MT y + MT - 1; each row tile is then
+// multiplied once per group, which re-reads the tile from L2 but gives a
+// short-K weight, whose row tiles alone cannot fill the chip, as many
+// workgroups as groups times tiles.  Plain launches have gridDim.y = 1.
 // ---------------------------------------------------------------------------
 template <int T, int RT, int U, bool H>
 __global__ __launch_bounds__(512) void k_mfma(KArgs a)
@@ -592,6 +598,16 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
     constexpr int MT = 16 * T, NT = 16 * RT, NTP = NT + 1;
     extern __shared__ float lds[];   // [waves][MT][NTP]
 
+    const int group = blockIdx.y;
+    if (group > 0) {                 // the launch covers M, so M > MT group here
+        const int m0 = MT * group;
+        const size_t osz = a.out_f32 ? 4 : 2;
+        a.x = static_cast<const char *>(a.x) + (size_t)m0 * a.x_pitch;
+        a.out = static_cast<char *>(a.out) + (size_t)m0 * a.ldo * osz;
+        if (a.res)
+            a.res = static_cast<const char *>(a.res) + (size_t)m0 * a.ldr * osz;
+        a.M -= m0;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int nthr = blockDim.x, nwaves = nthr >> 6;
@@ -709,7 +725,8 @@ __global__ __launch_bounds__(512) void k_mfma(KArgs a)
         }
         return;
     }
-    float *wsp = a.ws + (long)tile * (a.split - 1) * E;
+    // each token group's row tiles have nodes of their own
+    float *wsp = a.ws + ((long)group * a.n_tiles + tile) * (a.split - 1) * E;
     for (int e0 = tid; e0 < E; e0 += 4 * nthr) {
         int off[4];
         float v[4];

@@ -151,10 +151,11 @@ void raise_lds_limits()
 }
 
 // Floats of split-K exchange nodes a table entry needs: split - 1 nodes of
-// one tile's values per row tile (see swap_exchange in the kernels).
+// one tile's values per row tile and token group (see swap_exchange in the
+// kernels).
 size_t ws_floats(const Entry &en)
 {
-    return en.t.split > 1 ? (size_t)en.n_tiles * (en.t.split - 1) * tile_values(en.t) : 0;
+    return en.t.split > 1 ? (size_t)token_groups(en.t) * en.n_tiles * (en.t.split - 1) * tile_values(en.t) : 0;
 }
 
 // Static LDS of a kernel plus the device's per-workgroup limit, looked up
@@ -198,7 +199,9 @@ hipError_t launch(const Entry &en, KArgs a, hipStream_t stream)
     a.grid_q = (int)en.grid / nx;
     a.grid_r = (int)en.grid % nx;
     void *params[] = {&a};
-    return hipLaunchKernel(en.fn, dim3(en.grid), dim3(en.block), params, en.lds, stream);
+    // MFMAT: one grid row per group of 16 of the call's tokens
+    const unsigned groups = en.t.path == SKINNY_PATH_MFMAT ? (unsigned)(a.M + kTokenGroup - 1) / kTokenGroup : 1u;
+    return hipLaunchKernel(en.fn, dim3(en.grid, groups), dim3(en.block), params, en.lds, stream);
 }
 
 // Validation shared by the prepare entry points; no HIP call before it passes.
@@ -413,11 +416,16 @@ struct Harness {
     }
 
     // Mean time per launch of `iters` launches over the rotated copies at
-    // M = a.M; -1 if a launch failed.
+    // M = a.M, captured in a graph and replayed (the second replay timed), as
+    // decode steps run them: launched one by one from the host, a kernel of a
+    // few microseconds would be timed at the host's launch rate.  -1 if a
+    // launch failed.
     hipError_t time_once(const Entry &en, double &us)
     {
         us = -1.0;
-        hipError_t e = hipEventRecord(e0, st);
+        hipGraph_t g = nullptr;
+        hipGraphExec_t ge = nullptr;
+        hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
         if (e != hipSuccess)
             return e;
         bool ok = true;
@@ -425,14 +433,23 @@ struct Harness {
             a.W = (const char *)wcopies.p + wbytes * ((j + 1) % copies);
             ok = launch(en, a, st) == hipSuccess;
         }
-        if ((e = hipEventRecord(e1, st)) != hipSuccess || (e = hipEventSynchronize(e1)) != hipSuccess)
-            return e;
-        if (!ok) {
+        e = hipStreamEndCapture(st, &g);
+        if (!ok || e != hipSuccess) {
+            if (g)
+                (void)hipGraphDestroy(g);
             (void)hipGetLastError();
-            return hipSuccess;
+            return ok ? e : hipSuccess;        // a launch the device refused: not a candidate
         }
         float ms = 0.f;
-        if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess)
+        if ((e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0)) == hipSuccess &&
+            (e = hipGraphLaunch(ge, st)) == hipSuccess && (e = hipEventRecord(e0, st)) == hipSuccess &&
+            (e = hipGraphLaunch(ge, st)) == hipSuccess && (e = hipEventRecord(e1, st)) == hipSuccess &&
+            (e = hipEventSynchronize(e1)) == hipSuccess)
+            e = hipEventElapsedTime(&ms, e0, e1);
+        if (ge)
+            (void)hipGraphExecDestroy(ge);
+        (void)hipGraphDestroy(g);
+        if (e != hipSuccess)
             return e;
         us = 1000.0 * ms / iters;
         return hipSuccess;
@@ -643,8 +660,12 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
 // tails of the kernels unequally and can change which of them is fastest at
 // an M (the pages' backend choice is keyed on has_residual for the same
 // reason).  For each M, every distinct tactic of `table` whose token tile
-// serves M is timed at M with a residual, best of three rounds, and the
-// fastest is kept.
+// serves M is timed at M with a residual, best of three rounds; the fastest
+// replaces the plain table's entry only if it beats that entry's own time by
+// more than SKINNY_TUNE_RESIDUAL_MARGIN (relative, default 0.01, about the
+// spread of two timings of one tactic) -- or, where the entry is a dot2
+// kernel at M <= 8, by more than the dot2 margin the plain table was chosen
+// with.
 skinny_status tune_residual(const void *W, int N, int K, int ldw, int half, skinny_out_dtype od, int nxcd,
                             const Table &table, Table &res_table)
 {
@@ -662,6 +683,8 @@ skinny_status tune_residual(const void *W, int N, int K, int ldw, int half, skin
         ens.push_back(make_entry(t, N, K, half));
         max_ws = std::max(max_ws, ws_floats(ens.back()));
     }
+    const double margin = std::max(0.0, env_double("SKINNY_TUNE_RESIDUAL_MARGIN", 0.01));
+    const double dot2_margin = env_double("SKINNY_TUNE_DOT2_MARGIN", 0.02);
     Harness h;
     HIP_TRY(h.init(W, N, K, ldw, od, nxcd, max_ws));
     h.a.res = h.rbuf.p;
@@ -686,12 +709,21 @@ skinny_status tune_residual(const void *W, int N, int K, int ldw, int half, skin
             continue;
         std::vector<double> best;
         HIP_TRY(h.times_at(m, top, best));
-        int pick = -1;
-        for (size_t c = 0; c < top.size(); ++c)
+        int pick = -1, plain = -1;
+        for (size_t c = 0; c < top.size(); ++c) {
             if (best[c] >= 0 && (pick < 0 || best[c] < best[(size_t)pick]))
                 pick = (int)c;
+            if (memcmp(&used[idx[c]], &table[m - 1], sizeof(skinny_tactic)) == 0)
+                plain = (int)c;
+        }
         if (pick < 0)
             continue;
+        if (plain >= 0 && best[(size_t)plain] >= 0) {
+            const bool dot2 = m <= 8 && is_dot2_path(table[m - 1].path) && dot2_margin >= 0;
+            const double keep = dot2 ? std::max(margin, dot2_margin) : margin;
+            if (best[(size_t)pick] * (1.0 + keep) >= best[(size_t)plain])
+                pick = plain;
+        }
         res_table[m - 1] = used[idx[(size_t)pick]];
         if (env_flag("SKINNY_LOG") && memcmp(&res_table[m - 1], &table[m - 1], sizeof(skinny_tactic)) != 0)
             fprintf(stderr, "[skinny] N=%d K=%d M=%d with a residual: path %d mt %d split %d at %.3f us\n", N, K,

@@ -195,10 +195,24 @@ inline bool is_retired_path(int path)
     return path == SKINNY_PATH_DOT2X || path == SKINNY_PATH_MFMAD || path == SKINNY_PATH_MFMAS ||
            path == SKINNY_PATH_MFMAR || path == SKINNY_PATH_MFMAK;
 }
-// Values of one row tile's partial, the size of one exchange node
+// MFMAT: the 16-token MFMA kernel launched over token groups of 16; a launch
+// has ceil(M / 16) of them, a table entry at most mt / 16
+constexpr int kTokenGroup = 16;
+inline int token_groups(const skinny_tactic &t)
+{
+    return t.path == SKINNY_PATH_MFMAT ? t.mt / kTokenGroup : 1;
+}
+// MFMAT is enumerated only for weights of at most this many bytes: each
+// XCD's 4 MiB L2 then holds its share of the row tiles (an eighth) with
+// room to spare, so the groups' re-reads of a tile stay on chip
+constexpr long long kTokenGroupMaxWeightBytes = 16LL << 20;
+// Values of one row tile's partial (of one token group), the size of one
+// exchange node
 inline size_t tile_values(const skinny_tactic &t)
 {
-    return is_rgs_path(t.path) ? rgs_node_floats(t) : (size_t)t.mt * t.rows;
+    if (is_rgs_path(t.path))
+        return rgs_node_floats(t);
+    return (size_t)(t.path == SKINNY_PATH_MFMAT ? kTokenGroup : t.mt) * t.rows;
 }
 
 }  // namespace skinny

@@ -27,6 +27,8 @@ size_t tactic_lds_bytes(const skinny_tactic &t, int K8)
     switch (t.path) {
     case SKINNY_PATH_MFMA:
         return (size_t)t.waves * t.mt * (t.rows + 1) * sizeof(float);
+    case SKINNY_PATH_MFMAT:                    // one group's tile of the MFMA kernel
+        return (size_t)t.waves * kTokenGroup * (t.rows + 1) * sizeof(float);
     case SKINNY_PATH_MFMAX:
         return mfmax_own_lds_bytes(t.waves, t.mt);
     case SKINNY_PATH_MFMAW:
@@ -47,6 +49,10 @@ const KernelInfo *tactic_kernel(const skinny_tactic &t, int half)
         return find_kernel(t.path, t.mt, t.rows, t.unroll, half);
     case SKINNY_PATH_DOT2R:                    // the DOT2 kernels, another grid
         return find_kernel(SKINNY_PATH_DOT2, t.mt, t.rows, t.unroll, half);
+    case SKINNY_PATH_MFMAT:                    // the 16-token MFMA kernels over token groups
+        if (t.mt != 2 * kTokenGroup && t.mt != 4 * kTokenGroup)
+            return nullptr;
+        return find_kernel(SKINNY_PATH_MFMA, kTokenGroup, t.rows, t.unroll, half);
     case SKINNY_PATH_MFMAX:
         if (t.rows != 16 * t.waves || (t.unroll != 1 && t.unroll != 2))
             return nullptr;
@@ -141,15 +147,19 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
                       "chunks", t->split, stages, kRgsChunks);
             return SKINNY_ERR_INVALID_ARG;
         }
-    } else if (t->path == SKINNY_PATH_MFMA) {
+    } else if (t->path == SKINNY_PATH_MFMA || t->path == SKINNY_PATH_MFMAT) {
+        if (t->path == SKINNY_PATH_MFMAT && t->mt != 2 * kTokenGroup && t->mt != 4 * kTokenGroup) {
+            set_error("mt=%d: MFMAT serves at most 32 or 64 tokens, in groups of %d", t->mt, kTokenGroup);
+            return SKINNY_ERR_INVALID_ARG;
+        }
         const int steps = (k8 + 3) / 4;
         if (t->split > steps) {
             set_error("split=%d exceeds the %d 32-element K steps of a row", t->split, steps);
             return SKINNY_ERR_INVALID_ARG;
         }
     } else {
-        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 3 (MFMAX), 8 (DOT2R), 9 (MFMAW), 10 (MFMA4) or 11 (DOT2W)",
-                  t->path);
+        set_error("path=%d: must be 0 (DOT2), 1 (MFMA), 3 (MFMAX), 8 (DOT2R), 9 (MFMAW), 10 (MFMA4), 11 (DOT2W) "
+                  "or 12 (MFMAT)", t->path);
         return SKINNY_ERR_INVALID_ARG;
     }
     // the instance first: its fields are then small, so the LDS sizes below
@@ -159,7 +169,7 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
                   t->unroll);
         return SKINNY_ERR_INVALID_ARG;
     }
-    const size_t lds_limit = (t->path == SKINNY_PATH_MFMA) ? kMaxLds : kMaxLdsStaged;
+    const size_t lds_limit = (t->path == SKINNY_PATH_MFMA || t->path == SKINNY_PATH_MFMAT) ? kMaxLds : kMaxLdsStaged;
     if (tactic_lds_bytes(*t, k8) > lds_limit) {
         set_error("tactic needs %zu bytes of LDS (limit %zu)", tactic_lds_bytes(*t, k8), lds_limit);
         return SKINNY_ERR_INVALID_ARG;
@@ -182,18 +192,28 @@ int skinny_enumerate_tactics_ex(int N, int K, int cus, skinny_tactic *buf, int c
     const KernelInfo *ks = kernel_table(&nk);
     static const int kWaves[] = {1, 2, 4, 8};
     static const int kSplits[] = {1, 2, 3, 4, 5, 6, 8};
+    // a weight small enough for token groups (MFMAT) to re-read from L2
+    const bool small_weight = (long long)N * K * 2 <= kTokenGroupMaxWeightBytes;
     for (int i = 0; i < nk; ++i) {
         const KernelInfo &k = ks[i];
         if (k.half)
             continue;                                    // the same tactics as the BF16 twin
-        // the DOT2 kernels also run over equal row ranges (DOT2R)
-        const int paths[2] = {k.path, k.path == SKINNY_PATH_DOT2 ? SKINNY_PATH_DOT2R : -1};
-        for (int path : paths) {
+        // the DOT2 kernels also run over equal row ranges (DOT2R); the 16-token
+        // MFMA kernels also over 2 or 4 token groups (MFMAT)
+        struct { int path, mt; } uses[3] = {{k.path, k.mt}, {-1, 0}, {-1, 0}};
+        if (k.path == SKINNY_PATH_DOT2)
+            uses[1] = {SKINNY_PATH_DOT2R, k.mt};
+        if (k.path == SKINNY_PATH_MFMA && k.mt == kTokenGroup && small_weight) {
+            uses[1] = {SKINNY_PATH_MFMAT, 2 * kTokenGroup};
+            uses[2] = {SKINNY_PATH_MFMAT, 4 * kTokenGroup};
+        }
+        for (const auto &use : uses) {
+            const int path = use.path;
             if (path < 0)
                 continue;
             for (int w : kWaves) {
                 for (int s : kSplits) {
-                    skinny_tactic t = {path, k.mt, k.rows, w, k.unroll, s};
+                    skinny_tactic t = {path, use.mt, k.rows, w, k.unroll, s};
                     if (path == SKINNY_PATH_MFMAX) {
                         if (w != k.rows)                 // k.rows is the wave count
                             continue;
@@ -219,7 +239,8 @@ int skinny_enumerate_tactics_ex(int N, int K, int cus, skinny_tactic *buf, int c
                     if (skinny_tactic_check(&t, N, K) != SKINNY_OK)
                         continue;
                     const long long tiles = ((long long)N + t.rows - 1) / t.rows, chip = 8LL * cus;
-                    if (s > 1 && tiles * w >= chip && path != SKINNY_PATH_MFMAW && !is_rgs_path(path))
+                    if (s > 1 && tiles * token_groups(t) * w >= chip && path != SKINNY_PATH_MFMAW &&
+                        !is_rgs_path(path))
                         continue;   // enough waves already; a K split only adds traffic
                     if (path == SKINNY_PATH_DOT2R && tiles * s > chip)
                         continue;   // many workgroups per CU balance themselves
@@ -240,7 +261,7 @@ int skinny_enumerate_tactics_ex(int N, int K, int cus, skinny_tactic *buf, int c
                     } else if (path == SKINNY_PATH_MFMAX) {
                         if (k8 / s < 2 * kMfmaxChunks)
                             continue;
-                    } else if (path == SKINNY_PATH_MFMA) {
+                    } else if (path == SKINNY_PATH_MFMA || path == SKINNY_PATH_MFMAT) {
                         const int per_split = ((k8 + 3) / 4) / s;
                         if (per_split < w * k.unroll && !(w == 1 && s == 1 && k.unroll == 1))
                             continue;

@@ -250,6 +250,33 @@ def test_barrier_free_row_range_tactics():
             sk.tactic_check(bad, 6288, 1024)
 
 
+def test_token_group_tactics():
+    """MFMAT (path 12): the 16-token MFMA kernels over token groups, serving
+    at most 32 or 64 tokens.  Candidates only for weights of at most 16 MiB
+    (their groups re-read each row tile from L2), with the MFMA kernels'
+    rows, waves and unroll."""
+    small = [t for t in sk.enumerate_tactics(1536, 128) if t.path == sk.PATH_MFMAT]
+    assert {t.mt for t in small} == {32, 64}
+    assert {t.rows for t in small} == {16, 32, 64}
+    plain = {(t.rows, t.waves, t.unroll) for t in sk.enumerate_tactics(1536, 128)
+             if t.path == sk.PATH_MFMA and t.mt == 16 and t.split == 1}
+    assert {(t.rows, t.waves, t.unroll) for t in small if t.split == 1} == plain
+    assert any(t.path == sk.PATH_MFMAT for t in sk.enumerate_tactics(140, 7168))
+    assert any(t.path == sk.PATH_MFMAT for t in sk.enumerate_tactics(256, 512))
+    for n, k in ((6288, 7168), (3584, 7168), (7168, 18432), (1024, 8200)):   # 16 MiB and more
+        assert not any(t.path == sk.PATH_MFMAT for t in sk.enumerate_tactics(n, k)), (n, k)
+    assert any(t.path == sk.PATH_MFMAT for t in sk.enumerate_tactics(1024, 8192))   # exactly 16 MiB
+    sk.tactic_check(T(sk.PATH_MFMAT, 64, 16, 4, 1, 1), 1536, 128)
+    sk.tactic_check(T(sk.PATH_MFMAT, 32, 64, 2, 2, 2), 140, 7168)
+    for bad in (T(sk.PATH_MFMAT, 16, 16, 4, 1, 1),     # one group: that is MFMA
+                T(sk.PATH_MFMAT, 48, 16, 4, 1, 1),     # 32 or 64 tokens only
+                T(sk.PATH_MFMAT, 64, 48, 4, 1, 1),     # no 48-row MFMA instance
+                T(sk.PATH_MFMAT, 64, 64, 4, 4, 1),     # no 64-row MFMA instance with unroll 4
+                T(sk.PATH_MFMAT, 64, 16, 4, 1, 5)):    # 128 K: 4 steps of 32
+        with pytest.raises(ValueError):
+            sk.tactic_check(bad, 1536, 128)
+
+
 def test_table_rule_with_a_fake_timer():
     """table[M] = fastest candidate whose token tile >= M; ties to the
     smaller tile, then the lower index; failed candidates are skipped."""
@@ -310,6 +337,9 @@ def test_bench_names_the_kernel_of_every_tactic():
     assert bench.kernel_name(T(sk.PATH_DOT2R, 2, 4, 1, 2, 1)) == "k_dot2<2, 4, 2, false>"
     assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2)) == "k_mfmaw<2, 4, 4, 16, false>"
     assert bench.kernel_name(T(sk.PATH_MFMAW, 16, 32, 2, 1, 1)) == "k_mfmaw<1, 2, 2, 8, false>"
+    assert bench.kernel_name(T(sk.PATH_MFMAT, 64, 32, 4, 2, 1)) == "k_mfma<1, 2, 2, false>"
+    for t in sk.enumerate_tactics(1536, 128):
+        assert bench.kernel_name(t), t
 
 
 def test_shipped_table_is_legal_and_profiled():

@@ -138,7 +138,7 @@ def test_residual_exact(sk, od, inplace):
     else:
         r_dev = gu.dev_bf16(si.f32_to_bf16_bits(r_int.astype(np.float32)))
     tactics = _one_per_path(sk, n, k)
-    assert {t.path for t in tactics} == {0, 1, 3, 8, 9, 10, 11}
+    assert {t.path for t in tactics} == {0, 1, 3, 8, 9, 10, 11, 12}
     _say(f"[residual {od} {'inplace' if inplace else 'separate'}] {len(tactics)} tactics")
     for t in tactics:
         plan = sk.Prepared(w, out_dtype, table=gu.forced_table(t))

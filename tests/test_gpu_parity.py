@@ -278,27 +278,30 @@ DECODE_KERNEL_SETS = {
 }
 
 
-def shipped_table(sk, n, k):
-    """The 64-entry table the benchmark loads for an [n, k] weight (BF16 in
-    and out, 256 CUs), from the file shipped with the package."""
+def shipped_table(sk, n, k, od="bf16"):
+    """The 64-entry table the benchmark loads for an [n, k] weight (BF16 in,
+    `od` out, 256 CUs), from the file shipped with the package; the BF16-out
+    table when none ships for `od`."""
     path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                         "skinny_bf16_decode_amd", "tables", "mi355x_tuned.txt")
     with open(path) as f:
-        for line in f:
-            p = line.split()
-            if p[3:8] == ["256", str(n), str(k), "bf16", "bf16"]:
+        lines = [line.split() for line in f]
+    for want in (od, "bf16"):
+        for p in lines:
+            if p[3:8] == ["256", str(n), str(k), "bf16", want]:
                 return [sk.Tactic(*map(int, e.split("."))) for e in p[8:]]
     raise AssertionError(f"no shipped table for {n}x{k}")
 
 
 # the weights with a shipped table, by workload id
-SHIPPED = {2: (3584, 7168), 3: (6288, 7168), 5: (7168, 18432)}
+SHIPPED = {2: (3584, 7168), 3: (6288, 7168), 4: (1536, 128), 5: (7168, 18432)}
 
 
 @pytest.mark.parametrize("cid", sorted(SHIPPED))
 def test_shipped_tables_exact_full_size(sk, cid):
-    """The shipped table of each decode weight, forced, on integer inputs at
-    the full shape (x, W in {-3..3}, so every partial sum is exact in fp32):
+    """The shipped table of each weight (the fp32-out table for fp32 out
+    where one ships), forced, on integer inputs at the full shape (x, W in
+    {-3..3}, so every partial sum is exact in fp32):
     every M = 1..64 -- each kernel the table uses, at each M it serves --
     bit for bit, fp32 out equal to the oracle and BF16 out to its nearest-even
     rounding."""
@@ -309,9 +312,9 @@ def test_shipped_tables_exact_full_size(sk, cid):
     o, _ = oracle.gemm(x_bits, w_bits)
     _say(f"[shipped exact {n}x{k}] oracle {time.time() - t0:.1f}s")
     assert np.all(np.abs(o) < 2 ** 24)
-    table = shipped_table(sk, n, k)
     w = gu.dev_bf16(w_bits)
     for od in (torch.bfloat16, torch.float32):
+        table = shipped_table(sk, n, k, "f32" if od == torch.float32 else "bf16")
         plan = sk.Prepared(w, od, table=table)
         for m in range(1, 65):
             _check_exact(sk, plan, x_bits, o, m, f"{n}x{k} {od} M={m} {table[m - 1]}")
@@ -520,7 +523,7 @@ def test_split_k_exchange_exact(sk, remap, monkeypatch):
     w = gu.dev_bf16(w_bits)
     tactics = [t for t in sk.enumerate_tactics(n, k) if t.split > 1]
     _say(f"[split remap={remap}] {len(tactics)} tactics")
-    assert {t.path for t in tactics} >= {0, 1, 3, 8, 9, 10, 11}
+    assert {t.path for t in tactics} >= {0, 1, 3, 8, 9, 10, 11, 12}
     for t in tactics:
         plan = sk.Prepared(w, torch.float32, table=gu.forced_table(t))
         for rep in range(2):
