@@ -208,8 +208,9 @@ def kernel_name(t):
         args, name = (1, t.rows // 16, t.unroll), "k_mfma"
     elif t.path == 3:                        # MFMAX: unroll picks the grid, not the kernel
         args, name = (T, w), "k_mfmax"
-    elif t.path == 9:                        # MFMAW: row groups, waves, stage chunks
-        args, name = (T, t.rows // 16, w, 8 * t.unroll), "k_mfmaw"
+    elif t.path == 9:                        # MFMAW: row groups, waves, stage chunks, stages in flight
+        sc, depth = (16 if t.unroll in (2, 4) else 8), (2 if t.unroll <= 2 else 1)
+        args, name = (T, t.rows // 16, w, sc, depth), "k_mfmaw"
     elif t.path == 10:                       # MFMA4: token groups and row groups of 4, stages in flight
         args, name = ("true", t.mt // 4, t.rows // 4, t.unroll), "k_rgs"
     elif t.path == 11:                       # DOT2W: tokens, row groups of 4, stages in flight

@@ -130,9 +130,9 @@ typedef struct {
     int waves;  /* wavefronts per workgroup: 1,2,4,8 */
     int unroll; /* 16-byte weight loads per lane per row per pipeline stage: 1,2,4
                    (MFMAX: 1 = row tiles of 16 * waves rows, 2 = equal row ranges, its
-                   stage is fixed at 32 chunks; MFMAW: the stage width in 8-chunk units,
-                   1 or 2, two stages in flight; MFMA4, DOT2W: stages of 16 chunks in
-                   flight, 2 or 3) */
+                   stage is fixed at 32 chunks; MFMAW: 1 or 2 = stages of 8 or 16
+                   chunks, two in flight, 3 or 4 = the same, one in flight; MFMA4,
+                   DOT2W: stages of 16 chunks in flight, 2 or 3) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16 (MFMAW 1..4,
                    MFMA4 and DOT2W 1..8); their fp32 partials meet in the plan's
                    workspace, one agent-scope atomic swap per value and level */

@@ -997,13 +997,15 @@ __global__ __launch_bounds__(64 * NW) void k_mfmax(KArgs a)
 // 16 chunks (SC / 4 MFMA K-steps).  No wave waits for another until the end:
 //
 //  * the weight and the x of a stage are loaded row-contiguously -- each
-//    wave-wide load is 64 / SC rows (or tokens) x 16 SC bytes -- two stages
-//    ahead in registers, and re-laid out through the wave's own LDS tiles
-//    [16 RG][SC + 2] and [MT][SC + 2] (chunks) into A and B fragments.  The
-//    stage width sets the bytes a wave keeps in flight.  A stage's weight
-//    registers are refilled as soon as they are in LDS, its x registers only
-//    after its MFMAs: x comes from L2, and issuing it with the weight (or
-//    three stages ahead) measured slower;
+//    wave-wide load is 64 / SC rows (or tokens) x 16 SC bytes -- DEPTH (1 or
+//    2) stages ahead in registers, and re-laid out through the wave's own LDS
+//    tiles [16 RG][SC + 2] and [MT][SC + 2] (chunks) into A and B fragments.
+//    The stage width, the row groups and the depth set the bytes a wave keeps
+//    in flight: about 8 KiB of weight per wave (32 KiB per CU) measured
+//    best, so four row groups stream one stage ahead and two row groups two.
+//    A stage's weight registers are refilled as soon as they are in LDS, its
+//    x registers only after its MFMAs: x comes from L2, and issuing it with
+//    the weight (or three stages ahead) measured slower;
 //  * each B fragment feeds the MFMAs of all RG row groups, and the waves take
 //    disjoint K stages, so x is read once per workgroup and K stage however
 //    many rows the range has, with no x shared between waves;
@@ -1016,10 +1018,11 @@ __global__ __launch_bounds__(64 * NW) void k_mfmax(KArgs a)
 // k_mfmax).  Unlike MFMAX, whose waves share each x window and meet at a
 // barrier every two stages, no wave here waits on another's loads.
 // ---------------------------------------------------------------------------
-template <int T, int RG, int NW, int SC, bool H>
+template <int T, int RG, int NW, int SC, int DEPTH, bool H>
 __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
 {
     static_assert(SC == 8 || SC == 16, "stages of 8 or 16 chunks");
+    static_assert(DEPTH == 1 || DEPTH == 2, "one or two stages in flight");
     constexpr int RPL = 64 / SC;               // rows (tokens) per wave-wide load
     constexpr int NL = 16 / RPL;               // loads per 16 rows (tokens)
     constexpr int KS = SC / 4;                 // MFMA K-steps per stage
@@ -1087,7 +1090,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
 #pragma unroll
         for (int q = 0; q < NL * RG; ++q)
             wl[(RPL * q + lr) * PITCH + lc] = wv[q];
-        load_wt(wv, j + 2);
+        load_wt(wv, j + DEPTH);
         __builtin_amdgcn_sched_barrier(0);
         if (j < mine) {
 #pragma unroll
@@ -1112,22 +1115,31 @@ __global__ __launch_bounds__(64 * NW) void k_mfmaw(KArgs a)
                         acc[r][t] = mma16<H>(av[st], bv[st][t], acc[r][t]);
             }
         }
-        load_xt(xv, j + 2);
+        load_xt(xv, j + DEPTH);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Two stages in flight; every pass issues all of its loads (past the
+    // DEPTH stages in flight; every pass issues all of its loads (past the
     // wave's last stage they touch no memory), so the waits stay partial.
-    u32x4 wa[NL * RG], xa[NL * T], wb[NL * RG], xb[NL * T];
-    load_wt(wa, 0);
-    load_xt(xa, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_wt(wb, 1);
-    load_xt(xb, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int j = 0; j < mine; j += 2) {
-        step(wa, xa, j);
-        step(wb, xb, j + 1);
+    if constexpr (DEPTH == 2) {
+        u32x4 wa[NL * RG], xa[NL * T], wb[NL * RG], xb[NL * T];
+        load_wt(wa, 0);
+        load_xt(xa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_wt(wb, 1);
+        load_xt(xb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < mine; j += 2) {
+            step(wa, xa, j);
+            step(wb, xb, j + 1);
+        }
+    } else {
+        u32x4 wa[NL * RG], xa[NL * T];
+        load_wt(wa, 0);
+        load_xt(xa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < mine; ++j)
+            step(wa, xa, j);
     }
 
     // add the NW partial sums in wave order: value e = ((r T + t) 4 + q) 64 + lane

@@ -148,10 +148,12 @@ inline size_t mfmax_own_lds_bytes(int waves, int mt)
 {
     return (size_t)(16 * waves + mfmax_x_windows(mt) * mt) * (kMfmaxChunks + 2) * 16;
 }
-// MFMAW: stages of 8 unroll chunks (8 or 16); wave tiles [waves][rows + mt]
-// [stage + 2 chunks], which the waves' partial sums (rows x mt floats a wave)
-// reuse at the end -- the larger of the two per wave
-inline int mfmaw_stage_chunks(int unroll) { return 8 * unroll; }
+// MFMAW: unroll 1 and 2 are stages of 8 and 16 chunks two deep, 3 and 4 the
+// same one deep; wave tiles [waves][rows + mt][stage + 2 chunks], which the
+// waves' partial sums (rows x mt floats a wave) reuse at the end -- the
+// larger of the two per wave
+inline int mfmaw_stage_chunks(int unroll) { return unroll == 2 || unroll == 4 ? 16 : 8; }
+inline int mfmaw_depth(int unroll) { return unroll <= 2 ? 2 : 1; }
 constexpr size_t mfmaw_wave_lds_bytes(int rows, int mt, int stage_chunks)
 {
     return (size_t)(rows + mt) * (stage_chunks + 2) * 16 > (size_t)rows * mt * 4

@@ -123,8 +123,9 @@ skinny_status skinny_tactic_check(const skinny_tactic *t, int N, int K)
             return SKINNY_ERR_INVALID_ARG;
         }
     } else if (t->path == SKINNY_PATH_MFMAW) {
-        if (t->unroll != 1 && t->unroll != 2) {
-            set_error("unroll=%d: for MFMAW the stage width in 8-chunk units, 1 or 2", t->unroll);
+        if (t->unroll < 1 || t->unroll > 4) {
+            set_error("unroll=%d: for MFMAW 1 or 2 (stages of 8 or 16 chunks, two in flight) or 3 or 4 (the "
+                      "same, one in flight)", t->unroll);
             return SKINNY_ERR_INVALID_ARG;
         }
         const int sc = mfmaw_stage_chunks(t->unroll), stages = (k8 + sc - 1) / sc;

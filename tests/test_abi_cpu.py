@@ -228,22 +228,25 @@ def test_row_group_stream_tactics(path, tiles):
 
 def test_barrier_free_row_range_tactics():
     """MFMAW (path 9): ranges of at most 16, 32 or 64 rows (row groups of
-    16), with its compiled wave counts only, stages of 8 (unroll 1) or 16
-    chunks (unroll 2), and a K split no larger than its stage count; every
-    wave of every candidate owns at least two stages of its K part."""
+    16), with its compiled wave counts only, stages of 8 (unroll 1, 3) or 16
+    chunks (unroll 2, 4), two (unroll 1, 2) or one (3, 4) in flight, and a K
+    split no larger than its stage count; every wave of every candidate owns
+    at least two stages of its K part."""
     cands = [t for t in sk.enumerate_tactics(6288, 7168) if t.path == sk.PATH_MFMAW]
     assert {t.mt for t in cands} == {16, 32, 64}
-    assert {t.unroll for t in cands} == {1, 2}
+    assert {t.unroll for t in cands} == {1, 2, 3, 4}
     assert {t.rows for t in cands} == {16, 32, 64}
     for t in cands:
-        assert t.unroll in (1, 2) and t.rows % 16 == 0
-        assert (7168 // 8) // t.split >= 2 * t.waves * 8 * t.unroll
+        assert t.rows % 16 == 0
+        sc = 16 if t.unroll in (2, 4) else 8
+        assert (7168 // 8) // t.split >= 2 * t.waves * sc
     sk.tactic_check(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2), 6288, 7168)
     sk.tactic_check(T(sk.PATH_MFMAW, 16, 32, 2, 2, 1), 6288, 7168)
     for bad in (T(sk.PATH_MFMAW, 32, 64, 8, 2, 1),    # spills: not compiled
                 T(sk.PATH_MFMAW, 16, 48, 4, 2, 1),    # no 3-group instance
                 T(sk.PATH_MFMAW, 16, 24, 4, 2, 1),    # not whole row groups
-                T(sk.PATH_MFMAW, 16, 32, 4, 3, 1),    # stages of 8 or 16 chunks only
+                T(sk.PATH_MFMAW, 16, 32, 4, 5, 1),    # stages of 8 or 16 chunks, one or two deep
+                T(sk.PATH_MFMAW, 16, 32, 4, 3, 1),    # no one-deep instance of two row groups, 16 tokens
                 T(sk.PATH_MFMAW, 16, 32, 4, 2, 9),    # 128 chunks: 8 stages of 16
                 T(sk.PATH_MFMAW, 16, 32, 4, 1, 17)):  # 16 stages of 8
         with pytest.raises(ValueError):
@@ -335,8 +338,10 @@ def test_bench_names_the_kernel_of_every_tactic():
     assert bench.kernel_name(T(sk.PATH_DOT2W, 8, 28, 4, 2, 1)) == "k_rgs<false, 8, 7, 2, false>"
     assert bench.kernel_name(T(3, 32, 64, 4, 2, 2)) == "k_mfmax<2, 4, false>"
     assert bench.kernel_name(T(sk.PATH_DOT2R, 2, 4, 1, 2, 1)) == "k_dot2<2, 4, 2, false>"
-    assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2)) == "k_mfmaw<2, 4, 4, 16, false>"
-    assert bench.kernel_name(T(sk.PATH_MFMAW, 16, 32, 2, 1, 1)) == "k_mfmaw<1, 2, 2, 8, false>"
+    assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 64, 4, 2, 2)) == "k_mfmaw<2, 4, 4, 16, 2, false>"
+    assert bench.kernel_name(T(sk.PATH_MFMAW, 16, 32, 2, 1, 1)) == "k_mfmaw<1, 2, 2, 8, 2, false>"
+    assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 64, 4, 3, 2)) == "k_mfmaw<2, 4, 4, 8, 1, false>"
+    assert bench.kernel_name(T(sk.PATH_MFMAW, 32, 32, 4, 4, 1)) == "k_mfmaw<2, 2, 4, 16, 1, false>"
     assert bench.kernel_name(T(sk.PATH_MFMAT, 64, 32, 4, 2, 1)) == "k_mfma<1, 2, 2, false>"
     for t in sk.enumerate_tactics(1536, 128):
         assert bench.kernel_name(t), t
