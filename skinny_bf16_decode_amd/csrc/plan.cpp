@@ -1075,9 +1075,10 @@ skinny_status skinny_describe(const skinny_plan *p, int M, char *buf, size_t len
     const Entry &en = p->e[M];
     static const char *const kNames[] = {"dot2", "mfma16x16x32", "dot2x", "mfmax16x16x32", "mfmad16x16x32",
                                          "mfmas16x16x32", "mfmar16x16x32", "mfmak16x16x32", "dot2r",
-                                         "mfmaw16x16x32", "mfma4x4x4", "dot2w"};
+                                         "mfmaw16x16x32", "mfma4x4x4", "dot2w", "mfmat16x16x32"};
+    constexpr int kPaths = (int)(sizeof(kNames) / sizeof(kNames[0]));
     snprintf(buf, len, "%s mt=%d rows=%d waves=%d unroll=%d split=%d grid=%u block=%u lds=%u",
-             (t.path >= 0 && t.path <= 11) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
+             (t.path >= 0 && t.path < kPaths) ? kNames[t.path] : "?", t.mt, t.rows, t.waves, t.unroll, t.split,
              en.grid, en.block, en.lds);
     return SKINNY_OK;
 }

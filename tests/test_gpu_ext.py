@@ -142,6 +142,8 @@ def test_residual_exact(sk, od, inplace):
     _say(f"[residual {od} {'inplace' if inplace else 'separate'}] {len(tactics)} tactics")
     for t in tactics:
         plan = sk.Prepared(w, out_dtype, table=gu.forced_table(t))
+        name = plan.describe(t.mt).split()[0]
+        assert name.startswith(sk.PATH_NAMES[t.path]), (t, name)   # every path has its name
         for m in sorted({t.mt, max(1, t.mt - 3)}):
             out = gu.out_buffer(n, out_dtype)
             x = gu.dev_bf16(x_bits[:m])
