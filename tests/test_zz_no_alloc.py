@@ -65,6 +65,14 @@ def test_static_run_matches_plan_run_twice(sk):
     _one(sk, 1000, 4096, 13, sk.Tactic(sk.PATH_MFMA4, 16, 16, 2, 2, 3), 802)
 
 
+def test_static_run_token_groups_and_one_stage(sk):
+    # token groups: 3 groups of 16 tokens over 9 row tiles with an 8-way K
+    # split, each (group, tile) with nodes of its own in the static scratch;
+    # then the one-stage split-2 MFMAW the packed decode weight runs at M = 32
+    _one(sk, 140, 7168, 40, sk.Tactic(sk.PATH_MFMAT, 64, 16, 4, 1, 8), 804)
+    _one(sk, 6288, 7168, 32, sk.Tactic(sk.PATH_MFMAW, 32, 64, 4, 3, 2), 805)
+
+
 def test_static_run_without_split_and_limits(sk):
     """No split: no scratch at all.  A tactic whose exchange would exceed the
     static scratch is refused before any launch."""
