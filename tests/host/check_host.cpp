@@ -22,6 +22,32 @@ static const KernelInfo kKernels[] = {
 };
 #undef SK_PAIR
 
+// The partial values one workgroup of each instance swaps per split-K
+// exchange node, from the kernel's own template arguments: k_dot2<MT, R, U>
+// MT R, k_mfma<T, RT, U> (16 T)(16 RT), k_mfmax<T, NW> and k_mfmaw<T, RG, NW,
+// SC, DEPTH> 256 T NW and 256 T RG (4 values x 64 lanes per 16x16 tile), and
+// k_rgs<MFMA, T, RG, U> 64 lanes x the sums a lane keeps after its lane
+// reduction (the power of two >= 16 at least its 4 RG T (MFMA4) or RG T
+// (DOT2W) sums, over 16).
+constexpr int node_k_dot2(int mt, int r, int) { return mt * r; }
+constexpr int node_k_mfma(int t, int rt, int) { return 16 * t * 16 * rt; }
+constexpr int node_k_mfmax(int t, int nw) { return 256 * t * nw; }
+constexpr int node_k_mfmaw(int t, int rg, int, int, int) { return 256 * t * rg; }
+constexpr int node_k_rgs(bool mfma, int t, int rg, int)
+{
+    int p = 16;
+    while (p < (mfma ? 4 : 1) * rg * t)
+        p *= 2;
+    return p / 16 * 64;
+}
+#define SK_PAIR(PATH, MT, ROWS, U, KERNEL, ...) node_##KERNEL(__VA_ARGS__), node_##KERNEL(__VA_ARGS__)
+static const int kNodeValues[] = {
+#include "instances.def"
+};
+#undef SK_PAIR
+static_assert(sizeof(kNodeValues) / sizeof(kNodeValues[0]) == sizeof(kKernels) / sizeof(kKernels[0]),
+              "one node size per instance");
+
 const KernelInfo *kernel_table(int *count)
 {
     *count = (int)(sizeof(kKernels) / sizeof(kKernels[0]));
@@ -104,6 +130,34 @@ static void check_enumeration()
     CHECK(skinny_enumerate_tactics_ex(8, 8, 256, nullptr, 1) == -1, "NULL buffer");
     CHECK(skinny_enumerate_tactics_ex(8, 8, 256, &one, -1) == -1, "cap<0");
     CHECK(skinny_enumerate_tactics(INT_MIN, INT_MIN, nullptr, 0) == -1, "INT_MIN shape");
+}
+
+// The host sizes the exchange workspace with tile_values(t) floats per node
+// (times token_groups(t) for MFMAT); the kernel a tactic launches indexes
+// nodes of its own partial count.  The two must agree for every enumerated
+// tactic, or a split launch would swap past the workspace.
+static void check_exchange_nodes()
+{
+    int checked = 0;
+    for (const Shape &s : kShapes) {
+        if ((long long)s.N * s.K >= (1LL << 31))
+            continue;                                    // not a shape a plan accepts
+        for (const skinny_tactic &t : enumerate(s.N, s.K, 256)) {
+            const KernelInfo *k = tactic_kernel(t);
+            CHECK(k != nullptr, "path=%d mt=%d rows=%d: no instance", t.path, t.mt, t.rows);
+            if (!k)
+                continue;
+            const int node = kNodeValues[k - kKernels];
+            CHECK(tile_values(t) == (size_t)node, "N=%d K=%d path=%d mt=%d rows=%d waves=%d unroll=%d: host %zu, "
+                  "kernel %d values per node", s.N, s.K, t.path, t.mt, t.rows, t.waves, t.unroll, tile_values(t), node);
+            if (t.path == SKINNY_PATH_MFMAT)
+                CHECK(token_groups(t) * kTokenGroup == t.mt, "MFMAT mt=%d: groups %d", t.mt, token_groups(t));
+            else
+                CHECK(token_groups(t) == 1, "path=%d: %d token groups", t.path, token_groups(t));
+            ++checked;
+        }
+    }
+    CHECK(checked > 1000, "only %d tactics checked", checked);
 }
 
 // Tactics of arbitrary fields: the check must answer without undefined
@@ -362,6 +416,7 @@ int main(int argc, char **argv)
 {
     const char *dir = argc > 1 ? argv[1] : ".";
     check_enumeration();
+    check_exchange_nodes();
     check_tactic_fuzz();
     check_select_table();
     check_status_strings();
