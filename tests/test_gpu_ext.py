@@ -62,10 +62,12 @@ def _tight(got, o, s, mode, label, residual=False):
 
 
 def _one_per_path(sk, n, k):
-    """The first enumerated tactic of every (path, token tile, split > 1) kind."""
+    """The first enumerated tactic of every (path, token tile, split > 1) kind,
+    and for MFMAW of every stage form (unroll: 8 or 16 chunks, one or two
+    stages in flight)."""
     seen, pick = set(), []
     for t in sk.enumerate_tactics(n, k):
-        key = (t.path, t.mt, t.split > 1)
+        key = (t.path, t.mt, t.split > 1, t.unroll if t.path == sk.PATH_MFMAW else 0)
         if key not in seen:
             seen.add(key)
             pick.append(t)
