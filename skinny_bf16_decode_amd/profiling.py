@@ -6,7 +6,10 @@
 Reads the kernel-trace statistics (``*_kernel_stats.csv``) and the per-dispatch
 counter collections of a FETCH_SIZE run and a WRITE_SIZE run (KiB per
 dispatch), and optionally of a MfmaUtil run and an SQ_INSTS_VALU_MFMA_MOPS_BF16
-run (MFMA busy percent and MFMA operations per dispatch).  Counter values are scaled by the ratio of the known bytes of a
+run (MFMA busy percent and MFMA operations per dispatch) and of one run of the
+LDS and issue counters LDS_COUNTERS (LDS instructions, bank-conflict cycles,
+waits for LDS issue and for anything as a share of wave time, vector-memory
+reads, LDS data FIFO full cycles).  Counter values are scaled by the ratio of the known bytes of a
 calibration kernel to what the counter reports for it: ``k_probe_read``
 streams exactly 2*N*K bytes of one weight copy (FETCH_SIZE), and a 64 MiB
 device-to-device copy writes exactly 64 MiB (WRITE_SIZE).  Writes a short
@@ -44,6 +47,42 @@ def load_counters(path):
         for r in csv.DictReader(f):
             rows[r["Kernel_Name"]].append(float(r["Counter_Value"]))
     return rows
+
+
+# one --pmc pass: seven SQ counters (a pass may hold eight)
+LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY",
+                "SQ_INSTS_VMEM_RD", "SQ_LDS_DATA_FIFO_FULL")
+
+
+def load_counter_sets(path):
+    """kernel -> counter -> per-dispatch values, from a run of several counters."""
+    rows = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return rows
+
+
+def lds_table(path):
+    """Markdown rows of the LDS and issue counters per kernel.  SQ_WAIT_INST_LDS,
+    SQ_WAIT_ANY and SQ_WAVE_CYCLES are all wave quad-cycles, so their ratios
+    are shares of wave time."""
+    sets = load_counter_sets(path)
+    out = ["| kernel | dispatches | LDS instructions | bank-conflict cycles per LDS instruction | "
+           "waiting for LDS issue, % of wave time | waiting for anything, % of wave time | "
+           "VMEM read instructions | LDS data FIFO full cycles |", "|---|---|---|---|---|---|---|---|"]
+    for k in sorted(sets, key=_short):
+        if not _ours(k):
+            continue
+        c = {n: statistics.mean(v) for n, v in sets[k].items()}
+        lds, wave = c.get("SQ_INSTS_LDS", 0.0), c.get("SQ_WAVE_CYCLES", 0.0)
+        conflict = c.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds if lds else float("nan")
+        wait_lds = 100.0 * c.get("SQ_WAIT_INST_LDS", 0.0) / wave if wave else float("nan")
+        wait_any = 100.0 * c.get("SQ_WAIT_ANY", 0.0) / wave if wave else float("nan")
+        out.append(f"| `{_short(k)}` | {len(sets[k].get('SQ_INSTS_LDS', []))} | {lds:.3e} | {conflict:.3f} | "
+                   f"{wait_lds:.1f} | {wait_any:.1f} | {c.get('SQ_INSTS_VMEM_RD', 0.0):.3e} | "
+                   f"{c.get('SQ_LDS_DATA_FIFO_FULL', 0.0):.3e} |")
+    return out
 
 
 def load_stats(trace_dir):
@@ -90,6 +129,7 @@ def main():
     ap.add_argument("--title", default="skinny projection, 6288x7168 M sweep")
     ap.add_argument("--mfma-util", help="counter collection of a --pmc MfmaUtil run")
     ap.add_argument("--mfma-mops", help="counter collection of a --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 run")
+    ap.add_argument("--lds", help="counter collection of a --pmc run of LDS_COUNTERS")
     ap.add_argument("--fetch-scale", type=float,
                     help="FETCH_SIZE scale factor taken from a larger weight's calibration, for a weight "
                          "that stays in L2 (its own plain read fetches next to nothing from HBM)")
@@ -124,6 +164,11 @@ def main():
             if _ours(k):
                 lines.append(f"| `{_short(k)}` | {len(util[k])} | {statistics.mean(util[k]):.2f} | "
                              f"{statistics.mean(mops.get(k, [0.0])) * 512:.3e} |")
+    if args.lds:
+        lines += ["", "## LDS and issue (rocprofv3 --pmc " + " ".join(LDS_COUNTERS) + ")", "",
+                  "Per dispatch, summed over the chip; the wait shares are wave quad-cycles over "
+                  "SQ_WAVE_CYCLES.", ""]
+        lines += lds_table(args.lds)
     os.makedirs(os.path.dirname(os.path.abspath(args.out_md)), exist_ok=True)
     with open(args.out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
