@@ -125,12 +125,20 @@ class Setup:
         self.plans[c].run(self.x[:m], self.out[c, :m])
         return c
 
-    def per_m(self, stream, m, reps=10):
-        """µs per call at token count m, from a graph of 16 * copies calls."""
+    def per_m(self, stream, m, reps=10, min_s=5e-3):
+        """µs per call at token count m, from a graph of 16 * copies calls
+        replayed `reps` times -- or, for a graph that short replays finish in
+        under `min_s` (the small weights), as many times as fill `min_s`, after
+        a warm-up of a quarter of that, so that the timing does not catch the
+        clocks between states."""
         calls = 16 * self.copies
         g = capture(lambda: [self.run(i, m) for i in range(calls)], stream)
         time_graph(g, stream, 1)
         dt = time_graph(g, stream, reps)
+        if dt < min_s:
+            reps = int(reps * min_s / max(dt, 1e-9)) + 1
+            time_graph(g, stream, reps // 4 + 1)
+            dt = time_graph(g, stream, reps)
         return 1e6 * dt / (reps * calls)
 
 
