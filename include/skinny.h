@@ -153,10 +153,10 @@ typedef struct {
  *
  * Validates the arguments, then looks up the process-wide tactic table for
  * (device, N, K, out_dtype); on a miss it times every legal tactic on the
- * device with cache-cold weight copies at its full token tile (each timing a
- * replay of a captured graph of back-to-back launches, as decode steps run
- * them, so that a kernel of a few microseconds is not timed at the host's
- * launch rate), then times the
+ * device with cache-cold weight copies at its full token tile (each timing
+ * replays a captured graph of back-to-back launches, as decode steps run
+ * them, for at least 0.2 ms, so that a kernel of a few microseconds is not
+ * timed at the host's launch rate), then times the
  * few fastest whose tile is >= M (SKINNY_TUNE_REFINE of them, default 4; 0 or
  * 1 skips this pass), and the two fastest of every tile >= M, again at M
  * itself and keeps, for each M in 1..64, the fastest; then every tactic the

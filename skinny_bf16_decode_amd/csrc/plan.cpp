@@ -416,10 +416,11 @@ struct Harness {
     }
 
     // Mean time per launch of `iters` launches over the rotated copies at
-    // M = a.M, captured in a graph and replayed (the second replay timed), as
-    // decode steps run them: launched one by one from the host, a kernel of a
-    // few microseconds would be timed at the host's launch rate.  -1 if a
-    // launch failed.
+    // M = a.M, captured in a graph and replayed (the second replay timed, or
+    // for a replay shorter than kMinTimedMs enough further replays to fill
+    // it), as decode steps run them: launched one by one from the host, a
+    // kernel of a few microseconds would be timed at the host's launch rate.
+    // -1 if a launch failed.
     hipError_t time_once(const Entry &en, double &us)
     {
         us = -1.0;
@@ -441,19 +442,31 @@ struct Harness {
             return ok ? e : hipSuccess;        // a launch the device refused: not a candidate
         }
         float ms = 0.f;
+        int reps = 1;
         if ((e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0)) == hipSuccess &&
             (e = hipGraphLaunch(ge, st)) == hipSuccess && (e = hipEventRecord(e0, st)) == hipSuccess &&
             (e = hipGraphLaunch(ge, st)) == hipSuccess && (e = hipEventRecord(e1, st)) == hipSuccess &&
-            (e = hipEventSynchronize(e1)) == hipSuccess)
-            e = hipEventElapsedTime(&ms, e0, e1);
+            (e = hipEventSynchronize(e1)) == hipSuccess && (e = hipEventElapsedTime(&ms, e0, e1)) == hipSuccess &&
+            ms < kMinTimedMs) {
+            // a graph of short kernels: time enough replays to fill kMinTimedMs
+            reps = std::min(64, (int)(kMinTimedMs / std::max(ms, 1e-4f)) + 1);
+            if ((e = hipEventRecord(e0, st)) == hipSuccess) {
+                for (int r = 0; r < reps && e == hipSuccess; ++r)
+                    e = hipGraphLaunch(ge, st);
+                if (e == hipSuccess && (e = hipEventRecord(e1, st)) == hipSuccess &&
+                    (e = hipEventSynchronize(e1)) == hipSuccess)
+                    e = hipEventElapsedTime(&ms, e0, e1);
+            }
+        }
         if (ge)
             (void)hipGraphExecDestroy(ge);
         (void)hipGraphDestroy(g);
         if (e != hipSuccess)
             return e;
-        us = 1000.0 * ms / iters;
+        us = 1000.0 * ms / ((double)iters * reps);
         return hipSuccess;
     }
+    static constexpr float kMinTimedMs = 0.2f;
 
     // Entries `ens` at M = m, each timed three times round-robin: best[c] is
     // the best of three of ens[c] (-1 if it did not run).
