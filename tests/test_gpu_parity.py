@@ -80,6 +80,32 @@ def test_integer_probe_every_tactic(sk, shape, od):
         plan.close()
 
 
+def test_random_shapes_random_tactics_exact(sk):
+    """Seeded random shapes (N not a multiple of any tile, K = 8 j up to 4800),
+    each with a tactic drawn from its own candidate list and a random M up to
+    the tactic's tile, on integer inputs: fp32 out bit-identical to the oracle,
+    BF16 out to its nearest-even rounding, rows >= M untouched.  Covers range
+    and tile arithmetic at sizes the fixed probes do not."""
+    import torch
+    rng = np.random.default_rng(20261203)
+    paths = set()
+    for case in range(160):
+        n = int(rng.integers(1, 3000))
+        k = 8 * int(rng.integers(1, 601))
+        tactics = sk.enumerate_tactics(n, k)
+        t = tactics[int(rng.integers(0, len(tactics)))]
+        m = int(rng.integers(1, t.mt + 1))
+        od = torch.float32 if case % 2 else torch.bfloat16
+        x_bits, w_bits = si.small_int_case(50_000 + case, 64, n, k)
+        o, _ = oracle.gemm(x_bits[:m], w_bits)
+        plan = sk.Prepared(gu.dev_bf16(w_bits), od, table=gu.forced_table(t))
+        _check_exact(sk, plan, x_bits, o, m, f"case {case}: {n}x{k} M={m} {od} {t}")
+        plan.close()
+        paths.add(t.path)
+    _say(f"[random shapes] paths {sorted(paths)}")
+    assert len(paths) == 8                      # every path the enumeration offers
+
+
 def test_k_probe_every_tactic(sk):
     """One nonzero per weight row, at a column that sweeps every residue
     modulo 8, 64 and 512: any chunk dropped or duplicated at a lane, wave or
