@@ -219,6 +219,59 @@ def test_pitched_views_exact(sk, dtype):
         plan.close()
 
 
+def test_random_extended_calls_exact(sk):
+    """Seeded random combinations of the extended entry points on random
+    shapes, each with a tactic drawn from the shape's own candidates: BF16 or
+    FP16 inputs, row-pitched W, x and out (NaN patterns in the padding of W
+    and x, sentinels in out's), no residual, a separate one or out itself,
+    BF16 or fp32 out.  Integer inputs and an integer residual keep every sum
+    exact, so out must be RNE(O + R) (BF16) or O + R (fp32) bit for bit."""
+    import torch
+    rng = np.random.default_rng(1203)
+    seen = set()
+    for case in range(80):
+        n = int(rng.integers(1, 1500))
+        k = 8 * int(rng.integers(1, 301))
+        dtype = "f16" if rng.integers(0, 2) else "bf16"
+        od = torch.float32 if rng.integers(0, 2) else torch.bfloat16
+        mode = ("none", "separate", "inplace")[int(rng.integers(0, 3))]
+        ldw, ldx, ldo = k + 8 * int(rng.integers(0, 4)), k + 8 * int(rng.integers(0, 4)), n + int(rng.integers(0, 9))
+        tactics = sk.enumerate_tactics(n, k)
+        t = tactics[int(rng.integers(0, len(tactics)))]
+        m = int(rng.integers(1, t.mt + 1))
+        x_bits, w_bits = si.small_int_case(70_000 + case, m, n, k, dtype=dtype)
+        r_int = rng.integers(-100, 101, size=(m, n)) if mode != "none" else np.zeros((m, n), dtype=np.int64)
+        o, _ = oracle.gemm_residual(x_bits, w_bits, r_int.astype(np.float64), dtype=dtype)
+        junk = 0x7E00 if dtype == "f16" else 0x7FC0
+        wp = np.full((n, ldw), junk, dtype=np.uint16)
+        wp[:, :k] = w_bits
+        xp = np.full((m, ldx), junk, dtype=np.uint16)
+        xp[:, :k] = x_bits
+        to_dev = dev_f16 if dtype == "f16" else gu.dev_bf16
+        w, x = to_dev(wp)[:, :k], to_dev(xp)[:, :k]
+        plan = sk.Prepared(w, od, table=gu.forced_table(t))
+        buf = gu.out_buffer(ldo, od)
+        out = buf[:, :n]
+        r_dev = torch.from_numpy(r_int.astype(np.float32)).cuda().to(od)
+        res = None
+        if mode == "inplace":
+            out[:m].copy_(r_dev)
+            res = out[:m]
+        elif mode == "separate":
+            res = r_dev
+        plan.run(x, out[:m], residual=res)
+        torch.cuda.synchronize()
+        bits = gu.host_bits(buf)
+        sentinel = gu.SENTINEL_F32 if od == torch.float32 else gu.SENTINEL_BF16
+        label = f"case {case}: {n}x{k} ldw={ldw} ldx={ldx} ldo={ldo} M={m} {dtype}->{od} residual={mode} {t}"
+        assert np.all(bits[:m, n:] == sentinel), f"{label}: padding columns written"
+        assert np.all(bits[m:] == sentinel), f"{label}: rows >= M written"
+        assert np.array_equal(bits[:m, :n], _want_bits(o, od)), label
+        plan.close()
+        seen.add((t.path, dtype, mode))
+    _say(f"[random extended] {len(seen)} (path, input, residual) kinds")
+
+
 def test_run_ex_argument_errors(sk):
     """Pitches below the row length, unaligned pitches and a residual that
     overlaps out without being it are refused before any launch."""
