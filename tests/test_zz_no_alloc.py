@@ -73,6 +73,46 @@ def test_static_run_token_groups_and_one_stage(sk):
     _one(sk, 6288, 7168, 32, sk.Tactic(sk.PATH_MFMAW, 32, 64, 4, 3, 2), 805)
 
 
+def test_static_run_random_split_tactics(sk):
+    """Seeded random shapes, each with a split-K tactic drawn from its own
+    candidates, run through skinny_run_static and through a plan: the same
+    bits, exact against the oracle on integer inputs, rows >= M untouched.
+    The calls follow one another on the one static array, so each also
+    shows that the previous left every exchange node empty."""
+    import torch
+    rng = np.random.default_rng(31)
+    done = 0
+    while done < 40:
+        n = int(rng.integers(1, 2500))
+        k = 8 * int(rng.integers(2, 600))
+        split = [t for t in sk.enumerate_tactics(n, k) if t.split > 1]
+        if not split:
+            continue
+        t = split[int(rng.integers(0, len(split)))]
+        m = int(rng.integers(1, t.mt + 1))
+        od = torch.float32 if done % 2 else torch.bfloat16
+        x_bits, w_bits = si.small_int_case(90_000 + done, m, n, k)
+        o, _ = oracle.gemm(x_bits, w_bits)
+        w, x = gu.dev_bf16(w_bits), gu.dev_bf16(x_bits)
+        got = gu.out_buffer(n, od)
+        try:
+            sk.run_static(w, t, x, got[:m])
+        except ValueError as e:                 # an exchange larger than the static array
+            assert "static scratch" in str(e), e
+            continue
+        plan = sk.Prepared(w, od, table=gu.forced_table(t))
+        ref = gu.out_buffer(n, od)
+        plan.run(x, ref[:m])
+        torch.cuda.synchronize()
+        plan.close()
+        label = f"{n}x{k} M={m} {od} {t}"
+        assert gu.sentinel_intact(got, m), f"{label}: rows >= M written"
+        assert np.array_equal(gu.host_bits(got), gu.host_bits(ref)), f"{label}: differs from skinny_run_ex"
+        want = o.astype(np.float32).view(np.uint32) if od == torch.float32 else oracle.round_bf16(o)
+        assert np.array_equal(gu.host_bits(got)[:m], want), f"{label}: differs from the oracle"
+        done += 1
+
+
 def test_static_run_without_split_and_limits(sk):
     """No split: no scratch at all.  A tactic whose exchange would exceed the
     static scratch is refused before any launch."""
