@@ -417,7 +417,7 @@ def main():
                     help="skip the square 3584x7168 sweep reported beside the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the projection would shard W by rows, one shard per GPU, with no exchange "
               "inside the GEMM); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
