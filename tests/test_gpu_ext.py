@@ -272,6 +272,44 @@ def test_random_extended_calls_exact(sk):
     _say(f"[random extended] {len(seen)} (path, input, residual) kinds")
 
 
+def test_prepare_from_threads(sk, monkeypatch):
+    """skinny_prepare from four threads at once, two per shape, with no
+    stored table: the first prepare of a shape tunes (capturing its timing
+    graphs on its own stream) while the other threads allocate and wait for
+    the table cache; every plan must get the same table per shape and give
+    exact results on integer inputs."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    monkeypatch.delenv("SKINNY_TABLE_CACHE", raising=False)
+    shapes = [(264, 520), (1544, 136)]          # shapes no other test tunes: nothing cached yet
+    cases = {}
+    for i, (n, k) in enumerate(shapes):
+        x_bits, w_bits = si.small_int_case(300 + i, 64, n, k)
+        o, _ = oracle.gemm(x_bits, w_bits)
+        cases[(n, k)] = (gu.dev_bf16(x_bits), gu.dev_bf16(w_bits), o)
+    torch.cuda.synchronize()
+
+    def prepare(shape):
+        torch.cuda.set_device(0)
+        x, w, _ = cases[shape]
+        plan = sk.Prepared(w, torch.float32)
+        return shape, plan, [repr(plan.tactic(m)) for m in range(1, 65)]
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(prepare, [shapes[0], shapes[1], shapes[0], shapes[1]]))
+    tables = {}
+    for shape, plan, table in results:
+        assert tables.setdefault(shape, table) == table, f"{shape}: two threads got different tables"
+        x, _, o = cases[shape]
+        for m in (1, 7, 16, 33, 64):
+            out = gu.out_buffer(shape[0], torch.float32)
+            plan.run(x[:m], out[:m])
+            torch.cuda.synchronize()
+            assert gu.sentinel_intact(out, m), (shape, m)
+            assert np.array_equal(gu.host_bits(out)[:m], o[:m].astype(np.float32).view(np.uint32)), (shape, m)
+        plan.close()
+
+
 def test_run_ex_argument_errors(sk):
     """Pitches below the row length, unaligned pitches and a residual that
     overlaps out without being it are refused before any launch."""
