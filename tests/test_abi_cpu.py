@@ -349,10 +349,12 @@ def test_bench_names_the_kernel_of_every_tactic():
 
 def test_shipped_table_is_legal_and_profiled():
     """The tactic tables bench.py loads by default: one line per (chip,
-    shape, output type, residual or not), every entry legal for its shape with
-    a token tile >= M (the library ignores a line that fails this, and tunes
-    instead), and the shape's committed HBM traffic record names the kernel of
-    every token count its benchmark step runs (which adds no residual)."""
+    shape, input type, output type, residual or not), every entry legal for
+    its shape with a token tile >= M (the library ignores a line that fails
+    this, and tunes instead), and for BF16 inputs the shape's committed HBM
+    traffic record names the kernel of every token count its benchmark step
+    runs (which adds no residual).  FP16-input tables ship for the same
+    shapes."""
     import json
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     import bench
@@ -370,6 +372,7 @@ def test_shipped_table_is_legal_and_profiled():
             assert t.mt >= m
     assert len(heads) == len(lines)
     assert any(ln[4:8] == ["6288", "7168", "bf16", "bf16"] for ln in lines)
+    assert any(ln[4:8] == ["6288", "7168", "f16", "bf16"] for ln in lines)
     import skinny_inputs as si
     profiled = 0
     for ln in lines:
@@ -378,6 +381,8 @@ def test_shipped_table_is_legal_and_profiled():
             continue                                     # a sub-plan of the KDA projection
         if ln[7].endswith("+res"):
             continue                                     # runs with a residual: not in the profiled sweeps
+        if ln[6] != "bf16":
+            continue                                     # FP16 inputs: the profiled sweeps run BF16
         path = bench.traffic_record_path(wl, ln[7])
         if wl.cid == 1 and not os.path.exists(path):
             continue                                     # the tiny shape has no M sweep to profile

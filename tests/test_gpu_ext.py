@@ -9,6 +9,7 @@ those cases are compared bit for bit; random cases use the stated bound.
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -216,6 +217,42 @@ def test_pitched_views_exact(sk, dtype):
             assert np.all(bits[:m, n:] == gu.SENTINEL_F32), f"{t} M={m}: padding columns written"
             assert np.all(bits[m:] == gu.SENTINEL_F32), f"{t} M={m}: rows >= M written"
             assert np.array_equal(bits[:m, :n], _want_bits(o[:m], torch.float32)), f"{t} M={m}"
+        plan.close()
+
+
+def _shipped_f16_table(sk, n, k, od):
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "skinny_bf16_decode_amd", "tables", "mi355x_tuned.txt")
+    with open(path) as f:
+        for line in f:
+            p = line.split()
+            if p[3:8] == ["256", str(n), str(k), "f16", od]:
+                return [sk.Tactic(*map(int, e.split("."))) for e in p[8:]]
+    raise AssertionError(f"no shipped FP16 table for {n}x{k} {od}")
+
+
+@pytest.mark.parametrize("shape", [(6288, 7168), (3584, 7168), (7168, 18432), (1536, 128)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_f16_shipped_tables_exact_full_size(sk, shape):
+    """The shipped FP16-input tables, forced at their full shape on integer
+    FP16 inputs: every M = 1..64, BF16 out bit-identical to RNE(O) and (where
+    an fp32-out table ships) fp32 out to O."""
+    import torch
+    n, k = shape
+    x_bits, w_bits = si.small_int_case(4242 + n, 64, n, k, dtype="f16")
+    o, _ = oracle.gemm(x_bits, w_bits, dtype="f16")
+    w, x = dev_f16(w_bits), dev_f16(x_bits)
+    for od, name in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        if od == torch.float32 and shape != (1536, 128):
+            continue
+        table = _shipped_f16_table(sk, n, k, name)
+        plan = sk.Prepared(w, od, table=table)
+        for m in range(1, 65):
+            out = gu.out_buffer(n, od)
+            plan.run(x[:m], out[:m])
+            torch.cuda.synchronize()
+            assert gu.sentinel_intact(out, m), (shape, name, m)
+            assert np.array_equal(gu.host_bits(out)[:m], _want_bits(o[:m], od)), (shape, name, m, table[m - 1])
         plan.close()
 
 
