@@ -256,19 +256,22 @@ def test_f16_shipped_tables_exact_full_size(sk, shape):
         plan.close()
 
 
-def test_random_extended_calls_exact(sk):
-    """Seeded random combinations of the extended entry points on random
-    shapes, each with a tactic drawn from the shape's own candidates: BF16 or
+def _random_extended_cases(sk, seed, cases, n_hi, k8_hi, max_elems, case_seed):
+    """Seeded random combinations of the extended entry points: a random
+    shape (N < n_hi, K = 8 j with j < k8_hi and N K <= max_elems), a tactic
+    drawn from the shape's own candidates, a random M up to its tile, BF16 or
     FP16 inputs, row-pitched W, x and out (NaN patterns in the padding of W
     and x, sentinels in out's), no residual, a separate one or out itself,
     BF16 or fp32 out.  Integer inputs and an integer residual keep every sum
-    exact, so out must be RNE(O + R) (BF16) or O + R (fp32) bit for bit."""
+    exact, so out must be RNE(O + R) (BF16) or O + R (fp32) bit for bit, on
+    two calls in a row (the split-K exchange nodes are empty again after
+    each launch).  Returns the (path, input type, residual) kinds seen."""
     import torch
-    rng = np.random.default_rng(1203)
+    rng = np.random.default_rng(seed)
     seen = set()
-    for case in range(80):
-        n = int(rng.integers(1, 1500))
-        k = 8 * int(rng.integers(1, 301))
+    for case in range(cases):
+        n = int(rng.integers(1, n_hi))
+        k = 8 * int(rng.integers(1, max(2, min(k8_hi, max_elems // (8 * n) + 1))))
         dtype = "f16" if rng.integers(0, 2) else "bf16"
         od = torch.float32 if rng.integers(0, 2) else torch.bfloat16
         mode = ("none", "separate", "inplace")[int(rng.integers(0, 3))]
@@ -276,7 +279,7 @@ def test_random_extended_calls_exact(sk):
         tactics = sk.enumerate_tactics(n, k)
         t = tactics[int(rng.integers(0, len(tactics)))]
         m = int(rng.integers(1, t.mt + 1))
-        x_bits, w_bits = si.small_int_case(70_000 + case, m, n, k, dtype=dtype)
+        x_bits, w_bits = si.small_int_case(case_seed + case, m, n, k, dtype=dtype)
         r_int = rng.integers(-100, 101, size=(m, n)) if mode != "none" else np.zeros((m, n), dtype=np.int64)
         o, _ = oracle.gemm_residual(x_bits, w_bits, r_int.astype(np.float64), dtype=dtype)
         junk = 0x7E00 if dtype == "f16" else 0x7FC0
@@ -290,23 +293,44 @@ def test_random_extended_calls_exact(sk):
         buf = gu.out_buffer(ldo, od)
         out = buf[:, :n]
         r_dev = torch.from_numpy(r_int.astype(np.float32)).cuda().to(od)
-        res = None
-        if mode == "inplace":
-            out[:m].copy_(r_dev)
-            res = out[:m]
-        elif mode == "separate":
-            res = r_dev
-        plan.run(x, out[:m], residual=res)
-        torch.cuda.synchronize()
-        bits = gu.host_bits(buf)
-        sentinel = gu.SENTINEL_F32 if od == torch.float32 else gu.SENTINEL_BF16
         label = f"case {case}: {n}x{k} ldw={ldw} ldx={ldx} ldo={ldo} M={m} {dtype}->{od} residual={mode} {t}"
-        assert np.all(bits[:m, n:] == sentinel), f"{label}: padding columns written"
-        assert np.all(bits[m:] == sentinel), f"{label}: rows >= M written"
-        assert np.array_equal(bits[:m, :n], _want_bits(o, od)), label
+        for call in range(2):
+            res = None
+            if mode == "inplace":
+                out[:m].copy_(r_dev)
+                res = out[:m]
+            elif mode == "separate":
+                res = r_dev
+            plan.run(x, out[:m], residual=res)
+            torch.cuda.synchronize()
+            bits = gu.host_bits(buf)
+            sentinel = gu.SENTINEL_F32 if od == torch.float32 else gu.SENTINEL_BF16
+            assert np.all(bits[:m, n:] == sentinel), f"{label} call {call}: padding columns written"
+            assert np.all(bits[m:] == sentinel), f"{label} call {call}: rows >= M written"
+            assert np.array_equal(bits[:m, :n], _want_bits(o, od)), f"{label} call {call}"
         plan.close()
         seen.add((t.path, dtype, mode))
+        if (case + 1) % 100 == 0:
+            _say(f"  {case + 1}/{cases} cases exact")
+    return seen
+
+
+def test_random_extended_calls_exact(sk):
+    """80 random combinations of the extended entry points on shapes up to
+    1500 x 2400 (see _random_extended_cases)."""
+    seen = _random_extended_cases(sk, 1203, 80, 1500, 301, 1 << 62, 70_000)
     _say(f"[random extended] {len(seen)} (path, input, residual) kinds")
+
+
+def test_random_extended_calls_large_shapes_exact(sk):
+    """The same on shapes up to 20000 rows, K up to 20000 and 1.4e8 weight
+    elements (the long-K weight has 1.32e8), where row ranges, splits and
+    32-bit offsets reach their full size.  SKINNY_RANDOM_LARGE_CASES sets the
+    count (default 40)."""
+    cases = int(os.environ.get("SKINNY_RANDOM_LARGE_CASES", "40"))
+    seen = _random_extended_cases(sk, 20261204, cases, 20001, 2501, 140_000_000, 80_000)
+    _say(f"[random extended, large] {len(seen)} (path, input, residual) kinds, "
+         f"paths {sorted({p for p, _, _ in seen})}")
 
 
 def test_prepare_from_threads(sk, monkeypatch):
