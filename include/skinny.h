@@ -31,7 +31,10 @@
  *  - Every call returns a status; none aborts or throws.  After a failure,
  *    skinny_last_error() returns a thread-local text describing it.
  *  - A stream is passed as a hipStream_t cast to void*; NULL is the null
- *    stream.
+ *    stream of the current device.  A plan runs on streams of the device it
+ *    was prepared on; the run calls check nothing about devices, so a
+ *    stream of another device is the caller's error (the kernel would read
+ *    that device's addresses).
  */
 #ifndef SKINNY_H
 #define SKINNY_H
