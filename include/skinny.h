@@ -33,8 +33,8 @@
  *  - A stream is passed as a hipStream_t cast to void*; NULL is the null
  *    stream of the current device.  A plan runs on streams of the device it
  *    was prepared on; the run calls check nothing about devices, so a
- *    stream of another device is the caller's error (the kernel would read
- *    that device's addresses).
+ *    stream of another device is the caller's error (the kernel would run
+ *    there on addresses of the plan's device).
  */
 #ifndef SKINNY_H
 #define SKINNY_H
