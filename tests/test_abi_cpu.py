@@ -405,3 +405,20 @@ def test_launch_constant_division_is_exact(tmp_path):
     subprocess.run(["g++", "-O2", "-std=c++17", "-o", exe, os.path.join(here, "fastdiv_check.cpp")], check=True)
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.startswith("ok "), r.stdout + r.stderr
+
+
+def test_c_program_uses_the_abi(tmp_path):
+    """tests/c_abi/abi_from_c.c, a C99 program, compiles against the header
+    with -pedantic -Werror, links against libskinny.so and runs its host-only
+    checks (argument errors before any device call, the tactic and table
+    rules) without a GPU."""
+    src = os.path.join(ROOT, "tests", "c_abi", "abi_from_c.c")
+    exe = str(tmp_path / "abi_from_c")
+    lib_dir = os.path.dirname(sk.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                    os.path.join(ROOT, "include"), src, "-o", exe, "-L", lib_dir, "-lskinny",
+                    f"-Wl,-rpath,{lib_dir}"], check=True)
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert run.stdout.startswith("abi ok "), run.stdout
+    assert int(run.stdout.split()[2]) > 100
