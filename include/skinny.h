@@ -188,6 +188,11 @@ typedef struct {
  * every candidate's time; SKINNY_TUNE_ITERS sets the timed launches per
  * candidate; SKINNY_XCD_REMAP=0 stops placing the split-K workgroups of a row
  * tile on one XCD (a plan-time setting, for testing the exchange across XCDs).
+ * SKINNY_FORCE_TACTIC=path.mt.rows.waves.unroll.split (a table line's field
+ * syntax) skips tuning and the table file: the plan runs that tactic for
+ * every M <= mt and the 64-token MFMA tactic 1.64.16.1.1.1 above it, as
+ * skinny_prepare_tactics_ex would; a malformed or illegal value is
+ * SKINNY_ERR_INVALID_ARG before any device call.
  *
  * Synchronous.  Must not be called while the device is capturing a graph.
  * W is NOT copied: the plan keeps the pointer, W must stay allocated until

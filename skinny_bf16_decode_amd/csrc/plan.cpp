@@ -905,6 +905,23 @@ skinny_status skinny_prepare_ex(const void *W, int N, int K, int ldw, skinny_in_
     skinny_status s = check_prepare_args(W, N, K, ldw, (int)in_dtype, od, plan);
     if (s != SKINNY_OK)
         return s;
+    // SKINNY_FORCE_TACTIC: one tactic for every M its tile serves and the
+    // 64-token MFMA tactic above it, with no tuning and no table file
+    const char *force = getenv("SKINNY_FORCE_TACTIC");
+    if (force && *force) {
+        skinny_tactic ft;
+        if (!parse_tactic_text(force, &ft)) {
+            set_error("SKINNY_FORCE_TACTIC=\"%.64s\" is not path.mt.rows.waves.unroll.split", force);
+            return SKINNY_ERR_INVALID_ARG;
+        }
+        if ((s = skinny_tactic_check(&ft, N, K)) != SKINNY_OK)
+            return s;
+        const skinny_tactic above = {SKINNY_PATH_MFMA, SKINNY_MAX_M, 16, 1, 1, 1};
+        skinny_tactic table[SKINNY_MAX_M];
+        for (int m = 1; m <= SKINNY_MAX_M; ++m)
+            table[m - 1] = m <= ft.mt ? ft : above;
+        return skinny_prepare_tactics_ex(W, N, K, ldw, in_dtype, od, table, plan);
+    }
     const int half = in_dtype == SKINNY_IN_F16;
     int dev = 0, cus = 0;
     if ((s = current_gfx950(&dev, &cus)) != SKINNY_OK)

@@ -111,6 +111,9 @@ void set_error(const char *fmt, ...);
 // any table); save_table_file appends one.
 bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                       std::array<skinny_tactic, SKINNY_MAX_M> &table);
+// One tactic written as path.mt.rows.waves.unroll.split, the whole string
+// (the table lines' field syntax); false for anything else.
+bool parse_tactic_text(const char *text, skinny_tactic *t);
 bool load_table_file(const char *path, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                      std::array<skinny_tactic, SKINNY_MAX_M> &table);
 void format_table_line(int cus, int N, int K, int half, skinny_out_dtype od, int res,

@@ -106,6 +106,11 @@ bool parse_tactic(const char *s, const char *e, skinny_tactic *t)
 
 }  // namespace
 
+bool parse_tactic_text(const char *text, skinny_tactic *t)
+{
+    return text && t && parse_tactic(text, text + strlen(text), t);
+}
+
 bool parse_table_line(const char *line, int cus, int N, int K, int half, skinny_out_dtype od, int res,
                       std::array<skinny_tactic, SKINNY_MAX_M> &table)
 {

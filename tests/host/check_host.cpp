@@ -356,6 +356,33 @@ static void check_table_lines()
     }
 }
 
+// parse_tactic_text (SKINNY_FORCE_TACTIC) on a copy of exactly the string's size
+static bool parse_one(const std::string &s, skinny_tactic *t)
+{
+    std::vector<char> buf(s.begin(), s.end());
+    buf.push_back(0);
+    return parse_tactic_text(buf.data(), t);
+}
+
+static void check_tactic_text()
+{
+    skinny_tactic t;
+    CHECK(parse_one("9.32.64.4.3.2", &t) && same(t, skinny_tactic{9, 32, 64, 4, 3, 2}), "a tactic parses");
+    CHECK(parse_one("-1.0.2147483647.-2147483648.0.0", &t) && t.path == -1 && t.rows == INT_MAX &&
+              t.waves == INT_MIN,
+          "int-range fields parse (legality is skinny_tactic_check's)");
+    const char *bad[] = {"", "9", "9.32.64.4.3", "9.32.64.4.3.2.1", "9.32.64.4.3.2 ", " 9.32.64.4.3.2",
+                         "9.32.64.4.3.", ".9.32.64.4.3.2", "9..32.64.4.3.2", "9.32.64.4.3.2x", "9,32,64,4,3,2",
+                         "9.32.64.4.3.2147483648", "9.32.64.4.3.+2", "9.32.64.4.3.0x2", "9.32.64.4.3.2\n"};
+    for (const char *b : bad)
+        CHECK(!parse_one(b, &t), "refused \"%s\"", b);
+    CHECK(!parse_tactic_text(nullptr, &t) && !parse_tactic_text("1.1.1.1.1.1", nullptr), "NULL arguments");
+    // every prefix of a valid tactic but the whole is refused
+    const std::string good = "10.16.28.4.3.2";
+    for (size_t n = 0; n < good.size(); ++n)
+        CHECK(!parse_one(good.substr(0, n), &t), "prefix of %zu chars", n);
+}
+
 static void check_table_files(const char *dir)
 {
     const int N = 3584, K = 7168, cus = 256;
@@ -422,6 +449,7 @@ int main(int argc, char **argv)
     check_status_strings();
     check_fastdiv();
     check_table_lines();
+    check_tactic_text();
     check_table_files(dir);
     if (g_failures) {
         fprintf(stderr, "%d check(s) failed\n", g_failures);

@@ -422,3 +422,17 @@ def test_c_program_uses_the_abi(tmp_path):
     assert run.returncode == 0, run.stdout + run.stderr
     assert run.stdout.startswith("abi ok "), run.stdout
     assert int(run.stdout.split()[2]) > 100
+
+
+@pytest.mark.parametrize("value", ["garbage", "9.32.64.4.3", "9.32.64.4.3.2 ", "9.3.64.4.3.2",
+                                   "2.1.1.1.1.1", "9.32.64.4.3.99"])
+def test_forced_tactic_is_checked_before_any_device_call(monkeypatch, value):
+    """SKINNY_FORCE_TACTIC is parsed with the table lines' strict syntax and
+    checked like any tactic; a bad value is refused before the device is
+    touched (with no GPU here, reaching the device would give
+    SKINNY_ERR_DEVICE instead)."""
+    monkeypatch.setenv("SKINNY_FORCE_TACTIC", value)
+    st, plan = _prepare(0x1000, 6288, 7168)
+    assert st == 1, (st, sk.last_error())
+    assert plan.value is None
+    assert sk.last_error()

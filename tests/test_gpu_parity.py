@@ -475,6 +475,26 @@ def test_run_errors(sk):
     plan.close()
 
 
+def test_forced_tactic_environment(sk, monkeypatch):
+    """SKINNY_FORCE_TACTIC: no tuning and no table file; the plan runs the
+    named tactic for every M up to its tile and the 64-token MFMA tactic
+    above it, for runs with and without a residual, exact on integer inputs."""
+    import torch
+    n, k = 600, 1536
+    x_bits, w_bits = si.small_int_case(77, 64, n, k)
+    o, _ = oracle.gemm(x_bits, w_bits)
+    forced, above = sk.Tactic(9, 32, 64, 4, 3, 2), sk.Tactic(1, 64, 16, 1, 1, 1)
+    monkeypatch.setenv("SKINNY_FORCE_TACTIC", "9.32.64.4.3.2")
+    monkeypatch.delenv("SKINNY_TABLE_CACHE", raising=False)
+    plan = sk.Prepared(gu.dev_bf16(w_bits), torch.float32)
+    for m in range(1, 65):
+        want = repr(forced if m <= 32 else above)
+        assert repr(plan.tactic(m, False)) == want and repr(plan.tactic(m, True)) == want, m
+    for m in (1, 17, 32, 33, 64):
+        _check_exact(sk, plan, x_bits, o, m, f"forced M={m}")
+    plan.close()
+
+
 def test_table_cache_file_round_trip(sk, tmp_path):
     """SKINNY_TABLE_CACHE: a tuning process appends its two tables (without
     and with a residual); a second process loads both instead of tuning and
