@@ -159,10 +159,12 @@ typedef struct {
  * device with cache-cold weight copies at its full token tile (each timing
  * replays a captured graph of back-to-back launches, as decode steps run
  * them, for at least 0.2 ms, so that a kernel of a few microseconds is not
- * timed at the host's launch rate), then times the
- * few fastest whose tile is >= M (SKINNY_TUNE_REFINE of them, default 4; 0 or
- * 1 skips this pass), and the two fastest of every tile >= M, again at M
- * itself and keeps, for each M in 1..64, the fastest; then every tactic the
+ * timed at the host's launch rate), and each tactic of a 16-token or larger
+ * tile once more at M = 8, where such tiles serve most of their token
+ * counts; then times the few fastest whose tile is >= M (SKINNY_TUNE_REFINE
+ * of them, default 4; 0 or 1 skips this pass), the two fastest of every tile
+ * >= M and, for M < 16, the few fastest at M = 8, again at M itself and
+ * keeps, for each M in 1..64, the fastest; then every tactic the
  * table uses is timed again at each M its tile serves, and the fastest kept;
  * finally, at M <= 8, the quickest v_dot2 tactic replaces the choice when it
  * is within SKINNY_TUNE_DOT2_MARGIN (relative, default 0.02, the run-to-run

@@ -507,8 +507,11 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     const int copies = h.copies;
     auto time_once = [&](const Entry &en, double &us) { return h.time_once(en, us); };
 
-    // First pass: every candidate at its full token tile, best of two.
-    std::vector<double> times(count, -1.0);
+    // First pass: every candidate at its full token tile, best of two, and
+    // each candidate of a tile of 16 or more tokens also once at the small-M
+    // probe (8 tokens), where those tiles serve most of their token counts.
+    constexpr int kProbeM = 8;
+    std::vector<double> times(count, -1.0), probe_times(count, -1.0);
     std::vector<Entry> entries(count);
     for (int i = 0; i < count; ++i) {
         entries[i] = make_entry(cand[i], N, K, half);
@@ -533,6 +536,10 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
                 best = us;
         }
         times[i] = best;
+        if (best >= 0 && cand[i].mt >= 2 * kProbeM) {
+            a.M = kProbeM;
+            HIP_TRY(time_once(en, probe_times[i]));
+        }
     }
     HIP_TRY(hipStreamSynchronize(h.st));
     skinny_status s = skinny_select_table(cand.data(), times.data(), count, table.data());
@@ -540,10 +547,11 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
     // Second pass: for each M, the few fastest candidates of the first pass
     // whose tile serves M, and the two fastest of every token tile >= M, are
     // timed again at M itself (x and out of M rows), round-robin over three
-    // rounds, and the fastest is kept.  First-pass times at the full tile
-    // overstate a large tile at small M -- the best 16-token kernel at M = 4
-    // need not be among the fastest at M = 16 -- and single timings differ by
-    // a few per cent from run to run.
+    // rounds, and the fastest is kept; below 16 tokens so are the few fastest
+    // at the small-M probe.  First-pass times at the full tile overstate a
+    // large tile at small M -- the best 16-token kernel at M = 4 need not be
+    // among the fastest at M = 16 -- and single timings differ by a few per
+    // cent from run to run.
     const int refine = env_int("SKINNY_TUNE_REFINE", 4);
     // Candidates `top` at M = m, each timed three times round-robin: best[c]
     // is the best of three of top[c] (-1 if it did not run).
@@ -580,6 +588,16 @@ skinny_status tune(const void *W, int N, int K, int ldw, int half, skinny_out_dt
             if ((int)k < refine || per_tile[cand[i].mt] < 2)
                 top.push_back(i);
             ++per_tile[cand[i].mt];
+        }
+        if (m < 2 * kProbeM) {
+            std::vector<int> small;
+            for (int i : order)
+                if (probe_times[i] >= 0)
+                    small.push_back(i);
+            std::sort(small.begin(), small.end(), [&](int x, int y) { return probe_times[x] < probe_times[y]; });
+            for (size_t k = 0; k < small.size() && (int)k < refine; ++k)
+                if (std::find(top.begin(), top.end(), small[k]) == top.end())
+                    top.push_back(small[k]);
         }
         if (top.size() < 2)
             continue;
