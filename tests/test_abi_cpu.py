@@ -436,3 +436,17 @@ def test_forced_tactic_is_checked_before_any_device_call(monkeypatch, value):
     assert st == 1, (st, sk.last_error())
     assert plan.value is None
     assert sk.last_error()
+
+
+def test_tune_command_checks_shapes_before_the_gpu():
+    """python -m skinny_bf16_decode_amd.tune: shapes parse as NxK under the
+    library's shape rules; a bad one is refused before the GPU is touched."""
+    from skinny_bf16_decode_amd import tune
+    assert tune.parse_shape("6288x7168") == (6288, 7168)
+    assert tune.parse_shape("1X8") == (1, 8)
+    for bad in ("6288", "6288x", "x7168", "6288x7169", "0x512", "64x0", "-1x8", "6288*7168", "1x2x3", "a x8"):
+        with pytest.raises(ValueError):
+            tune.parse_shape(bad)
+    with pytest.raises(SystemExit) as e:
+        tune.main(["--file", "/nonexistent/t.txt", "6288x7169"])
+    assert e.value.code == 2

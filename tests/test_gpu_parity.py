@@ -495,6 +495,28 @@ def test_forced_tactic_environment(sk, monkeypatch):
     plan.close()
 
 
+def test_tune_command_appends_then_loads(sk, tmp_path):
+    """python -m skinny_bf16_decode_amd.tune tunes a shape the file does not
+    hold and appends its two tables; run again on the same file, it loads
+    them instead of tuning and appends nothing."""
+    import os
+    import subprocess
+    path = tmp_path / "tables.txt"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    cmd = [sys.executable, "-m", "skinny_bf16_decode_amd.tune", "--file", str(path), "--out", "f32", "328x520"]
+    env = dict(os.environ, SKINNY_LOG="1")
+    env.pop("SKINNY_TABLE_CACHE", None)
+    first = subprocess.run(cmd, cwd=root, env=env, capture_output=True, text=True, timeout=240)
+    assert first.returncode == 0, first.stderr[-2000:]
+    assert "tuned N=328 K=520" in first.stderr and "328x520 bf16->f32" in first.stdout
+    lines = path.read_text().splitlines()
+    assert [ln.split()[4:8] for ln in lines] == [["328", "520", "bf16", "f32"], ["328", "520", "bf16", "f32+res"]]
+    second = subprocess.run(cmd, cwd=root, env=env, capture_output=True, text=True, timeout=240)
+    assert second.returncode == 0, second.stderr[-2000:]
+    assert "table loaded from" in second.stderr and "tuned N=328" not in second.stderr
+    assert path.read_text().splitlines() == lines
+
+
 def test_table_cache_file_round_trip(sk, tmp_path):
     """SKINNY_TABLE_CACHE: a tuning process appends its two tables (without
     and with a residual); a second process loads both instead of tuning and
