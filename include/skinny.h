@@ -138,7 +138,8 @@ typedef struct {
                    DOT2W: stages of 16 chunks in flight, 2 or 3) */
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16 (MFMAW 1..4,
                    MFMA4 and DOT2W 1..8); their fp32 partials meet in the plan's
-                   workspace, one agent-scope atomic swap per value and level */
+                   workspace by agent-scope atomic swaps, one per value and tree
+                   level (MFMAX and MFMAW: one 64-bit swap per pair of values) */
 } skinny_tactic;
 
 /*
