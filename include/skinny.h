@@ -139,7 +139,8 @@ typedef struct {
     int split;  /* workgroups splitting K per row tile (1 = none), 1..16 (MFMAW 1..4,
                    MFMA4 and DOT2W 1..8); their fp32 partials meet in the plan's
                    workspace by agent-scope atomic swaps, one per value and tree
-                   level (MFMAX and MFMAW: one 64-bit swap per pair of values) */
+                   level (MFMAX, and MFMAW where each thread holds an even count
+                   of values: one 64-bit swap per pair) */
 } skinny_tactic;
 
 /*
