@@ -150,6 +150,57 @@ def small_int_case(seed: int, m: int, n: int, k: int, lo: int = -3, hi: int = 3,
     return f32_to_bf16_bits(x), f32_to_bf16_bits(wt)
 
 
+def _int_bits_table(values, dtype: str = "bf16") -> np.ndarray:
+    v = np.asarray(values, dtype=np.float32)
+    return f32_to_f16_bits(v) if dtype == "f16" else f32_to_bf16_bits(v)
+
+
+def int_block_rows(k: int, block_elems: int = 1 << 27) -> int:
+    """Rows per independently seeded block of int_weight_blocks (about
+    block_elems elements per block, 128 Mi by default)."""
+    return max(1, block_elems // k)
+
+
+def int_weight_blocks(seed: int, n: int, k: int, values=(-3, -2, -1, 0, 1, 2, 3), block_elems: int = 1 << 27):
+    """Yield (row0, bits) for the row blocks of an [n, k] BF16 weight whose
+    entries are drawn uniformly from the small integers `values` (exact in
+    BF16).  Block b (rows b * int_block_rows(k, block_elems) on) has its own generator
+    seeded (seed, b), so a weight of billions of elements is built block by
+    block and any block can be drawn again alone (int_weight_rows)."""
+    table = _int_bits_table(values)
+    per = int_block_rows(k, block_elems)
+    for b, row0 in enumerate(range(0, n, per)):
+        rows = min(per, n - row0)
+        rng = np.random.default_rng([seed, b])
+        idx = rng.integers(0, len(values), size=(rows, k), dtype=np.uint8)
+        yield row0, table[idx]
+
+
+def int_weight_rows(seed: int, n: int, k: int, rows, values=(-3, -2, -1, 0, 1, 2, 3),
+                    block_elems: int = 1 << 27) -> np.ndarray:
+    """Rows `rows` (any order) of the weight int_weight_blocks(seed, n, k,
+    values, block_elems) yields, drawn again from their blocks only: uint16
+    [len(rows), k]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    per = int_block_rows(k, block_elems)
+    table = _int_bits_table(values)
+    out = np.empty((rows.shape[0], k), dtype=np.uint16)
+    for b in np.unique(rows // per):
+        row0 = int(b) * per
+        nrows = min(per, n - row0)
+        rng = np.random.default_rng([seed, int(b)])
+        block = table[rng.integers(0, len(values), size=(nrows, k), dtype=np.uint8)]
+        sel = np.nonzero(rows // per == b)[0]
+        out[sel] = block[rows[sel] - row0]
+    return out
+
+
+def int_matrix(seed: int, m: int, k: int, values=(-3, -2, -1, 0, 1, 2, 3)) -> np.ndarray:
+    """An [m, k] BF16 matrix of entries drawn uniformly from `values`."""
+    rng = np.random.default_rng(seed)
+    return _int_bits_table(values)[rng.integers(0, len(values), size=(m, k), dtype=np.uint8)]
+
+
 def tie_case(n: int, k: int, m: int = 1):
     """Inputs whose exact dot products are odd integers above 256.
 

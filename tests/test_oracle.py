@@ -183,3 +183,24 @@ def test_thread_count_changes_nothing_but_speed():
     assert oracle.threads() == all_threads
     o, s = oracle.gemm(x_bits[:8], w_bits)
     assert np.array_equal(o, o1) and np.array_equal(s, s1)
+
+
+def test_block_seeded_integer_weight():
+    """skinny_inputs.int_weight_blocks (the maximum-size GPU tests' weight):
+    blocks tile the rows in order, each block is seeded on its own so
+    int_weight_rows draws any rows again alone, and every entry is one of
+    the given integers, exact in BF16."""
+    n, k, be = 20, 300, 1000                             # 3 rows per block: six whole blocks and a ragged one
+    assert si.int_block_rows(k, be) == 3 and si.int_block_rows(k) == (1 << 27) // k
+    blocks = list(si.int_weight_blocks(11, n, k, (-1, 0, 1), be))
+    assert [r0 for r0, _ in blocks] == list(range(0, n, 3))
+    full = np.concatenate([b for _, b in blocks])
+    assert full.shape == (n, k)
+    assert set(np.unique(si.bf16_bits_to_f32(full))) == {-1.0, 0.0, 1.0}
+    rows = [19, 0, 2, 3, 18, 5, 5]
+    assert np.array_equal(si.int_weight_rows(11, n, k, rows, (-1, 0, 1), be), full[rows])
+    other = np.concatenate([b for _, b in si.int_weight_blocks(12, n, k, (-1, 0, 1), be)])
+    assert not np.array_equal(full, other)
+    assert not np.array_equal(full[:3], full[3:6])     # blocks are drawn independently
+    x = si.int_matrix(3, 4, 64)
+    assert set(np.unique(si.bf16_bits_to_f32(x))) <= set(range(-3, 4))
