@@ -106,6 +106,31 @@ def test_random_shapes_random_tactics_exact(sk):
     assert len(paths) == 8                      # every path the enumeration offers
 
 
+@pytest.mark.parametrize("shape", [(1, 8), (15, 8), (17, 24), (3, 128)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_degenerate_shapes_every_tactic(sk, shape):
+    """The smallest shapes: one weight row, one 16-byte chunk per row (K = 8),
+    fewer rows than any tile.  Every candidate tactic, forced, at its full
+    tile and a ragged M, then the tuned plan at every M = 1..64, exact on
+    integer inputs with rows >= M untouched."""
+    import torch
+    n, k = shape
+    x_bits, w_bits = si.small_int_case(9100 + n * 1000 + k, 64, n, k)
+    o, _ = oracle.gemm(x_bits, w_bits)
+    w = gu.dev_bf16(w_bits)
+    tactics = sk.enumerate_tactics(n, k)
+    _say(f"[degenerate {n}x{k}] {len(tactics)} tactics")
+    for i, t in enumerate(tactics):
+        od = torch.float32 if i % 2 else torch.bfloat16
+        plan = sk.Prepared(w, od, table=gu.forced_table(t))
+        for m in sorted({t.mt, max(1, t.mt // 2 + 1)}):
+            _check_exact(sk, plan, x_bits, o, m, f"{n}x{k} {t} M={m} {od}")
+        plan.close()
+    plan = sk.Prepared(w, torch.float32)
+    for m in range(1, 65):
+        _check_exact(sk, plan, x_bits, o, m, f"{n}x{k} tuned M={m}")
+    plan.close()
+
+
 def test_k_probe_every_tactic(sk):
     """One nonzero per weight row, at a column that sweeps every residue
     modulo 8, 64 and 512: any chunk dropped or duplicated at a lane, wave or
