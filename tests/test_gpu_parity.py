@@ -131,6 +131,59 @@ def test_degenerate_shapes_every_tactic(sk, shape):
     plan.close()
 
 
+def test_nan_and_inf_propagate_every_tactic(sk):
+    """A NaN in one x row makes its whole output row NaN; a +Inf in another
+    makes out[.][n] +Inf, -Inf or NaN as W[n] at that column is positive,
+    negative or zero; the other rows stay exact -- for every candidate
+    tactic at its own token tile (a 1- or 2-token tile runs once per special
+    row), BF16 and fp32 out.  The K-split exchange stores values XOR a
+    signalling-NaN pattern with zero meaning empty; NaN and Inf partials must
+    pass through it like any other value."""
+    import torch
+    n, k = 72, 520
+    x_bits, w_bits = si.small_int_case(9300, 66, n, k)
+    x_bits = x_bits.copy()
+    x_bits[0, 5] = 0x7FC0                        # NaN
+    x_bits[1, 9] = 0x7F80                        # +Inf
+    o, _ = oracle.gemm(x_bits[2:], w_bits)      # the other rows are finite
+    wcol = si.bf16_bits_to_f32(w_bits[:, 9])
+    want_inf = np.where(wcol > 0, np.inf, np.where(wcol < 0, -np.inf, np.nan))
+    w = gu.dev_bf16(w_bits)
+    x = gu.dev_bf16(x_bits)
+    tactics = sk.enumerate_tactics(n, k)
+    _say(f"[nan/inf] {len(tactics)} tactics, {sum(t.split > 1 for t in tactics)} with a K split")
+    assert {t.path for t in tactics} >= {0, 1, 3, 8, 9, 10, 11, 12}
+    assert any(t.split > 1 for t in tactics)
+
+    def check(plan, od, first, m, label):
+        out = gu.out_buffer(n, od)
+        plan.run(x[first:first + m], out[:m])
+        torch.cuda.synchronize()
+        assert gu.sentinel_intact(out, m), f"{label}: rows >= M written"
+        got = out[:m].float().cpu().numpy().astype(np.float64)
+        bits = gu.host_bits(out)[:m]
+        for r in range(m):
+            src = first + r
+            if src == 0:
+                assert np.all(np.isnan(got[r])), f"{label}: NaN row"
+            elif src == 1:
+                assert np.array_equal(np.isnan(got[r]), np.isnan(want_inf)), f"{label}: Inf row NaN pattern"
+                fin = ~np.isnan(want_inf)
+                assert np.array_equal(got[r][fin], want_inf[fin]), f"{label}: Inf row signs"
+            elif od == torch.float32:
+                assert np.array_equal(got[r], o[src - 2]), f"{label}: finite row {src}"
+            else:
+                assert np.array_equal(bits[r], oracle.round_bf16(o[src - 2])), f"{label}: finite row {src}"
+
+    for i, t in enumerate(tactics):
+        od = torch.float32 if i % 2 else torch.bfloat16
+        plan = sk.Prepared(w, od, table=gu.forced_table(t))
+        check(plan, od, 0, t.mt, f"{t} {od}")
+        if t.mt < 2:
+            check(plan, od, 1, 1, f"{t} {od} (Inf row)")
+        plan.close()
+
+
 def test_k_probe_every_tactic(sk):
     """One nonzero per weight row, at a column that sweeps every residue
     modulo 8, 64 and 512: any chunk dropped or duplicated at a lane, wave or
