@@ -371,6 +371,56 @@ def test_prepare_from_threads(sk, monkeypatch):
         plan.close()
 
 
+def test_concurrent_plans_on_streams(sk):
+    """Four threads, each with its own plan (a K-split tactic, so each plan's
+    exchange workspace is in use) and its own stream, launch 24 runs each
+    without waiting, at changing M, into 24 output buffers; all four streams
+    run at once.  Every output must be exact on integer inputs afterwards: no
+    plan sees another's partials."""
+    import threading
+    import torch
+    n, k = 600, 1536
+    tactics = [sk.Tactic(9, 32, 64, 4, 3, 2), sk.Tactic(1, 64, 16, 2, 1, 4), sk.Tactic(10, 16, 28, 2, 2, 3),
+               sk.Tactic(3, 32, 64, 4, 2, 2)]
+    cases = []
+    for i, t in enumerate(tactics):
+        x_bits, w_bits = si.small_int_case(9400 + i, 64, n, k)
+        o, _ = oracle.gemm(x_bits, w_bits)
+        plan = sk.Prepared(gu.dev_bf16(w_bits), torch.float32, table=gu.forced_table(t))
+        outs = [gu.out_buffer(n, torch.float32) for _ in range(24)]
+        cases.append((t, gu.dev_bf16(x_bits), plan, outs, o))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            torch.cuda.set_device(0)
+            t, x, plan, outs, _ = cases[i]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for j, out in enumerate(outs):
+                    m = 1 + (j * 7 + i) % t.mt
+                    plan.run(x[:m], out[:m], stream=stream)
+            stream.synchronize()
+        except Exception as e:                  # reported by the main thread
+            errors.append((i, e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i, (t, _, plan, outs, o) in enumerate(cases):
+        for j, out in enumerate(outs):
+            m = 1 + (j * 7 + i) % t.mt
+            assert gu.sentinel_intact(out, m), f"{t} run {j}: rows >= M written"
+            got = gu.host_bits(out)[:m]
+            assert np.array_equal(got, o[:m].astype(np.float32).view(np.uint32)), f"{t} run {j} M={m}"
+        plan.close()
+
+
 def test_run_ex_argument_errors(sk):
     """Pitches below the row length, unaligned pitches and a residual that
     overlaps out without being it are refused before any launch."""
